@@ -1,0 +1,237 @@
+"""CPU oracle for the SMC-SD verify / resample / KV pointer-exchange path.
+
+TEST INFRASTRUCTURE.  Only the test suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The product path
+(``smc_verification_resampling_amd``) never imports it, and this package never
+imports the product path: the two share no code.
+
+The arithmetic lives in ``smcsd_oracle.c`` (plain C99, fp64, ascending-order sums);
+this module only builds it with gcc and marshals numpy arrays through ctypes.
+bf16 logits are passed as their uint16 bit patterns (dtype code 1); fp32 as float32
+(dtype code 0).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from typing import Dict, Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "smcsd_oracle.c")
+LIB = os.path.join(HERE, "liboracle_smcsd.so")
+
+ST_NAN_INPUT = 1
+ST_EMPTY_ROW = 2
+ST_NOSPACE = 4
+ST_DEGENERATE_WEIGHTS = 8
+
+TAG_BONUS = 1
+TAG_RESAMPLE = 2
+TAG_SPS_ACCEPT = 3
+TAG_SPS_FINAL = 4
+
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        tmp = LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+               "-fPIC", "-shared", SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def configure(lib):
+    """Declare the C signatures on a loaded oracle library."""
+    P = ctypes.c_void_p
+    i64, u64, dbl = ctypes.c_int64, ctypes.c_uint64, ctypes.c_double
+    lib.orc_philox4x32_10.argtypes = [P, P, P]
+    lib.orc_philox4x32_10.restype = None
+    lib.orc_uniform.argtypes = [u64, ctypes.c_uint32, u64, ctypes.c_uint32, ctypes.c_int]
+    lib.orc_uniform.restype = dbl
+    lib.orc_row_lse.argtypes = [P, ctypes.c_int, i64, dbl, P]
+    lib.orc_row_lse.restype = dbl
+    lib.orc_verify_smc.argtypes = [P, P, ctypes.c_int, i64, ctypes.c_int, P, ctypes.c_int, P,
+                                   dbl, dbl, u64, u64, P, P, P, P, P, P, P, P, P]
+    lib.orc_verify_smc.restype = ctypes.c_int
+    lib.orc_verify_sps.argtypes = [P, P, ctypes.c_int, i64, ctypes.c_int, P, ctypes.c_int, P,
+                                   dbl, u64, u64, P, P, P, P, P, P, P, P]
+    lib.orc_verify_sps.restype = ctypes.c_int
+    lib.orc_resample.argtypes = [P, ctypes.c_int, ctypes.c_int, dbl, u64, u64,
+                                 P, P, P, P, P, P, P]
+    lib.orc_resample.restype = ctypes.c_int
+    lib.orc_kv_reassign.argtypes = [P, P, ctypes.c_int, ctypes.c_int, P, ctypes.c_int,
+                                    ctypes.c_int, i64, ctypes.c_int, P, P, P, ctypes.c_int,
+                                    P, P, P]
+    lib.orc_kv_reassign.restype = ctypes.c_int
+    lib.orc_max_threads.restype = ctypes.c_int
+    return lib
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            _lib = configure(ctypes.CDLL(LIB))
+    return _lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def max_threads() -> int:
+    return int(_load().orc_max_threads())
+
+
+def _logit_array(x: np.ndarray):
+    """(contiguous array, dtype code): float32 -> 0, uint16 (bf16 bits) -> 1."""
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float32:
+        return x, 0
+    if x.dtype == np.uint16:
+        return x, 1
+    raise TypeError("logits must be float32 or uint16 (bf16 bit patterns), got %s" % x.dtype)
+
+
+# --------------------------------------------------------------------------- RNG
+def philox4x32_10(ctr, key) -> np.ndarray:
+    c = np.ascontiguousarray(np.asarray(ctr, dtype=np.uint32).reshape(4))
+    k = np.ascontiguousarray(np.asarray(key, dtype=np.uint32).reshape(2))
+    out = np.zeros(4, dtype=np.uint32)
+    _load().orc_philox4x32_10(_p(c), _p(k), _p(out))
+    return out
+
+
+def uniform(seed: int, index: int, t: int, tag: int, word: int = 0) -> float:
+    return float(_load().orc_uniform(seed, index, t, tag, word))
+
+
+# --------------------------------------------------------------------------- rows
+def row_lse(row: np.ndarray, T: float = 1.0):
+    """(LSE of z = row / T in fp64, status bits)."""
+    r, code = _logit_array(row.reshape(-1))
+    st = np.zeros(1, dtype=np.int32)
+    val = _load().orc_row_lse(_p(r), code, r.shape[0], T, _p(st))
+    return float(val), int(st[0])
+
+
+# --------------------------------------------------------------------------- verify
+def verify_smc(target: np.ndarray, draft: np.ndarray, draft_tokens: np.ndarray, T: float,
+               alpha: float, seed: int, t: int, lw_in: np.ndarray,
+               rng_index: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """SMC verify for nseq sequences.  target [nseq, K+1, V], draft [nseq, K, V]."""
+    tg, code = _logit_array(target)
+    nseq, K1, V = tg.shape
+    K = K1 - 1
+    dr, code2 = _logit_array(draft.reshape(nseq, K, V))
+    assert code == code2
+    tok = np.ascontiguousarray(draft_tokens, dtype=np.int32).reshape(nseq, K)
+    idx = np.arange(nseq, dtype=np.int64) if rng_index is None else \
+        np.ascontiguousarray(rng_index, dtype=np.int64)
+    lw = np.ascontiguousarray(lw_in, dtype=np.float64).reshape(nseq)
+    out = {
+        "lw": np.zeros(nseq, np.float64),
+        "tokens": np.zeros((nseq, K + 1), np.int32),
+        "logp": np.zeros((nseq, K + 1), np.float64),
+        "lse": np.zeros((nseq, 2 * K + 1), np.float64),
+        "u": np.zeros(nseq, np.float64),
+        "margin": np.zeros(nseq, np.float64),
+        "status": np.zeros(1, np.int32),
+    }
+    logq_buf = np.zeros((nseq, max(K, 1)), np.float64)
+    _load().orc_verify_smc(_p(tg), _p(dr), code, V, nseq, _p(idx), K, _p(tok), T, alpha, seed, t,
+                           _p(lw), _p(out["lw"]), _p(out["tokens"]), _p(out["logp"]),
+                           _p(logq_buf), _p(out["lse"]), _p(out["u"]), _p(out["margin"]),
+                           _p(out["status"]))
+    out["logq"] = logq_buf[:, :K].copy()
+    out["status"] = int(out["status"][0])
+    return out
+
+
+def verify_sps(target: np.ndarray, draft: np.ndarray, draft_tokens: np.ndarray, T: float,
+               seed: int, t: int, rng_index: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """SpS modified-rejection verify.  target [nseq, K+1, V], draft [nseq, K, V]."""
+    tg, code = _logit_array(target)
+    nseq, K1, V = tg.shape
+    K = K1 - 1
+    dr, code2 = _logit_array(draft.reshape(nseq, K, V))
+    assert code == code2
+    tok = np.ascontiguousarray(draft_tokens, dtype=np.int32).reshape(nseq, K)
+    idx = np.arange(nseq, dtype=np.int64) if rng_index is None else \
+        np.ascontiguousarray(rng_index, dtype=np.int64)
+    out = {
+        "tokens": np.zeros((nseq, K + 1), np.int32),
+        "num_tokens": np.zeros(nseq, np.int32),
+        "logp": np.zeros((nseq, K + 1), np.float64),
+        "lse": np.zeros((nseq, 2 * K + 1), np.float64),
+        "margin_accept": np.zeros(nseq, np.float64),
+        "margin_final": np.zeros(nseq, np.float64),
+        "status": np.zeros(1, np.int32),
+    }
+    logq_buf = np.zeros((nseq, max(K, 1)), np.float64)
+    _load().orc_verify_sps(_p(tg), _p(dr), code, V, nseq, _p(idx), K, _p(tok), T, seed, t,
+                           _p(out["tokens"]), _p(out["num_tokens"]), _p(out["logp"]),
+                           _p(logq_buf), _p(out["lse"]), _p(out["margin_accept"]),
+                           _p(out["margin_final"]), _p(out["status"]))
+    out["logq"] = logq_buf[:, :K].copy()
+    out["status"] = int(out["status"][0])
+    return out
+
+
+# --------------------------------------------------------------------------- resample
+def resample(lw_in: np.ndarray, tau: float, seed: int, t: int) -> Dict[str, np.ndarray]:
+    """ESS + systematic resampling per prompt.  lw_in float32 [B, N]."""
+    lw = np.ascontiguousarray(lw_in, dtype=np.float32)
+    B, N = lw.shape
+    out = {
+        "lw": np.zeros((B, N), np.float64),
+        "ancestors": np.zeros((B, N), np.int32),
+        "ess": np.zeros(B, np.float64),
+        "resampled": np.zeros(B, np.int32),
+        "margin_ess": np.zeros(B, np.float64),
+        "margin_pos": np.zeros((B, N), np.float64),
+        "status": np.zeros(1, np.int32),
+    }
+    rc = _load().orc_resample(_p(lw), B, N, tau, seed, t, _p(out["lw"]), _p(out["ancestors"]),
+                              _p(out["ess"]), _p(out["resampled"]), _p(out["margin_ess"]),
+                              _p(out["margin_pos"]), _p(out["status"]))
+    if rc != 0:
+        raise MemoryError("orc_resample failed")
+    out["status"] = int(out["status"][0])
+    return out
+
+
+# --------------------------------------------------------------------------- KV
+def kv_reassign(ancestors: np.ndarray, resampled: np.ndarray, tables: np.ndarray, block_size: int,
+                seq_len: int, reserve: int, refcounts: np.ndarray, free_list: np.ndarray,
+                free_top: int) -> Dict[str, np.ndarray]:
+    """Refcounted block-table pointer exchange + reservation.  Returns new copies."""
+    anc = np.ascontiguousarray(ancestors, dtype=np.int32)
+    B, N = anc.shape
+    res = np.ascontiguousarray(resampled, dtype=np.int32).reshape(B)
+    T = np.array(tables, dtype=np.int32, copy=True, order="C")
+    S, M = T.shape
+    assert S == B * N
+    rc = np.array(refcounts, dtype=np.int32, copy=True)
+    fl = np.array(free_list, dtype=np.int32, copy=True)
+    P = rc.shape[0]
+    top = np.array([free_top], dtype=np.int32)
+    cow = np.full((S, 3), -1, dtype=np.int32)
+    ncow = np.zeros(1, dtype=np.int32)
+    st = np.zeros(1, dtype=np.int32)
+    r = _load().orc_kv_reassign(_p(anc), _p(res), B, N, _p(T), M, block_size, seq_len, reserve,
+                                _p(rc), _p(fl), _p(top), P, _p(cow), _p(ncow), _p(st))
+    if r != 0:
+        raise ValueError("orc_kv_reassign rejected its arguments (capacity or allocation)")
+    return {"tables": T, "refcounts": rc, "free_list": fl, "free_top": int(top[0]),
+            "cow": cow[: int(ncow[0])].copy(), "cow_count": int(ncow[0]), "status": int(st[0])}

@@ -1,0 +1,173 @@
+"""Pins of the oracle's refcounted block-table pointer exchange - CPU only.
+
+Brute force: a deep-copy model keeps every particle's token list explicitly; the
+block-table model (the oracle) plus a per-block token store, written through the
+tables and patched with the oracle's copy-on-write list, must reproduce every list
+after every round.  A block freed while still referenced, a wrong gather, a missing
+copy-on-write or a double allocation all corrupt some particle's tokens.
+Invariants: rc[b] = number of table references; live and free blocks partition the
+pool; no table entry has rc = 0; identity ancestors leave the tables unchanged.
+"""
+import math
+
+import numpy as np
+import pytest
+
+
+def _initial(B, N, M, bs, P, ctx0, shared):
+    T = np.full((B * N, M), -1, np.int32)
+    rc = np.zeros(P, np.int32)
+    fl = np.arange(P - 1, -1, -1, dtype=np.int32)
+    nb0 = math.ceil(ctx0 / bs)
+    nxt = 0
+    if shared:
+        for b in range(B):
+            T[b * N:(b + 1) * N, :nb0] = np.arange(nxt, nxt + nb0)
+            rc[nxt:nxt + nb0] = N
+            nxt += nb0
+    else:
+        for g in range(B * N):
+            T[g, :nb0] = np.arange(nxt, nxt + nb0)
+            rc[nxt:nxt + nb0] = 1
+            nxt += nb0
+    return T, rc, fl, P - nxt
+
+
+def _check_invariants(st, P):
+    T, rc, fl, top = st["tables"], st["refcounts"], st["free_list"], st["free_top"]
+    refs = np.bincount(T[T >= 0], minlength=P)
+    assert np.array_equal(refs, rc), "refcount != number of table references"
+    free = fl[:top]
+    assert len(np.unique(free)) == top, "duplicate block on the free stack"
+    assert np.all(rc[free] == 0), "a free block is still referenced"
+    live = np.nonzero(rc)[0]
+    assert len(live) + top == P, "live and free blocks do not partition the pool"
+
+
+def _tokens_via_tables(store, T, g, L, bs):
+    return [store[T[g, p // bs]][p % bs] for p in range(L)]
+
+
+@pytest.mark.parametrize("shared", [False, True])
+@pytest.mark.parametrize("bs,K,ctx0", [(4, 2, 16), (16, 4, 35), (3, 5, 7), (8, 7, 0)])
+@pytest.mark.parametrize("sorted_ancestors", [True, False])
+def test_block_tables_reproduce_deep_copy_model(orc, shared, bs, K, ctx0, sorted_ancestors):
+    rng = np.random.default_rng(hash((shared, bs, K, ctx0, sorted_ancestors)) & 0xFFFF)
+    B, N, rounds = 3, 6, 25
+    R = K + 1
+    M = math.ceil((ctx0 + (rounds + 1) * R) / bs)
+    P = B * N * M
+    T, rc, fl, top = _initial(B, N, M, bs, P, ctx0, shared)
+    # token store per block; prompt tokens written through the initial tables
+    store = np.full((P, bs), -1, np.int64)
+    tokens = []
+    for g in range(B * N):
+        b = g // N
+        prompt = [1000 * b + p for p in range(ctx0)]
+        tokens.append(list(prompt))
+        for p, tkn in enumerate(prompt):
+            store[T[g, p // bs], p % bs] = tkn
+    L = ctx0
+    # reservation before round 0 (identity ancestors)
+    st = orc.kv_reassign(np.tile(np.arange(N), (B, 1)), np.zeros(B), T, bs, L, R, rc, fl, top)
+    assert st["status"] == 0
+    for src, dst, n in st["cow"]:
+        store[dst, :n] = store[src, :n]
+    _check_invariants(st, P)
+    for rnd in range(rounds):
+        T = st["tables"]
+        # the round writes K+1 new tokens per particle into its reserved slots
+        for g in range(B * N):
+            new = [int(x) for x in rng.integers(0, 10**6, R)]
+            for j, tkn in enumerate(new):
+                p = L + j
+                store[T[g, p // bs], p % bs] = tkn
+            tokens[g].extend(new)
+        L += R
+        resampled = (rng.random(B) < 0.6).astype(np.int32)
+        if sorted_ancestors:
+            anc = np.sort(rng.integers(0, N, (B, N)), axis=1).astype(np.int32)
+        else:
+            anc = rng.integers(0, N, (B, N)).astype(np.int32)
+        before = T.copy()
+        st = orc.kv_reassign(anc, resampled, T, bs, L, R, st["refcounts"], st["free_list"],
+                             st["free_top"])
+        assert st["status"] == 0
+        for src, dst, n in st["cow"]:
+            assert n == L % bs
+            store[dst, :n] = store[src, :n]
+        new_tokens = []
+        for g in range(B * N):
+            b, i = divmod(g, N)
+            a = anc[b, i] if resampled[b] else i
+            new_tokens.append(list(tokens[b * N + a]))
+        tokens = new_tokens
+        _check_invariants(st, P)
+        for g in range(B * N):
+            assert _tokens_via_tables(store, st["tables"], g, L, bs) == tokens[g]
+        # identity prompts keep their committed slots; nobody rewrites full blocks below floor(L/bs)
+        for b in range(B):
+            if not resampled[b]:
+                rows = slice(b * N, (b + 1) * N)
+                assert np.array_equal(st["tables"][rows, :L // bs], before[rows, :L // bs])
+
+
+def test_identity_is_noop_and_all_equal_ancestors(orc):
+    B, N, bs, M = 1, 4, 4, 10
+    P = B * N * M
+    T, rc, fl, top = _initial(B, N, M, bs, P, 8, False)
+    st = orc.kv_reassign(np.tile(np.arange(N), (B, 1)), np.ones(B), T, bs, 8, 0, rc, fl, top)
+    assert np.array_equal(st["tables"], T) and np.array_equal(st["refcounts"], rc)
+    st = orc.kv_reassign(np.full((1, N), 2), np.ones(1), T, bs, 8, 0, rc, fl, top)
+    for g in range(N):
+        assert np.array_equal(st["tables"][g], T[2])
+    assert np.all(st["refcounts"][T[2, :2]] == N)
+    # six blocks freed (particles 0, 1, 3), pushed in descending order: pops return ascending
+    assert st["free_top"] == top + 6
+    assert list(st["free_list"][top:top + 6]) == sorted(
+        [int(x) for x in T[[0, 1, 3], :2].ravel()], reverse=True)
+
+
+def test_hand_worked_round():
+    """A round worked by hand from the rules (no oracle involved in the expectation).
+    B=1, N=3, bs=4, L=6 (slots 0,1 allocated; slot 1 is a partial tail with 2 tokens),
+    tables: g0 -> [0, 1], g1 -> [2, 3], g2 -> [4, 5]; rc = 1 for blocks 0..5;
+    free stack (bottom..top) = [9, 8, 7, 6] so pops return 6, 7, 8, 9, ...
+    Ancestors (0, 0, 2): c = (2, 0, 1).
+      increments: blocks 0, 1 -> rc 2.  decrements: blocks 2, 3 -> rc 0 -> freed.
+      push descending: stack = [9, 8, 7, 6, 3, 2] (top = 2).
+      tables: g0 -> [0, 1], g1 -> [0, 1], g2 -> [4, 5].
+    Reserve R=3 positions 6..8: tail slot 1 (L mod bs = 2), fresh slot 2.
+      g0: block 1 has rc 2 and g1 > g0 also holds it -> COW: pop 2, rc[1] = 1,
+          rc[2] = 1, g0 slot 1 = 2, emit (1, 2, 2); fresh slot 2: pop 3.
+      g1: block 1 now has rc 1 but the decision uses the post-exchange state
+          (rc 2, no higher holder) -> keep; fresh slot 2: pop 6.
+      g2: block 5 rc 1 -> keep; fresh slot 2: pop 7.
+    Final tables: [0, 2, 3], [0, 1, 6], [4, 5, 7]; top = 6 - 4 = ... stack length 6 -> 2."""
+    import oracle
+    T = np.full((3, 4), -1, np.int32)
+    T[0, :2] = [0, 1]
+    T[1, :2] = [2, 3]
+    T[2, :2] = [4, 5]
+    rc = np.zeros(10, np.int32)
+    rc[:6] = 1
+    fl = np.zeros(10, np.int32)
+    fl[:4] = [9, 8, 7, 6]
+    st = oracle.kv_reassign(np.array([[0, 0, 2]]), np.array([1]), T, 4, 6, 3, rc, fl, 4)
+    assert st["tables"][:, :3].tolist() == [[0, 2, 3], [0, 1, 6], [4, 5, 7]]
+    assert st["cow"].tolist() == [[1, 2, 2]]
+    assert st["free_top"] == 2 and st["free_list"][:2].tolist() == [9, 8]
+    expect_rc = np.zeros(10, np.int32)
+    expect_rc[[0]] = 2
+    expect_rc[[1, 2, 3, 4, 5, 6, 7]] = 1
+    assert st["refcounts"].tolist() == expect_rc.tolist()
+
+
+def test_nospace_is_reported(orc):
+    B, N, bs, M = 1, 2, 4, 6
+    T, rc, fl, top = _initial(B, N, M, bs, 5, 4, False)   # pool of 5: 2 used, 3 free
+    st = orc.kv_reassign(np.tile(np.arange(N), (B, 1)), np.zeros(B), T, bs, 4, 9, rc, fl, top)
+    # each sequence needs 3 fresh slots (positions 4..12 -> slots 1..3): 6 > 3 free
+    assert st["status"] & orc.ST_NOSPACE
+    assert st["free_top"] == 0
+    assert st["tables"][0, 1:4].tolist() == [2, 3, 4] and st["tables"][1, 1:4].tolist() == [-1, -1, -1]

@@ -1,0 +1,216 @@
+"""Distribution-level pins of the oracle, by brute force on a tiny vocabulary (CPU only).
+
+Setting: V = 8, K = 2, prefix-dependent target and draft logit tables (every prefix
+of length <= 4 has its own seeded Normal rows), so the continuation space of one
+round is 8^3.
+
+* SpS is exact (the speculative-sampling notes, section 1 and Theorem 1 cited in
+  section 6): running the oracle's SpS verify round after round, the first three
+  emitted tokens follow the target law pi(y) = p(y1) p(y2|y1) p(y3|y1,y2).
+* SMC-SD is an importance-weighted resampler (SMC explainers, section 2): one round
+  with N particles, forced resampling and a uniformly chosen output particle follows
+  the sampling-importance-resampling law
+      P_N(y) = N Q(y) E[ w(y) / (w(y) + S_{N-1}) ],
+  Q(y) = q(y1) q(y2|y1) p(y3|y1,y2),  w(y) = pi_alpha(y) / Q(y),  S_{N-1} a sum of
+  N-1 independent weights of Q-draws, computed exactly by enumeration.  Checked for
+  alpha = 1 and the power target alpha = 4.
+* The L1 distance ||P_N - pi||_1 decays at least like N^(-1/2) (SMC explainers,
+  section 3: the L1 bias is O(1/sqrt(N)); bias and MSE O(1/N)).
+"""
+import numpy as np
+import pytest
+from scipy import special, stats
+
+V, K = 8, 2
+
+
+def _tables(seed, depth_max=4, sigma_t=1.0, sigma_d=0.5):
+    """tgt[d] [V^d, V] and drf[d] [V^d, V]: logits for every prefix of length d."""
+    rng = np.random.default_rng(seed)
+    tgt, drf = {}, {}
+    for d in range(depth_max + 1):
+        t = rng.normal(0, sigma_t, (V ** d, V)).astype(np.float32)
+        tgt[d] = t
+        drf[d] = (t + rng.normal(0, sigma_d, t.shape)).astype(np.float32)
+    return tgt, drf
+
+
+def _softmax(x):
+    return special.softmax(x.astype(np.float64), axis=-1)
+
+
+def _sample_rows(rng, probs):
+    c = np.cumsum(probs, axis=-1)
+    u = rng.random((probs.shape[0], 1))
+    return np.minimum((c < u * c[:, -1:]).sum(-1), V - 1).astype(np.int64)
+
+
+def _target_law(tgt):
+    p0 = _softmax(tgt[0][0])
+    p1 = _softmax(tgt[1])
+    p2 = _softmax(tgt[2])
+    pi = np.zeros((V, V, V))
+    for a in range(V):
+        for b in range(V):
+            pi[a, b, :] = p0[a] * p1[a, b] * p2[a * V + b]
+    return pi.reshape(-1)
+
+
+def _chi2_pvalue(counts, probs, min_expected=5.0):
+    exp = probs * counts.sum()
+    order = np.argsort(exp)
+    # merge the smallest cells until every merged cell expects >= min_expected
+    obs_m, exp_m, acc_o, acc_e = [], [], 0.0, 0.0
+    for i in order:
+        acc_o += counts[i]
+        acc_e += exp[i]
+        if acc_e >= min_expected:
+            obs_m.append(acc_o); exp_m.append(acc_e)
+            acc_o = acc_e = 0.0
+    if acc_e > 0:
+        obs_m[-1] += acc_o; exp_m[-1] += acc_e
+    return stats.chisquare(np.array(obs_m), np.array(exp_m)).pvalue
+
+
+# --------------------------------------------------------------------------- SpS
+def test_sps_law_equals_target(orc):
+    tgt, drf = _tables(2024)
+    pi = _target_law(tgt)
+    rng = np.random.default_rng(99)
+    runs = 60000
+    emitted = [[] for _ in range(runs)]
+    code = np.zeros(runs, np.int64)
+    length = np.zeros(runs, np.int64)
+    rnd = 0
+    active = np.arange(runs)
+    while len(active):
+        len_at_start = length[active].copy()
+        for d in (0, 1, 2):
+            grp = active[len_at_start == d]
+            if not len(grp):
+                continue
+            c0 = code[grp]
+            # Extend: the draft proposes K tokens from its own conditionals
+            x1 = _sample_rows(rng, _softmax(drf[d][c0]))
+            c1 = c0 * V + x1
+            x2 = _sample_rows(rng, _softmax(drf[d + 1][c1]))
+            c2 = c1 * V + x2
+            t_rows = np.stack([tgt[d][c0], tgt[d + 1][c1], tgt[d + 2][c2]], axis=1)
+            d_rows = np.stack([drf[d][c0], drf[d + 1][c1]], axis=1)
+            toks = np.stack([x1, x2], axis=1).astype(np.int32)
+            out = orc.verify_sps(t_rows, d_rows, toks, 1.0, seed=77, t=rnd,
+                                 rng_index=grp.astype(np.int64))
+            for j, r in enumerate(grp):
+                n = int(out["num_tokens"][j])
+                new = out["tokens"][j, :n].tolist()
+                assert all(0 <= v < V for v in new) and 1 <= n <= K + 1
+                emitted[r].extend(new)
+                for v in new:
+                    if length[r] < 3:
+                        code[r] = code[r] * V + v
+                        length[r] += 1
+        rnd += 1
+        active = np.array([r for r in active if length[r] < 3], dtype=np.int64)
+    ys = np.array([e[0] * 64 + e[1] * 8 + e[2] for e in emitted])
+    counts = np.bincount(ys, minlength=V ** 3).astype(np.float64)
+    assert _chi2_pvalue(counts, pi) > 1e-4
+
+
+# --------------------------------------------------------------------------- SMC-SD
+def _sir_law(tgt, drf, N, alpha):
+    """Exact P_N over the 512 one-round continuations; also returns pi_alpha normalised."""
+    p0, p1, p2 = _softmax(tgt[0][0]), _softmax(tgt[1]), _softmax(tgt[2])
+    q0, q1 = _softmax(drf[0][0]), _softmax(drf[1])
+    Q = np.zeros((V, V, V))
+    W = np.zeros((V, V, V))
+    PI = np.zeros((V, V, V))
+    for a in range(V):
+        for b in range(V):
+            pa, pb, pc = p0[a], p1[a, b], p2[a * V + b]
+            Q[a, b] = q0[a] * q1[a, b] * pc
+            W[a, b] = (pa ** alpha) * (pb ** alpha) * (pc ** (alpha - 1)) / (q0[a] * q1[a, b])
+            PI[a, b] = (pa * pb) ** alpha * pc ** alpha
+    Q, W, PI = Q.reshape(-1), W.reshape(-1), PI.reshape(-1)
+    PI = PI / PI.sum()
+    # distribution of S_{N-1}: enumerate atoms (merge equal weights)
+    wv, inv = np.unique(W, return_inverse=True)
+    wp = np.bincount(inv, weights=Q)
+    s_vals, s_probs = np.array([0.0]), np.array([1.0])
+    for _ in range(N - 1):
+        sv = (s_vals[:, None] + wv[None, :]).reshape(-1)
+        sp = (s_probs[:, None] * wp[None, :]).reshape(-1)
+        keep = sp > 1e-15
+        s_vals, s_probs = sv[keep], sp[keep]
+    E = np.array([np.sum(s_probs * (w / (w + s_vals))) for w in W])
+    P = N * Q * E
+    return P, PI
+
+
+def _smc_samples(orc, tgt, drf, N, alpha, runs, seed):
+    rng = np.random.default_rng(seed)
+    S = runs * N
+    x1 = _sample_rows(rng, np.repeat(_softmax(drf[0][[0]]), S, 0))
+    x2 = _sample_rows(rng, _softmax(drf[1][x1]))
+    c2 = x1 * V + x2
+    t_rows = np.stack([np.repeat(tgt[0][[0]], S, 0), tgt[1][x1], tgt[2][c2]], axis=1)
+    d_rows = np.stack([np.repeat(drf[0][[0]], S, 0), drf[1][x1]], axis=1)
+    toks = np.stack([x1, x2], axis=1).astype(np.int32)
+    out = orc.verify_smc(t_rows, d_rows, toks, 1.0, alpha, seed=seed, t=0,
+                         lw_in=np.zeros(S, np.float32), rng_index=np.arange(S, dtype=np.int64))
+    assert np.all(out["tokens"] >= 0)
+    lw = out["lw"].astype(np.float32).reshape(runs, N)
+    res = orc.resample(lw, 2.0, seed, 0)              # tau > 1 forces resampling
+    assert np.all(res["resampled"] == 1)
+    pick = rng.integers(0, N, runs)
+    anc = res["ancestors"][np.arange(runs), pick]
+    g = np.arange(runs) * N + anc
+    y = out["tokens"][g]
+    return y[:, 0] * 64 + y[:, 1] * 8 + y[:, 2]
+
+
+@pytest.mark.parametrize("N,alpha", [(4, 1.0), (3, 4.0)])
+def test_smc_round_follows_sir_law(orc, N, alpha):
+    tgt, drf = _tables(31337)
+    P, PI = _sir_law(tgt, drf, N, alpha)
+    assert abs(P.sum() - 1.0) < 1e-9
+    ys = _smc_samples(orc, tgt, drf, N, alpha, runs=60000, seed=5)
+    counts = np.bincount(ys, minlength=V ** 3).astype(np.float64)
+    assert _chi2_pvalue(counts, P) > 1e-4
+    # the SIR law is measurably different from both the target and the proposal,
+    # so the chi-square test above has power against a wrong weight
+    assert np.abs(P - PI).sum() > 0.02
+
+
+def _sir_law_mc(tgt, drf, N, samples, seed):
+    """P_N with E[w/(w+S_{N-1})] by Rao-Blackwellised Monte Carlo over S_{N-1}."""
+    P1, PI = _sir_law(tgt, drf, 1, 1.0)          # N = 1: the proposal Q itself
+    Q = P1
+    p0, p1, p2 = _softmax(tgt[0][0]), _softmax(tgt[1]), _softmax(tgt[2])
+    q0, q1 = _softmax(drf[0][0]), _softmax(drf[1])
+    W = np.zeros((V, V, V))
+    for a in range(V):
+        for b in range(V):
+            W[a, b] = p0[a] * p1[a, b] / (q0[a] * q1[a, b])
+    W = W.reshape(-1)
+    rng = np.random.default_rng(seed)
+    draws = rng.choice(V ** 3, size=(samples, N - 1), p=Q / Q.sum())
+    S = W[draws].sum(1)
+    E = np.array([np.mean(w / (w + S)) for w in W])
+    return N * Q * E, PI
+
+
+def test_l1_bias_decays_with_particles():
+    """||P_N - pi||_1 shrinks at least like N^(-1/2): exact laws for N <= 4, Monte Carlo
+    (2e5 draws of S_{N-1}) for N = 8 .. 64."""
+    tgt, drf = _tables(31337)
+    Ns = [1, 2, 4, 8, 16, 32, 64]
+    l1 = []
+    for N in Ns:
+        if N <= 4:
+            P, PI = _sir_law(tgt, drf, N, 1.0)
+        else:
+            P, PI = _sir_law_mc(tgt, drf, N, 200000, seed=N)
+        l1.append(np.abs(P - PI).sum())
+    slope = np.polyfit(np.log(Ns), np.log(l1), 1)[0]
+    assert np.all(np.diff(l1) < 0), l1
+    assert slope <= -0.4, (Ns, l1, slope)

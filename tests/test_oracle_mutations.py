@@ -1,0 +1,123 @@
+"""The oracle's pins have power: each plausible mistake, planted in a private copy of
+the oracle's C source (CPU only, never the HIP path), makes at least one pin fail.
+
+Each case names a text substitution in smcsd_oracle.c (a dropped term, a wrong sign,
+a wrong index or row, a transposed operand, a wrong comparison) and the pin tests
+expected to catch it.  The variant library is compiled into a temporary directory
+and swapped in for the duration of the case only.
+"""
+import contextlib
+import ctypes
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+from tests import test_oracle_kv as kv
+from tests import test_oracle_laws as laws
+from tests import test_oracle_resample as rs
+from tests import test_oracle_rng as rng_t
+from tests import test_oracle_verify as vf
+from tests.helpers import rocrand_probe
+
+SRC = open(oracle.SRC).read()
+
+
+@contextlib.contextmanager
+def planted(old: str, new: str):
+    assert SRC.count(old) >= 1, "mutation anchor not found: %r" % old
+    src = SRC.replace(old, new)
+    d = tempfile.mkdtemp(prefix="orc_mut_")
+    c_path = os.path.join(d, "m.c")
+    so_path = os.path.join(d, "m.so")
+    with open(c_path, "w") as f:
+        f.write(src)
+    subprocess.run(["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+                    c_path, "-o", so_path, "-lm"], check=True)
+    saved = oracle._load()
+    oracle._lib = oracle.configure(ctypes.CDLL(so_path))
+    try:
+        yield
+    finally:
+        oracle._lib = saved
+
+
+def _caught(pins) -> bool:
+    for fn in pins:
+        try:
+            fn()
+        except AssertionError:
+            return True
+    return False
+
+
+O = oracle
+NEEDS_PROBE = rocrand_probe.available()
+
+CASES = [
+    ("weight sign of log q", "incr += alpha * lp - lq;", "incr += alpha * lp + lq;",
+     [lambda: vf.test_weight_identity_by_enumeration(O, 1.0)]),
+    ("bonus term dropped (power mode)", "incr += (alpha - 1.0) * lpK;", "incr += 0.0 * lpK;",
+     [lambda: vf.test_weight_identity_by_enumeration(O, 4.0)]),
+    ("alpha on bonus instead of alpha-1", "incr += (alpha - 1.0) * lpK;", "incr += alpha * lpK;",
+     [lambda: vf.test_weight_identity_by_enumeration(O, 1.0)]),
+    ("LSE without the max shift", "return zmax + log(s);", "return log(s);",
+     [lambda: vf.test_row_lse_matches_scipy_fp32(O, 1.0, 1000)]),
+    ("temperature ignored in target gather",
+     "double lp = load_elem(trow, dtype, x) / T - L[k];",
+     "double lp = load_elem(trow, dtype, x) - L[k];",
+     [lambda: vf.test_verify_gather_and_weights_vs_log_softmax(O, "f32", 1.0)]),
+    ("log q gathered from the target row",
+     "double lq = load_elem(drow, dtype, x) / T - L[K + 1 + k];",
+     "double lq = load_elem(trow, dtype, x) / T - L[K + 1 + k];",
+     [lambda: vf.test_verify_gather_and_weights_vs_log_softmax(O, "f32", 1.0)]),
+    ("bonus drawn from row K-1",
+     "const void *brow = row_ptr(tgt, dtype, (int64_t)s * (K + 1) + K, V);",
+     "const void *brow = row_ptr(tgt, dtype, (int64_t)s * (K + 1) + K - 1, V);",
+     [lambda: vf.test_bonus_chi_square_against_target(O)]),
+    ("uniform loses its top bit", "(double)(out[word & 3] >> 8)", "(double)(out[word & 3] >> 9)",
+     [lambda: rng_t.test_uniform_chi_square(O)]),
+    ("Philox key bump uses the wrong Weyl constant", "k0 += weyl0;", "k0 += weyl1;",
+     [lambda: rng_t.test_philox_matches_rocrand_block_function(O)] if NEEDS_PROBE else []),
+    ("Philox round mixes the wrong high half", "uint32_t n0 = hi1 ^ c1 ^ k0;",
+     "uint32_t n0 = hi0 ^ c1 ^ k0;",
+     [lambda: rng_t.test_philox_matches_rocrand_block_function(O)] if NEEDS_PROBE else []),
+    ("counter words t_hi and tag swapped",
+     "uint32_t ctr[4] = {index, (uint32_t)t, (uint32_t)(t >> 32), tag};",
+     "uint32_t ctr[4] = {index, (uint32_t)t, tag, (uint32_t)(t >> 32)};",
+     [lambda: rng_t.test_uniform_counter_layout_matches_rocrand(O)] if NEEDS_PROBE else []),
+    ("ESS without the square", "double e = s1 * s1 / s2;", "double e = s1 / s2;",
+     [lambda: rs.test_ess_closed_forms(O)]),
+    ("threshold not strict", "int do_res = e < tau * (double)N;", "int do_res = e <= tau * (double)N;",
+     [lambda: rs.test_ess_bounds_and_strict_threshold(O)]),
+    ("systematic offset dropped", "double pos = ((double)i + u0) / (double)N;",
+     "double pos = ((double)i) / (double)N;",
+     [lambda: rs.test_offspring_unbiased_monte_carlo(O)]),
+    ("weights not reset after resampling",
+     "for (int n = 0; n < N; ++n) lw_out[(int64_t)b * N + n] = 0.0;", "",
+     [lambda: rs.test_systematic_matches_searchsorted(O)] if NEEDS_PROBE else []),
+    ("refcount increments skipped for two offspring", "if (cnt[j] > 1)\n", "if (cnt[j] > 2)\n",
+     [lambda: kv.test_block_tables_reproduce_deep_copy_model(O, True, 4, 2, 16, True)]),
+    ("copy-on-write never done", "needs_cow[g] = 1;", "needs_cow[g] = 0;",
+     [lambda: kv.test_block_tables_reproduce_deep_copy_model(O, False, 4, 2, 16, True)]),
+    ("freed blocks pushed ascending", "return (x < y) - (x > y);", "return (x > y) - (x < y);",
+     [lambda: kv.test_identity_is_noop_and_all_equal_ancestors(O)]),
+    ("gather ignores the ancestors", "old[(int64_t)a[i] * nb_old + s]", "old[(int64_t)i * nb_old + s]",
+     [lambda: kv.test_block_tables_reproduce_deep_copy_model(O, False, 4, 2, 16, True)]),
+    ("SpS residual without the positive part", "double rho = p - q > 0.0 ? p - q : 0.0;",
+     "double rho = fabs(p - q);", [lambda: laws.test_sps_law_equals_target(O)]),
+    ("SpS accepts every draft", "if (!(r < ratio)) {", "if (!(r < 1.0)) {",
+     [lambda: laws.test_sps_law_equals_target(O)]),
+    ("SMC weight uses q/p", "incr += alpha * lp - lq;", "incr += lq - alpha * lp;",
+     [lambda: laws.test_smc_round_follows_sir_law(O, 4, 1.0)]),
+]
+
+
+@pytest.mark.parametrize("name,old,new,pins", CASES, ids=[c[0] for c in CASES])
+def test_planted_mistake_is_caught(name, old, new, pins):
+    if not pins:
+        pytest.skip("the pin for this case needs the rocRAND probe")
+    with planted(old, new):
+        assert _caught(pins), "planted mistake not caught: " + name
