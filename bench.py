@@ -1,0 +1,263 @@
+"""Benchmark: SMC-SD verify + resample + KV pointer-exchange steps per second on one MI355X.
+
+Workload (default): B=32 prompts x N=16 particles, K=4 draft tokens, V=128256, bf16 logits
+with the Zipf generator (one seeded vocabulary permutation, noise 0.3; draft = target +
+Normal(0, 0.8)), temperature 0.8, tau = 0.5, 2048-token shared prefix in 16-token blocks.
+A step is one pass of the whole hot path over one batch: smcsd_verify (LSE pass, gathers,
+bonus token, weight update), smcsd_resample (ESS, systematic resampling), smcsd_kv_reassign
+(refcounted block-table exchange + reservation).  Inputs are resident in HBM: four distinct
+logit sets (4.7 GB, far above the 256 MB last-level cache) are generated untimed and step t
+uses set t mod 4.
+
+Prints one JSON line.  `roofline` covers the dominant work: each smcsd_verify call is
+bracketed by HIP events on the stream it is launched on, and its algorithmic bytes
+(B*N*(2K+1)*V*2 logit bytes) are divided by the average duration.  `cpu_baseline` times the
+CPU oracle on a bounded sample of the same workload and scales it to steps/s.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c3_batched")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the verify / resample / KV path shards by prompt "
+              "with no exchange, and this build runs on a single MI355X (got --gpus %d)"
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import smc_verification_resampling_amd as sm
+    from workloads import configs, synth
+
+    cfg = configs.get(args.workload)
+    dev = "cuda"
+    torch.cuda.init()
+    B, N, K, V, S = cfg.B, cfg.N, cfg.K, cfg.V, cfg.S
+    print("[bench] generating %d logit sets of %.2f GB" % (cfg.n_sets, cfg.logit_bytes_per_step / 1e9),
+          file=sys.stderr, flush=True)
+    base = synth.zipf_base(cfg, dev) if cfg.target_kind == "zipf" else None
+    sets = []
+    for s in range(cfg.n_sets):
+        t, d = synth.make_logit_set(cfg, s, dev, base)
+        sets.append((t, d, synth.sample_draft_tokens(cfg, d, s)))
+
+    i32 = dict(dtype=torch.int32, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    lw = torch.zeros(S, **f32)
+    kv = synth.initial_kv(cfg)
+    tables = torch.from_numpy(kv["tables"]).to(dev)
+    rc = torch.from_numpy(kv["refcounts"]).to(dev)
+    fl = torch.from_numpy(kv["free_list"]).to(dev)
+    top = torch.from_numpy(kv["free_top"]).to(dev)
+    L0 = int(kv["seq_len"])
+    ws_v = sm.alloc_workspace(sm.OP_VERIFY_SMC, B, N, K, V)
+    ws_kv = sm.alloc_workspace(sm.OP_KV, B, N, P=cfg.pool)
+    tokens = torch.zeros((S, K + 1), **i32)
+    num = torch.zeros(S, **i32)
+    logp = torch.zeros((S, K + 1), **f32)
+    logq = torch.zeros((S, K), **f32)
+    status = torch.zeros(1, **i32)
+    anc = torch.zeros((B, N), **i32)
+    ess = torch.zeros(B, **f32)
+    resampled = torch.zeros(B, **i32)
+    cow = torch.zeros((S, 3), **i32)
+    ncow = torch.zeros(1, **i32)
+    seed = cfg.rng_seed
+    state = {"L": L0}
+
+    def kv_call(a, r):
+        sm.kv_reassign(a, r, B, N, tables, cfg.block_size, state["L"], K + 1, rc, fl, top, cow, ncow,
+                       status, ws_kv)
+
+    def reset():
+        lw.zero_()
+        tables.copy_(torch.from_numpy(kv["tables"]))
+        rc.copy_(torch.from_numpy(kv["refcounts"]))
+        fl.copy_(torch.from_numpy(kv["free_list"]))
+        top.copy_(torch.from_numpy(kv["free_top"]))
+        state["L"] = L0
+        kv_call(torch.arange(N, **i32).repeat(B, 1), torch.zeros(B, **i32))
+
+    # the block pool holds M_cap slots per sequence: restart the episode before it fills
+    max_rounds = cfg.iters
+
+    def step(t, ev=None):
+        tgt, drf, toks = sets[t % cfg.n_sets]
+        if ev is not None:
+            ev[0].record()
+        sm.verify(tgt, drf, toks, B, N, K, V, cfg.temperature, cfg.alpha, sm.MODE_SMC, seed, t,
+                  tokens, status, ws_v, log_weights=lw, out_num_tokens=num, out_logp=logp,
+                  out_logq=logq)
+        if ev is not None:
+            ev[1].record()
+        sm.resample(lw.view(B, N), B, N, cfg.tau, seed, t, anc, ess, resampled, status)
+        state["L"] += K + 1
+        kv_call(anc, resampled)
+
+    reset()
+    for t in range(args.warmup):
+        if t and t % max_rounds == 0:
+            reset()
+        step(t)
+    torch.cuda.synchronize()
+    reset()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps (episode restarts are pure state resets, outside it)
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    chunks = []
+    t_total = 0.0
+    done = 0
+    while done < args.steps:
+        n = min(max_rounds, args.steps - done)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            step(done + i, events[done + i])
+        torch.cuda.synchronize()
+        t_total += time.perf_counter() - t0
+        done += n
+        chunks.append(n)
+        if done < args.steps:
+            reset()
+            torch.cuda.synchronize()
+    st = int(status.cpu()[0])
+    verify_ms = [a.elapsed_time(b) for a, b in events]
+    verify_avg_s = float(np.mean(verify_ms)) / 1e3
+    ms_per_step = t_total / args.steps * 1e3
+    steps_per_s = args.steps / t_total
+    bytes_per_verify = cfg.logit_bytes_per_step
+    achieved_gbs = bytes_per_verify / verify_avg_s / 1e9
+    step_gbs = bytes_per_verify * steps_per_s / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, sets, args.cpu_seconds)
+
+    out = {
+        "metric": "SMC verify+resample steps/s; HBM GB/s % of peak (V=128256,N=16,K=4,B=32)",
+        "value": round(steps_per_s, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "%s: B=%d prompts x N=%d particles, K=%d, V=%d, %s logits (%s), T=%g, "
+                        "alpha=%g, tau=%g, ctx %d in %d-token blocks%s" % (
+                            cfg.name, B, N, K, V, cfg.dtype, cfg.target_kind, cfg.temperature,
+                            cfg.alpha, cfg.tau, cfg.ctx0, cfg.block_size,
+                            ", shared prefix" if cfg.shared_prefix else ""),
+            "step": "smcsd_verify + smcsd_resample + smcsd_kv_reassign",
+            "logit_sets": cfg.n_sets,
+            "algorithmic_bytes_per_step": bytes_per_verify,
+            "step_hbm_gbs": round(step_gbs, 1),
+            "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+            "status": st,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "smcsd_verify (LSE pass + finalize)",
+            "achieved": round(achieved_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_launch_us": round(verify_avg_s * 1e6, 2),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+def cpu_baseline(cfg, sets, budget_s):
+    """The oracle as it stands, on a bounded sample: verify on a subset of sequences (scaled
+    to the full batch), resample and KV exchange on the whole batch."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from workloads import synth
+
+    B, N, K, S = cfg.B, cfg.N, cfg.K, cfg.S
+    nsamp = min(S, 32)
+    tgt, drf, toks = sets[0]
+    sel = torch.arange(nsamp, device=tgt.device)
+
+    def host(x):
+        x = x.contiguous()
+        if x.dtype == torch.bfloat16:
+            return x.view(torch.int16).cpu().numpy().view(np.uint16)
+        return x.cpu().numpy()
+
+    th, dh, xh = host(tgt[sel]), host(drf[sel]), toks[sel].cpu().numpy()
+    lw = np.zeros(nsamp, np.float32)
+    kv = synth.initial_kv(cfg)
+    T, rc, fl, top = kv["tables"], kv["refcounts"], kv["free_list"], int(kv["free_top"][0])
+    L = int(kv["seq_len"])
+    ident = np.tile(np.arange(N, dtype=np.int32), (B, 1))
+    o = oracle.kv_reassign(ident, np.zeros(B, np.int32), T, cfg.block_size, L, K + 1, rc, fl, top)
+    rng = np.random.default_rng(0)
+    t_verify = t_rest = 0.0
+    reps = 0
+    t_start = time.perf_counter()
+    while reps < 2 or time.perf_counter() - t_start < budget_s:
+        a = time.perf_counter()
+        v = oracle.verify_smc(th, dh, xh, float(np.float32(cfg.temperature)), cfg.alpha,
+                              cfg.rng_seed, reps, lw)
+        b = time.perf_counter()
+        lwfull = rng.normal(0, 2, (B, N)).astype(np.float32)
+        r = oracle.resample(lwfull, float(np.float32(cfg.tau)), cfg.rng_seed, reps)
+        L += K + 1
+        o = oracle.kv_reassign(r["ancestors"], r["resampled"], o["tables"], cfg.block_size, L,
+                               K + 1, o["refcounts"], o["free_list"], o["free_top"])
+        c = time.perf_counter()
+        t_verify += b - a
+        t_rest += c - b
+        reps += 1
+        if L + 2 * (K + 1) > cfg.M_cap * cfg.block_size:
+            break
+        del v
+    per_step = t_verify / reps * (S / nsamp) + t_rest / reps
+    return {
+        "value": round(1.0 / per_step, 4),
+        "unit": "steps/s",
+        "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": "%d reps: verify on %d of %d sequences (scaled x%d), resample + KV exchange on "
+                  "all %d prompts; fp64 C, OpenMP over rows" % (reps, nsamp, S, S // nsamp, B),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,213 @@
+/*
+ * smcsd.h - C ABI of the MI355X (gfx950) SMC-SD verify / resample / KV pointer-exchange
+ * library (libsmcsd.so).
+ *
+ * The method: Sequential Monte Carlo speculative decoding as described by the two
+ * explainers of "Faster LLM Inference via Sequential Monte Carlo" (gist.science,
+ * Chinese and Spanish pages).  Each round, a draft model extends N particles by K
+ * tokens; the target model scores all of them in one batched pass and adds one bonus
+ * token per particle; each particle's importance weight is updated with the
+ * target/draft probability ratio; when the effective sample size (ESS) falls below a
+ * threshold the population is resampled by weight, and the KV cache follows by
+ * exchanging block pointers and reference counts, never copying KV data (methodology
+ * section, "core flow" and "system optimisation design"; Spanish page, "Resumen
+ * Tecnico" section 2).  The speculative-sampling notes ("Accelerating-Large-Language-
+ * Model-Decoding-with-Speculative-Sampling", section 1 and section 4.2) define the
+ * secondary SpS mode: modified rejection sampling on the same logits.
+ *
+ * Conventions for every entry point
+ *   - Array arguments are DEVICE pointers owned by the caller; the library allocates
+ *     nothing, keeps no state between calls and never synchronises the stream.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All work is
+ *     enqueued on it, in call order.
+ *   - Host-detectable argument errors return a negative code before anything is
+ *     enqueued (SMCSD_EINVAL, SMCSD_EDTYPE, SMCSD_EWORKSPACE); a failed launch returns
+ *     SMCSD_EHIP.  0 means the work was enqueued.
+ *   - Conditions found on the device are OR'ed into the caller's int32 `status` word
+ *     (SMCSD_ST_*), which the caller zeroes and reads after its own synchronisation.
+ *     Kernels bounds-check every index they read from device memory (tokens,
+ *     ancestors, block ids) and flag SMCSD_ST_BAD_INPUT instead of faulting.
+ *   - Calls that share a workspace or state arrays must not overlap in time.
+ *
+ * Randomness (the pages name no generator): Philox4x32-10 (Salmon et al., SC'11) with
+ * key = (seed low, seed high) and counter = (stream index, step low, step high, tag);
+ * a uniform is (word >> 8) * 2^-24.  Tags: 1 bonus token (index = sequence g),
+ * 2 resampling offset (index = prompt b), 3 | (k/4) << 8 SpS acceptance of draft k
+ * (word k mod 4), 4 SpS final token.  Results depend only on (inputs, seed, step):
+ * runs are bit-reproducible and resumable.
+ */
+#ifndef SMCSD_H
+#define SMCSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SMCSD_VERSION 1
+
+/* logits element type */
+#define SMCSD_DTYPE_F32 0
+#define SMCSD_DTYPE_BF16 1
+
+/* verify mode */
+#define SMCSD_MODE_SMC 0
+#define SMCSD_MODE_SPS 1
+
+/* host return codes */
+#define SMCSD_OK 0
+#define SMCSD_EINVAL (-1)
+#define SMCSD_EDTYPE (-2)
+#define SMCSD_EHIP (-3)
+#define SMCSD_EWORKSPACE (-4)
+
+/* device status bits (sticky, OR'ed into *status) */
+#define SMCSD_ST_NAN_INPUT 1          /* a NaN or +inf logit in a row that was read      */
+#define SMCSD_ST_EMPTY_ROW 2          /* a row with no finite logit (all -inf)           */
+#define SMCSD_ST_NOSPACE 4            /* the free stack ran out during a reservation      */
+#define SMCSD_ST_DEGENERATE_WEIGHTS 8 /* a prompt whose weights are all zero or NaN       */
+#define SMCSD_ST_BAD_INPUT 16         /* token, ancestor or block id out of range         */
+
+/* workspace query ops */
+#define SMCSD_OP_VERIFY_SMC 0
+#define SMCSD_OP_VERIFY_SPS 1
+#define SMCSD_OP_KV 2
+
+/* Library version (SMCSD_VERSION). */
+int smcsd_version(void);
+
+/* Static text for a host return code or a single device status bit. */
+const char *smcsd_status_string(int code);
+
+/*
+ * Device workspace bytes for one call.
+ *   SMCSD_OP_VERIFY_SMC / _SPS: B, N, K, V as passed to smcsd_verify (P ignored).
+ *   SMCSD_OP_KV: B, N and the pool size P (K, V ignored).  The KV workspace must be
+ *   zero-filled before its first use; every smcsd_kv_reassign call leaves the part that
+ *   must start at zero (its freed-block bitmap) zeroed again.
+ * Returns 0 for invalid sizes.
+ */
+size_t smcsd_workspace_bytes(int op, int B, int N, int K, int V, int64_t P);
+
+/*
+ * smcsd_verify - the Score, Bonus and Reweight steps of one SMC-SD round (SMC mode),
+ * or the SpS modified-rejection verify (SpS mode), over B*N sequences.
+ * Defining passages: SMC explainers, methodology "core flow" (score the K drafted
+ * tokens of every particle in one batched target pass, add one bonus token per
+ * sequence, reweight by the target/draft ratio; always K+1 tokens per round); the
+ * speculative-sampling notes, section 1 (draft K, score in parallel, accept or
+ * resample so the output follows the target) and section 4.2.
+ *
+ * Sequences and layout.  Output sequence g in [0, B*N) reads source sequence
+ * src = g * seq_step (seq_step = 1 for SMC; seq_step = N_smc selects particle 0 of
+ * each prompt for an SpS comparison on the same tensors).  Row k of src starts at
+ *   target_logits + (src*(K+1) + k) * row_stride   (k = 0..K, element units)
+ *   draft_logits  + (src*K     + k) * row_stride   (k = 0..K-1)
+ * with V valid elements per row (row_stride >= V).  dtype = SMCSD_DTYPE_BF16 or
+ * SMCSD_DTYPE_F32; pointers must be element-aligned (16-byte alignment is fastest).
+ * draft_tokens [src, K] int32 in [0, V); lse_in (nullable) [src, 2K+1] fp32.
+ *
+ * Arithmetic.  z = logit / temperature.  Each row's log-normaliser
+ * LSE = max z + ln sum exp(z - max z) is accumulated in fp32 in one streaming pass.
+ *   logp_k = z^t_k[x_k] - LSE^t_k,  logq_k = z^d_k[x_k] - LSE^d_k   (k < K)
+ * SMC mode: bonus = min{v : sum_{w<=v} softmax(z^t_K)_w > u}, u = U(seed; g, step,
+ * tag 1); logp_K = its log-probability; then
+ *   log_weights[g] += sum_{k<K} (alpha*logp_k - logq_k) + (alpha-1)*logp_K
+ * (alpha = 1: the plain target/draft ratio; alpha != 1: power-sampling target
+ * alpha*log p, not renormalised).  out_tokens[g] = (x_0..x_{K-1}, bonus),
+ * out_num_tokens[g] = K+1.
+ * SpS mode: keep x_k while r_k < p_k(x_k)/q_k(x_k) (r_k = U(seed; g, step, 3|(k/4)<<8,
+ * word k mod 4)); at the first rejection k* draw from max(0, p - q) renormalised
+ * (p if that residual is empty), else a bonus from p_K (u = U(seed; g, step, 4));
+ * out_tokens[g] = accepted drafts then the drawn token, padded with -1;
+ * out_num_tokens[g] = k*+1 (K+1 if all accepted); out_logp[g][K] = target
+ * log-probability of the drawn token at its position; log_weights is not touched.
+ * If lse_in is given (SpS mode only) the LSE pass is skipped and lse_in is used.
+ *
+ * Outputs (indexed by g): out_tokens [B*N, K+1] int32 (required); out_num_tokens
+ * [B*N], out_logp [B*N, K+1], out_logq [B*N, K], out_lse [B*N, 2K+1] (target rows
+ * 0..K then draft rows 0..K-1), all nullable.  log_weights [B*N] fp32 in/out
+ * (required in SMC mode).
+ * Limits: 0 <= K <= 32, V >= 1, temperature finite > 0, alpha finite.
+ * B*N = 0 is a no-op.  workspace: smcsd_workspace_bytes(SMCSD_OP_VERIFY_*, ...).
+ */
+int smcsd_verify(const void *target_logits, const void *draft_logits, int dtype,
+                 int64_t row_stride, int seq_step, const int32_t *draft_tokens, int B, int N,
+                 int K, int V, float temperature, float alpha, int mode, uint64_t seed,
+                 uint64_t step, const float *lse_in, float *log_weights, int32_t *out_tokens,
+                 int32_t *out_num_tokens, float *out_logp, float *out_logq, float *out_lse,
+                 int32_t *status, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * smcsd_resample - ESS and resampling per prompt (the Resample step: compute the
+ * effective sample size every round and, when it is below the threshold, copy
+ * high-weight particles and drop low-weight ones; SMC explainers, methodology
+ * "core flow").  The ESS formula and the scheme are readings: with m = max_n lw,
+ * w_n = exp(lw_n - m) in fp64, ESS = (sum w)^2 / sum w^2 clamped to [1, N];
+ * prompt b resamples iff ESS < tau*N; systematic resampling with one offset
+ * u0 = U(seed; b, step, tag 2): ancestors[b, i] = min{j : C_j > (i+u0)/N} with
+ * C_j = sum_{i<=j} w_i / sum w (clamped to N-1, non-decreasing in i); the prompt's
+ * log-weights are then reset to 0.  Otherwise ancestors[b, i] = i and log_weights
+ * are unchanged.
+ * Arrays: log_weights [B, N] fp32 in/out; ancestors [B, N] int32, ess [B] fp32,
+ * resampled [B] int32 (0/1) out.  Limits: 1 <= N <= 1024, tau finite.
+ * A prompt whose weights are all zero or NaN keeps identity ancestors, gets ess = 0
+ * and sets SMCSD_ST_DEGENERATE_WEIGHTS.
+ */
+int smcsd_resample(float *log_weights, int B, int N, float tau, uint64_t seed, uint64_t step,
+                   int32_t *ancestors, float *ess, int32_t *resampled, int32_t *status,
+                   void *stream);
+
+/*
+ * smcsd_kv_reassign - the KV cache after resampling by pointer exchange and
+ * reference counts, with prefixes shared across particles and no KV data copied
+ * (SMC explainers, "system optimisation design": KV cache; Spanish page, cache
+ * management).  Block-table rules (readings; the pages give only the principle):
+ *
+ * State: block_tables [B*N, M_cap] int32 block ids (-1 = unallocated); every sequence
+ * has positions [0, seq_len) allocated in slots [0, ceil(seq_len/block_size)); slots
+ * beyond hold -1.  refcounts [P] = number of table references per block; the free
+ * stack is free_list[0 .. *free_top) with its top at index *free_top - 1.
+ * Phase 1, prompts with resampled[b] != 0: c_j = #{i : ancestors[b,i] = j};
+ * refcounts of every allocated block of old table j change by c_j - 1 (all increments
+ * before any decrement); blocks reaching 0 are freed; new table i = old table
+ * ancestors[b,i].  The freed blocks of the call are pushed in descending id order.
+ * Phase 2, all prompts: reserve positions [seq_len, seq_len + reserve_tokens).  From
+ * the post-phase-1 state, a sequence whose partial tail block (slot
+ * floor(seq_len/block_size) when seq_len mod block_size != 0) has refcount > 1 and is
+ * also held by a higher-index sequence of its prompt does copy-on-write: it pops a
+ * fresh block d, the old block loses one reference, and (old, d, seq_len mod
+ * block_size) is appended to cow [B*N, 3] - the caller copies that many token
+ * entries of KV data from old to d before writing the round.  Then every slot in
+ * [ceil(seq_len/bs), ceil((seq_len+reserve_tokens)/bs)) pops a fresh block with
+ * refcount 1.  Pops run in ascending (sequence, slot) order; when the stack is empty
+ * the slot keeps its value (-1, or the shared tail) and SMCSD_ST_NOSPACE is set.
+ * *cow_count = number of copy-on-write entries written.
+ * Call once with identity ancestors (resampled all 0) before the first round to
+ * reserve its K+1 slots; after round t call with seq_len = tokens now held
+ * (previous seq_len + K+1).
+ * Limits: 1 <= N <= 1024; ceil((seq_len+reserve_tokens)/block_size) <= M_cap.
+ * workspace: smcsd_workspace_bytes(SMCSD_OP_KV, B, N, 0, 0, P), zero-filled before
+ * first use (each call leaves its freed-block bitmap zeroed again).
+ */
+int smcsd_kv_reassign(const int32_t *ancestors, const int32_t *resampled, int B, int N,
+                      int32_t *block_tables, int M_cap, int block_size, int64_t seq_len,
+                      int reserve_tokens, int32_t *refcounts, int32_t *free_list,
+                      int32_t *free_top, int64_t P, int32_t *cow, int32_t *cow_count,
+                      int32_t *status, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * smcsd_philox4x32_10 - the library's device Philox4x32-10 block function (SC'11),
+ * exposed so its bit-exactness can be checked: out[i] = Philox(counters[i],
+ * keys[i]) for i < n.  counters [n, 4], keys [n, 2], out [n, 4] uint32 device arrays.
+ */
+int smcsd_philox4x32_10(const uint32_t *counters, const uint32_t *keys, int n, uint32_t *out,
+                        void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMCSD_H */

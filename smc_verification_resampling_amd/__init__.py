@@ -1,0 +1,194 @@
+"""Python binding of libsmcsd.so - the MI355X (gfx950) SMC-SD verify / resample / KV path.
+
+Argument marshalling only: every step of the path runs in the library's HIP kernels.
+Tensors must be device (HIP) tensors; this module checks placement, dtype, contiguity
+and sizes so that no host pointer or short buffer reaches a kernel, passes raw pointers
+and the current torch stream, and turns negative return codes into ``SmcsdError``.
+There is no fallback: if the library is not built, importing a call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsmcsd.so")
+
+DTYPE_F32, DTYPE_BF16 = 0, 1
+MODE_SMC, MODE_SPS = 0, 1
+OP_VERIFY_SMC, OP_VERIFY_SPS, OP_KV = 0, 1, 2
+
+ST_NAN_INPUT = 1
+ST_EMPTY_ROW = 2
+ST_NOSPACE = 4
+ST_DEGENERATE_WEIGHTS = 8
+ST_BAD_INPUT = 16
+
+EXPORTED = ("smcsd_version", "smcsd_status_string", "smcsd_workspace_bytes", "smcsd_verify",
+            "smcsd_resample", "smcsd_kv_reassign", "smcsd_philox4x32_10")
+
+_DT = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
+
+
+class SmcsdError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libsmcsd.so and declare the C signatures (no GPU work)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise SmcsdError("libsmcsd.so is not built (%s); run __graft_entry__.build()" % path)
+    lib = ctypes.CDLL(path)
+    P, i32, i64, u64, f32, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint64,
+                                 ctypes.c_float, ctypes.c_size_t)
+    lib.smcsd_version.restype = i32
+    lib.smcsd_status_string.argtypes = [i32]
+    lib.smcsd_status_string.restype = ctypes.c_char_p
+    lib.smcsd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i64]
+    lib.smcsd_workspace_bytes.restype = sz
+    lib.smcsd_verify.argtypes = [P, P, i32, i64, i32, P, i32, i32, i32, i32, f32, f32, i32, u64,
+                                 u64, P, P, P, P, P, P, P, P, P, sz, P]
+    lib.smcsd_verify.restype = i32
+    lib.smcsd_resample.argtypes = [P, i32, i32, f32, u64, u64, P, P, P, P, P]
+    lib.smcsd_resample.restype = i32
+    lib.smcsd_kv_reassign.argtypes = [P, P, i32, i32, P, i32, i32, i64, i32, P, P, P, i64, P, P,
+                                      P, P, sz, P]
+    lib.smcsd_kv_reassign.restype = i32
+    lib.smcsd_philox4x32_10.argtypes = [P, P, i32, P, P]
+    lib.smcsd_philox4x32_10.restype = i32
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _L():
+    return _lib if _lib is not None else load_library()
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise SmcsdError("%s failed: %s (%d)" % (what, _L().smcsd_status_string(rc).decode(), rc))
+
+
+def status_string(code: int) -> str:
+    return _L().smcsd_status_string(code).decode()
+
+
+def version() -> int:
+    return int(_L().smcsd_version())
+
+
+def workspace_bytes(op: int, B: int, N: int, K: int = 0, V: int = 1, P: int = 0) -> int:
+    return int(_L().smcsd_workspace_bytes(op, B, N, K, V, P))
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype=None, min_numel: int = 0,
+         contiguous: bool = True):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise SmcsdError("%s must be a device tensor" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise SmcsdError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if contiguous and not t.is_contiguous():
+        raise SmcsdError("%s must be contiguous" % name)
+    if t.numel() < min_numel:
+        raise SmcsdError("%s holds %d elements, needs %d" % (name, t.numel(), min_numel))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def alloc_workspace(op: int, B: int, N: int, K: int = 0, V: int = 1, P: int = 0,
+                    device=None) -> torch.Tensor:
+    """Zero-filled device workspace of the size the library asks for."""
+    n = workspace_bytes(op, B, N, K, V, P)
+    if n == 0:
+        raise SmcsdError("invalid workspace sizes")
+    return torch.zeros(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: Optional[torch.Tensor],
+           B: int, N: int, K: int, V: int, temperature: float, alpha: float, mode: int, seed: int,
+           step: int, out_tokens: torch.Tensor, status: torch.Tensor, workspace: torch.Tensor,
+           log_weights: Optional[torch.Tensor] = None, out_num_tokens=None, out_logp=None,
+           out_logq=None, out_lse=None, lse_in=None, seq_step: int = 1,
+           row_stride: Optional[int] = None, stream=None) -> None:
+    """smcsd_verify.  target [*, K+1, row_stride], draft [*, K, row_stride] (bf16 or fp32)."""
+    if target.dtype not in _DT:
+        raise SmcsdError("logits must be bfloat16 or float32")
+    rs = V if row_stride is None else int(row_stride)
+    S = B * N
+    nsrc = (S - 1) * seq_step + 1 if S > 0 else 0
+    tp = _dev(target, "target", target.dtype, nsrc * (K + 1) * rs - (rs - V) if S else 0)
+    dp = _dev(draft, "draft", target.dtype, nsrc * K * rs - (rs - V) if S and K else 0) \
+        if K > 0 else None
+    xp = _dev(draft_tokens, "draft_tokens", torch.int32, nsrc * K) if K > 0 else None
+    lw = _dev(log_weights, "log_weights", torch.float32, S)
+    rc = _L().smcsd_verify(
+        tp, dp, _DT[target.dtype], rs, seq_step, xp, B, N, K, V, float(temperature), float(alpha),
+        mode, int(seed) & (2**64 - 1), int(step) & (2**64 - 1),
+        _dev(lse_in, "lse_in", torch.float32, nsrc * (2 * K + 1)), lw,
+        _dev(out_tokens, "out_tokens", torch.int32, S * (K + 1)),
+        _dev(out_num_tokens, "out_num_tokens", torch.int32, S),
+        _dev(out_logp, "out_logp", torch.float32, S * (K + 1)),
+        _dev(out_logq, "out_logq", torch.float32, S * K),
+        _dev(out_lse, "out_lse", torch.float32, S * (2 * K + 1)),
+        _dev(status, "status", torch.int32, 1),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
+    _check(rc, "smcsd_verify")
+
+
+def resample(log_weights: torch.Tensor, B: int, N: int, tau: float, seed: int, step: int,
+             ancestors: torch.Tensor, ess: torch.Tensor, resampled: torch.Tensor,
+             status: torch.Tensor, stream=None) -> None:
+    """smcsd_resample over log_weights [B, N]."""
+    rc = _L().smcsd_resample(
+        _dev(log_weights, "log_weights", torch.float32, B * N), B, N, float(tau),
+        int(seed) & (2**64 - 1), int(step) & (2**64 - 1),
+        _dev(ancestors, "ancestors", torch.int32, B * N), _dev(ess, "ess", torch.float32, B),
+        _dev(resampled, "resampled", torch.int32, B), _dev(status, "status", torch.int32, 1),
+        _stream(stream))
+    _check(rc, "smcsd_resample")
+
+
+def kv_reassign(ancestors: torch.Tensor, resampled: torch.Tensor, B: int, N: int,
+                block_tables: torch.Tensor, block_size: int, seq_len: int, reserve_tokens: int,
+                refcounts: torch.Tensor, free_list: torch.Tensor, free_top: torch.Tensor,
+                cow: torch.Tensor, cow_count: torch.Tensor, status: torch.Tensor,
+                workspace: torch.Tensor, stream=None) -> None:
+    """smcsd_kv_reassign.  block_tables [B*N, M_cap] int32; refcounts / free_list [P] int32."""
+    if block_tables.dim() != 2 or block_tables.shape[0] != B * N:
+        raise SmcsdError("block_tables must be [B*N, M_cap]")
+    M_cap = block_tables.shape[1]
+    P = refcounts.numel()
+    rc = _L().smcsd_kv_reassign(
+        _dev(ancestors, "ancestors", torch.int32, B * N), _dev(resampled, "resampled", torch.int32, B),
+        B, N, _dev(block_tables, "block_tables", torch.int32), M_cap, block_size, int(seq_len),
+        reserve_tokens, _dev(refcounts, "refcounts", torch.int32), _dev(free_list, "free_list",
+                                                                       torch.int32, P),
+        _dev(free_top, "free_top", torch.int32, 1), P, _dev(cow, "cow", torch.int32, 3 * B * N),
+        _dev(cow_count, "cow_count", torch.int32, 1), _dev(status, "status", torch.int32, 1),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
+    _check(rc, "smcsd_kv_reassign")
+
+
+def philox4x32_10(counters: torch.Tensor, keys: torch.Tensor, out: torch.Tensor, stream=None):
+    """Device Philox4x32-10 blocks: counters [n, 4], keys [n, 2] -> out [n, 4] (int32 views)."""
+    n = counters.shape[0]
+    rc = _L().smcsd_philox4x32_10(_dev(counters, "counters", torch.int32, 4 * n),
+                                  _dev(keys, "keys", torch.int32, 2 * n), n,
+                                  _dev(out, "out", torch.int32, 4 * n), _stream(stream))
+    _check(rc, "smcsd_philox4x32_10")

@@ -1,0 +1,144 @@
+// capi.hip - extern "C" entry points of libsmcsd.so: argument validation, dtype
+// dispatch and launch.  Declarations and the full contract are in include/smcsd.h.
+#include <cmath>
+
+#include "../../include/smcsd.h"
+#include "internal.hpp"
+
+using namespace smcsd;
+
+namespace {
+
+inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline int hip_rc(hipError_t e) { return e == hipSuccess ? SMCSD_OK : SMCSD_EHIP; }
+
+inline bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int smcsd_version(void) { return SMCSD_VERSION; }
+
+const char *smcsd_status_string(int code) {
+  switch (code) {
+    case SMCSD_OK: return "ok";
+    case SMCSD_EINVAL: return "invalid argument";
+    case SMCSD_EDTYPE: return "unsupported dtype";
+    case SMCSD_EHIP: return "HIP launch error";
+    case SMCSD_EWORKSPACE: return "workspace too small or missing";
+    case SMCSD_ST_NAN_INPUT: return "NaN or +inf logit";
+    case SMCSD_ST_EMPTY_ROW: return "row with no finite logit";
+    case SMCSD_ST_NOSPACE: return "block pool exhausted";
+    case SMCSD_ST_DEGENERATE_WEIGHTS: return "all particle weights zero or NaN";
+    case SMCSD_ST_BAD_INPUT: return "token, ancestor or block id out of range";
+    default: return "unknown code";
+  }
+}
+
+size_t smcsd_workspace_bytes(int op, int B, int N, int K, int V, int64_t P) {
+  if (B < 0 || N < 0) return 0;
+  const int64_t S = (int64_t)B * N;
+  if (op == SMCSD_OP_VERIFY_SMC || op == SMCSD_OP_VERIFY_SPS) {
+    if (K < 0 || K > kMaxK || V < 1) return 0;
+    return verify_ws_layout(S, K, V, op == SMCSD_OP_VERIFY_SPS ? 1 : 0).total;
+  }
+  if (op == SMCSD_OP_KV) {
+    if (P < 1) return 0;
+    return kv_ws_layout(S, P).total;
+  }
+  return 0;
+}
+
+int smcsd_verify(const void *target_logits, const void *draft_logits, int dtype,
+                 int64_t row_stride, int seq_step, const int32_t *draft_tokens, int B, int N,
+                 int K, int V, float temperature, float alpha, int mode, uint64_t seed,
+                 uint64_t step, const float *lse_in, float *log_weights, int32_t *out_tokens,
+                 int32_t *out_num_tokens, float *out_logp, float *out_logq, float *out_lse,
+                 int32_t *status, void *workspace, size_t workspace_bytes, void *stream) {
+  if (dtype != SMCSD_DTYPE_F32 && dtype != SMCSD_DTYPE_BF16) return SMCSD_EDTYPE;
+  if (mode != SMCSD_MODE_SMC && mode != SMCSD_MODE_SPS) return SMCSD_EINVAL;
+  if (B < 0 || N < 0 || K < 0 || K > kMaxK || V < 1 || seq_step < 1) return SMCSD_EINVAL;
+  if (row_stride < V) return SMCSD_EINVAL;
+  if (!(temperature > 0.0f) || !std::isfinite(temperature) || !std::isfinite(alpha))
+    return SMCSD_EINVAL;
+  const int64_t S = (int64_t)B * N;
+  if (S == 0) return SMCSD_OK;
+  if (S > INT32_MAX / 2) return SMCSD_EINVAL;
+  const size_t esz = dtype == SMCSD_DTYPE_BF16 ? 2 : 4;
+  if (!target_logits || !aligned(target_logits, esz)) return SMCSD_EINVAL;
+  if (K > 0 && (!draft_logits || !aligned(draft_logits, esz) || !draft_tokens)) return SMCSD_EINVAL;
+  if (!out_tokens || !status) return SMCSD_EINVAL;
+  if (mode == SMCSD_MODE_SMC && (!log_weights || lse_in)) return SMCSD_EINVAL;
+  const size_t need = verify_ws_layout(S, K, V, mode == SMCSD_MODE_SPS ? 1 : 0).total;
+  if (!workspace || workspace_bytes < need) return SMCSD_EWORKSPACE;
+
+  VerifyArgs a{};
+  a.tgt = target_logits;
+  a.drf = draft_logits;
+  a.dtype = dtype;
+  a.row_stride = row_stride;
+  a.seq_step = seq_step;
+  a.draft_tokens = draft_tokens;
+  a.nseq = (int)S;
+  a.K = K;
+  a.V = V;
+  a.c = (float)(1.4426950408889634073599246810018921 / (double)temperature);
+  a.alpha = alpha;
+  a.mode = mode;
+  a.seed = seed;
+  a.step = step;
+  a.lse_in = lse_in;
+  a.log_weights = log_weights;
+  a.out_tokens = out_tokens;
+  a.out_num_tokens = out_num_tokens;
+  a.out_logp = out_logp;
+  a.out_logq = out_logq;
+  a.out_lse = out_lse;
+  a.status = status;
+  a.ws = static_cast<char *>(workspace);
+  a.stream = as_stream(stream);
+  return hip_rc(launch_verify(a));
+}
+
+int smcsd_resample(float *log_weights, int B, int N, float tau, uint64_t seed, uint64_t step,
+                   int32_t *ancestors, float *ess, int32_t *resampled, int32_t *status,
+                   void *stream) {
+  if (B < 0 || N < 1 || N > kMaxN || !std::isfinite(tau)) return SMCSD_EINVAL;
+  if (B == 0) return SMCSD_OK;
+  if (!log_weights || !ancestors || !ess || !resampled || !status) return SMCSD_EINVAL;
+  return hip_rc(launch_resample(log_weights, B, N, tau, seed, step, ancestors, ess, resampled,
+                                status, as_stream(stream)));
+}
+
+int smcsd_kv_reassign(const int32_t *ancestors, const int32_t *resampled, int B, int N,
+                      int32_t *block_tables, int M_cap, int block_size, int64_t seq_len,
+                      int reserve_tokens, int32_t *refcounts, int32_t *free_list,
+                      int32_t *free_top, int64_t P, int32_t *cow, int32_t *cow_count,
+                      int32_t *status, void *workspace, size_t workspace_bytes, void *stream) {
+  if (B < 0 || N < 1 || N > kMaxN || M_cap < 1 || block_size < 1 || seq_len < 0 ||
+      reserve_tokens < 0 || P < 1 || P > INT32_MAX)
+    return SMCSD_EINVAL;
+  if (ceil_div(seq_len + reserve_tokens, block_size) > M_cap) return SMCSD_EINVAL;
+  if (B == 0) return SMCSD_OK;
+  if ((int64_t)B * N > INT32_MAX / 4) return SMCSD_EINVAL;
+  if (!ancestors || !resampled || !block_tables || !refcounts || !free_list || !free_top || !cow ||
+      !cow_count || !status)
+    return SMCSD_EINVAL;
+  const size_t need = kv_ws_layout((int64_t)B * N, P).total;
+  if (!workspace || workspace_bytes < need) return SMCSD_EWORKSPACE;
+  return hip_rc(launch_kv(ancestors, resampled, B, N, block_tables, M_cap, block_size, seq_len,
+                          reserve_tokens, refcounts, free_list, free_top, P, cow, cow_count, status,
+                          static_cast<char *>(workspace), as_stream(stream)));
+}
+
+int smcsd_philox4x32_10(const uint32_t *counters, const uint32_t *keys, int n, uint32_t *out,
+                        void *stream) {
+  if (n < 0) return SMCSD_EINVAL;
+  if (n == 0) return SMCSD_OK;
+  if (!counters || !keys || !out) return SMCSD_EINVAL;
+  return hip_rc(launch_philox(counters, keys, n, out, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,197 @@
+// device.hpp - gfx950 device helpers for the SMC-SD verify / resample / KV kernels.
+//
+// Wave64 throughout: reductions and scans use 64-lane shuffles, then LDS across the
+// waves of a workgroup.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/smcsd.h"
+
+namespace smcsd {
+
+constexpr int kWave = 64;
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr double kLn2 = 0.693147180559945309417232121458176568;
+constexpr double kLog2e = 1.442695040888963407359924681001892137;
+
+// ---------------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11).  Each of the ten rounds takes
+// the 64-bit products of counter words 0 and 2 with the two round multipliers; the
+// new counter is (hi(w2*M1) ^ w1 ^ k0, lo(w2*M1), hi(w0*M0) ^ w3 ^ k1, lo(w0*M0)).
+// The key advances by the two Weyl increments after every round.
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ void philox_block(uint32_t c[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t w0 = c[0], w2 = c[2];
+    const uint32_t lo0 = w0 * 0xD2511F53u, hi0 = __umulhi(w0, 0xD2511F53u);
+    const uint32_t lo1 = w2 * 0xCD9E8D57u, hi1 = __umulhi(w2, 0xCD9E8D57u);
+    c[0] = hi1 ^ c[1] ^ k0;
+    c[1] = lo1;
+    c[2] = hi0 ^ c[3] ^ k1;
+    c[3] = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+}
+
+// Counter layout: (stream index, step low, step high, tag); key: (seed low, seed high).
+// The uniform keeps the top 24 bits of one output word: exact in fp32 and fp64.
+__device__ __forceinline__ double philox_uniform(uint64_t seed, uint32_t index, uint64_t step,
+                                                 uint32_t tag, int word) {
+  uint32_t c[4] = {index, (uint32_t)step, (uint32_t)(step >> 32), tag};
+  philox_block(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+  const uint32_t w = word == 0 ? c[0] : word == 1 ? c[1] : word == 2 ? c[2] : c[3];
+  return (double)(w >> 8) * (1.0 / 16777216.0);
+}
+
+// ---------------------------------------------------------------------------------
+// element access
+// ---------------------------------------------------------------------------------
+template <int DT> struct Elt;
+template <> struct Elt<SMCSD_DTYPE_F32> {
+  static constexpr int kBytes = 4;
+  static constexpr int kPerVec = 4;  // elements per 16-byte vector
+  __device__ __forceinline__ static float load(const char *row, int64_t v) {
+    return reinterpret_cast<const float *>(row)[v];
+  }
+  __device__ __forceinline__ static void unpack(const uint4 &w, float (&x)[4]) {
+    x[0] = __uint_as_float(w.x);
+    x[1] = __uint_as_float(w.y);
+    x[2] = __uint_as_float(w.z);
+    x[3] = __uint_as_float(w.w);
+  }
+};
+template <> struct Elt<SMCSD_DTYPE_BF16> {
+  static constexpr int kBytes = 2;
+  static constexpr int kPerVec = 8;
+  __device__ __forceinline__ static float load(const char *row, int64_t v) {
+    return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(row)[v] << 16);
+  }
+  // bf16 is the upper half of an fp32: widening is a shift or a mask.
+  __device__ __forceinline__ static void unpack(const uint4 &w, float (&x)[8]) {
+    x[0] = __uint_as_float(w.x << 16);
+    x[1] = __uint_as_float(w.x & 0xFFFF0000u);
+    x[2] = __uint_as_float(w.y << 16);
+    x[3] = __uint_as_float(w.y & 0xFFFF0000u);
+    x[4] = __uint_as_float(w.z << 16);
+    x[5] = __uint_as_float(w.z & 0xFFFF0000u);
+    x[6] = __uint_as_float(w.w << 16);
+    x[7] = __uint_as_float(w.w & 0xFFFF0000u);
+  }
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------------
+// Online log-sum-exp state over raw logits x with scale c = log2(e) / T:
+//   m  = running max of x,   mc = m * c (rounded once, reused everywhere),
+//   s  = sum 2^(x*c - mc).
+// -inf logits add exactly 0; a NaN or +inf logit turns s into NaN, which the
+// consumers report as NAN_INPUT.  mc is 0 while m is -inf.
+// ---------------------------------------------------------------------------------
+struct Lse {
+  float m, mc, s;
+};
+
+__device__ __forceinline__ Lse lse_init() { return Lse{kNegInf, 0.0f, 0.0f}; }
+
+template <int NV>
+__device__ __forceinline__ void lse_update(Lse &st, const float (&x)[NV], float c) {
+  float vmax = x[0];
+#pragma unroll
+  for (int i = 1; i < NV; ++i) vmax = fmaxf(vmax, x[i]);
+  if (vmax > st.m) {
+    const float mcn = __fmul_rn(vmax, c);
+    st.s = (st.m == kNegInf) ? st.s * 0.0f : st.s * fast_exp2(st.mc - mcn);
+    st.m = vmax;
+    st.mc = mcn;
+  }
+  float e[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) e[i] = fast_exp2(fmaf(x[i], c, -st.mc));
+  // pairwise tree keeps the dependency chain short
+#pragma unroll
+  for (int w = 1; w < NV; w *= 2)
+#pragma unroll
+    for (int i = 0; i + w < NV; i += 2 * w) e[i] += e[i + w];
+  st.s += e[0];
+}
+
+__device__ __forceinline__ Lse lse_combine(const Lse &a, const Lse &b, float c) {
+  const float M = fmaxf(a.m, b.m);
+  if (M == kNegInf) return Lse{kNegInf, 0.0f, a.s + b.s};
+  const float Mc = __fmul_rn(M, c);
+  const float ta = (a.m == kNegInf) ? a.s * 0.0f : a.s * fast_exp2(a.mc - Mc);
+  const float tb = (b.m == kNegInf) ? b.s * 0.0f : b.s * fast_exp2(b.mc - Mc);
+  return Lse{M, Mc, ta + tb};
+}
+
+__device__ __forceinline__ Lse lse_shfl_xor(const Lse &a, int mask) {
+  return Lse{__shfl_xor(a.m, mask, kWave), __shfl_xor(a.mc, mask, kWave),
+             __shfl_xor(a.s, mask, kWave)};
+}
+
+// Workgroup reduction of the online state; the result is valid in thread 0.
+template <int BLOCK>
+__device__ __forceinline__ Lse lse_block_reduce(Lse st, float c, Lse *lds) {
+#pragma unroll
+  for (int mask = 1; mask < kWave; mask <<= 1) st = lse_combine(st, lse_shfl_xor(st, mask), c);
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  if (lane == 0) lds[wave] = st;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int w = 1; w < BLOCK / kWave; ++w) st = lse_combine(st, lds[w], c);
+  }
+  return st;
+}
+
+// ---------------------------------------------------------------------------------
+// scans and sums
+// ---------------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ T wave_inclusive_scan(T v) {
+  const int lane = threadIdx.x % kWave;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const T o = __shfl_up(v, d, kWave);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// Exclusive scan across the workgroup; *total receives the sum.  lds holds
+// BLOCK / 64 elements.  Every thread must call it.
+template <typename T, int BLOCK>
+__device__ __forceinline__ T block_exclusive_scan(T v, T *lds, T *total) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const T inc = wave_inclusive_scan(v);
+  if (lane == kWave - 1) lds[wave] = inc;
+  __syncthreads();
+  T base = T(0), tot = T(0);
+#pragma unroll
+  for (int w = 0; w < BLOCK / kWave; ++w) {
+    const T x = lds[w];
+    if (w < wave) base += x;
+    tot += x;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + inc - v;
+}
+
+template <typename T, int BLOCK>
+__device__ __forceinline__ T block_sum(T v, T *lds) {
+  T tot;
+  block_exclusive_scan<T, BLOCK>(v, lds, &tot);
+  return tot;
+}
+
+__device__ __forceinline__ void flag(int32_t *status, int32_t bits) {
+  if (bits) atomicOr(status, bits);
+}
+
+}  // namespace smcsd

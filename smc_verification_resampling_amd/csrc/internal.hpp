@@ -1,0 +1,98 @@
+// internal.hpp - launch geometry and workspace layout shared by the library's sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace smcsd {
+
+// Streaming LSE pass: one workgroup reduces one tile = (row, chunk of the vocabulary).
+constexpr int kStreamBlock = 256;
+constexpr int kStreamUnroll = 8;
+// elements per tile: 32 KiB of logits for both dtypes
+constexpr int kChunkElemsBf16 = 16384;
+constexpr int kChunkElemsF32 = 8192;
+constexpr int kChunkElemsMin = kChunkElemsF32;  // workspace is sized for the smaller tile
+
+constexpr int kFinalBlock = 256;
+constexpr int kMaxK = 32;
+constexpr int kMaxN = 1024;
+
+inline int chunk_elems(int dtype) { return dtype == 1 ? kChunkElemsBf16 : kChunkElemsF32; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Verify workspace: [row partials float2 x nseq*(2K+1)*chunks]
+//                   [kstar int32 x nseq][L2 pair double2 x nseq][residual partials float2 x nseq*chunks]
+struct VerifyWs {
+  size_t part, kstar, l2, part2, total;
+};
+inline VerifyWs verify_ws_layout(int64_t nseq, int K, int V, int mode) {
+  VerifyWs w{};
+  const int64_t chunks = ceil_div(V, kChunkElemsMin);
+  size_t off = 0;
+  w.part = off;
+  off += align256(sizeof(float) * 2 * (size_t)(nseq * (2 * K + 1) * chunks));
+  if (mode == 1) {
+    w.kstar = off;
+    off += align256(sizeof(int32_t) * (size_t)nseq);
+    w.l2 = off;
+    off += align256(sizeof(double) * 2 * (size_t)nseq);
+    w.part2 = off;
+    off += align256(sizeof(float) * 2 * (size_t)(nseq * chunks));
+  }
+  w.total = off;
+  return w;
+}
+
+// KV workspace: [freed bitmap uint32 x ceil(P/32)][needs_cow int32 x B*N]
+struct KvWs {
+  size_t bitmap, cow_flags, total;
+};
+inline KvWs kv_ws_layout(int64_t S, int64_t P) {
+  KvWs w{};
+  size_t off = 0;
+  w.bitmap = off;
+  off += align256(sizeof(uint32_t) * (size_t)ceil_div(P, 32));
+  w.cow_flags = off;
+  off += align256(sizeof(int32_t) * (size_t)S);
+  w.total = off;
+  return w;
+}
+
+struct VerifyArgs {
+  const void *tgt, *drf;
+  int dtype;
+  int64_t row_stride;
+  int seq_step;
+  const int32_t *draft_tokens;
+  int nseq, K, V;
+  float c;      // log2(e) / T, rounded once on the host
+  float alpha;
+  int mode;
+  uint64_t seed, step;
+  const float *lse_in;
+  float *log_weights;
+  int32_t *out_tokens, *out_num_tokens;
+  float *out_logp, *out_logq, *out_lse;
+  int32_t *status;
+  char *ws;
+  hipStream_t stream;
+};
+
+hipError_t launch_verify(const VerifyArgs &a);
+
+hipError_t launch_resample(float *lw, int B, int N, float tau, uint64_t seed, uint64_t step,
+                           int32_t *anc, float *ess, int32_t *resampled, int32_t *status,
+                           hipStream_t stream);
+
+hipError_t launch_kv(const int32_t *anc, const int32_t *resampled, int B, int N, int32_t *tables,
+                     int M_cap, int bs, int64_t L, int R, int32_t *rc, int32_t *free_list,
+                     int32_t *free_top, int64_t P, int32_t *cow, int32_t *cow_count,
+                     int32_t *status, char *ws, hipStream_t stream);
+
+hipError_t launch_philox(const uint32_t *ctr, const uint32_t *key, int n, uint32_t *out,
+                         hipStream_t stream);
+
+}  // namespace smcsd

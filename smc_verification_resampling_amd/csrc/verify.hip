@@ -1,0 +1,554 @@
+// verify.hip - Score / Bonus / Reweight of an SMC-SD round, and the SpS verify, on gfx950.
+//
+// The verify step is a bandwidth-bound reduction over B*N*(2K+1) rows of V logits
+// (SMC explainers, methodology: verification as fixed-size vectorised operations; the
+// target scores all drafted positions in one batched pass and adds a bonus token).
+// No MFMA: nothing here is a contraction.
+//
+// Kernels
+//   k_lse_partials   grid = tiles (row, 32 KiB vocabulary chunk), 256 threads.  One
+//                    streaming pass with 16-byte loads; per lane an online (max, sum of
+//                    2^(x*c - max*c)); wave shuffles + LDS combine; writes one (max, sum)
+//                    pair per tile.  Bonus rows are ordered last so that the chunk the
+//                    finalize kernel re-reads is among the most recently streamed bytes.
+//   k_smc_finalize   grid = sequences.  Combines the chunk pairs in fp64 into each row's
+//                    normaliser, gathers the draft-token log-probabilities, draws the bonus
+//                    token by inverse CDF (selects the chunk from the pairs, re-reads only
+//                    that chunk) and updates the log-weight.
+//   k_sps_decide / k_sps_residual / k_sps_final
+//                    SpS: acceptance tests from the gathered log-probabilities, one pass
+//                    over the residual max(0, p - q) (or p_K) of the single row pair that is
+//                    needed, and its inverse CDF.
+#include <algorithm>
+#include <climits>
+
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace smcsd {
+
+struct RowMap {
+  const char *tgt, *drf;
+  int64_t row_bytes;  // bytes between consecutive rows
+  int seq_step;
+  int K;
+  __device__ __forceinline__ const char *row(int g, int slot) const {
+    const int64_t src = (int64_t)g * seq_step;
+    if (slot <= K) return tgt + (src * (K + 1) + slot) * row_bytes;
+    return drf + (src * K + (slot - K - 1)) * row_bytes;
+  }
+};
+
+// One chunk pair (m, s) re-expressed relative to the row's Mc, in fp64.  -inf chunks add
+// 0 (their s is 0, or NaN if the chunk held a NaN, which then propagates).
+__device__ __forceinline__ double chunk_term(float2 p, float c, float Mc) {
+  if (p.x == kNegInf) return (double)p.y * 0.0;
+  return (double)p.y * exp2((double)__fmul_rn(p.x, c) - (double)Mc);
+}
+
+// ---------------------------------------------------------------------------------
+// Streaming LSE pass
+// ---------------------------------------------------------------------------------
+template <int DT>
+__global__ __launch_bounds__(kStreamBlock) void k_lse_partials(RowMap rm, int nseq, int V,
+                                                                int chunk_elems, int chunks,
+                                                                float c, float2 *__restrict__ part,
+                                                                int64_t ntiles) {
+  using E = Elt<DT>;
+  constexpr int EPV = E::kPerVec;
+  __shared__ Lse lds[kStreamBlock / kWave];
+  const int K = rm.K;
+  const int R = 2 * K + 1;
+  const int64_t nonbonus_rows = (int64_t)nseq * 2 * K;
+  const int tid = threadIdx.x;
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int64_t row_id = t / chunks;
+    const int ch = (int)(t - row_id * chunks);
+    int g, slot;
+    if (row_id < nonbonus_rows) {
+      g = (int)(row_id / (2 * K));
+      const int j = (int)(row_id - (int64_t)g * 2 * K);
+      slot = j < K ? j : j + 1;
+    } else {
+      g = (int)(row_id - nonbonus_rows);
+      slot = K;
+    }
+    const char *row = rm.row(g, slot);
+    const int64_t e0 = (int64_t)ch * chunk_elems;
+    const int64_t e1 = min((int64_t)V, e0 + (int64_t)chunk_elems);
+    const uintptr_t addr0 = (uintptr_t)(row + e0 * E::kBytes);
+    int64_t head = (int64_t)((16 - (addr0 & 15)) & 15) / E::kBytes;
+    if (head > e1 - e0) head = e1 - e0;
+    const int64_t a0 = e0 + head;
+    const int64_t nvec = (e1 - a0) / EPV;
+    const int64_t a1 = a0 + nvec * EPV;
+
+    Lse st = lse_init();
+    if (tid < head) {
+      const float x[1] = {E::load(row, e0 + tid)};
+      lse_update<1>(st, x, c);
+    }
+    if (tid < e1 - a1) {
+      const float x[1] = {E::load(row, a1 + tid)};
+      lse_update<1>(st, x, c);
+    }
+    const uint4 *vp = reinterpret_cast<const uint4 *>(row + a0 * E::kBytes);
+    for (int64_t v0 = 0; v0 < nvec; v0 += (int64_t)kStreamBlock * kStreamUnroll) {
+      uint4 buf[kStreamUnroll];
+#pragma unroll
+      for (int u = 0; u < kStreamUnroll; ++u) {
+        const int64_t v = v0 + u * kStreamBlock + tid;
+        if (v < nvec) buf[u] = vp[v];
+      }
+#pragma unroll
+      for (int u = 0; u < kStreamUnroll; ++u) {
+        const int64_t v = v0 + u * kStreamBlock + tid;
+        if (v < nvec) {
+          float x[EPV];
+          E::unpack(buf[u], x);
+          lse_update<EPV>(st, x, c);
+        }
+      }
+    }
+    st = lse_block_reduce<kStreamBlock>(st, c, lds);
+    if (tid == 0) part[((int64_t)g * R + slot) * chunks + ch] = make_float2(st.m, st.s);
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Row normalisers from the chunk pairs (thread r handles row slot r).
+// L2 = log2 of sum_v 2^(x_v * c) = Mc + log2(S).
+// ---------------------------------------------------------------------------------
+struct RowNorm {
+  float Mc;
+  double S, L2;
+  int flags;
+};
+
+__device__ __forceinline__ RowNorm row_norm(const float2 *p, int chunks, float c) {
+  float M = kNegInf;
+  for (int i = 0; i < chunks; ++i) M = fmaxf(M, p[i].x);
+  RowNorm r{};
+  r.Mc = M == kNegInf ? 0.0f : __fmul_rn(M, c);
+  double S = 0.0;
+  for (int i = 0; i < chunks; ++i) S += chunk_term(p[i], c, r.Mc);
+  r.S = S;
+  r.L2 = (double)r.Mc + log2(S);
+  r.flags = 0;
+  if (isnan(S) || isinf(S)) r.flags |= SMCSD_ST_NAN_INPUT;
+  else if (M == kNegInf) r.flags |= SMCSD_ST_EMPTY_ROW;
+  return r;
+}
+
+// Inverse CDF inside one chunk [e0, e1) of a row: the first v whose running sum
+// base + sum_{w<=v} val(w) exceeds target.  val() is evaluated in fp32 and accumulated in
+// fp64.  Thread ranges are contiguous; thread 0 picks the owning range sequentially, then
+// the owner walks it.  If rounding leaves no crossing, the last v with val > 0 in the
+// owner's range (or the chunk) is returned.  Every thread must call it.
+template <int BLOCK, typename ValFn>
+__device__ __forceinline__ int chunk_inverse_cdf(int64_t e0, int64_t e1, double base,
+                                                 double target, ValFn val, double *loc_lds,
+                                                 int *misc_lds) {
+  const int tid = threadIdx.x;
+  const int64_t n = e1 - e0;
+  const int64_t per = (n + BLOCK - 1) / BLOCK;
+  const int64_t t0 = min(e1, e0 + tid * per);
+  const int64_t t1 = min(e1, t0 + per);
+  double loc = 0.0;
+  int last = -1;
+  for (int64_t v = t0; v < t1; ++v) {
+    const float x = val(v);
+    loc += (double)x;
+    if (x > 0.0f) last = (int)v;
+  }
+  loc_lds[tid] = loc;
+  if (tid == 0) {
+    misc_lds[0] = -1;  // owner
+    misc_lds[1] = -1;  // chunk-wide last positive
+    misc_lds[2] = -1;  // result
+  }
+  __syncthreads();
+  if (last >= 0) atomicMax(&misc_lds[1], last);
+  if (tid == 0) {
+    double run = base;
+    int owner = -1;
+    for (int t = 0; t < BLOCK; ++t) {
+      if (run + loc_lds[t] > target) {
+        owner = t;
+        break;
+      }
+      run += loc_lds[t];
+    }
+    misc_lds[0] = owner;
+    loc_lds[BLOCK] = run;
+  }
+  __syncthreads();
+  if (tid == misc_lds[0]) {
+    double run = loc_lds[BLOCK];
+    int pick = last;
+    for (int64_t v = t0; v < t1; ++v) {
+      run += (double)val(v);
+      if (run > target) {
+        pick = (int)v;
+        break;
+      }
+    }
+    misc_lds[2] = pick;
+  }
+  __syncthreads();
+  const int res = misc_lds[0] >= 0 ? misc_lds[2] : misc_lds[1];
+  __syncthreads();
+  return res;
+}
+
+// ---------------------------------------------------------------------------------
+// SMC finalize: one workgroup per sequence
+// ---------------------------------------------------------------------------------
+template <int DT>
+__global__ __launch_bounds__(kFinalBlock) void k_smc_finalize(
+    RowMap rm, const int32_t *__restrict__ draft_tokens, int V, int chunk_elems, int chunks,
+    float c, float alpha, uint64_t seed, uint64_t step, const float2 *__restrict__ part,
+    float *__restrict__ lw, int32_t *__restrict__ out_tokens, int32_t *__restrict__ out_num,
+    float *__restrict__ out_logp, float *__restrict__ out_logq, float *__restrict__ out_lse,
+    int32_t *status) {
+  using E = Elt<DT>;
+  const int K = rm.K, R = 2 * K + 1;
+  const int g = blockIdx.x, tid = threadIdx.x;
+  __shared__ float sMc[2 * kMaxK + 1];
+  __shared__ double sS[2 * kMaxK + 1], sL2[2 * kMaxK + 1];
+  __shared__ double sLogp[kMaxK + 1], sLogq[kMaxK + 1];
+  __shared__ int32_t sTok[kMaxK + 1];
+  __shared__ double sLoc[kFinalBlock + 1];
+  __shared__ int sMisc[4];
+  __shared__ int sFlags;
+  if (tid == 0) sFlags = 0;
+  __syncthreads();
+
+  if (tid < R) {
+    const RowNorm rn = row_norm(part + ((int64_t)g * R + tid) * chunks, chunks, c);
+    sMc[tid] = rn.Mc;
+    sS[tid] = rn.S;
+    sL2[tid] = rn.L2;
+    if (rn.flags) atomicOr(&sFlags, rn.flags);
+  }
+  __syncthreads();
+
+  const int64_t src = (int64_t)g * rm.seq_step;
+  if (tid < 2 * K) {
+    const int k = tid < K ? tid : tid - K;
+    const int slot = tid < K ? k : K + 1 + k;
+    const int32_t x = draft_tokens[src * K + k];
+    double lp = __builtin_nan("");
+    if (x < 0 || x >= V) {
+      atomicOr(&sFlags, SMCSD_ST_BAD_INPUT);
+    } else {
+      const float xv = E::load(rm.row(g, slot), x);
+      lp = ((double)xv * (double)c - sL2[slot]) * kLn2;
+    }
+    if (tid < K) {
+      sLogp[k] = lp;
+      sTok[k] = x;
+    } else {
+      sLogq[k] = lp;
+    }
+  }
+
+  // Bonus: u = U(seed; g, step, BONUS); token = first v with F_v > u, in the unnormalised
+  // domain: running sum of 2^(x*c - Mc_K) against u * S_K.
+  const double SK = sS[K];
+  const float McK = sMc[K];
+  const double u = philox_uniform(seed, (uint32_t)g, step, 1u, 0);
+  const double target = u * SK;
+  const float2 *pk = part + ((int64_t)g * R + K) * chunks;
+  const char *brow = rm.row(g, K);
+  int bonus = -1;
+  if (isfinite(SK) && SK > 0.0) {
+    double base = 0.0;
+    int ch = chunks - 1;
+    for (int i = 0; i < chunks; ++i) {
+      const double si = chunk_term(pk[i], c, McK);
+      if (base + si > target) {
+        ch = i;
+        break;
+      }
+      base += si;
+    }
+    if (base > target) base = target;  // unreachable in exact arithmetic
+    const int64_t e0 = (int64_t)ch * chunk_elems;
+    const int64_t e1 = min((int64_t)V, e0 + (int64_t)chunk_elems);
+    auto val = [&](int64_t v) -> float { return fast_exp2(fmaf(E::load(brow, v), c, -McK)); };
+    bonus = chunk_inverse_cdf<kFinalBlock>(e0, e1, base, target, val, sLoc, sMisc);
+  }
+  __syncthreads();
+
+  if (tid == 0) {
+    double lpK = __builtin_nan("");
+    if (bonus >= 0) lpK = ((double)E::load(brow, bonus) * (double)c - sL2[K]) * kLn2;
+    double incr = 0.0;
+    for (int k = 0; k < K; ++k) incr += (double)alpha * sLogp[k] - sLogq[k];
+    incr += ((double)alpha - 1.0) * lpK;
+    lw[g] = (float)((double)lw[g] + incr);
+    int32_t *tok = out_tokens + (int64_t)g * (K + 1);
+    for (int k = 0; k < K; ++k) tok[k] = sTok[k];
+    tok[K] = bonus;
+    if (out_num) out_num[g] = K + 1;
+    if (out_logp) {
+      for (int k = 0; k < K; ++k) out_logp[(int64_t)g * (K + 1) + k] = (float)sLogp[k];
+      out_logp[(int64_t)g * (K + 1) + K] = (float)lpK;
+    }
+    if (out_logq)
+      for (int k = 0; k < K; ++k) out_logq[(int64_t)g * K + k] = (float)sLogq[k];
+    if (out_lse)
+      for (int r = 0; r < R; ++r) out_lse[(int64_t)g * R + r] = (float)(sL2[r] * kLn2);
+    if (sFlags) atomicOr(status, sFlags);
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// SpS
+// ---------------------------------------------------------------------------------
+// Per row: the element probability is 2^(x*c - Mc) * inv (inv = 1/S); from lse_in the
+// pair is (LSE*log2(e), 1).  ws_norm[g] = {Mc_p, inv_p, Mc_q, inv_q} for row pair k*.
+template <int DT>
+__global__ __launch_bounds__(kWave) void k_sps_decide(
+    RowMap rm, const int32_t *__restrict__ draft_tokens, int V, int chunks, float c,
+    uint64_t seed, uint64_t step, const float2 *__restrict__ part, const float *__restrict__ lse_in,
+    int32_t *__restrict__ ws_kstar, float4 *__restrict__ ws_norm, int32_t *__restrict__ out_tokens,
+    int32_t *__restrict__ out_num, float *__restrict__ out_logp, float *__restrict__ out_logq,
+    float *__restrict__ out_lse, int32_t *status) {
+  using E = Elt<DT>;
+  const int K = rm.K, R = 2 * K + 1;
+  const int g = blockIdx.x, tid = threadIdx.x;
+  const int64_t src = (int64_t)g * rm.seq_step;
+  __shared__ double sL2[2 * kMaxK + 1], sS[2 * kMaxK + 1];
+  __shared__ float sMc[2 * kMaxK + 1];
+  __shared__ double sLogp[kMaxK + 1], sLogq[kMaxK + 1];
+  __shared__ int32_t sTok[kMaxK + 1];
+  __shared__ int sFlags;
+  if (tid == 0) sFlags = 0;
+  __syncthreads();
+  for (int r = tid; r < R; r += kWave) {
+    if (lse_in) {
+      const double L2 = (double)lse_in[src * R + r] * kLog2e;
+      sL2[r] = L2;
+      sS[r] = 1.0;
+      sMc[r] = (float)L2;
+      if (isnan(L2) || L2 == __builtin_inf()) atomicOr(&sFlags, SMCSD_ST_NAN_INPUT);
+      else if (L2 == -__builtin_inf()) atomicOr(&sFlags, SMCSD_ST_EMPTY_ROW);
+    } else {
+      const RowNorm rn = row_norm(part + ((int64_t)g * R + r) * chunks, chunks, c);
+      sL2[r] = rn.L2;
+      sS[r] = rn.S;
+      sMc[r] = rn.Mc;
+      if (rn.flags) atomicOr(&sFlags, rn.flags);
+    }
+  }
+  __syncthreads();
+  for (int j = tid; j < 2 * K; j += kWave) {
+    const int k = j < K ? j : j - K;
+    const int slot = j < K ? k : K + 1 + k;
+    const int32_t x = draft_tokens[src * K + k];
+    double lp = __builtin_nan("");
+    if (x < 0 || x >= V) atomicOr(&sFlags, SMCSD_ST_BAD_INPUT);
+    else lp = ((double)E::load(rm.row(g, slot), x) * (double)c - sL2[slot]) * kLn2;
+    if (j < K) {
+      sLogp[k] = lp;
+      sTok[k] = x;
+    } else {
+      sLogq[k] = lp;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int kstar = K;
+    for (int k = 0; k < K; ++k) {
+      const double ratio = exp(sLogp[k] - sLogq[k]);
+      const double r = philox_uniform(seed, (uint32_t)g, step, 3u | ((uint32_t)(k / 4) << 8), k % 4);
+      if (!(r < ratio)) {
+        kstar = k;
+        break;
+      }
+    }
+    ws_kstar[g] = kstar;
+    const int qs = K + 1 + kstar;
+    ws_norm[g] = make_float4(sMc[kstar], (float)(1.0 / sS[kstar]), kstar < K ? sMc[qs] : 0.0f,
+                             kstar < K ? (float)(1.0 / sS[qs]) : 0.0f);
+    int32_t *tok = out_tokens + (int64_t)g * (K + 1);
+    for (int k = 0; k <= K; ++k) tok[k] = k < kstar ? sTok[k] : -1;
+    if (out_num) out_num[g] = kstar + 1;
+    if (out_logp)
+      for (int k = 0; k < K; ++k) out_logp[(int64_t)g * (K + 1) + k] = (float)sLogp[k];
+    if (out_logq)
+      for (int k = 0; k < K; ++k) out_logq[(int64_t)g * K + k] = (float)sLogq[k];
+    if (out_lse)
+      for (int r = 0; r < R; ++r) out_lse[(int64_t)g * R + r] = (float)(sL2[r] * kLn2);
+    if (sFlags) atomicOr(status, sFlags);
+  }
+}
+
+// Residual element values, identical in the pass and in the re-read.
+template <int DT>
+__device__ __forceinline__ float sps_p(const char *row, int64_t v, float c, float Mc, float inv) {
+  return fast_exp2(fmaf(Elt<DT>::load(row, v), c, -Mc)) * inv;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kStreamBlock) void k_sps_residual(
+    RowMap rm, int V, int chunk_elems, int chunks, float c, const int32_t *__restrict__ ws_kstar,
+    const float4 *__restrict__ ws_norm, float2 *__restrict__ part2, int64_t ntiles) {
+  __shared__ float red[kStreamBlock / kWave];
+  const int K = rm.K;
+  const int tid = threadIdx.x;
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int g = (int)(t / chunks);
+    const int ch = (int)(t - (int64_t)g * chunks);
+    const int kstar = ws_kstar[g];
+    const float4 nm = ws_norm[g];
+    const char *prow = rm.row(g, kstar);
+    const char *qrow = kstar < K ? rm.row(g, K + 1 + kstar) : nullptr;
+    const int64_t e0 = (int64_t)ch * chunk_elems;
+    const int64_t e1 = min((int64_t)V, e0 + (int64_t)chunk_elems);
+    float srho = 0.0f, sp = 0.0f;
+    for (int64_t v = e0 + tid; v < e1; v += kStreamBlock) {
+      const float p = sps_p<DT>(prow, v, c, nm.x, nm.y);
+      sp += p;
+      if (qrow) srho += fmaxf(p - sps_p<DT>(qrow, v, c, nm.z, nm.w), 0.0f);
+    }
+    srho = block_sum<float, kStreamBlock>(srho, red);
+    sp = block_sum<float, kStreamBlock>(sp, red);
+    if (tid == 0) part2[(int64_t)g * chunks + ch] = make_float2(srho, sp);
+    __syncthreads();
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kFinalBlock) void k_sps_final(
+    RowMap rm, int V, int chunk_elems, int chunks, float c, uint64_t seed, uint64_t step,
+    const int32_t *__restrict__ ws_kstar, const float4 *__restrict__ ws_norm,
+    const float2 *__restrict__ part2, int32_t *__restrict__ out_tokens, float *__restrict__ out_logp,
+    int32_t *status) {
+  const int K = rm.K;
+  const int g = blockIdx.x, tid = threadIdx.x;
+  __shared__ double sLoc[kFinalBlock + 1];
+  __shared__ int sMisc[4];
+  const int kstar = ws_kstar[g];
+  const float4 nm = ws_norm[g];
+  const char *prow = rm.row(g, kstar);
+  const char *qrow = kstar < K ? rm.row(g, K + 1 + kstar) : nullptr;
+  const float2 *p2 = part2 + (int64_t)g * chunks;
+  double Rt = 0.0, Pt = 0.0;
+  for (int i = 0; i < chunks; ++i) {
+    Rt += (double)p2[i].x;
+    Pt += (double)p2[i].y;
+  }
+  const bool use_rho = qrow != nullptr && Rt > 0.0;
+  const double total = use_rho ? Rt : Pt;
+  const double u = philox_uniform(seed, (uint32_t)g, step, 4u, 0);
+  const double target = u * total;
+  int tok = -1;
+  if (isfinite(total) && total > 0.0) {
+    double base = 0.0;
+    int ch = chunks - 1;
+    for (int i = 0; i < chunks; ++i) {
+      const double si = use_rho ? (double)p2[i].x : (double)p2[i].y;
+      if (base + si > target) {
+        ch = i;
+        break;
+      }
+      base += si;
+    }
+    const int64_t e0 = (int64_t)ch * chunk_elems;
+    const int64_t e1 = min((int64_t)V, e0 + (int64_t)chunk_elems);
+    auto val = [&](int64_t v) -> float {
+      const float p = sps_p<DT>(prow, v, c, nm.x, nm.y);
+      return use_rho ? fmaxf(p - sps_p<DT>(qrow, v, c, nm.z, nm.w), 0.0f) : p;
+    };
+    tok = chunk_inverse_cdf<kFinalBlock>(e0, e1, base, target, val, sLoc, sMisc);
+  }
+  if (tid == 0) {
+    out_tokens[(int64_t)g * (K + 1) + kstar] = tok;
+    if (out_logp) {
+      // log p of the drawn token: (x*c - L2)*ln2 with L2 = Mc + log2(1/inv)
+      double lp = __builtin_nan("");
+      if (tok >= 0)
+        lp = ((double)Elt<DT>::load(prow, tok) * (double)c - ((double)nm.x - log2((double)nm.y))) *
+             kLn2;
+      out_logp[(int64_t)g * (K + 1) + K] = (float)lp;
+    }
+    if (tok < 0) atomicOr(status, isnan(total) ? SMCSD_ST_NAN_INPUT : SMCSD_ST_EMPTY_ROW);
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Philox check kernel
+// ---------------------------------------------------------------------------------
+__global__ void k_philox(const uint32_t *__restrict__ ctr, const uint32_t *__restrict__ key, int n,
+                         uint32_t *__restrict__ out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  uint32_t c[4] = {ctr[4 * i], ctr[4 * i + 1], ctr[4 * i + 2], ctr[4 * i + 3]};
+  philox_block(c, key[2 * i], key[2 * i + 1]);
+  out[4 * i] = c[0];
+  out[4 * i + 1] = c[1];
+  out[4 * i + 2] = c[2];
+  out[4 * i + 3] = c[3];
+}
+
+// ---------------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------------
+template <int DT>
+static hipError_t launch_verify_t(const VerifyArgs &a) {
+  const int esz = Elt<DT>::kBytes;
+  const int ce = chunk_elems(DT);
+  const int chunks = (int)ceil_div(a.V, ce);
+  const int K = a.K, R = 2 * K + 1;
+  RowMap rm{static_cast<const char *>(a.tgt), static_cast<const char *>(a.drf),
+            a.row_stride * esz, a.seq_step, K};
+  const VerifyWs w = verify_ws_layout(a.nseq, K, a.V, a.mode);
+  float2 *part = reinterpret_cast<float2 *>(a.ws + w.part);
+  const int64_t ntiles = (int64_t)a.nseq * R * chunks;
+  const unsigned grid = (unsigned)std::min<int64_t>(ntiles, (int64_t)1 << 30);
+
+  if (a.mode == SMCSD_MODE_SMC) {
+    hipLaunchKernelGGL(k_lse_partials<DT>, dim3(grid), dim3(kStreamBlock), 0, a.stream, rm, a.nseq,
+                       a.V, ce, chunks, a.c, part, ntiles);
+    hipLaunchKernelGGL(k_smc_finalize<DT>, dim3(a.nseq), dim3(kFinalBlock), 0, a.stream, rm,
+                       a.draft_tokens, a.V, ce, chunks, a.c, a.alpha, a.seed, a.step, part,
+                       a.log_weights, a.out_tokens, a.out_num_tokens, a.out_logp, a.out_logq,
+                       a.out_lse, a.status);
+    return hipGetLastError();
+  }
+  int32_t *kstar = reinterpret_cast<int32_t *>(a.ws + w.kstar);
+  float4 *norm = reinterpret_cast<float4 *>(a.ws + w.l2);
+  float2 *part2 = reinterpret_cast<float2 *>(a.ws + w.part2);
+  if (!a.lse_in)
+    hipLaunchKernelGGL(k_lse_partials<DT>, dim3(grid), dim3(kStreamBlock), 0, a.stream, rm, a.nseq,
+                       a.V, ce, chunks, a.c, part, ntiles);
+  hipLaunchKernelGGL(k_sps_decide<DT>, dim3(a.nseq), dim3(kWave), 0, a.stream, rm, a.draft_tokens,
+                     a.V, chunks, a.c, a.seed, a.step, part, a.lse_in, kstar, norm, a.out_tokens,
+                     a.out_num_tokens, a.out_logp, a.out_logq, a.out_lse, a.status);
+  const int64_t ntiles2 = (int64_t)a.nseq * chunks;
+  hipLaunchKernelGGL(k_sps_residual<DT>, dim3((unsigned)std::min<int64_t>(ntiles2, (int64_t)1 << 30)),
+                     dim3(kStreamBlock), 0, a.stream, rm, a.V, ce, chunks, a.c, kstar, norm, part2,
+                     ntiles2);
+  hipLaunchKernelGGL(k_sps_final<DT>, dim3(a.nseq), dim3(kFinalBlock), 0, a.stream, rm, a.V, ce,
+                     chunks, a.c, a.seed, a.step, kstar, norm, part2, a.out_tokens, a.out_logp,
+                     a.status);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify(const VerifyArgs &a) {
+  if (a.dtype == SMCSD_DTYPE_BF16) return launch_verify_t<SMCSD_DTYPE_BF16>(a);
+  return launch_verify_t<SMCSD_DTYPE_F32>(a);
+}
+
+hipError_t launch_philox(const uint32_t *ctr, const uint32_t *key, int n, uint32_t *out,
+                         hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_philox, dim3((n + 255) / 256), dim3(256), 0, stream, ctr, key, n, out);
+  return hipGetLastError();
+}
+
+}  // namespace smcsd

@@ -1,0 +1,295 @@
+"""Lock-step parity harness: SMC-SD rounds on the GPU through the C ABI, every call
+checked against the CPU oracle on the same inputs and the same state at call entry.
+
+Bar (per call):
+  * integer outputs (draft tokens echoed, bonus tokens, resampling decisions, ancestors,
+    block tables, refcounts, free stack, copy-on-write list, SpS tokens) bit-exact,
+    except at decisions whose oracle margin is below 1e-6 - those are flagged and
+    counted; a mismatch there is allowed, an unflagged mismatch is not;
+  * log-weights within 1e-4 absolute; row log-normalisers within 1e-5 relative;
+    gathered log-probabilities within 1e-5 * max(1, |ref|); ESS within 1e-6 relative.
+The oracle receives the GPU's state at call entry, so one flagged decision cannot
+cascade into later calls.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+import time
+
+import numpy as np
+import torch
+
+import oracle
+import smc_verification_resampling_amd as sm
+from workloads import synth
+from workloads.configs import Config
+
+MARGIN = 1e-6
+TOL_LW = 1e-4
+TOL_LSE_REL = 1e-5
+TOL_LOGP = 1e-5
+TOL_ESS_REL = 1e-6
+
+
+def host_logits(x: torch.Tensor) -> np.ndarray:
+    x = x.contiguous()
+    if x.dtype == torch.bfloat16:
+        return x.view(torch.int16).cpu().numpy().view(np.uint16)
+    return x.cpu().numpy()
+
+
+@dataclasses.dataclass
+class Stats:
+    decisions: int = 0
+    flagged: int = 0
+    flagged_mismatch: int = 0
+    unflagged_mismatch: int = 0
+    max_dlw: float = 0.0
+    max_rel_lse: float = 0.0
+    max_dlogp: float = 0.0
+    max_rel_ess: float = 0.0
+    verify_rows_checked: int = 0
+    kv_calls_checked: int = 0
+    resample_events: int = 0
+    sps_checked: int = 0
+    notes: list = dataclasses.field(default_factory=list)
+
+    def decision(self, same: bool, margin: float, what: str):
+        self.decisions += 1
+        flagged = margin < MARGIN
+        self.flagged += int(flagged)
+        if not same:
+            if flagged:
+                self.flagged_mismatch += 1
+            else:
+                self.unflagged_mismatch += 1
+                if len(self.notes) < 20:
+                    self.notes.append("%s (margin %.3g)" % (what, margin))
+        return same or flagged
+
+    def assert_ok(self):
+        msg = ("decisions=%d flagged=%d flagged_mismatch=%d unflagged_mismatch=%d max_dlw=%.3g "
+               "max_rel_lse=%.3g max_dlogp=%.3g max_rel_ess=%.3g notes=%s" % (
+                   self.decisions, self.flagged, self.flagged_mismatch, self.unflagged_mismatch,
+                   self.max_dlw, self.max_rel_lse, self.max_dlogp, self.max_rel_ess, self.notes[:5]))
+        assert self.unflagged_mismatch == 0, msg
+        assert self.max_dlw <= TOL_LW, msg
+        assert self.max_rel_lse <= TOL_LSE_REL, msg
+        assert self.max_dlogp <= TOL_LOGP, msg
+        assert self.max_rel_ess <= TOL_ESS_REL, msg
+        return msg
+
+
+class Pipeline:
+    """GPU state of one configuration plus the lock-step checks."""
+
+    def __init__(self, cfg: Config, sample: int | None = None, sps_sample: int | None = None,
+                 device: str = "cuda", check: bool = True):
+        self.cfg = cfg
+        self.dev = device
+        self.sample = sample
+        self.sps_sample = sps_sample
+        self.check = check
+        self.stats = Stats()
+        base = synth.zipf_base(cfg, device) if cfg.target_kind == "zipf" else None
+        self.sets = []
+        for s in range(cfg.n_sets):
+            t, d = synth.make_logit_set(cfg, s, device, base)
+            self.sets.append((t, d, synth.sample_draft_tokens(cfg, d, s)))
+        B, N, K, S = cfg.B, cfg.N, cfg.K, cfg.S
+        i32 = dict(dtype=torch.int32, device=device)
+        f32 = dict(dtype=torch.float32, device=device)
+        self.lw = torch.zeros(S, **f32)
+        kv = synth.initial_kv(cfg)
+        self.tables = torch.from_numpy(kv["tables"]).to(device)
+        self.rc = torch.from_numpy(kv["refcounts"]).to(device)
+        self.free_list = torch.from_numpy(kv["free_list"]).to(device)
+        self.free_top = torch.from_numpy(kv["free_top"]).to(device)
+        self.L = int(kv["seq_len"])
+        self.ws_v = sm.alloc_workspace(sm.OP_VERIFY_SMC, B, N, K, cfg.V, device=device)
+        self.ws_kv = sm.alloc_workspace(sm.OP_KV, B, N, P=cfg.pool, device=device)
+        self.tokens = torch.zeros((S, K + 1), **i32)
+        self.num = torch.zeros(S, **i32)
+        self.logp = torch.zeros((S, K + 1), **f32)
+        self.logq = torch.zeros((S, max(K, 1)), **f32)
+        self.lse = torch.zeros((S, 2 * K + 1), **f32)
+        self.status = torch.zeros(1, **i32)
+        self.anc = torch.zeros((B, N), **i32)
+        self.ess = torch.zeros(B, **f32)
+        self.resampled = torch.zeros(B, **i32)
+        self.cow = torch.zeros((S, 3), **i32)
+        self.cow_count = torch.zeros(1, **i32)
+        if cfg.sps:
+            self.ws_sps = sm.alloc_workspace(sm.OP_VERIFY_SPS, B, 1, K, cfg.V, device=device)
+            self.sps_tokens = torch.zeros((B, K + 1), **i32)
+            self.sps_num = torch.zeros(B, **i32)
+            self.sps_logp = torch.zeros((B, K + 1), **f32)
+            self.sps_status = torch.zeros(1, **i32)
+        self.seed = cfg.rng_seed
+        self.T32 = float(np.float32(cfg.temperature))
+        self.tau32 = float(np.float32(cfg.tau))
+        self.alpha32 = float(np.float32(cfg.alpha))
+        # reserve the first round's K+1 slots (identity ancestors)
+        ident = torch.arange(N, **i32).repeat(B, 1)
+        self._kv(ident, torch.zeros(B, **i32), t=-1)
+
+    # ------------------------------------------------------------------ KV
+    def _kv_snapshot(self):
+        return (self.tables.cpu().numpy(), self.rc.cpu().numpy(), self.free_list.cpu().numpy(),
+                int(self.free_top.cpu()[0]))
+
+    def _kv(self, anc, res, t):
+        cfg = self.cfg
+        before = self._kv_snapshot() if self.check else None
+        self.status.zero_()
+        sm.kv_reassign(anc, res, cfg.B, cfg.N, self.tables, cfg.block_size, self.L, cfg.K + 1,
+                       self.rc, self.free_list, self.free_top, self.cow, self.cow_count,
+                       self.status, self.ws_kv)
+        if not self.check:
+            return
+        torch.cuda.synchronize()
+        T0, rc0, fl0, top0 = before
+        o = oracle.kv_reassign(anc.cpu().numpy().reshape(cfg.B, cfg.N), res.cpu().numpy(), T0,
+                               cfg.block_size, self.L, cfg.K + 1, rc0, fl0, top0)
+        st = int(self.status.cpu()[0])
+        top = int(self.free_top.cpu()[0])
+        ncow = int(self.cow_count.cpu()[0])
+        ok = (st == o["status"] and top == o["free_top"] and ncow == o["cow_count"]
+              and np.array_equal(self.tables.cpu().numpy(), o["tables"])
+              and np.array_equal(self.rc.cpu().numpy(), o["refcounts"])
+              and np.array_equal(self.free_list.cpu().numpy()[:top], o["free_list"][:top])
+              and np.array_equal(self.cow.cpu().numpy()[:ncow], o["cow"]))
+        self.stats.decision(ok, math.inf, "kv state at t=%d" % t)
+        self.stats.kv_calls_checked += 1
+
+    # ------------------------------------------------------------------ round
+    def _select(self, t, S, k):
+        if k is None or k >= S:
+            return np.arange(S, dtype=np.int64)
+        r = np.random.default_rng(1000003 * (t + 7))
+        pick = set(r.choice(S, size=k, replace=False).tolist())
+        pick.add(0 if t % 2 == 0 else S - 1)
+        return np.array(sorted(pick), dtype=np.int64)
+
+    def round(self, t: int):
+        cfg = self.cfg
+        B, N, K, S = cfg.B, cfg.N, cfg.K, cfg.S
+        tgt, drf, toks = self.sets[t % cfg.n_sets]
+        lw_before = self.lw.clone() if self.check else None
+        self.status.zero_()
+        sm.verify(tgt, drf, toks, B, N, K, cfg.V, cfg.temperature, cfg.alpha, sm.MODE_SMC,
+                  self.seed, t, self.tokens, self.status, self.ws_v, log_weights=self.lw,
+                  out_num_tokens=self.num, out_logp=self.logp, out_logq=self.logq,
+                  out_lse=self.lse)
+        lw_post = self.lw.clone() if self.check else None
+        st_verify = self.status.clone()
+        sm.resample(self.lw.view(B, N), B, N, cfg.tau, self.seed, t, self.anc, self.ess,
+                    self.resampled, self.status)
+        if cfg.sps:
+            self.sps_status.zero_()
+            sm.verify(tgt, drf, toks, B, 1, K, cfg.V, cfg.temperature, 1.0, sm.MODE_SPS,
+                      self.seed, t, self.sps_tokens, self.sps_status, self.ws_sps,
+                      out_num_tokens=self.sps_num, out_logp=self.sps_logp, seq_step=N)
+        if self.check:
+            torch.cuda.synchronize()
+            self._check_verify(t, tgt, drf, toks, lw_before, lw_post, int(st_verify.cpu()[0]))
+            self._check_resample(t, lw_post)
+            if cfg.sps:
+                self._check_sps(t, tgt, drf, toks)
+        self.L += K + 1
+        self._kv(self.anc, self.resampled, t)
+
+    def _check_verify(self, t, tgt, drf, toks, lw_before, lw_post, status):
+        cfg = self.cfg
+        K = cfg.K
+        sel = self._select(t, cfg.S, self.sample)
+        selt = torch.from_numpy(sel).to(self.dev)
+        x = toks[selt].cpu().numpy()
+        o = oracle.verify_smc(host_logits(tgt[selt]), host_logits(drf[selt]) if K else
+                              np.zeros((len(sel), 0, cfg.V), np.float32 if cfg.dtype == "f32"
+                                       else np.uint16),
+                              x, self.T32, self.alpha32, self.seed, t,
+                              lw_before[selt].cpu().numpy(), rng_index=sel)
+        st = self.stats
+        assert status == o["status"], (status, o["status"])
+        gt = self.tokens[selt].cpu().numpy()
+        assert np.array_equal(gt[:, :K], x)
+        assert np.all(self.num[selt].cpu().numpy() == K + 1)
+        glw = lw_post[selt].cpu().numpy().astype(np.float64)
+        glse = self.lse[selt].cpu().numpy().astype(np.float64)
+        glp = self.logp[selt].cpu().numpy().astype(np.float64)
+        glq = self.logq[selt].cpu().numpy()[:, :K].astype(np.float64)
+        for i, g in enumerate(sel):
+            same = gt[i, K] == o["tokens"][i, K]
+            st.decision(same, o["margin"][i], "bonus g=%d t=%d" % (g, t))
+            if same:
+                st.max_dlw = max(st.max_dlw, abs(glw[i] - o["lw"][i]))
+                st.max_dlogp = max(st.max_dlogp, abs(glp[i, K] - o["logp"][i, K]) /
+                                   max(1.0, abs(o["logp"][i, K])))
+        rel = np.abs(glse - o["lse"]) / np.maximum(np.abs(o["lse"]), 1e-30)
+        st.max_rel_lse = max(st.max_rel_lse, float(rel.max()))
+        if K:
+            d = np.abs(glp[:, :K] - o["logp"][:, :K]) / np.maximum(1.0, np.abs(o["logp"][:, :K]))
+            st.max_dlogp = max(st.max_dlogp, float(d.max()))
+            d = np.abs(glq - o["logq"]) / np.maximum(1.0, np.abs(o["logq"]))
+            st.max_dlogp = max(st.max_dlogp, float(d.max()))
+        st.verify_rows_checked += len(sel) * (2 * K + 1)
+
+    def _check_resample(self, t, lw_post):
+        cfg = self.cfg
+        B, N = cfg.B, cfg.N
+        lwp = lw_post.cpu().numpy().reshape(B, N)
+        o = oracle.resample(lwp, self.tau32, self.seed, t)
+        st = self.stats
+        gres = self.resampled.cpu().numpy()
+        ganc = self.anc.cpu().numpy()
+        gess = self.ess.cpu().numpy().astype(np.float64)
+        glw = self.lw.cpu().numpy().reshape(B, N)
+        for b in range(B):
+            if o["ess"][b] > 0:
+                st.max_rel_ess = max(st.max_rel_ess, abs(gess[b] - o["ess"][b]) / o["ess"][b])
+            same = gres[b] == o["resampled"][b]
+            st.decision(same, o["margin_ess"][b], "resample decision b=%d t=%d" % (b, t))
+            if not same:
+                continue
+            if gres[b]:
+                st.resample_events += 1
+                assert np.all(glw[b] == 0.0)
+                for i in range(N):
+                    st.decision(ganc[b, i] == o["ancestors"][b, i], o["margin_pos"][b, i],
+                                "ancestor b=%d i=%d t=%d" % (b, i, t))
+            else:
+                assert np.array_equal(ganc[b], np.arange(N))
+                assert np.array_equal(glw[b], lwp[b])
+
+    def _check_sps(self, t, tgt, drf, toks):
+        cfg = self.cfg
+        K, N = cfg.K, cfg.N
+        selb = self._select(t, cfg.B, self.sps_sample)
+        src = torch.from_numpy(selb * N).to(self.dev)
+        o = oracle.verify_sps(host_logits(tgt[src]), host_logits(drf[src]), toks[src].cpu().numpy(),
+                              self.T32, self.seed, t, rng_index=selb)
+        gt = self.sps_tokens.cpu().numpy()[selb]
+        gn = self.sps_num.cpu().numpy()[selb]
+        assert int(self.sps_status.cpu()[0]) == o["status"]
+        for i, b in enumerate(selb):
+            same = gn[i] == o["num_tokens"][i] and np.array_equal(gt[i], o["tokens"][i])
+            margin = min(o["margin_accept"][i], o["margin_final"][i])
+            self.stats.decision(same, margin, "sps b=%d t=%d" % (b, t))
+            self.stats.sps_checked += 1
+
+
+def run(cfg: Config, iters: int, sample=None, sps_sample=None, label=""):
+    t0 = time.time()
+    p = Pipeline(cfg, sample=sample, sps_sample=sps_sample)
+    print("[%s%s] setup %.1fs" % (cfg.name, label, time.time() - t0), flush=True)
+    for t in range(iters):
+        p.round(t)
+        if (t + 1) % max(1, iters // 8) == 0 or t + 1 == iters:
+            print("[%s%s] round %d/%d  %.1fs  decisions=%d flagged=%d unflagged_mismatch=%d" % (
+                cfg.name, label, t + 1, iters, time.time() - t0, p.stats.decisions, p.stats.flagged,
+                p.stats.unflagged_mismatch), flush=True)
+    msg = p.stats.assert_ok()
+    print("[%s%s] OK %s" % (cfg.name, label, msg), flush=True)
+    return p

@@ -1,0 +1,112 @@
+"""The C-ABI library loads, exports every entry point include/smcsd.h declares, and rejects
+bad arguments on the host before any launch (CPU only: no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import smc_verification_resampling_amd as sm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "smcsd.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(smcsd_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sm.LIB_PATH):
+        import __graft_entry__  # noqa: F401
+        from smc_verification_resampling_amd import build
+        build.build()
+    return sm.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert set(names) == set(sm.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", sm.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (smcsd_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+
+
+def test_gfx950_code_object_present(lib):
+    data = open(sm.LIB_PATH, "rb").read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in data
+
+
+def test_version_and_status_strings(lib):
+    assert lib.smcsd_version() == 1
+    assert sm.status_string(0) == "ok"
+    assert "workspace" in sm.status_string(-4)
+    assert "pool" in sm.status_string(sm.ST_NOSPACE)
+
+
+def test_workspace_sizes(lib):
+    v = sm.workspace_bytes(sm.OP_VERIFY_SMC, 32, 16, 4, 128256)
+    assert v >= 32 * 16 * 9 * 16 * 8           # (max, sum) pair per row and 8192-element chunk
+    assert sm.workspace_bytes(sm.OP_VERIFY_SPS, 16, 1, 8, 128256) > 0
+    assert sm.workspace_bytes(sm.OP_KV, 32, 16, 0, 0, 145920) >= 145920 // 8
+    assert sm.workspace_bytes(sm.OP_VERIFY_SMC, 1, 1, 33, 10) == 0   # K above the limit
+    assert sm.workspace_bytes(sm.OP_KV, 1, 1, 0, 0, 0) == 0
+
+
+def _verify_rc(lib, **kw):
+    a = dict(tgt=ctypes.c_void_p(0x1000), drf=ctypes.c_void_p(0x1000), dtype=1, rs=64, step=1,
+             tok=ctypes.c_void_p(0x1000), B=1, N=1, K=1, V=64, T=1.0, alpha=1.0, mode=0, lse=None,
+             lw=ctypes.c_void_p(0x1000), out=ctypes.c_void_p(0x1000), st=ctypes.c_void_p(0x1000),
+             ws=ctypes.c_void_p(0x1000), wsb=1 << 20)
+    a.update(kw)
+    return lib.smcsd_verify(a["tgt"], a["drf"], a["dtype"], a["rs"], a["step"], a["tok"], a["B"],
+                            a["N"], a["K"], a["V"], a["T"], a["alpha"], a["mode"], 0, 0, a["lse"],
+                            a["lw"], a["out"], None, None, None, None, a["st"], a["ws"], a["wsb"],
+                            None)
+
+
+def test_verify_host_validation(lib):
+    assert _verify_rc(lib, dtype=7) == -2
+    assert _verify_rc(lib, K=33) == -1
+    assert _verify_rc(lib, V=0) == -1
+    assert _verify_rc(lib, rs=10) == -1                       # row stride below V
+    assert _verify_rc(lib, T=0.0) == -1
+    assert _verify_rc(lib, T=float("nan")) == -1
+    assert _verify_rc(lib, tgt=None) == -1
+    assert _verify_rc(lib, tgt=ctypes.c_void_p(0x1001)) == -1  # not element-aligned
+    assert _verify_rc(lib, lw=None) == -1                      # SMC mode needs log-weights
+    assert _verify_rc(lib, wsb=16) == -4
+    assert _verify_rc(lib, ws=None) == -4
+    assert _verify_rc(lib, mode=3) == -1
+    assert _verify_rc(lib, B=0) == 0                            # empty batch: nothing enqueued
+
+
+def test_resample_and_kv_host_validation(lib):
+    p = ctypes.c_void_p(0x1000)
+    assert lib.smcsd_resample(p, 1, 0, 0.5, 0, 0, p, p, p, p, None) == -1
+    assert lib.smcsd_resample(p, 1, 1025, 0.5, 0, 0, p, p, p, p, None) == -1
+    assert lib.smcsd_resample(p, 1, 4, float("inf"), 0, 0, p, p, p, p, None) == -1
+    assert lib.smcsd_resample(p, 0, 4, 0.5, 0, 0, p, p, p, p, None) == 0
+    # capacity: ceil((L + R) / bs) must fit M_cap
+    assert lib.smcsd_kv_reassign(p, p, 1, 4, p, 3, 4, 10, 3, p, p, p, 100, p, p, p, p, 1 << 20,
+                                 None) == -1
+    assert lib.smcsd_kv_reassign(p, p, 1, 4, p, 4, 4, 10, 3, p, p, p, 100, p, p, p, None, 1 << 20,
+                                 None) == -4
+    assert lib.smcsd_kv_reassign(p, p, 0, 4, p, 4, 4, 10, 3, p, p, p, 100, p, p, p, p, 1 << 20,
+                                 None) == 0
+    assert lib.smcsd_philox4x32_10(p, p, -1, p, None) == -1
+    assert lib.smcsd_philox4x32_10(p, p, 0, p, None) == 0
+
+
+def test_binding_refuses_host_tensors(lib):
+    import torch
+    t = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(sm.SmcsdError):
+        sm.philox4x32_10(t.view(1, 4), torch.zeros(2, dtype=torch.int32).view(1, 2), t.view(1, 4))

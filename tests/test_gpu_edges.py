@@ -1,0 +1,294 @@
+"""GPU edge cases, each checked against the oracle through the C ABI."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import smc_verification_resampling_amd as sm
+from tests import gpu_harness as H
+from workloads import configs as C
+from workloads import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+
+
+def _i32(*shape):
+    return torch.zeros(shape, dtype=torch.int32, device="cuda")
+
+
+def _f32(*shape):
+    return torch.zeros(shape, dtype=torch.float32, device="cuda")
+
+
+def _verify_case(target, draft, toks, K, V, T, alpha, seed, step, lw0, row_stride=None):
+    """One SMC verify on the GPU vs the oracle; returns (gpu dict, oracle dict)."""
+    S = toks.shape[0]
+    out = dict(tokens=_i32(S, K + 1), num=_i32(S), logp=_f32(S, K + 1), logq=_f32(S, max(K, 1)),
+               lse=_f32(S, 2 * K + 1), status=_i32(1))
+    lw = torch.tensor(lw0, dtype=torch.float32, device="cuda")
+    ws = sm.alloc_workspace(sm.OP_VERIFY_SMC, S, 1, K, V)
+    sm.verify(target, draft, toks, S, 1, K, V, T, alpha, sm.MODE_SMC, seed, step, out["tokens"],
+              out["status"], ws, log_weights=lw, out_num_tokens=out["num"], out_logp=out["logp"],
+              out_logq=out["logq"], out_lse=out["lse"], row_stride=row_stride)
+    torch.cuda.synchronize()
+    rs = V if row_stride is None else row_stride
+    th = H.host_logits(target).reshape(S, K + 1, rs)[:, :, :V]
+    dh = H.host_logits(draft).reshape(S, K, rs)[:, :, :V] if K else \
+        np.zeros((S, 0, V), th.dtype)
+    o = oracle.verify_smc(np.ascontiguousarray(th), np.ascontiguousarray(dh),
+                          toks.cpu().numpy(), float(np.float32(T)), float(np.float32(alpha)), seed,
+                          step, np.asarray(lw0, np.float32))
+    g = {k: v.cpu().numpy() for k, v in out.items()}
+    g["lw"] = lw.cpu().numpy()
+    return g, o
+
+
+def _assert_verify_parity(g, o, K):
+    assert int(g["status"][0]) == o["status"]
+    assert np.array_equal(g["tokens"][:, :K], o["tokens"][:, :K])
+    for i in range(len(o["lw"])):
+        if o["margin"][i] >= H.MARGIN:
+            assert g["tokens"][i, K] == o["tokens"][i, K], (i, o["margin"][i])
+            assert abs(g["lw"][i] - o["lw"][i]) <= H.TOL_LW
+    fin = np.isfinite(o["lse"])
+    assert np.all(np.abs(g["lse"][fin] - o["lse"][fin]) <= H.TOL_LSE_REL * np.abs(o["lse"][fin]))
+
+
+@pytest.mark.parametrize("dtype,V,pad", [("bf16", 1001, 0), ("bf16", 1001, 3), ("f32", 37, 2),
+                                         ("bf16", 1, 0), ("f32", 5, 0), ("bf16", 16385, 1),
+                                         ("f32", 8193, 0), ("bf16", 32768, 0)])
+def test_ragged_and_misaligned_rows(dtype, V, pad):
+    """Rows whose length or stride is not a multiple of the 16-byte vector (so rows start
+    misaligned), single-element rows, and tiles split one element past a boundary."""
+    K, S = 3, 5
+    rs = V + pad
+    g = torch.Generator(device="cuda").manual_seed(V * 7 + pad)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tgt = (2 * torch.randn((S, K + 1, rs), generator=g, device="cuda")).to(dt)
+    drf = (tgt[:, :K].float() + torch.randn((S, K, rs), generator=g, device="cuda")).to(dt)
+    toks = torch.randint(0, V, (S, K), generator=g, device="cuda", dtype=torch.int32)
+    gg, o = _verify_case(tgt, drf, toks, K, V, 0.8, 1.0, 77, 5, np.zeros(S), row_stride=rs)
+    _assert_verify_parity(gg, o, K)
+
+
+@pytest.mark.parametrize("K", [0, 1, 32])
+def test_k_extremes(K):
+    S, V = 4, 3000
+    g = torch.Generator(device="cuda").manual_seed(K + 11)
+    tgt = torch.randn((S, K + 1, V), generator=g, device="cuda").to(torch.bfloat16)
+    drf = torch.randn((S, max(K, 1), V), generator=g, device="cuda").to(torch.bfloat16)[:, :K]
+    drf = drf.contiguous()
+    toks = torch.randint(0, V, (S, K), generator=g, device="cuda", dtype=torch.int32)
+    gg, o = _verify_case(tgt, drf, toks, K, V, 1.0, 4.0, 3, 9, np.full(S, 0.25))
+    _assert_verify_parity(gg, o, K)
+
+
+def test_masked_empty_and_nan_rows():
+    S, K, V = 4, 2, 700
+    tgt = torch.zeros((S, K + 1, V), dtype=torch.float32, device="cuda")
+    drf = torch.zeros((S, K, V), dtype=torch.float32, device="cuda")
+    tgt[0, K, :] = -math.inf
+    tgt[0, K, 123] = 2.0                    # one-hot bonus row
+    tgt[1, K, :] = -math.inf
+    tgt[1, K, [5, 600]] = 0.0              # two tokens, everything else masked
+    toks = torch.zeros((S, K), dtype=torch.int32, device="cuda")
+    gg, o = _verify_case(tgt, drf, toks, K, V, 1.0, 1.0, 1, 2, np.zeros(S))
+    _assert_verify_parity(gg, o, K)
+    assert gg["tokens"][0, K] == 123 and gg["tokens"][1, K] in (5, 600)
+    # an all -inf draft row -> EMPTY_ROW; a NaN -> NAN_INPUT (same bits on both sides)
+    drf[2, 1, :] = -math.inf
+    tgt[3, 0, 17] = math.nan
+    gg, o = _verify_case(tgt, drf, toks, K, V, 1.0, 1.0, 1, 2, np.zeros(S))
+    assert int(gg["status"][0]) == o["status"] == sm.ST_EMPTY_ROW | sm.ST_NAN_INPUT
+
+
+def test_bad_token_flagged_not_faulting():
+    S, K, V = 2, 2, 100
+    tgt = torch.zeros((S, K + 1, V), dtype=torch.float32, device="cuda")
+    drf = torch.zeros((S, K, V), dtype=torch.float32, device="cuda")
+    toks = torch.tensor([[0, 1], [V, -1]], dtype=torch.int32, device="cuda")
+    st = _i32(1)
+    ws = sm.alloc_workspace(sm.OP_VERIFY_SMC, S, 1, K, V)
+    sm.verify(tgt, drf, toks, S, 1, K, V, 1.0, 1.0, sm.MODE_SMC, 0, 0, _i32(S, K + 1), st, ws,
+              log_weights=_f32(S))
+    torch.cuda.synchronize()
+    assert int(st.cpu()[0]) & sm.ST_BAD_INPUT
+
+
+def test_philox_bit_exact_against_oracle():
+    rng = np.random.default_rng(4)
+    n = 4096
+    ctr = rng.integers(0, 2**32, (n, 4), dtype=np.uint64).astype(np.uint32)
+    key = rng.integers(0, 2**32, (n, 2), dtype=np.uint64).astype(np.uint32)
+    out = _i32(n, 4)
+    sm.philox4x32_10(torch.from_numpy(ctr.view(np.int32)).cuda(),
+                     torch.from_numpy(key.view(np.int32)).cuda(), out)
+    got = out.cpu().numpy().view(np.uint32)
+    ref = np.stack([oracle.philox4x32_10(c, k) for c, k in zip(ctr, key)])
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 64, 1000, 1024])
+def test_resample_particle_counts(N):
+    B = 7
+    rng = np.random.default_rng(N)
+    lw0 = rng.normal(0, 2.0, (B, N)).astype(np.float32)
+    lw0[1] = 0.0                            # equal weights: ESS = N exactly
+    lw0[2] = -np.inf
+    lw0[2, N // 2] = 0.0                    # one live particle
+    for tau in (0.5, 1.5):
+        lw = torch.from_numpy(lw0.copy()).cuda()
+        anc, ess, res, st = _i32(B, N), _f32(B), _i32(B), _i32(1)
+        sm.resample(lw, B, N, tau, 99, 3, anc, ess, res, st)
+        torch.cuda.synchronize()
+        o = oracle.resample(lw0, float(np.float32(tau)), 99, 3)
+        assert int(st.cpu()[0]) == o["status"]
+        gres, ganc = res.cpu().numpy(), anc.cpu().numpy()
+        for b in range(B):
+            if o["margin_ess"][b] >= H.MARGIN:
+                assert gres[b] == o["resampled"][b]
+                if gres[b]:
+                    ok = o["margin_pos"][b] >= H.MARGIN
+                    assert np.array_equal(ganc[b][ok], o["ancestors"][b][ok])
+            assert abs(ess.cpu().numpy()[b] - o["ess"][b]) <= 1e-6 * o["ess"][b]
+
+
+def test_resample_degenerate_weights():
+    lw0 = np.full((2, 8), -np.inf, np.float32)
+    lw0[1, 3] = np.nan
+    lw = torch.from_numpy(lw0).cuda()
+    anc, ess, res, st = _i32(2, 8), _f32(2), _i32(2), _i32(1)
+    sm.resample(lw, 2, 8, 0.5, 1, 1, anc, ess, res, st)
+    torch.cuda.synchronize()
+    assert int(st.cpu()[0]) == sm.ST_DEGENERATE_WEIGHTS
+    assert np.array_equal(anc.cpu().numpy(), np.tile(np.arange(8), (2, 1)))
+    assert np.all(res.cpu().numpy() == 0)
+
+
+def _kv_gpu(anc, res, B, N, T, bs, L, R, rc, fl, top):
+    tables = torch.from_numpy(T.copy()).cuda()
+    rcd = torch.from_numpy(rc.copy()).cuda()
+    fld = torch.from_numpy(fl.copy()).cuda()
+    topd = torch.tensor([top], dtype=torch.int32, device="cuda")
+    cow, ncow, st = _i32(B * N, 3), _i32(1), _i32(1)
+    ws = sm.alloc_workspace(sm.OP_KV, B, N, P=rc.size)
+    sm.kv_reassign(torch.from_numpy(anc).cuda(), torch.from_numpy(res).cuda(), B, N, tables, bs, L,
+                   R, rcd, fld, topd, cow, ncow, st, ws)
+    torch.cuda.synchronize()
+    nbits = 4 * ((rc.size + 31) // 32)
+    assert int(ws[:nbits].sum().cpu()) == 0    # the freed-block bitmap is left zeroed
+    n = int(ncow.cpu()[0])
+    return dict(tables=tables.cpu().numpy(), refcounts=rcd.cpu().numpy(),
+                free_list=fld.cpu().numpy(), free_top=int(topd.cpu()[0]), cow=cow.cpu().numpy()[:n],
+                cow_count=n, status=int(st.cpu()[0]))
+
+
+def _kv_equal(g, o):
+    top = o["free_top"]
+    return (g["status"] == o["status"] and g["free_top"] == top and g["cow_count"] == o["cow_count"]
+            and np.array_equal(g["tables"], o["tables"])
+            and np.array_equal(g["refcounts"], o["refcounts"])
+            and np.array_equal(g["free_list"][:top], o["free_list"][:top])
+            and np.array_equal(g["cow"], o["cow"]))
+
+
+@pytest.mark.parametrize("shared", [False, True])
+@pytest.mark.parametrize("N", [1, 5, 128, 1024])
+def test_kv_random_rounds(shared, N):
+    """Random (also unsorted) ancestor maps over several rounds, bit-exact vs the oracle."""
+    B, bs, K, ctx0, rounds = 3, 4, 2, 10, 6
+    R = K + 1
+    M = math.ceil((ctx0 + (rounds + 1) * R) / bs)
+    cfg = C.C1.scaled(B=B, N=N, K=K, ctx0=ctx0, block_size=bs, shared_prefix=shared,
+                      iters=rounds)
+    kv = synth.initial_kv(cfg)
+    T, rc, fl, top, L = kv["tables"], kv["refcounts"], kv["free_list"], int(kv["free_top"][0]), ctx0
+    assert T.shape[1] == M
+    rng = np.random.default_rng(N * 3 + shared)
+    ident = np.tile(np.arange(N, dtype=np.int32), (B, 1))
+    o = oracle.kv_reassign(ident, np.zeros(B, np.int32), T, bs, L, R, rc, fl, top)
+    g = _kv_gpu(ident, np.zeros(B, np.int32), B, N, T, bs, L, R, rc, fl, top)
+    assert _kv_equal(g, o)
+    for r in range(rounds):
+        T, rc, fl, top = o["tables"], o["refcounts"], o["free_list"], o["free_top"]
+        L += R
+        anc = rng.integers(0, N, (B, N)).astype(np.int32)
+        if r % 2 == 0:
+            anc.sort(axis=1)
+        res = (rng.random(B) < 0.7).astype(np.int32)
+        o = oracle.kv_reassign(anc, res, T, bs, L, R, rc, fl, top)
+        g = _kv_gpu(anc, res, B, N, T, bs, L, R, rc, fl, top)
+        assert _kv_equal(g, o), r
+
+
+def test_kv_nospace_and_bad_ancestor():
+    B, N, bs, M = 1, 2, 4, 6
+    cfg = C.C1.scaled(B=B, N=N, K=8, ctx0=4, block_size=bs, iters=0)
+    kv = synth.initial_kv(cfg)
+    P = 5
+    T = kv["tables"][:, :M].copy()
+    rc = np.zeros(P, np.int32)
+    rc[[0, 1]] = 1
+    fl = np.arange(P - 1, -1, -1, dtype=np.int32)
+    ident = np.tile(np.arange(N, dtype=np.int32), (B, 1))
+    o = oracle.kv_reassign(ident, np.zeros(B, np.int32), T, bs, 4, 9, rc, fl, 3)
+    g = _kv_gpu(ident, np.zeros(B, np.int32), B, N, T, bs, 4, 9, rc, fl, 3)
+    assert o["status"] == sm.ST_NOSPACE and _kv_equal(g, o)
+    bad = np.array([[0, 7]], np.int32)
+    g = _kv_gpu(bad, np.ones(B, np.int32), B, N, T, bs, 4, 0, rc, fl, 3)
+    assert g["status"] & sm.ST_BAD_INPUT
+    assert np.array_equal(g["tables"], T)
+
+
+def test_empty_batch_is_noop():
+    st = _i32(1)
+    sm.verify(_f32(1, 2, 4), _f32(1, 1, 4), _i32(1, 1), 0, 4, 1, 4, 1.0, 1.0, sm.MODE_SMC, 0, 0,
+              _i32(1, 2), st, sm.alloc_workspace(sm.OP_VERIFY_SMC, 1, 1, 1, 4),
+              log_weights=_f32(1))
+    torch.cuda.synchronize()
+    assert int(st.cpu()[0]) == 0
+
+
+def _final_state(p):
+    return [x.cpu().numpy().copy() for x in (p.lw, p.tables, p.rc, p.free_list, p.free_top,
+                                             p.tokens, p.anc)]
+
+
+def test_determinism_and_resume():
+    """Two runs are bit-identical; 6 rounds + copy of the state + 6 rounds equals 12 rounds
+    straight (the counter-based RNG depends only on seed, round and index)."""
+    cfg = C.downsized(C.C3, B=2, V=50000, iters=12)
+    a = H.Pipeline(cfg, check=False)
+    for t in range(12):
+        a.round(t)
+    b = H.Pipeline(cfg, check=False)
+    for t in range(12):
+        b.round(t)
+    torch.cuda.synchronize()
+    for x, y in zip(_final_state(a), _final_state(b)):
+        assert np.array_equal(x, y)
+    c = H.Pipeline(cfg, check=False)
+    for t in range(6):
+        c.round(t)
+    torch.cuda.synchronize()
+    saved = {k: getattr(c, k).clone() for k in ("lw", "tables", "rc", "free_list", "free_top")}
+    L = c.L
+    d = H.Pipeline(cfg, check=False)
+    for k, v in saved.items():
+        getattr(d, k).copy_(v)
+    d.L = L
+    for t in range(6, 12):
+        d.round(t)
+    torch.cuda.synchronize()
+    for x, y in zip(_final_state(a), _final_state(d)):
+        assert np.array_equal(x, y)
