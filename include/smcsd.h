@@ -85,8 +85,8 @@ const char *smcsd_status_string(int code);
  * Device workspace bytes for one call.
  *   SMCSD_OP_VERIFY_SMC / _SPS: B, N, K, V as passed to smcsd_verify (P ignored).
  *   SMCSD_OP_KV: B, N and the pool size P (K, V ignored).  The KV workspace must be
- *   zero-filled before its first use; every smcsd_kv_reassign call leaves the part that
- *   must start at zero (its freed-block bitmap) zeroed again.
+ *   zero-filled before its first use; every smcsd_kv_reassign call leaves the parts that
+ *   must start at zero (its freed-block bitmap and arrival counter) zeroed again.
  * Returns 0 for invalid sizes.
  */
 size_t smcsd_workspace_bytes(int op, int B, int N, int K, int V, int64_t P);
@@ -130,7 +130,7 @@ size_t smcsd_workspace_bytes(int op, int B, int N, int K, int V, int64_t P);
  * [B*N], out_logp [B*N, K+1], out_logq [B*N, K], out_lse [B*N, 2K+1] (target rows
  * 0..K then draft rows 0..K-1), all nullable.  log_weights [B*N] fp32 in/out
  * (required in SMC mode).
- * Limits: 0 <= K <= 32, V >= 1, temperature finite > 0, alpha finite.
+ * Limits: 0 <= K <= 32, 1 <= V <= 2^24, temperature finite > 0, alpha finite.
  * B*N = 0 is a no-op.  workspace: smcsd_workspace_bytes(SMCSD_OP_VERIFY_*, ...).
  */
 int smcsd_verify(const void *target_logits, const void *draft_logits, int dtype,
@@ -175,9 +175,10 @@ int smcsd_resample(float *log_weights, int B, int N, float tau, uint64_t seed, u
  * before any decrement); blocks reaching 0 are freed; new table i = old table
  * ancestors[b,i].  The freed blocks of the call are pushed in descending id order.
  * Phase 2, all prompts: reserve positions [seq_len, seq_len + reserve_tokens).  From
- * the post-phase-1 state, a sequence whose partial tail block (slot
- * floor(seq_len/block_size) when seq_len mod block_size != 0) has refcount > 1 and is
- * also held by a higher-index sequence of its prompt does copy-on-write: it pops a
+ * the post-phase-1 tables, a sequence whose partial tail block (slot
+ * floor(seq_len/block_size) when seq_len mod block_size != 0) is also held by a
+ * higher-index sequence of its prompt (the highest holder keeps the block) does
+ * copy-on-write: it pops a
  * fresh block d, the old block loses one reference, and (old, d, seq_len mod
  * block_size) is appended to cow [B*N, 3] - the caller copies that many token
  * entries of KV data from old to d before writing the round.  Then every slot in
@@ -190,7 +191,7 @@ int smcsd_resample(float *log_weights, int B, int N, float tau, uint64_t seed, u
  * (previous seq_len + K+1).
  * Limits: 1 <= N <= 1024; ceil((seq_len+reserve_tokens)/block_size) <= M_cap.
  * workspace: smcsd_workspace_bytes(SMCSD_OP_KV, B, N, 0, 0, P), zero-filled before
- * first use (each call leaves its freed-block bitmap zeroed again).
+ * first use (each call leaves its freed-block bitmap and counter zeroed again).
  */
 int smcsd_kv_reassign(const int32_t *ancestors, const int32_t *resampled, int B, int N,
                       int32_t *block_tables, int M_cap, int block_size, int64_t seq_len,

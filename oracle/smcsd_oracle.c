@@ -468,10 +468,11 @@ int orc_resample(const float *lw_in, int B, int N, double tau, uint64_t seed, ui
 /*   then T'_i = T_{a_i} (slot values only - no KV data moves).                 */
 /* Freed blocks of the whole call are pushed in descending id order, so the next */
 /* pops return ascending ids.                                                    */
-/* Phase 2, all prompts: reserve positions [L, L+R).  With the state after phase */
-/* 1, a sequence whose partial tail block (slot floor(L/bs), when L mod bs != 0) */
-/* has rc > 1 and is also held by a higher-index sequence of the same prompt     */
-/* does copy-on-write: pop d, rc[old] -= 1, rc[d] = 1, T'[g][slot] = d, and emit */
+/* Phase 2, all prompts: reserve positions [L, L+R).  With the tables after     */
+/* phase 1, a sequence whose partial tail block (slot floor(L/bs), when L mod bs */
+/* != 0) is also held by a higher-index sequence of the same prompt (so the     */
+/* block is shared: the highest holder keeps it) does copy-on-write: pop d,     */
+/* rc[old] -= 1, rc[d] = 1, T'[g][slot] = d, and emit                           */
 /* (old, d, L mod bs) - the caller copies those L mod bs token entries.  Then    */
 /* every slot in [ceil(L/bs), ceil((L+R)/bs)) pops a fresh block with rc = 1.     */
 /* Pops run in ascending (sequence, slot) order.  An empty stack sets NOSPACE    */
@@ -536,7 +537,7 @@ int orc_kv_reassign(const int32_t *ancestors, const int32_t *resampled, int B, i
         for (int g = 0; g < S; ++g) {
             int b = g / N;
             int32_t blk = tables[(int64_t)g * M_cap + ts];
-            if (blk < 0 || rc[blk] <= 1) continue;
+            if (blk < 0) continue;
             for (int h = g + 1; h < (b + 1) * N; ++h)
                 if (tables[(int64_t)h * M_cap + ts] == blk) {
                     needs_cow[g] = 1;

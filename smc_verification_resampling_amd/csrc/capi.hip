@@ -41,12 +41,12 @@ size_t smcsd_workspace_bytes(int op, int B, int N, int K, int V, int64_t P) {
   if (B < 0 || N < 0) return 0;
   const int64_t S = (int64_t)B * N;
   if (op == SMCSD_OP_VERIFY_SMC || op == SMCSD_OP_VERIFY_SPS) {
-    if (K < 0 || K > kMaxK || V < 1) return 0;
+    if (K < 0 || K > kMaxK || V < 1 || V > kMaxV) return 0;
     return verify_ws_layout(S, K, V, op == SMCSD_OP_VERIFY_SPS ? 1 : 0).total;
   }
   if (op == SMCSD_OP_KV) {
     if (P < 1) return 0;
-    return kv_ws_layout(S, P).total;
+    return kv_ws_layout(B, S, P).total;
   }
   return 0;
 }
@@ -59,7 +59,8 @@ int smcsd_verify(const void *target_logits, const void *draft_logits, int dtype,
                  int32_t *status, void *workspace, size_t workspace_bytes, void *stream) {
   if (dtype != SMCSD_DTYPE_F32 && dtype != SMCSD_DTYPE_BF16) return SMCSD_EDTYPE;
   if (mode != SMCSD_MODE_SMC && mode != SMCSD_MODE_SPS) return SMCSD_EINVAL;
-  if (B < 0 || N < 0 || K < 0 || K > kMaxK || V < 1 || seq_step < 1) return SMCSD_EINVAL;
+  if (B < 0 || N < 0 || K < 0 || K > kMaxK || V < 1 || V > kMaxV || seq_step < 1)
+    return SMCSD_EINVAL;
   if (row_stride < V) return SMCSD_EINVAL;
   if (!(temperature > 0.0f) || !std::isfinite(temperature) || !std::isfinite(alpha))
     return SMCSD_EINVAL;
@@ -126,7 +127,7 @@ int smcsd_kv_reassign(const int32_t *ancestors, const int32_t *resampled, int B,
   if (!ancestors || !resampled || !block_tables || !refcounts || !free_list || !free_top || !cow ||
       !cow_count || !status)
     return SMCSD_EINVAL;
-  const size_t need = kv_ws_layout((int64_t)B * N, P).total;
+  const size_t need = kv_ws_layout(B, (int64_t)B * N, P).total;
   if (!workspace || workspace_bytes < need) return SMCSD_EWORKSPACE;
   return hip_rc(launch_kv(ancestors, resampled, B, N, block_tables, M_cap, block_size, seq_len,
                           reserve_tokens, refcounts, free_list, free_top, P, cow, cow_count, status,

@@ -57,7 +57,7 @@ template <> struct Elt<SMCSD_DTYPE_F32> {
   __device__ __forceinline__ static float load(const char *row, int64_t v) {
     return reinterpret_cast<const float *>(row)[v];
   }
-  __device__ __forceinline__ static void unpack(const uint4 &w, float (&x)[4]) {
+  __device__ __forceinline__ static void unpack(const uint4 &w, float *x) {
     x[0] = __uint_as_float(w.x);
     x[1] = __uint_as_float(w.y);
     x[2] = __uint_as_float(w.z);
@@ -71,7 +71,7 @@ template <> struct Elt<SMCSD_DTYPE_BF16> {
     return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(row)[v] << 16);
   }
   // bf16 is the upper half of an fp32: widening is a shift or a mask.
-  __device__ __forceinline__ static void unpack(const uint4 &w, float (&x)[8]) {
+  __device__ __forceinline__ static void unpack(const uint4 &w, float *x) {
     x[0] = __uint_as_float(w.x << 16);
     x[1] = __uint_as_float(w.x & 0xFFFF0000u);
     x[2] = __uint_as_float(w.y << 16);
@@ -84,6 +84,28 @@ template <> struct Elt<SMCSD_DTYPE_BF16> {
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 16-byte streaming load that does not keep the line in the caches (the logits are read
+// once per step; a read-only stream measured ~7.0 TB/s this way versus ~6.3 TB/s with
+// ordinary loads on the MI355X).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const uint4 *p) {
+  const u32x4_t r = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+  return make_uint4(r.x, r.y, r.z, r.w);
+}
+
+// -inf in every element of a 16-byte vector (fills the lanes past a row's end)
+template <int DT> struct NegInfVec;
+template <> struct NegInfVec<SMCSD_DTYPE_F32> {
+  __device__ __forceinline__ static uint4 get() {
+    return make_uint4(0xFF800000u, 0xFF800000u, 0xFF800000u, 0xFF800000u);
+  }
+};
+template <> struct NegInfVec<SMCSD_DTYPE_BF16> {
+  __device__ __forceinline__ static uint4 get() {
+    return make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
+  }
+};
 
 // ---------------------------------------------------------------------------------
 // Online log-sum-exp state over raw logits x with scale c = log2(e) / T:

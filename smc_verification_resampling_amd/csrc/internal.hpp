@@ -18,6 +18,7 @@ constexpr int kChunkElemsMin = kChunkElemsF32;  // workspace is sized for the sm
 constexpr int kFinalBlock = 256;
 constexpr int kMaxK = 32;
 constexpr int kMaxN = 1024;
+constexpr int kMaxV = 1 << 24;  // finalize keeps one fp64 term per vocabulary chunk in LDS
 
 inline int chunk_elems(int dtype) { return dtype == 1 ? kChunkElemsBf16 : kChunkElemsF32; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -47,16 +48,22 @@ inline VerifyWs verify_ws_layout(int64_t nseq, int K, int V, int mode) {
 }
 
 // KV workspace: [freed bitmap uint32 x ceil(P/32)][needs_cow int32 x B*N]
+//               [copy-on-write count int32 x B][arrival counter int32]
+// The bitmap and the counter must be zero before a call and are zero after it.
 struct KvWs {
-  size_t bitmap, cow_flags, total;
+  size_t bitmap, cow_flags, cow_per_prompt, done, total;
 };
-inline KvWs kv_ws_layout(int64_t S, int64_t P) {
+inline KvWs kv_ws_layout(int64_t B, int64_t S, int64_t P) {
   KvWs w{};
   size_t off = 0;
   w.bitmap = off;
   off += align256(sizeof(uint32_t) * (size_t)ceil_div(P, 32));
   w.cow_flags = off;
   off += align256(sizeof(int32_t) * (size_t)S);
+  w.cow_per_prompt = off;
+  off += align256(sizeof(int32_t) * (size_t)B);
+  w.done = off;
+  off += align256(sizeof(int32_t));
   w.total = off;
   return w;
 }

@@ -43,7 +43,7 @@ struct RowMap {
 // 0 (their s is 0, or NaN if the chunk held a NaN, which then propagates).
 __device__ __forceinline__ double chunk_term(float2 p, float c, float Mc) {
   if (p.x == kNegInf) return (double)p.y * 0.0;
-  return (double)p.y * exp2((double)__fmul_rn(p.x, c) - (double)Mc);
+  return (double)p.y * (double)fast_exp2(__fmul_rn(p.x, c) - Mc);
 }
 
 // ---------------------------------------------------------------------------------
@@ -92,23 +92,20 @@ __global__ __launch_bounds__(kStreamBlock) void k_lse_partials(RowMap rm, int ns
       const float x[1] = {E::load(row, a1 + tid)};
       lse_update<1>(st, x, c);
     }
+    // body: kStreamUnroll 16-byte vectors per lane in flight, then one max / rescale
+    // for the whole group of kStreamUnroll*EPV elements
     const uint4 *vp = reinterpret_cast<const uint4 *>(row + a0 * E::kBytes);
     for (int64_t v0 = 0; v0 < nvec; v0 += (int64_t)kStreamBlock * kStreamUnroll) {
       uint4 buf[kStreamUnroll];
 #pragma unroll
       for (int u = 0; u < kStreamUnroll; ++u) {
         const int64_t v = v0 + u * kStreamBlock + tid;
-        if (v < nvec) buf[u] = vp[v];
+        buf[u] = v < nvec ? load_stream(vp + v) : NegInfVec<DT>::get();
       }
+      float x[kStreamUnroll * EPV];
 #pragma unroll
-      for (int u = 0; u < kStreamUnroll; ++u) {
-        const int64_t v = v0 + u * kStreamBlock + tid;
-        if (v < nvec) {
-          float x[EPV];
-          E::unpack(buf[u], x);
-          lse_update<EPV>(st, x, c);
-        }
-      }
+      for (int u = 0; u < kStreamUnroll; ++u) E::unpack(buf[u], x + u * EPV);
+      lse_update<kStreamUnroll * EPV>(st, x, c);
     }
     st = lse_block_reduce<kStreamBlock>(st, c, lds);
     if (tid == 0) part[((int64_t)g * R + slot) * chunks + ch] = make_float2(st.m, st.s);
@@ -142,69 +139,134 @@ __device__ __forceinline__ RowNorm row_norm(const float2 *p, int chunks, float c
 }
 
 // Inverse CDF inside one chunk [e0, e1) of a row: the first v whose running sum
-// base + sum_{w<=v} val(w) exceeds target.  val() is evaluated in fp32 and accumulated in
-// fp64.  Thread ranges are contiguous; thread 0 picks the owning range sequentially, then
-// the owner walks it.  If rounding leaves no crossing, the last v with val > 0 in the
-// owner's range (or the chunk) is returned.  Every thread must call it.
-template <int BLOCK, typename ValFn>
+// base + sum_{w<=v} val(w) exceeds target.  The chunk is cut into units of 8 consecutive
+// elements; fn.unit_sum(a, b) evaluates a unit with coalesced 16-byte loads where the row
+// allows it, and the unit sums go to LDS.  One workgroup exclusive scan (fp64) over
+// per-thread runs of units finds the owning thread, which walks its units and then the
+// elements of the one unit that crosses (fn.val, the same fp32 value the unit sum used).
+// Rounding can leave no crossing where the oracle's margin is at rounding level; then the
+// last element with a positive value before the crossing point is returned.  Every thread
+// must call it; the result is returned to every thread.
+constexpr int kMaxUnits = kChunkElemsBf16 / 8;
+
+template <int BLOCK, typename Fn>
+__device__ __forceinline__ int last_positive_in_unit(const Fn &fn, int64_t a, int64_t b) {
+  for (int64_t v = b - 1; v >= a; --v)
+    if (fn.val(v) > 0.0f) return (int)v;
+  return -1;
+}
+
+template <int BLOCK, typename Fn>
 __device__ __forceinline__ int chunk_inverse_cdf(int64_t e0, int64_t e1, double base,
-                                                 double target, ValFn val, double *loc_lds,
-                                                 int *misc_lds) {
+                                                 double target, const Fn &fn, float *usum,
+                                                 double *scan_lds, int *misc) {
   const int tid = threadIdx.x;
-  const int64_t n = e1 - e0;
-  const int64_t per = (n + BLOCK - 1) / BLOCK;
-  const int64_t t0 = min(e1, e0 + tid * per);
-  const int64_t t1 = min(e1, t0 + per);
+  const int nunits = (int)((e1 - e0 + 7) / 8);
+  for (int u = tid; u < nunits; u += BLOCK) {
+    const int64_t a = e0 + 8 * (int64_t)u;
+    usum[u] = fn.unit_sum(a, min(e1, a + 8));
+  }
+  if (tid == 0) {
+    misc[0] = INT_MAX;  // owner thread
+    misc[1] = -1;       // last unit with a positive sum
+    misc[2] = -1;       // result
+  }
+  __syncthreads();
+  const int upt = (nunits + BLOCK - 1) / BLOCK;
+  const int u0 = min(nunits, tid * upt), u1 = min(nunits, u0 + upt);
   double loc = 0.0;
-  int last = -1;
-  for (int64_t v = t0; v < t1; ++v) {
-    const float x = val(v);
+  int lastu = -1;
+  for (int u = u0; u < u1; ++u) {
+    const float x = usum[u];
     loc += (double)x;
-    if (x > 0.0f) last = (int)v;
+    if (x > 0.0f) lastu = u;
   }
-  loc_lds[tid] = loc;
-  if (tid == 0) {
-    misc_lds[0] = -1;  // owner
-    misc_lds[1] = -1;  // chunk-wide last positive
-    misc_lds[2] = -1;  // result
-  }
+  double tot;
+  const double start = base + block_exclusive_scan<double, BLOCK>(loc, scan_lds, &tot);
+  if (u1 > u0 && start + loc > target) atomicMin(&misc[0], tid);
+  if (lastu >= 0) atomicMax(&misc[1], lastu);
   __syncthreads();
-  if (last >= 0) atomicMax(&misc_lds[1], last);
-  if (tid == 0) {
-    double run = base;
-    int owner = -1;
-    for (int t = 0; t < BLOCK; ++t) {
-      if (run + loc_lds[t] > target) {
-        owner = t;
-        break;
+  const int owner = misc[0];
+  if (owner != INT_MAX ? tid == owner : tid == 0) {
+    int pick = -1;
+    int lastu_seen = -1;  // last unit with a positive sum before the crossing
+    if (owner != INT_MAX) {
+      double run = start;
+      for (int u = u0; u < u1; ++u) {
+        const float x = usum[u];
+        if (run + (double)x > target) {
+          const int64_t a = e0 + 8 * (int64_t)u, b = min(e1, a + 8);
+          for (int64_t v = a; v < b; ++v) {
+            const float y = fn.val(v);
+            if (y > 0.0f) lastu_seen = -2 - (int)v;  // remember the element itself
+            run += (double)y;
+            if (run > target) {
+              pick = (int)v;
+              break;
+            }
+          }
+          break;
+        }
+        run += (double)x;
+        if (x > 0.0f) lastu_seen = u;
       }
-      run += loc_lds[t];
+    } else {
+      lastu_seen = misc[1];
     }
-    misc_lds[0] = owner;
-    loc_lds[BLOCK] = run;
+    if (pick < 0 && lastu_seen <= -2) pick = -2 - lastu_seen;
+    if (pick < 0 && lastu_seen >= 0) {
+      const int64_t a = e0 + 8 * (int64_t)lastu_seen;
+      pick = last_positive_in_unit<BLOCK>(fn, a, min(e1, a + 8));
+    }
+    misc[2] = pick;
   }
   __syncthreads();
-  if (tid == misc_lds[0]) {
-    double run = loc_lds[BLOCK];
-    int pick = last;
-    for (int64_t v = t0; v < t1; ++v) {
-      run += (double)val(v);
-      if (run > target) {
-        pick = (int)v;
-        break;
-      }
-    }
-    misc_lds[2] = pick;
-  }
-  __syncthreads();
-  const int res = misc_lds[0] >= 0 ? misc_lds[2] : misc_lds[1];
+  const int res = misc[2];
   __syncthreads();
   return res;
 }
 
+// Bonus-row element value 2^(x*c - Mc) and its 8-element unit sums.
+template <int DT>
+struct ExpRow {
+  const char *row;
+  float c, Mc;
+  bool vec;  // row base 16-byte aligned: every unit is one (bf16) or two (fp32) 16-byte loads
+  __device__ __forceinline__ float val(int64_t v) const {
+    return fast_exp2(fmaf(Elt<DT>::load(row, v), c, -Mc));
+  }
+  __device__ __forceinline__ float unit_sum(int64_t a, int64_t b) const {
+    if (vec && b - a == 8) {
+      const uint4 *p = reinterpret_cast<const uint4 *>(row + a * Elt<DT>::kBytes);
+      float x[8];
+      if constexpr (DT == SMCSD_DTYPE_BF16) {
+        Elt<DT>::unpack(p[0], x);
+      } else {
+        float y[4], z[4];
+        Elt<DT>::unpack(p[0], y);
+        Elt<DT>::unpack(p[1], z);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[i] = y[i];
+          x[4 + i] = z[i];
+        }
+      }
+      float e[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) e[i] = fast_exp2(fmaf(x[i], c, -Mc));
+      return ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+    }
+    float sum = 0.0f;
+    for (int64_t v = a; v < b; ++v) sum += val(v);
+    return sum;
+  }
+};
+
 // ---------------------------------------------------------------------------------
 // SMC finalize: one workgroup per sequence
 // ---------------------------------------------------------------------------------
+constexpr int kMaxChunks = kMaxV / kChunkElemsF32;
+
 template <int DT>
 __global__ __launch_bounds__(kFinalBlock) void k_smc_finalize(
     RowMap rm, const int32_t *__restrict__ draft_tokens, int V, int chunk_elems, int chunks,
@@ -219,33 +281,55 @@ __global__ __launch_bounds__(kFinalBlock) void k_smc_finalize(
   __shared__ double sS[2 * kMaxK + 1], sL2[2 * kMaxK + 1];
   __shared__ double sLogp[kMaxK + 1], sLogq[kMaxK + 1];
   __shared__ int32_t sTok[kMaxK + 1];
-  __shared__ double sLoc[kFinalBlock + 1];
+  __shared__ double sTermK[kMaxChunks];
+  __shared__ float sUnit[kMaxUnits];
+  __shared__ double sScan[kFinalBlock / kWave];
   __shared__ int sMisc[4];
+  __shared__ int sCh;
+  __shared__ double sBase;
   __shared__ int sFlags;
   if (tid == 0) sFlags = 0;
-  __syncthreads();
 
-  if (tid < R) {
-    const RowNorm rn = row_norm(part + ((int64_t)g * R + tid) * chunks, chunks, c);
-    sMc[tid] = rn.Mc;
-    sS[tid] = rn.S;
-    sL2[tid] = rn.L2;
-    if (rn.flags) atomicOr(&sFlags, rn.flags);
+  // issue the draft-token gathers first so their latency overlaps the row combine
+  const int64_t src = (int64_t)g * rm.seq_step;
+  int32_t x = 0;
+  float xv = 0.0f;
+  int slot = 0;
+  if (tid < 2 * K) {
+    const int k = tid < K ? tid : tid - K;
+    slot = tid < K ? k : K + 1 + k;
+    x = draft_tokens[src * K + k];
+    if (x >= 0 && x < V) xv = E::load(rm.row(g, slot), x);
   }
   __syncthreads();
 
-  const int64_t src = (int64_t)g * rm.seq_step;
+  // row normalisers: chunk pairs combined in fp64 (row K also keeps its chunk terms)
+  if (tid < R) {
+    const float2 *p = part + ((int64_t)g * R + tid) * chunks;
+    float M = kNegInf;
+    for (int i = 0; i < chunks; ++i) M = fmaxf(M, p[i].x);
+    const float Mc = M == kNegInf ? 0.0f : __fmul_rn(M, c);
+    double S = 0.0;
+    for (int i = 0; i < chunks; ++i) {
+      const double t = chunk_term(p[i], c, Mc);
+      if (tid == K) sTermK[i] = t;
+      S += t;
+    }
+    sMc[tid] = Mc;
+    sS[tid] = S;
+    sL2[tid] = (double)Mc + log2(S);
+    int fl = 0;
+    if (isnan(S) || isinf(S)) fl |= SMCSD_ST_NAN_INPUT;
+    else if (M == kNegInf) fl |= SMCSD_ST_EMPTY_ROW;
+    if (fl) atomicOr(&sFlags, fl);
+  }
+  __syncthreads();
+
   if (tid < 2 * K) {
     const int k = tid < K ? tid : tid - K;
-    const int slot = tid < K ? k : K + 1 + k;
-    const int32_t x = draft_tokens[src * K + k];
     double lp = __builtin_nan("");
-    if (x < 0 || x >= V) {
-      atomicOr(&sFlags, SMCSD_ST_BAD_INPUT);
-    } else {
-      const float xv = E::load(rm.row(g, slot), x);
-      lp = ((double)xv * (double)c - sL2[slot]) * kLn2;
-    }
+    if (x < 0 || x >= V) atomicOr(&sFlags, SMCSD_ST_BAD_INPUT);
+    else lp = ((double)xv * (double)c - sL2[slot]) * kLn2;
     if (tid < K) {
       sLogp[k] = lp;
       sTok[k] = x;
@@ -254,53 +338,52 @@ __global__ __launch_bounds__(kFinalBlock) void k_smc_finalize(
     }
   }
 
-  // Bonus: u = U(seed; g, step, BONUS); token = first v with F_v > u, in the unnormalised
-  // domain: running sum of 2^(x*c - Mc_K) against u * S_K.
+  // Bonus: u = U(seed; g, step, BONUS); first v whose running sum of 2^(x*c - Mc_K)
+  // exceeds u * S_K (the unnormalised CDF; the common factor 2^Mc_K cancels).
   const double SK = sS[K];
-  const float McK = sMc[K];
   const double u = philox_uniform(seed, (uint32_t)g, step, 1u, 0);
   const double target = u * SK;
-  const float2 *pk = part + ((int64_t)g * R + K) * chunks;
   const char *brow = rm.row(g, K);
   int bonus = -1;
   if (isfinite(SK) && SK > 0.0) {
-    double base = 0.0;
-    int ch = chunks - 1;
-    for (int i = 0; i < chunks; ++i) {
-      const double si = chunk_term(pk[i], c, McK);
-      if (base + si > target) {
-        ch = i;
-        break;
+    if (tid == 0) {
+      double base = 0.0;
+      int ch = chunks - 1;
+      for (int i = 0; i < chunks; ++i) {
+        if (base + sTermK[i] > target) {
+          ch = i;
+          break;
+        }
+        base += sTermK[i];
       }
-      base += si;
+      sCh = ch;
+      sBase = base;
     }
-    if (base > target) base = target;  // unreachable in exact arithmetic
-    const int64_t e0 = (int64_t)ch * chunk_elems;
+    __syncthreads();
+    const int64_t e0 = (int64_t)sCh * chunk_elems;
     const int64_t e1 = min((int64_t)V, e0 + (int64_t)chunk_elems);
-    auto val = [&](int64_t v) -> float { return fast_exp2(fmaf(E::load(brow, v), c, -McK)); };
-    bonus = chunk_inverse_cdf<kFinalBlock>(e0, e1, base, target, val, sLoc, sMisc);
+    const ExpRow<DT> fn{brow, c, sMc[K], ((uintptr_t)brow & 15) == 0};
+    bonus = chunk_inverse_cdf<kFinalBlock>(e0, e1, sBase, target, fn, sUnit, sScan, sMisc);
   }
   __syncthreads();
 
+  double lpK = __builtin_nan("");
+  if (bonus >= 0) lpK = ((double)E::load(brow, bonus) * (double)c - sL2[K]) * kLn2;
+  int32_t *tok = out_tokens + (int64_t)g * (K + 1);
+  if (tid < K) {
+    tok[tid] = sTok[tid];
+    if (out_logp) out_logp[(int64_t)g * (K + 1) + tid] = (float)sLogp[tid];
+    if (out_logq) out_logq[(int64_t)g * K + tid] = (float)sLogq[tid];
+  }
+  if (out_lse && tid < R) out_lse[(int64_t)g * R + tid] = (float)(sL2[tid] * kLn2);
   if (tid == 0) {
-    double lpK = __builtin_nan("");
-    if (bonus >= 0) lpK = ((double)E::load(brow, bonus) * (double)c - sL2[K]) * kLn2;
     double incr = 0.0;
     for (int k = 0; k < K; ++k) incr += (double)alpha * sLogp[k] - sLogq[k];
     incr += ((double)alpha - 1.0) * lpK;
     lw[g] = (float)((double)lw[g] + incr);
-    int32_t *tok = out_tokens + (int64_t)g * (K + 1);
-    for (int k = 0; k < K; ++k) tok[k] = sTok[k];
     tok[K] = bonus;
     if (out_num) out_num[g] = K + 1;
-    if (out_logp) {
-      for (int k = 0; k < K; ++k) out_logp[(int64_t)g * (K + 1) + k] = (float)sLogp[k];
-      out_logp[(int64_t)g * (K + 1) + K] = (float)lpK;
-    }
-    if (out_logq)
-      for (int k = 0; k < K; ++k) out_logq[(int64_t)g * K + k] = (float)sLogq[k];
-    if (out_lse)
-      for (int r = 0; r < R; ++r) out_lse[(int64_t)g * R + r] = (float)(sL2[r] * kLn2);
+    if (out_logp) out_logp[(int64_t)g * (K + 1) + K] = (float)lpK;
     if (sFlags) atomicOr(status, sFlags);
   }
 }
@@ -422,6 +505,24 @@ __global__ __launch_bounds__(kStreamBlock) void k_sps_residual(
   }
 }
 
+// Residual (or target) row values for the SpS draw; scalar loads because the two rows
+// may sit at different alignments.
+template <int DT>
+struct ResidRow {
+  const char *prow, *qrow;
+  float c, Mcp, invp, Mcq, invq;
+  bool use_rho;
+  __device__ __forceinline__ float val(int64_t v) const {
+    const float p = sps_p<DT>(prow, v, c, Mcp, invp);
+    return use_rho ? fmaxf(p - sps_p<DT>(qrow, v, c, Mcq, invq), 0.0f) : p;
+  }
+  __device__ __forceinline__ float unit_sum(int64_t a, int64_t b) const {
+    float s = 0.0f;
+    for (int64_t v = a; v < b; ++v) s += val(v);
+    return s;
+  }
+};
+
 template <int DT>
 __global__ __launch_bounds__(kFinalBlock) void k_sps_final(
     RowMap rm, int V, int chunk_elems, int chunks, float c, uint64_t seed, uint64_t step,
@@ -430,7 +531,8 @@ __global__ __launch_bounds__(kFinalBlock) void k_sps_final(
     int32_t *status) {
   const int K = rm.K;
   const int g = blockIdx.x, tid = threadIdx.x;
-  __shared__ double sLoc[kFinalBlock + 1];
+  __shared__ float sUnit[kMaxUnits];
+  __shared__ double sScan[kFinalBlock / kWave];
   __shared__ int sMisc[4];
   const int kstar = ws_kstar[g];
   const float4 nm = ws_norm[g];
@@ -460,11 +562,8 @@ __global__ __launch_bounds__(kFinalBlock) void k_sps_final(
     }
     const int64_t e0 = (int64_t)ch * chunk_elems;
     const int64_t e1 = min((int64_t)V, e0 + (int64_t)chunk_elems);
-    auto val = [&](int64_t v) -> float {
-      const float p = sps_p<DT>(prow, v, c, nm.x, nm.y);
-      return use_rho ? fmaxf(p - sps_p<DT>(qrow, v, c, nm.z, nm.w), 0.0f) : p;
-    };
-    tok = chunk_inverse_cdf<kFinalBlock>(e0, e1, base, target, val, sLoc, sMisc);
+    const ResidRow<DT> fn{prow, qrow, c, nm.x, nm.y, nm.z, nm.w, use_rho};
+    tok = chunk_inverse_cdf<kFinalBlock>(e0, e1, base, target, fn, sUnit, sScan, sMisc);
   }
   if (tid == 0) {
     out_tokens[(int64_t)g * (K + 1) + kstar] = tok;
