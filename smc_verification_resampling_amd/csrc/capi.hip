@@ -123,7 +123,7 @@ int smcsd_kv_reassign(const int32_t *ancestors, const int32_t *resampled, int B,
     return SMCSD_EINVAL;
   if (ceil_div(seq_len + reserve_tokens, block_size) > M_cap) return SMCSD_EINVAL;
   if (B == 0) return SMCSD_OK;
-  if ((int64_t)B * N > INT32_MAX / 4) return SMCSD_EINVAL;
+  if ((int64_t)B * N * M_cap >= INT32_MAX) return SMCSD_EINVAL;  // 32-bit table indexing
   if (!ancestors || !resampled || !block_tables || !refcounts || !free_list || !free_top || !cow ||
       !cow_count || !status)
     return SMCSD_EINVAL;

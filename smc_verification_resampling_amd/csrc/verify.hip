@@ -150,21 +150,16 @@ __device__ __forceinline__ RowNorm row_norm(const float2 *p, int chunks, float c
 constexpr int kMaxUnits = kChunkElemsBf16 / 8;
 
 template <int BLOCK, typename Fn>
-__device__ __forceinline__ int last_positive_in_unit(const Fn &fn, int64_t a, int64_t b) {
-  for (int64_t v = b - 1; v >= a; --v)
-    if (fn.val(v) > 0.0f) return (int)v;
-  return -1;
-}
-
-template <int BLOCK, typename Fn>
 __device__ __forceinline__ int chunk_inverse_cdf(int64_t e0, int64_t e1, double base,
                                                  double target, const Fn &fn, float *usum,
                                                  double *scan_lds, int *misc) {
   const int tid = threadIdx.x;
   const int nunits = (int)((e1 - e0 + 7) / 8);
   for (int u = tid; u < nunits; u += BLOCK) {
+    typename Fn::Raw raw;
     const int64_t a = e0 + 8 * (int64_t)u;
-    usum[u] = fn.unit_sum(a, min(e1, a + 8));
+    fn.load(a, min(e1, a + 8), raw);
+    usum[u] = fn.reduce(raw);
   }
   if (tid == 0) {
     misc[0] = INT_MAX;  // owner thread
@@ -189,34 +184,40 @@ __device__ __forceinline__ int chunk_inverse_cdf(int64_t e0, int64_t e1, double 
   const int owner = misc[0];
   if (owner != INT_MAX ? tid == owner : tid == 0) {
     int pick = -1;
-    int lastu_seen = -1;  // last unit with a positive sum before the crossing
+    int lastu = -1;        // last unit with a positive sum before the crossing
+    int64_t lastpos = -1;  // last element with a positive value inside the crossing unit
     if (owner != INT_MAX) {
       double run = start;
       for (int u = u0; u < u1; ++u) {
         const float x = usum[u];
         if (run + (double)x > target) {
           const int64_t a = e0 + 8 * (int64_t)u, b = min(e1, a + 8);
-          for (int64_t v = a; v < b; ++v) {
-            const float y = fn.val(v);
-            if (y > 0.0f) lastu_seen = -2 - (int)v;  // remember the element itself
+          typename Fn::Raw raw;
+          fn.load(a, b, raw);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            if (pick >= 0 || a + i >= b) continue;
+            const float y = fn.val_from_raw(raw, i);
+            if (y > 0.0f) lastpos = a + i;
             run += (double)y;
-            if (run > target) {
-              pick = (int)v;
-              break;
-            }
+            if (run > target) pick = (int)(a + i);
           }
           break;
         }
         run += (double)x;
-        if (x > 0.0f) lastu_seen = u;
+        if (x > 0.0f) lastu = u;
       }
     } else {
-      lastu_seen = misc[1];
+      lastu = misc[1];
     }
-    if (pick < 0 && lastu_seen <= -2) pick = -2 - lastu_seen;
-    if (pick < 0 && lastu_seen >= 0) {
-      const int64_t a = e0 + 8 * (int64_t)lastu_seen;
-      pick = last_positive_in_unit<BLOCK>(fn, a, min(e1, a + 8));
+    if (pick < 0 && lastpos >= 0) pick = (int)lastpos;
+    if (pick < 0 && lastu >= 0) {
+      const int64_t a = e0 + 8 * (int64_t)lastu, b = min(e1, a + 8);
+      typename Fn::Raw raw;
+      fn.load(a, b, raw);
+#pragma unroll
+      for (int i = 7; i >= 0; --i)
+        if (pick < 0 && a + i < b && fn.val_from_raw(raw, i) > 0.0f) pick = (int)(a + i);
     }
     misc[2] = pick;
   }
@@ -226,39 +227,30 @@ __device__ __forceinline__ int chunk_inverse_cdf(int64_t e0, int64_t e1, double 
   return res;
 }
 
-// Bonus-row element value 2^(x*c - Mc) and its 8-element unit sums.
+// Bonus-row element value 2^(x*c - Mc) over 8-element units.  The unit load is eight
+// unrolled scalar loads at clamped in-bounds indices: branch-free, any row alignment.
 template <int DT>
 struct ExpRow {
   const char *row;
   float c, Mc;
-  bool vec;  // row base 16-byte aligned: every unit is one (bf16) or two (fp32) 16-byte loads
-  __device__ __forceinline__ float val(int64_t v) const {
-    return fast_exp2(fmaf(Elt<DT>::load(row, v), c, -Mc));
-  }
-  __device__ __forceinline__ float unit_sum(int64_t a, int64_t b) const {
-    if (vec && b - a == 8) {
-      const uint4 *p = reinterpret_cast<const uint4 *>(row + a * Elt<DT>::kBytes);
-      float x[8];
-      if constexpr (DT == SMCSD_DTYPE_BF16) {
-        Elt<DT>::unpack(p[0], x);
-      } else {
-        float y[4], z[4];
-        Elt<DT>::unpack(p[0], y);
-        Elt<DT>::unpack(p[1], z);
+  struct Raw {
+    float x[8];
+  };
+  __device__ __forceinline__ void load(int64_t a, int64_t b, Raw &r) const {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[i] = y[i];
-          x[4 + i] = z[i];
-        }
-      }
-      float e[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) e[i] = fast_exp2(fmaf(x[i], c, -Mc));
-      return ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+    for (int i = 0; i < 8; ++i) {
+      const float x = Elt<DT>::load(row, min(a + i, b - 1));
+      r.x[i] = a + i < b ? x : kNegInf;
     }
-    float sum = 0.0f;
-    for (int64_t v = a; v < b; ++v) sum += val(v);
-    return sum;
+  }
+  __device__ __forceinline__ float val_from_raw(const Raw &r, int i) const {
+    return fast_exp2(fmaf(r.x[i], c, -Mc));
+  }
+  __device__ __forceinline__ float reduce(const Raw &r) const {
+    float e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) e[i] = val_from_raw(r, i);
+    return ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
   }
 };
 
@@ -266,6 +258,7 @@ struct ExpRow {
 // SMC finalize: one workgroup per sequence
 // ---------------------------------------------------------------------------------
 constexpr int kMaxChunks = kMaxV / kChunkElemsF32;
+constexpr int kMaxPartLds = 1024;  // chunk pairs of one sequence staged in LDS (else read in place)
 
 template <int DT>
 __global__ __launch_bounds__(kFinalBlock) void k_smc_finalize(
@@ -283,6 +276,7 @@ __global__ __launch_bounds__(kFinalBlock) void k_smc_finalize(
   __shared__ int32_t sTok[kMaxK + 1];
   __shared__ double sTermK[kMaxChunks];
   __shared__ float sUnit[kMaxUnits];
+  __shared__ float2 sPart[kMaxPartLds];
   __shared__ double sScan[kFinalBlock / kWave];
   __shared__ int sMisc[4];
   __shared__ int sCh;
@@ -290,7 +284,8 @@ __global__ __launch_bounds__(kFinalBlock) void k_smc_finalize(
   __shared__ int sFlags;
   if (tid == 0) sFlags = 0;
 
-  // issue the draft-token gathers first so their latency overlaps the row combine
+  // One round of loads up front: the draft tokens, this sequence's chunk pairs (staged
+  // in LDS), then the draft-token logits.
   const int64_t src = (int64_t)g * rm.seq_step;
   int32_t x = 0;
   float xv = 0.0f;
@@ -299,13 +294,18 @@ __global__ __launch_bounds__(kFinalBlock) void k_smc_finalize(
     const int k = tid < K ? tid : tid - K;
     slot = tid < K ? k : K + 1 + k;
     x = draft_tokens[src * K + k];
-    if (x >= 0 && x < V) xv = E::load(rm.row(g, slot), x);
   }
+  const int npart = R * chunks;
+  const bool part_in_lds = npart <= kMaxPartLds;
+  const float2 *gpart = part + (int64_t)g * npart;
+  if (part_in_lds)
+    for (int i = tid; i < npart; i += kFinalBlock) sPart[i] = gpart[i];
+  if (tid < 2 * K && x >= 0 && x < V) xv = E::load(rm.row(g, slot), x);
   __syncthreads();
 
   // row normalisers: chunk pairs combined in fp64 (row K also keeps its chunk terms)
   if (tid < R) {
-    const float2 *p = part + ((int64_t)g * R + tid) * chunks;
+    const float2 *p = (part_in_lds ? sPart : gpart) + tid * chunks;
     float M = kNegInf;
     for (int i = 0; i < chunks; ++i) M = fmaxf(M, p[i].x);
     const float Mc = M == kNegInf ? 0.0f : __fmul_rn(M, c);
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(kFinalBlock) void k_smc_finalize(
     __syncthreads();
     const int64_t e0 = (int64_t)sCh * chunk_elems;
     const int64_t e1 = min((int64_t)V, e0 + (int64_t)chunk_elems);
-    const ExpRow<DT> fn{brow, c, sMc[K], ((uintptr_t)brow & 15) == 0};
+    const ExpRow<DT> fn{brow, c, sMc[K]};
     bonus = chunk_inverse_cdf<kFinalBlock>(e0, e1, sBase, target, fn, sUnit, sScan, sMisc);
   }
   __syncthreads();
@@ -512,13 +512,33 @@ struct ResidRow {
   const char *prow, *qrow;
   float c, Mcp, invp, Mcq, invq;
   bool use_rho;
-  __device__ __forceinline__ float val(int64_t v) const {
-    const float p = sps_p<DT>(prow, v, c, Mcp, invp);
-    return use_rho ? fmaxf(p - sps_p<DT>(qrow, v, c, Mcq, invq), 0.0f) : p;
+  struct Raw {
+    float p[8], q[8];
+  };
+  __device__ __forceinline__ float val_from(float xp, float xq) const {
+    const float p = fast_exp2(fmaf(xp, c, -Mcp)) * invp;
+    return use_rho ? fmaxf(p - fast_exp2(fmaf(xq, c, -Mcq)) * invq, 0.0f) : p;
   }
-  __device__ __forceinline__ float unit_sum(int64_t a, int64_t b) const {
+  __device__ __forceinline__ float val(int64_t v) const {
+    return val_from(Elt<DT>::load(prow, v), use_rho ? Elt<DT>::load(qrow, v) : 0.0f);
+  }
+  __device__ __forceinline__ void load(int64_t a, int64_t b, Raw &r) const {
+    const char *qr = use_rho ? qrow : prow;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t v = min(a + i, b - 1);
+      const float xp = Elt<DT>::load(prow, v), xq = Elt<DT>::load(qr, v);
+      r.p[i] = a + i < b ? xp : kNegInf;
+      r.q[i] = xq;
+    }
+  }
+  __device__ __forceinline__ float val_from_raw(const Raw &r, int i) const {
+    return val_from(r.p[i], r.q[i]);
+  }
+  __device__ __forceinline__ float reduce(const Raw &r) const {
     float s = 0.0f;
-    for (int64_t v = a; v < b; ++v) s += val(v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += val_from(r.p[i], r.q[i]);
     return s;
   }
 };

@@ -292,3 +292,59 @@ def test_determinism_and_resume():
     torch.cuda.synchronize()
     for x, y in zip(_final_state(a), _final_state(d)):
         assert np.array_equal(x, y)
+
+
+def test_kv_more_sequences_than_the_lds_prefix():
+    """B*N above the 8192 sequences whose allocation offsets fit in LDS: the pops take the
+    per-thread path."""
+    B, N, bs, K, ctx0, rounds = 9, 1024, 4, 2, 6, 3
+    R = K + 1
+    cfg = C.C1.scaled(B=B, N=N, K=K, ctx0=ctx0, block_size=bs, shared_prefix=True, iters=rounds)
+    kv = synth.initial_kv(cfg)
+    T, rc, fl, top, L = kv["tables"], kv["refcounts"], kv["free_list"], int(kv["free_top"][0]), ctx0
+    rng = np.random.default_rng(5)
+    ident = np.tile(np.arange(N, dtype=np.int32), (B, 1))
+    o = oracle.kv_reassign(ident, np.zeros(B, np.int32), T, bs, L, R, rc, fl, top)
+    g = _kv_gpu(ident, np.zeros(B, np.int32), B, N, T, bs, L, R, rc, fl, top)
+    assert _kv_equal(g, o)
+    for r in range(rounds):
+        T, rc, fl, top = o["tables"], o["refcounts"], o["free_list"], o["free_top"]
+        L += R
+        anc = np.sort(rng.integers(0, N, (B, N)), axis=1).astype(np.int32)
+        res = (rng.random(B) < 0.8).astype(np.int32)
+        o = oracle.kv_reassign(anc, res, T, bs, L, R, rc, fl, top)
+        g = _kv_gpu(anc, res, B, N, T, bs, L, R, rc, fl, top)
+        assert _kv_equal(g, o), r
+
+
+def test_many_chunks_per_sequence():
+    """K=32 with a long fp32 row: more chunk pairs per sequence than the finalize stages in
+    LDS, so it reads them in place."""
+    S, K, V = 2, 32, 140001
+    g = torch.Generator(device="cuda").manual_seed(3)
+    tgt = torch.randn((S, K + 1, V), generator=g, device="cuda")
+    drf = tgt[:, :K] + torch.randn((S, K, V), generator=g, device="cuda")
+    toks = torch.randint(0, V, (S, K), generator=g, device="cuda", dtype=torch.int32)
+    gg, o = _verify_case(tgt, drf.contiguous(), toks, K, V, 0.8, 1.0, 5, 6, np.zeros(S))
+    _assert_verify_parity(gg, o, K)
+
+
+@pytest.mark.parametrize("L,R", [(12, 0), (8, 4), (10, 2), (9, 0)])
+def test_kv_table_filled_to_capacity(L, R):
+    """The reservation reaches the last slot (or the table is already full): one sequence
+    whose table has exactly M_cap slots."""
+    B, N, bs, M = 1, 1, 4, 3
+    P = 8
+    T = np.full((1, M), -1, np.int32)
+    nb = math.ceil(L / bs)
+    T[0, :nb] = np.arange(nb)
+    rc = np.zeros(P, np.int32)
+    rc[:nb] = 1
+    fl = np.zeros(P, np.int32)
+    free = list(range(P - 1, nb - 1, -1))
+    fl[:len(free)] = free
+    anc = np.zeros((1, 1), np.int32)
+    for res in (0, 1):
+        o = oracle.kv_reassign(anc, np.array([res], np.int32), T, bs, L, R, rc, fl, len(free))
+        g = _kv_gpu(anc, np.array([res], np.int32), B, N, T, bs, L, R, rc, fl, len(free))
+        assert _kv_equal(g, o)
