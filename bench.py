@@ -29,6 +29,40 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 EVENT_EVERY = 8
 
+# HBM bytes per smcsd_verify call (k_lse_partials + k_smc_finalize) on c3_batched, from two
+# rocprofv3 passes (FETCH_SIZE, WRITE_SIZE) scaled by the same counters on a 1 GiB device
+# copy; profiles/smcsd_verify_c3_batched_hbm_bytes.md has the commands and figures.  Valid
+# only for the kernel sources they were taken on: any change to them reports null.
+VERIFY_TRAFFIC = {
+    "workload": "c3_batched",
+    "bytes": 1201197736,
+    "sources": {
+        "smc_verification_resampling_amd/csrc/verify.hip":
+            "a53d5170ce5502c35d2ccd3896221a5f1d67afe57c40575af559d68d5e8b6155",
+        "smc_verification_resampling_amd/csrc/device.hpp":
+            "8eebb3623c154d2390187910f7ad3e76c2d01d3570560f325d2d399f31996905",
+        "smc_verification_resampling_amd/csrc/internal.hpp":
+            "c98198c498fc2786e95ab7edf985ffea08e05e41ceca0ac6a5c218c270406d92",
+    },
+}
+
+
+def verify_traffic(workload):
+    """Counter-measured HBM bytes per verify call, or None if the workload differs or the
+    kernel sources changed since the counters were taken."""
+    import hashlib
+
+    if workload != VERIFY_TRAFFIC["workload"]:
+        return None
+    for rel, digest in VERIFY_TRAFFIC["sources"].items():
+        try:
+            with open(os.path.join(ROOT, rel), "rb") as f:
+                if hashlib.sha256(f.read()).hexdigest() != digest:
+                    return None
+        except OSError:
+            return None
+    return VERIFY_TRAFFIC["bytes"]
+
 
 def _parse():
     ap = argparse.ArgumentParser()
@@ -201,7 +235,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": verify_traffic(cfg.name),
             "avg_launch_us": round(verify_avg_s * 1e6, 2),
             "launches_timed": len(verify_ms),
         },
