@@ -82,7 +82,8 @@ int smcsd_version(void);
 const char *smcsd_status_string(int code);
 
 /*
- * Device workspace bytes for one call.
+ * Device workspace bytes for one call.  Workspaces are caller-owned device buffers whose
+ * start must be 256-byte aligned (SMCSD_EWORKSPACE otherwise).
  *   SMCSD_OP_VERIFY_SMC / _SPS: B, N, K, V as passed to smcsd_verify (P ignored).
  *   SMCSD_OP_KV: B, N and the pool size P (K, V ignored).  The KV workspace must be
  *   zero-filled before its first use; every smcsd_kv_reassign call leaves the parts that

@@ -4,6 +4,7 @@
 
 #include "../../include/smcsd.h"
 #include "internal.hpp"
+#include "kv_layout.hpp"
 
 using namespace smcsd;
 
@@ -46,7 +47,7 @@ size_t smcsd_workspace_bytes(int op, int B, int N, int K, int V, int64_t P) {
   }
   if (op == SMCSD_OP_KV) {
     if (P < 1) return 0;
-    return kv_ws_layout(B, S, P).total;
+    return kv_ws_layout(S, P).total;
   }
   return 0;
 }
@@ -73,7 +74,7 @@ int smcsd_verify(const void *target_logits, const void *draft_logits, int dtype,
   if (!out_tokens || !status) return SMCSD_EINVAL;
   if (mode == SMCSD_MODE_SMC && (!log_weights || lse_in)) return SMCSD_EINVAL;
   const size_t need = verify_ws_layout(S, K, V, mode == SMCSD_MODE_SPS ? 1 : 0).total;
-  if (!workspace || workspace_bytes < need) return SMCSD_EWORKSPACE;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) return SMCSD_EWORKSPACE;
 
   VerifyArgs a{};
   a.tgt = target_logits;
@@ -127,8 +128,8 @@ int smcsd_kv_reassign(const int32_t *ancestors, const int32_t *resampled, int B,
   if (!ancestors || !resampled || !block_tables || !refcounts || !free_list || !free_top || !cow ||
       !cow_count || !status)
     return SMCSD_EINVAL;
-  const size_t need = kv_ws_layout(B, (int64_t)B * N, P).total;
-  if (!workspace || workspace_bytes < need) return SMCSD_EWORKSPACE;
+  const size_t need = kv_ws_layout((int64_t)B * N, P).total;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) return SMCSD_EWORKSPACE;
   return hip_rc(launch_kv(ancestors, resampled, B, N, block_tables, M_cap, block_size, seq_len,
                           reserve_tokens, refcounts, free_list, free_top, P, cow, cow_count, status,
                           static_cast<char *>(workspace), as_stream(stream)));

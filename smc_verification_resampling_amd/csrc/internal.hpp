@@ -47,30 +47,6 @@ inline VerifyWs verify_ws_layout(int64_t nseq, int K, int V, int mode) {
   return w;
 }
 
-// KV workspace: [freed bitmap uint32 x ceil(P/32)][needs_cow int32 x B*N]
-//               [copy-on-write exclusive prefix int32 x B*N][arrival counter][top, F]
-// The bitmap and the counter must be zero before a call and are zero after it.
-struct KvWs {
-  size_t bitmap, cow_flags, cow_excl, done, scal, total;
-};
-inline KvWs kv_ws_layout(int64_t B, int64_t S, int64_t P) {
-  (void)B;
-  KvWs w{};
-  size_t off = 0;
-  w.bitmap = off;
-  off += align256(sizeof(uint32_t) * (size_t)ceil_div(P, 32));
-  w.cow_flags = off;
-  off += align256(sizeof(int32_t) * (size_t)S);
-  w.cow_excl = off;
-  off += align256(sizeof(int32_t) * (size_t)S);
-  w.done = off;
-  off += align256(sizeof(int32_t));
-  w.scal = off;
-  off += align256(sizeof(int32_t) * 4);
-  w.total = off;
-  return w;
-}
-
 struct VerifyArgs {
   const void *tgt, *drf;
   int dtype;

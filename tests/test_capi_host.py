@@ -84,6 +84,7 @@ def test_verify_host_validation(lib):
     assert _verify_rc(lib, lw=None) == -1                      # SMC mode needs log-weights
     assert _verify_rc(lib, wsb=16) == -4
     assert _verify_rc(lib, ws=None) == -4
+    assert _verify_rc(lib, ws=ctypes.c_void_p(0x1010)) == -4    # workspace not 256-byte aligned
     assert _verify_rc(lib, mode=3) == -1
     assert _verify_rc(lib, B=0) == 0                            # empty batch: nothing enqueued
 
@@ -99,6 +100,8 @@ def test_resample_and_kv_host_validation(lib):
                                  None) == -1
     assert lib.smcsd_kv_reassign(p, p, 1, 4, p, 4, 4, 10, 3, p, p, p, 100, p, p, p, None, 1 << 20,
                                  None) == -4
+    assert lib.smcsd_kv_reassign(p, p, 1, 4, p, 4, 4, 10, 3, p, p, p, 100, p, p, p,
+                                 ctypes.c_void_p(0x1010), 1 << 20, None) == -4
     assert lib.smcsd_kv_reassign(p, p, 0, 4, p, 4, 4, 10, 3, p, p, p, 100, p, p, p, p, 1 << 20,
                                  None) == 0
     assert lib.smcsd_philox4x32_10(p, p, -1, p, None) == -1
