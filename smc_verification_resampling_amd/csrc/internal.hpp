@@ -15,7 +15,6 @@ constexpr int kChunkElemsBf16 = 16384;
 constexpr int kChunkElemsF32 = 8192;
 constexpr int kChunkElemsMin = kChunkElemsF32;  // workspace is sized for the smaller tile
 
-constexpr int kFinalBlock = 1024;  // more waves, not unrolled code, give the re-read its parallelism
 constexpr int kMaxK = 32;
 constexpr int kMaxN = 1024;
 constexpr int kMaxV = 1 << 24;  // finalize keeps one fp64 term per vocabulary chunk in LDS

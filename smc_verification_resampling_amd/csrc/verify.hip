@@ -140,86 +140,127 @@ __device__ __forceinline__ RowNorm row_norm(const float2 *p, int chunks, float c
 
 // Inverse CDF inside one chunk [e0, e1) of a row: the first v whose running sum
 // base + sum_{w<=v} val(w) exceeds target.  The chunk is cut into units of 8 consecutive
-// elements; fn.unit_sum(a, b) evaluates a unit with coalesced 16-byte loads where the row
-// allows it, and the unit sums go to LDS.  One workgroup exclusive scan (fp64) over
-// per-thread runs of units finds the owning thread, which walks its units and then the
-// elements of the one unit that crosses (fn.val, the same fp32 value the unit sum used).
-// Rounding can leave no crossing where the oracle's margin is at rounding level; then the
-// last element with a positive value before the crossing point is returned.  Every thread
-// must call it; the result is returned to every thread.
-constexpr int kMaxUnits = kChunkElemsBf16 / 8;
+// elements; thread t loads units [t*UPT, (t+1)*UPT) once and keeps them in registers.
+// Unit sums are fp32 (fn.reduce), running sums fp64.  One workgroup exclusive scan finds
+// the owning thread, which walks its own units element by element (fn.val_from_raw, the
+// same fp32 values the unit sums used).  Rounding can leave no crossing where the oracle's
+// margin is at rounding level; then the last element with a positive value before the
+// crossing point is returned.  Every thread must call it; every thread gets the index
+// (-1 if there is none) and *logit the pick's logit (fn.logit).  UPT * 8 * BLOCK must
+// cover the chunk.
+// Workgroup sizes of the kernels that re-read one chunk: the SMC finalize runs one
+// workgroup per sequence (hundreds at a time), the SpS draw one per SpS sequence (few).
+constexpr int kSmcFinalBlock = 256;
+constexpr int kSpsFinalBlock = 1024;
 
-template <int BLOCK, typename Fn>
+// 8-element units per thread when a BLOCK-thread workgroup re-reads one chunk
+template <int DT, int BLOCK>
+constexpr int kUnitsPerThread = (DT == SMCSD_DTYPE_BF16 ? kChunkElemsBf16 : kChunkElemsF32) / 8 /
+                                BLOCK;
+static_assert(kChunkElemsF32 % (8 * kSpsFinalBlock) == 0 && kChunkElemsF32 % (8 * kSmcFinalBlock) == 0,
+              "a chunk must split evenly into the workgroup's units");
+
+template <int BLOCK, int UPT, typename Fn>
 __device__ __forceinline__ int chunk_inverse_cdf(int64_t e0, int64_t e1, double base,
-                                                 double target, const Fn &fn, float *usum,
-                                                 double *scan_lds, int *misc) {
+                                                 double target, const Fn &fn, double *scan_lds,
+                                                 int *misc, float *logit) {
   const int tid = threadIdx.x;
   const int nunits = (int)((e1 - e0 + 7) / 8);
-  for (int u = tid; u < nunits; u += BLOCK) {
-    typename Fn::Raw raw;
+  typename Fn::Raw raw[UPT];
+  float us[UPT];
+#pragma unroll
+  for (int i = 0; i < UPT; ++i) {
+    const int u = min(tid * UPT + i, nunits - 1);  // clamped: every load is in bounds
     const int64_t a = e0 + 8 * (int64_t)u;
-    fn.load(a, min(e1, a + 8), raw);
-    usum[u] = fn.reduce(raw);
+    fn.load(a, min(e1, a + 8), raw[i]);
   }
   if (tid == 0) {
     misc[0] = INT_MAX;  // owner thread
     misc[1] = -1;       // last unit with a positive sum
     misc[2] = -1;       // result
   }
-  __syncthreads();
-  const int upt = (nunits + BLOCK - 1) / BLOCK;
-  const int u0 = min(nunits, tid * upt), u1 = min(nunits, u0 + upt);
   double loc = 0.0;
   int lastu = -1;
-  for (int u = u0; u < u1; ++u) {
-    const float x = usum[u];
-    loc += (double)x;
-    if (x > 0.0f) lastu = u;
+#pragma unroll
+  for (int i = 0; i < UPT; ++i) {
+    const int u = tid * UPT + i;
+    us[i] = u < nunits ? fn.reduce(raw[i]) : 0.0f;
+    loc += (double)us[i];
+    if (us[i] > 0.0f) lastu = u;
   }
   double tot;
   const double start = base + block_exclusive_scan<double, BLOCK>(loc, scan_lds, &tot);
-  if (u1 > u0 && start + loc > target) atomicMin(&misc[0], tid);
-  if (lastu >= 0) atomicMax(&misc[1], lastu);
+  // one LDS atomic per wave: the first crossing lane, the wave's last positive unit
+  const int lane = tid % kWave;
+  const unsigned long long cross = __ballot(tid * UPT < nunits && start + loc > target);
+  int lu = lastu;
+#pragma unroll
+  for (int m = kWave / 2; m >= 1; m >>= 1) lu = max(lu, __shfl_xor(lu, m, kWave));
+  if (lane == 0) {
+    if (cross) atomicMin(&misc[0], tid + __ffsll(cross) - 1);
+    if (lu >= 0) atomicMax(&misc[1], lu);
+  }
   __syncthreads();
-  const int owner = misc[0];
-  if (owner != INT_MAX ? tid == owner : tid == 0) {
-    int pick = -1;
-    int lastu = -1;        // last unit with a positive sum before the crossing
-    int64_t lastpos = -1;  // last element with a positive value inside the crossing unit
+  const int owner = misc[0], last_all = misc[1];
+  const int who = owner != INT_MAX ? owner : (last_all >= 0 ? last_all / UPT : -1);
+  if (tid == who) {
+    int pick_i = -1, pick_j = -1;
     if (owner != INT_MAX) {
       double run = start;
-      for (int u = u0; u < u1; ++u) {
-        const float x = usum[u];
-        if (run + (double)x > target) {
-          const int64_t a = e0 + 8 * (int64_t)u, b = min(e1, a + 8);
-          typename Fn::Raw raw;
-          fn.load(a, b, raw);
+      int lastpos_i = -1, lastpos_j = -1;  // last positive element inside the crossing unit
+      int lastu_i = -1;                     // last own unit with a positive sum before it
+      bool crossed = false;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            if (pick >= 0 || a + i >= b) continue;
-            const float y = fn.val_from_raw(raw, i);
-            if (y > 0.0f) lastpos = a + i;
+      for (int i = 0; i < UPT; ++i) {
+        if (crossed || tid * UPT + i >= nunits) continue;
+        if (run + (double)us[i] > target) {
+          crossed = true;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            if (pick_i >= 0) continue;
+            const float y = fn.val_from_raw(raw[i], j);
+            if (y > 0.0f) {
+              lastpos_i = i;
+              lastpos_j = j;
+            }
             run += (double)y;
-            if (run > target) pick = (int)(a + i);
+            if (run > target) {
+              pick_i = i;
+              pick_j = j;
+            }
           }
-          break;
+        } else {
+          run += (double)us[i];
+          if (us[i] > 0.0f) lastu_i = i;
         }
-        run += (double)x;
-        if (x > 0.0f) lastu = u;
       }
+      if (pick_i < 0 && lastpos_i >= 0) {
+        pick_i = lastpos_i;
+        pick_j = lastpos_j;
+      }
+      if (pick_i < 0 && lastu_i >= 0) pick_i = lastu_i;
     } else {
-      lastu = misc[1];
+      pick_i = last_all - tid * UPT;
     }
-    if (pick < 0 && lastpos >= 0) pick = (int)lastpos;
-    if (pick < 0 && lastu >= 0) {
-      const int64_t a = e0 + 8 * (int64_t)lastu, b = min(e1, a + 8);
-      typename Fn::Raw raw;
-      fn.load(a, b, raw);
+    if (pick_i >= 0 && pick_j < 0) {
+      // last positive element of unit pick_i
 #pragma unroll
-      for (int i = 7; i >= 0; --i)
-        if (pick < 0 && a + i < b && fn.val_from_raw(raw, i) > 0.0f) pick = (int)(a + i);
+      for (int i = 0; i < UPT; ++i)
+        if (i == pick_i)
+#pragma unroll
+          for (int j = 7; j >= 0; --j)
+            if (pick_j < 0 && fn.val_from_raw(raw[i], j) > 0.0f) pick_j = j;
     }
-    misc[2] = pick;
+    if (pick_i >= 0 && pick_j >= 0) {
+      float x = 0.0f;
+#pragma unroll
+      for (int i = 0; i < UPT; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (i == pick_i && j == pick_j) x = fn.logit(raw[i], j);
+      misc[2] = (int)(e0 + 8 * (int64_t)(tid * UPT + pick_i) + pick_j);
+      *logit = x;
+    }
   }
   __syncthreads();
   const int res = misc[2];
@@ -233,19 +274,28 @@ template <int DT>
 struct ExpRow {
   const char *row;
   float c, Mc;
+  bool vec;  // the row starts 16-byte aligned: whole units are read as 16-byte vectors
   struct Raw {
     float x[8];
   };
   __device__ __forceinline__ void load(int64_t a, int64_t b, Raw &r) const {
+    using E = Elt<DT>;
+    if (vec && a + 8 <= b) {
+      const uint4 *p = reinterpret_cast<const uint4 *>(row + a * E::kBytes);
+#pragma unroll
+      for (int q = 0; q < 8 / E::kPerVec; ++q) E::unpack(p[q], r.x + q * E::kPerVec);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float x = Elt<DT>::load(row, min(a + i, b - 1));
+      const float x = E::load(row, min(a + i, b - 1));
       r.x[i] = a + i < b ? x : kNegInf;
     }
   }
   __device__ __forceinline__ float val_from_raw(const Raw &r, int i) const {
     return fast_exp2(fmaf(r.x[i], c, -Mc));
   }
+  __device__ __forceinline__ float logit(const Raw &r, int i) const { return r.x[i]; }
   __device__ __forceinline__ float reduce(const Raw &r) const {
     float e[8];
 #pragma unroll
@@ -261,7 +311,7 @@ constexpr int kMaxChunks = kMaxV / kChunkElemsF32;
 constexpr int kMaxPartLds = 1024;  // chunk pairs of one sequence staged in LDS (else read in place)
 
 template <int DT>
-__global__ __launch_bounds__(kFinalBlock) void k_smc_finalize(
+__global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
     RowMap rm, const int32_t *__restrict__ draft_tokens, int V, int chunk_elems, int chunks,
     float c, float alpha, uint64_t seed, uint64_t step, const float2 *__restrict__ part,
     float *__restrict__ lw, int32_t *__restrict__ out_tokens, int32_t *__restrict__ out_num,
@@ -275,14 +325,15 @@ __global__ __launch_bounds__(kFinalBlock) void k_smc_finalize(
   __shared__ double sLogp[kMaxK + 1], sLogq[kMaxK + 1];
   __shared__ int32_t sTok[kMaxK + 1];
   __shared__ double sTermK[kMaxChunks];
-  __shared__ float sUnit[kMaxUnits];
   __shared__ float2 sPart[kMaxPartLds];
-  __shared__ double sScan[kFinalBlock / kWave];
+  __shared__ double sScan[kSmcFinalBlock / kWave];
   __shared__ int sMisc[4];
   __shared__ int sCh;
   __shared__ double sBase;
+  __shared__ float sPickLogit;
   __shared__ int sFlags;
   if (tid == 0) sFlags = 0;
+  const float lw_old = tid == 0 ? lw[g] : 0.0f;  // loaded early: used only at the end
 
   // One round of loads up front: the draft tokens, this sequence's chunk pairs (staged
   // in LDS), then the draft-token logits.
@@ -299,7 +350,7 @@ __global__ __launch_bounds__(kFinalBlock) void k_smc_finalize(
   const bool part_in_lds = npart <= kMaxPartLds;
   const float2 *gpart = part + (int64_t)g * npart;
   if (part_in_lds)
-    for (int i = tid; i < npart; i += kFinalBlock) sPart[i] = gpart[i];
+    for (int i = tid; i < npart; i += kSmcFinalBlock) sPart[i] = gpart[i];
   if (tid < 2 * K && x >= 0 && x < V) xv = E::load(rm.row(g, slot), x);
   __syncthreads();
 
@@ -362,13 +413,13 @@ __global__ __launch_bounds__(kFinalBlock) void k_smc_finalize(
     __syncthreads();
     const int64_t e0 = (int64_t)sCh * chunk_elems;
     const int64_t e1 = min((int64_t)V, e0 + (int64_t)chunk_elems);
-    const ExpRow<DT> fn{brow, c, sMc[K]};
-    bonus = chunk_inverse_cdf<kFinalBlock>(e0, e1, sBase, target, fn, sUnit, sScan, sMisc);
+    const ExpRow<DT> fn{brow, c, sMc[K], (reinterpret_cast<uintptr_t>(brow) & 15) == 0};
+    bonus = chunk_inverse_cdf<kSmcFinalBlock, kUnitsPerThread<DT, kSmcFinalBlock>>(
+        e0, e1, sBase, target, fn, sScan, sMisc, &sPickLogit);
   }
-  __syncthreads();
 
   double lpK = __builtin_nan("");
-  if (bonus >= 0) lpK = ((double)E::load(brow, bonus) * (double)c - sL2[K]) * kLn2;
+  if (bonus >= 0) lpK = ((double)sPickLogit * (double)c - sL2[K]) * kLn2;
   int32_t *tok = out_tokens + (int64_t)g * (K + 1);
   if (tid < K) {
     tok[tid] = sTok[tid];
@@ -380,7 +431,7 @@ __global__ __launch_bounds__(kFinalBlock) void k_smc_finalize(
     double incr = 0.0;
     for (int k = 0; k < K; ++k) incr += (double)alpha * sLogp[k] - sLogq[k];
     incr += ((double)alpha - 1.0) * lpK;
-    lw[g] = (float)((double)lw[g] + incr);
+    lw[g] = (float)((double)lw_old + incr);
     tok[K] = bonus;
     if (out_num) out_num[g] = K + 1;
     if (out_logp) out_logp[(int64_t)g * (K + 1) + K] = (float)lpK;
@@ -535,6 +586,7 @@ struct ResidRow {
   __device__ __forceinline__ float val_from_raw(const Raw &r, int i) const {
     return val_from(r.p[i], r.q[i]);
   }
+  __device__ __forceinline__ float logit(const Raw &r, int i) const { return r.p[i]; }
   __device__ __forceinline__ float reduce(const Raw &r) const {
     float s = 0.0f;
 #pragma unroll
@@ -544,16 +596,16 @@ struct ResidRow {
 };
 
 template <int DT>
-__global__ __launch_bounds__(kFinalBlock) void k_sps_final(
+__global__ __launch_bounds__(kSpsFinalBlock) void k_sps_final(
     RowMap rm, int V, int chunk_elems, int chunks, float c, uint64_t seed, uint64_t step,
     const int32_t *__restrict__ ws_kstar, const float4 *__restrict__ ws_norm,
     const float2 *__restrict__ part2, int32_t *__restrict__ out_tokens, float *__restrict__ out_logp,
     int32_t *status) {
   const int K = rm.K;
   const int g = blockIdx.x, tid = threadIdx.x;
-  __shared__ float sUnit[kMaxUnits];
-  __shared__ double sScan[kFinalBlock / kWave];
+  __shared__ double sScan[kSpsFinalBlock / kWave];
   __shared__ int sMisc[4];
+  __shared__ float sPickLogit;
   const int kstar = ws_kstar[g];
   const float4 nm = ws_norm[g];
   const char *prow = rm.row(g, kstar);
@@ -583,7 +635,8 @@ __global__ __launch_bounds__(kFinalBlock) void k_sps_final(
     const int64_t e0 = (int64_t)ch * chunk_elems;
     const int64_t e1 = min((int64_t)V, e0 + (int64_t)chunk_elems);
     const ResidRow<DT> fn{prow, qrow, c, nm.x, nm.y, nm.z, nm.w, use_rho};
-    tok = chunk_inverse_cdf<kFinalBlock>(e0, e1, base, target, fn, sUnit, sScan, sMisc);
+    tok = chunk_inverse_cdf<kSpsFinalBlock, kUnitsPerThread<DT, kSpsFinalBlock>>(
+        e0, e1, base, target, fn, sScan, sMisc, &sPickLogit);
   }
   if (tid == 0) {
     out_tokens[(int64_t)g * (K + 1) + kstar] = tok;
@@ -591,8 +644,7 @@ __global__ __launch_bounds__(kFinalBlock) void k_sps_final(
       // log p of the drawn token: (x*c - L2)*ln2 with L2 = Mc + log2(1/inv)
       double lp = __builtin_nan("");
       if (tok >= 0)
-        lp = ((double)Elt<DT>::load(prow, tok) * (double)c - ((double)nm.x - log2((double)nm.y))) *
-             kLn2;
+        lp = ((double)sPickLogit * (double)c - ((double)nm.x - log2((double)nm.y))) * kLn2;
       out_logp[(int64_t)g * (K + 1) + K] = (float)lp;
     }
     if (tok < 0) atomicOr(status, isnan(total) ? SMCSD_ST_NAN_INPUT : SMCSD_ST_EMPTY_ROW);
@@ -633,7 +685,7 @@ static hipError_t launch_verify_t(const VerifyArgs &a) {
   if (a.mode == SMCSD_MODE_SMC) {
     hipLaunchKernelGGL(k_lse_partials<DT>, dim3(grid), dim3(kStreamBlock), 0, a.stream, rm, a.nseq,
                        a.V, ce, chunks, a.c, part, ntiles);
-    hipLaunchKernelGGL(k_smc_finalize<DT>, dim3(a.nseq), dim3(kFinalBlock), 0, a.stream, rm,
+    hipLaunchKernelGGL(k_smc_finalize<DT>, dim3(a.nseq), dim3(kSmcFinalBlock), 0, a.stream, rm,
                        a.draft_tokens, a.V, ce, chunks, a.c, a.alpha, a.seed, a.step, part,
                        a.log_weights, a.out_tokens, a.out_num_tokens, a.out_logp, a.out_logq,
                        a.out_lse, a.status);
@@ -652,7 +704,7 @@ static hipError_t launch_verify_t(const VerifyArgs &a) {
   hipLaunchKernelGGL(k_sps_residual<DT>, dim3((unsigned)std::min<int64_t>(ntiles2, (int64_t)1 << 30)),
                      dim3(kStreamBlock), 0, a.stream, rm, a.V, ce, chunks, a.c, kstar, norm, part2,
                      ntiles2);
-  hipLaunchKernelGGL(k_sps_final<DT>, dim3(a.nseq), dim3(kFinalBlock), 0, a.stream, rm, a.V, ce,
+  hipLaunchKernelGGL(k_sps_final<DT>, dim3(a.nseq), dim3(kSpsFinalBlock), 0, a.stream, rm, a.V, ce,
                      chunks, a.c, a.seed, a.step, kstar, norm, part2, a.out_tokens, a.out_logp,
                      a.status);
   return hipGetLastError();
