@@ -142,6 +142,42 @@ __device__ __forceinline__ void lse_update(Lse &st, const float (&x)[NV], float 
   st.s += e[0];
 }
 
+// lse_update over NV elements that also hands back gs[q], the sum of 2^(x*c - mc) over the
+// q-th run of G consecutive elements, relative to the updated mc.  The pairwise tree first
+// sums each run, then the runs: the same tree, and total, as lse_update.
+template <int NV, int G>
+__device__ __forceinline__ void lse_update_g(Lse &st, const float (&x)[NV], float c,
+                                             float (&gs)[NV / G]) {
+  float vmax = x[0];
+#pragma unroll
+  for (int i = 1; i < NV; ++i) vmax = fmaxf(vmax, x[i]);
+  if (vmax > st.m) {
+    const float mcn = __fmul_rn(vmax, c);
+    st.s = (st.m == kNegInf) ? st.s * 0.0f : st.s * fast_exp2(st.mc - mcn);
+    st.m = vmax;
+    st.mc = mcn;
+  }
+#pragma unroll
+  for (int q = 0; q < NV / G; ++q) {
+    float e[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) e[i] = fast_exp2(fmaf(x[q * G + i], c, -st.mc));
+#pragma unroll
+    for (int w = 1; w < G; w *= 2)
+#pragma unroll
+      for (int i = 0; i + w < G; i += 2 * w) e[i] += e[i + w];
+    gs[q] = e[0];
+  }
+  float t[NV / G];
+#pragma unroll
+  for (int q = 0; q < NV / G; ++q) t[q] = gs[q];
+#pragma unroll
+  for (int w = 1; w < NV / G; w *= 2)
+#pragma unroll
+    for (int q = 0; q + w < NV / G; q += 2 * w) t[q] += t[q + w];
+  st.s += t[0];
+}
+
 __device__ __forceinline__ Lse lse_combine(const Lse &a, const Lse &b, float c) {
   const float M = fmaxf(a.m, b.m);
   if (M == kNegInf) return Lse{kNegInf, 0.0f, a.s + b.s};

@@ -23,10 +23,14 @@ inline int chunk_elems(int dtype) { return dtype == 1 ? kChunkElemsBf16 : kChunk
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Verify workspace: [row partials float2 x nseq*(2K+1)*chunks]
+// A tile of the bonus row also sums its kSlabs slabs (one slab = the kStreamBlock vectors a
+// workgroup loads together) so that the bonus draw re-reads one slab, not the whole chunk.
+constexpr int kSlabs = kStreamUnroll;
+
+// Verify workspace: [row partials float2 x nseq*(2K+1)*chunks][bonus slab sums float x nseq*chunks*kSlabs]
 //                   [kstar int32 x nseq][L2 pair double2 x nseq][residual partials float2 x nseq*chunks]
 struct VerifyWs {
-  size_t part, kstar, l2, part2, total;
+  size_t part, sub, kstar, l2, part2, total;
 };
 inline VerifyWs verify_ws_layout(int64_t nseq, int K, int V, int mode) {
   VerifyWs w{};
@@ -34,6 +38,8 @@ inline VerifyWs verify_ws_layout(int64_t nseq, int K, int V, int mode) {
   size_t off = 0;
   w.part = off;
   off += align256(sizeof(float) * 2 * (size_t)(nseq * (2 * K + 1) * chunks));
+  w.sub = off;
+  off += align256(sizeof(float) * (size_t)(nseq * chunks * kSlabs));
   if (mode == 1) {
     w.kstar = off;
     off += align256(sizeof(int32_t) * (size_t)nseq);

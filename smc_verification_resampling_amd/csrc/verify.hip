@@ -9,12 +9,14 @@
 //   k_lse_partials   grid = tiles (row, 32 KiB vocabulary chunk), 256 threads.  One
 //                    streaming pass with 16-byte loads; per lane an online (max, sum of
 //                    2^(x*c - max*c)); wave shuffles + LDS combine; writes one (max, sum)
-//                    pair per tile.  Bonus rows are ordered last so that the chunk the
-//                    finalize kernel re-reads is among the most recently streamed bytes.
+//                    pair per tile.  Tiles of the bonus row (position K) also write the
+//                    sums of their 8 slabs (one slab = the 256 vectors loaded together),
+//                    so the bonus draw re-reads one slab instead of a whole chunk.
 //   k_smc_finalize   grid = sequences.  Combines the chunk pairs in fp64 into each row's
 //                    normaliser, gathers the draft-token log-probabilities, draws the bonus
-//                    token by inverse CDF (selects the chunk from the pairs, re-reads only
-//                    that chunk) and updates the log-weight.
+//                    token by inverse CDF (selects the chunk from the pairs and the slab
+//                    from the slab sums, re-reads only that slab) and updates the
+//                    log-weight.
 //   k_sps_decide / k_sps_residual / k_sps_final
 //                    SpS: acceptance tests from the gathered log-probabilities, one pass
 //                    over the residual max(0, p - q) (or p_K) of the single row pair that is
@@ -49,29 +51,49 @@ __device__ __forceinline__ double chunk_term(float2 p, float c, float Mc) {
 // ---------------------------------------------------------------------------------
 // Streaming LSE pass
 // ---------------------------------------------------------------------------------
+// Elements of one slab: the kStreamBlock vectors a workgroup loads in one unrolled step.
+template <int DT>
+constexpr int kSlabElems = kStreamBlock * Elt<DT>::kPerVec;
+static_assert(kChunkElemsBf16 == kSlabs * kSlabElems<SMCSD_DTYPE_BF16> &&
+                  kChunkElemsF32 == kSlabs * kSlabElems<SMCSD_DTYPE_F32>,
+              "a tile is one unrolled step: vector group u of every thread is slab u");
+
+// Slab of element v of a tile whose vector body starts at a0 (head elements go to slab 0,
+// tail elements to the slab their index falls in, capped at the last).
+template <int DT>
+__device__ __forceinline__ int slab_of(int64_t v, int64_t a0) {
+  return v < a0 ? 0 : (int)min((int64_t)kSlabs - 1, (v - a0) / kSlabElems<DT>);
+}
+
 template <int DT>
 __global__ __launch_bounds__(kStreamBlock) void k_lse_partials(RowMap rm, int nseq, int V,
                                                                 int chunk_elems, int chunks,
                                                                 float c, float2 *__restrict__ part,
+                                                                float *__restrict__ sub,
                                                                 int64_t ntiles) {
   using E = Elt<DT>;
   constexpr int EPV = E::kPerVec;
   __shared__ Lse lds[kStreamBlock / kWave];
+  __shared__ float sSlab[kStreamBlock / kWave][kSlabs];
+  __shared__ float sSlabT[kStreamBlock][kSlabs + 1];  // per-thread slab sums (bonus tiles)
+  __shared__ float sTileMc;
   const int K = rm.K;
   const int R = 2 * K + 1;
-  const int64_t nonbonus_rows = (int64_t)nseq * 2 * K;
   const int tid = threadIdx.x;
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int64_t row_id = t / chunks;
     const int ch = (int)(t - row_id * chunks);
+    // bonus rows first: their tiles do extra work, which then overlaps the stream of the
+    // other rows instead of lengthening the kernel's tail
     int g, slot;
-    if (row_id < nonbonus_rows) {
-      g = (int)(row_id / (2 * K));
-      const int j = (int)(row_id - (int64_t)g * 2 * K);
-      slot = j < K ? j : j + 1;
-    } else {
-      g = (int)(row_id - nonbonus_rows);
+    if (row_id < nseq) {
+      g = (int)row_id;
       slot = K;
+    } else {
+      const int64_t r = row_id - nseq;
+      g = (int)(r / (2 * K));
+      const int j = (int)(r - (int64_t)g * 2 * K);
+      slot = j < K ? j : j + 1;
     }
     const char *row = rm.row(g, slot);
     const int64_t e0 = (int64_t)ch * chunk_elems;
@@ -84,18 +106,26 @@ __global__ __launch_bounds__(kStreamBlock) void k_lse_partials(RowMap rm, int ns
     const int64_t a1 = a0 + nvec * EPV;
 
     Lse st = lse_init();
+    float xh = kNegInf, xt = kNegInf;
     if (tid < head) {
-      const float x[1] = {E::load(row, e0 + tid)};
+      xh = E::load(row, e0 + tid);
+      const float x[1] = {xh};
       lse_update<1>(st, x, c);
     }
     if (tid < e1 - a1) {
-      const float x[1] = {E::load(row, a1 + tid)};
+      xt = E::load(row, a1 + tid);
+      const float x[1] = {xt};
       lse_update<1>(st, x, c);
     }
-    // body: kStreamUnroll 16-byte vectors per lane in flight, then one max / rescale
-    // for the whole group of kStreamUnroll*EPV elements
+    // body: kStreamUnroll 16-byte vectors per lane in flight, then one max / rescale for
+    // the whole group of kStreamUnroll*EPV elements.  A tile is at most one such group.
+    const bool bonus = slot == K;
+    if (bonus) {
+#pragma unroll
+      for (int u = 0; u < kSlabs; ++u) sSlabT[tid][u] = 0.0f;
+    }
     const uint4 *vp = reinterpret_cast<const uint4 *>(row + a0 * E::kBytes);
-    for (int64_t v0 = 0; v0 < nvec; v0 += (int64_t)kStreamBlock * kStreamUnroll) {
+    for (int64_t v0 = 0; v0 < nvec; v0 += (int64_t)kStreamBlock * kStreamUnroll) {  // one pass
       uint4 buf[kStreamUnroll];
 #pragma unroll
       for (int u = 0; u < kStreamUnroll; ++u) {
@@ -105,10 +135,52 @@ __global__ __launch_bounds__(kStreamBlock) void k_lse_partials(RowMap rm, int ns
       float x[kStreamUnroll * EPV];
 #pragma unroll
       for (int u = 0; u < kStreamUnroll; ++u) E::unpack(buf[u], x + u * EPV);
-      lse_update<kStreamUnroll * EPV>(st, x, c);
+      float gs[kSlabs];
+      lse_update_g<kStreamUnroll * EPV, EPV>(st, x, c, gs);
+      // bonus tiles park this thread's slab sums in LDS (no registers held across the
+      // workgroup reduction)
+      if (bonus) {
+#pragma unroll
+        for (int u = 0; u < kSlabs; ++u) sSlabT[tid][u] = gs[u];
+      }
     }
+    const float my_m = st.m, my_mc = st.mc;
     st = lse_block_reduce<kStreamBlock>(st, c, lds);
     if (tid == 0) part[((int64_t)g * R + slot) * chunks + ch] = make_float2(st.m, st.s);
+    if (bonus) {
+      // slab sums relative to the tile's m*c: this thread's sums rescaled, plus its head
+      // and tail elements, then summed over the workgroup
+      if (tid == 0) sTileMc = st.mc;
+      __syncthreads();
+      const float Mc = sTileMc;
+      const float f = my_m == kNegInf ? 0.0f : fast_exp2(my_mc - Mc);
+      float slab[kSlabs];
+#pragma unroll
+      for (int u = 0; u < kSlabs; ++u) slab[u] = sSlabT[tid][u] * f;
+      if (tid < head) slab[0] += fast_exp2(fmaf(xh, c, -Mc));
+      if (tid < e1 - a1) {
+        const float t = fast_exp2(fmaf(xt, c, -Mc));
+        const int st_slab = slab_of<DT>(a1 + tid, a0);
+#pragma unroll
+        for (int u = 0; u < kSlabs; ++u)
+          if (u == st_slab) slab[u] += t;
+      }
+      const int lane = tid % kWave, wave = tid / kWave;
+#pragma unroll
+      for (int u = 0; u < kSlabs; ++u) {
+        float v = slab[u];
+#pragma unroll
+        for (int m = kWave / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+        if (lane == 0) sSlab[wave][u] = v;
+      }
+      __syncthreads();
+      if (tid < kSlabs) {
+        float t = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kStreamBlock / kWave; ++w) t += sSlab[w][tid];
+        sub[((int64_t)g * chunks + ch) * kSlabs + tid] = t;
+      }
+    }
     __syncthreads();
   }
 }
@@ -309,12 +381,20 @@ struct ExpRow {
 // ---------------------------------------------------------------------------------
 constexpr int kMaxChunks = kMaxV / kChunkElemsF32;
 constexpr int kMaxPartLds = 1024;  // chunk pairs of one sequence staged in LDS (else read in place)
+constexpr int kMaxSubLds = 1024;   // bonus slab sums of one sequence staged in LDS
+// units per thread for the finalize's one-slab re-read: a slab plus a head or tail of
+// fewer than 8 elements each
+constexpr int kSmcUnits = 2;
+static_assert(kSlabElems<SMCSD_DTYPE_BF16> + 16 <= 8 * kSmcFinalBlock * kSmcUnits &&
+                  kSlabElems<SMCSD_DTYPE_F32> + 16 <= 8 * kSmcFinalBlock * kSmcUnits,
+              "the finalize workgroup must cover one slab");
 
 template <int DT>
 __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
     RowMap rm, const int32_t *__restrict__ draft_tokens, int V, int chunk_elems, int chunks,
     float c, float alpha, uint64_t seed, uint64_t step, const float2 *__restrict__ part,
-    float *__restrict__ lw, int32_t *__restrict__ out_tokens, int32_t *__restrict__ out_num,
+    const float *__restrict__ sub, float *__restrict__ lw, int32_t *__restrict__ out_tokens,
+    int32_t *__restrict__ out_num,
     float *__restrict__ out_logp, float *__restrict__ out_logq, float *__restrict__ out_lse,
     int32_t *status) {
   using E = Elt<DT>;
@@ -326,9 +406,10 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
   __shared__ int32_t sTok[kMaxK + 1];
   __shared__ double sTermK[kMaxChunks];
   __shared__ float2 sPart[kMaxPartLds];
+  __shared__ float sSub[kMaxSubLds];
   __shared__ double sScan[kSmcFinalBlock / kWave];
   __shared__ int sMisc[4];
-  __shared__ int sCh;
+  __shared__ int64_t sLo, sHi;
   __shared__ double sBase;
   __shared__ float sPickLogit;
   __shared__ int sFlags;
@@ -351,6 +432,11 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
   const float2 *gpart = part + (int64_t)g * npart;
   if (part_in_lds)
     for (int i = tid; i < npart; i += kSmcFinalBlock) sPart[i] = gpart[i];
+  const int nsub = chunks * kSlabs;
+  const bool sub_in_lds = nsub <= kMaxSubLds;
+  const float *gsub = sub + (int64_t)g * nsub;
+  if (sub_in_lds)
+    for (int i = tid; i < nsub; i += kSmcFinalBlock) sSub[i] = gsub[i];
   if (tid < 2 * K && x >= 0 && x < V) xv = E::load(rm.row(g, slot), x);
   __syncthreads();
 
@@ -398,6 +484,8 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
   int bonus = -1;
   if (isfinite(SK) && SK > 0.0) {
     if (tid == 0) {
+      // the chunk, then the slab inside it, whose running sum first exceeds the target
+      // (if rounding leaves none, the last one with a positive sum)
       double base = 0.0;
       int ch = chunks - 1;
       for (int i = 0; i < chunks; ++i) {
@@ -407,15 +495,50 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
         }
         base += sTermK[i];
       }
-      sCh = ch;
+      if (ch == chunks - 1 && !(base > target)) {
+        // no crossing: restart the last chunk from its own prefix
+        base = 0.0;
+        for (int i = 0; i < chunks - 1; ++i) base += sTermK[i];
+      }
+      const float2 pk = (part_in_lds ? sPart : gpart)[K * chunks + ch];
+      const double fk =
+          pk.x == kNegInf ? 0.0 : (double)fast_exp2(__fmul_rn(pk.x, c) - sMc[K]);
+      const float *sb = (sub_in_lds ? sSub : gsub) + ch * kSlabs;
+      int sl = -1, last = kSlabs - 1;
+      double base_last = base;
+      for (int u = 0; u < kSlabs; ++u) {
+        const double t = (double)sb[u] * fk;
+        if (base + t > target) {
+          sl = u;
+          break;
+        }
+        if (t > 0.0) {
+          last = u;
+          base_last = base;
+        }
+        base += t;
+      }
+      if (sl < 0) {
+        sl = last;
+        base = base_last;
+      }
+      // slab bounds: the vector body starts at the first 16-byte aligned element
+      const int64_t e0 = (int64_t)ch * chunk_elems;
+      const int64_t e1 = min((int64_t)V, e0 + (int64_t)chunk_elems);
+      const uintptr_t addr0 = reinterpret_cast<uintptr_t>(brow + e0 * E::kBytes);
+      const int64_t a0 = e0 + min((int64_t)(((16 - (addr0 & 15)) & 15) / E::kBytes), e1 - e0);
+      sLo = sl == 0 ? e0 : min(e1, a0 + (int64_t)sl * kSlabElems<DT>);
+      sHi = sl == kSlabs - 1 ? e1 : min(e1, a0 + (int64_t)(sl + 1) * kSlabElems<DT>);
       sBase = base;
     }
     __syncthreads();
-    const int64_t e0 = (int64_t)sCh * chunk_elems;
-    const int64_t e1 = min((int64_t)V, e0 + (int64_t)chunk_elems);
-    const ExpRow<DT> fn{brow, c, sMc[K], (reinterpret_cast<uintptr_t>(brow) & 15) == 0};
-    bonus = chunk_inverse_cdf<kSmcFinalBlock, kUnitsPerThread<DT, kSmcFinalBlock>>(
-        e0, e1, sBase, target, fn, sScan, sMisc, &sPickLogit);
+    const int64_t lo = sLo, hi = sHi;
+    if (hi > lo) {
+      const ExpRow<DT> fn{brow, c, sMc[K],
+                          (reinterpret_cast<uintptr_t>(brow + lo * E::kBytes) & 15) == 0};
+      bonus = chunk_inverse_cdf<kSmcFinalBlock, kSmcUnits>(lo, hi, sBase, target, fn, sScan, sMisc,
+                                                           &sPickLogit);
+    }
   }
 
   double lpK = __builtin_nan("");
@@ -679,14 +802,15 @@ static hipError_t launch_verify_t(const VerifyArgs &a) {
             a.row_stride * esz, a.seq_step, K};
   const VerifyWs w = verify_ws_layout(a.nseq, K, a.V, a.mode);
   float2 *part = reinterpret_cast<float2 *>(a.ws + w.part);
+  float *sub = reinterpret_cast<float *>(a.ws + w.sub);
   const int64_t ntiles = (int64_t)a.nseq * R * chunks;
   const unsigned grid = (unsigned)std::min<int64_t>(ntiles, (int64_t)1 << 30);
 
   if (a.mode == SMCSD_MODE_SMC) {
     hipLaunchKernelGGL(k_lse_partials<DT>, dim3(grid), dim3(kStreamBlock), 0, a.stream, rm, a.nseq,
-                       a.V, ce, chunks, a.c, part, ntiles);
+                       a.V, ce, chunks, a.c, part, sub, ntiles);
     hipLaunchKernelGGL(k_smc_finalize<DT>, dim3(a.nseq), dim3(kSmcFinalBlock), 0, a.stream, rm,
-                       a.draft_tokens, a.V, ce, chunks, a.c, a.alpha, a.seed, a.step, part,
+                       a.draft_tokens, a.V, ce, chunks, a.c, a.alpha, a.seed, a.step, part, sub,
                        a.log_weights, a.out_tokens, a.out_num_tokens, a.out_logp, a.out_logq,
                        a.out_lse, a.status);
     return hipGetLastError();
@@ -696,7 +820,7 @@ static hipError_t launch_verify_t(const VerifyArgs &a) {
   float2 *part2 = reinterpret_cast<float2 *>(a.ws + w.part2);
   if (!a.lse_in)
     hipLaunchKernelGGL(k_lse_partials<DT>, dim3(grid), dim3(kStreamBlock), 0, a.stream, rm, a.nseq,
-                       a.V, ce, chunks, a.c, part, ntiles);
+                       a.V, ce, chunks, a.c, part, sub, ntiles);
   hipLaunchKernelGGL(k_sps_decide<DT>, dim3(a.nseq), dim3(kWave), 0, a.stream, rm, a.draft_tokens,
                      a.V, chunks, a.c, a.seed, a.step, part, a.lse_in, kstar, norm, a.out_tokens,
                      a.out_num_tokens, a.out_logp, a.out_logq, a.out_lse, a.status);
