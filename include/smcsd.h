@@ -86,8 +86,9 @@ const char *smcsd_status_string(int code);
  * start must be 256-byte aligned (SMCSD_EWORKSPACE otherwise).
  *   SMCSD_OP_VERIFY_SMC / _SPS: B, N, K, V as passed to smcsd_verify (P ignored).
  *   SMCSD_OP_KV: B, N and the pool size P (K, V ignored).  The KV workspace must be
- *   zero-filled before its first use; every smcsd_kv_reassign call leaves the parts that
- *   must start at zero (its freed-block bitmap and arrival counter) zeroed again.
+ *   zero-filled before its first use and then passed, unmodified, to every later call
+ *   with the same B, N and P: calls keep its contents consistent (it alternates two
+ *   freed-block bitmaps and clears the one the previous call used).
  * Returns 0 for invalid sizes.
  */
 size_t smcsd_workspace_bytes(int op, int B, int N, int K, int V, int64_t P);
@@ -192,7 +193,7 @@ int smcsd_resample(float *log_weights, int B, int N, float tau, uint64_t seed, u
  * (previous seq_len + K+1).
  * Limits: 1 <= N <= 1024; ceil((seq_len+reserve_tokens)/block_size) <= M_cap.
  * workspace: smcsd_workspace_bytes(SMCSD_OP_KV, B, N, 0, 0, P), zero-filled before
- * first use (each call leaves its freed-block bitmap and counter zeroed again).
+ * first use and kept, unmodified, between calls.
  */
 int smcsd_kv_reassign(const int32_t *ancestors, const int32_t *resampled, int B, int N,
                       int32_t *block_tables, int M_cap, int block_size, int64_t seq_len,

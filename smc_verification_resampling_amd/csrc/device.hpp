@@ -207,6 +207,56 @@ __device__ __forceinline__ Lse lse_block_reduce(Lse st, float c, Lse *lds) {
   return st;
 }
 
+// Workgroup reduction of the online state together with NS sums that share its
+// reference (each is relative to the thread's mc and is rescaled with s at every
+// combine).  Results valid in thread 0: the state, and the sums relative to its mc.
+template <int BLOCK, int NS>
+__device__ __forceinline__ Lse lse_block_reduce_with(Lse st, float (&v)[NS], float c,
+                                                     float *lds) {
+  auto combine = [&](float om, float omc, float os, const float *ov) {
+    const float M = fmaxf(st.m, om);
+    if (M == kNegInf) {
+      st.s += os;
+#pragma unroll
+      for (int q = 0; q < NS; ++q) v[q] += ov[q];
+      return;
+    }
+    const float Mc = __fmul_rn(M, c);
+    const bool ainf = st.m == kNegInf, binf = om == kNegInf;
+    const float fa = ainf ? 0.0f : fast_exp2(st.mc - Mc);
+    const float fb = binf ? 0.0f : fast_exp2(omc - Mc);
+    st.s = (ainf ? st.s * 0.0f : st.s * fa) + (binf ? os * 0.0f : os * fb);
+#pragma unroll
+    for (int q = 0; q < NS; ++q) v[q] = (ainf ? v[q] * 0.0f : v[q] * fa) + (binf ? ov[q] * 0.0f : ov[q] * fb);
+    st.m = M;
+    st.mc = Mc;
+  };
+#pragma unroll
+  for (int mask = 1; mask < kWave; mask <<= 1) {
+    float ov[NS];
+#pragma unroll
+    for (int q = 0; q < NS; ++q) ov[q] = __shfl_xor(v[q], mask, kWave);
+    combine(__shfl_xor(st.m, mask, kWave), __shfl_xor(st.mc, mask, kWave),
+            __shfl_xor(st.s, mask, kWave), ov);
+  }
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  constexpr int kRec = 3 + NS;
+  if (lane == 0) {
+    lds[wave * kRec + 0] = st.m;
+    lds[wave * kRec + 1] = st.mc;
+    lds[wave * kRec + 2] = st.s;
+#pragma unroll
+    for (int q = 0; q < NS; ++q) lds[wave * kRec + 3 + q] = v[q];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int w = 1; w < BLOCK / kWave; ++w)
+      combine(lds[w * kRec + 0], lds[w * kRec + 1], lds[w * kRec + 2], lds + w * kRec + 3);
+  }
+  return st;
+}
+
 // ---------------------------------------------------------------------------------
 // scans and sums
 // ---------------------------------------------------------------------------------

@@ -6,20 +6,22 @@
 // management).  Integer work only, two launches per call, bit-deterministic although it
 // uses atomics:
 //   * k_kv, one workgroup per prompt: the exchange over column tiles of the prompt's
-//     tables staged in LDS.  Columns whose entries are all equal (shared prefixes) keep
-//     their blocks and counts and are skipped.  Down each other column, a run of equal
-//     blocks gets one refcount update, sum over the run of (c_j - 1); all increments are
-//     performed (waited for, then a barrier) before any decrement, so a block that stays
-//     referenced never reaches 0, and the decrement that brings a count to 0 marks the
-//     block in a freed bitmap exactly once (a block lives in one column of one prompt).
-//     Then the gathered tables and the copy-on-write decision for the partial tail.  The
-//     last workgroup to finish (a device-scope counter with release / acquire fences)
-//     counts the freed blocks per group of bitmap words, lays out every sequence's pops
-//     and sets the new stack top.
-//   * k_kv_pop, one thread per bitmap word and one per sequence: a freed block's rank in
-//     ascending id order fixes its stack position (pushed in descending id order) and,
-//     if that pop is requested, the table slot it fills; sequences take their remaining
-//     pops from the old stack and write their copy-on-write records.
+//     tables staged in LDS.  Down each column (one thread per column and 16-row segment)
+//     a run of equal blocks gets one refcount change, sum over the run of (c_j - 1); all
+//     increments are performed (waited for, then a barrier) before any decrement, so a
+//     block that stays referenced never reaches 0, and the decrement that brings a count
+//     to 0 marks the block in a freed bitmap and counts it in its group of 8192 ids,
+//     exactly once.  Then the gathered tables and the copy-on-write decision for the
+//     partial tail.
+//   * k_kv_pop_fast (up to 8192 sequences), one thread per bitmap word and one per
+//     sequence: every workgroup first forms the group-count prefix and the copy-on-write
+//     prefix itself; a freed block's rank in ascending id order fixes its stack position
+//     (pushed in descending id order) and, if that pop is requested, the table slot it
+//     fills; sequences take their remaining pops from the old stack.
+//   * with more sequences, the last k_kv workgroup to finish (a device-scope counter with
+//     release / acquire fences) lays out the pops for k_kv_pop instead.
+// The bitmap and group counts alternate between two buffers by call parity, so a call
+// clears the pair its predecessor used while nobody reads it.
 #include "device.hpp"
 #include "internal.hpp"
 #include "kv_layout.hpp"
@@ -31,6 +33,7 @@ constexpr int kKvTileInts = 8192;  // table entries staged per column tile (32 K
 constexpr int kStage = 16;         // table loads in flight per thread while staging
 constexpr int kNegBatch = 4;       // decrements in flight per thread
 constexpr int kHash = 2 * kMaxN;   // open-addressing table of the tail blocks (load <= 1/2)
+constexpr int kSeg = 16;           // table rows one thread walks down a column
 
 // Wait until every memory operation this wave issued (atomics included) has completed.
 __device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
@@ -59,26 +62,40 @@ __device__ __forceinline__ int tail_hash(int32_t blk) {
   return (int)(((uint32_t)blk * 0x9E3779B1u) >> 21) & (kHash - 1);
 }
 
+struct KvBufs {
+  uint32_t *bitmap2;  // two bitmaps of nwp words
+  int32_t *gcount2;   // two arrays of ngp group counts
+  int nwords, ngroups, nwp, ngp;
+  int32_t *cow_src, *cow_excl, *gbase, *popmap, *done, *ctr, *scal;
+};
+
 __global__ __launch_bounds__(kKvBlock) void k_kv(
     const int32_t *__restrict__ anc, const int32_t *__restrict__ resampled, int B, int N,
     int32_t *__restrict__ T, int M_cap, int nb_old, int nb_new, int tail_slot, int tail_mod,
-    int32_t *__restrict__ rc, int P, int32_t *__restrict__ free_top,
-    uint32_t *__restrict__ bitmap, int32_t *__restrict__ cow_src, int32_t *__restrict__ cow_excl,
-    int32_t *__restrict__ gbase, int32_t *__restrict__ popmap, int32_t *__restrict__ scal,
-    int32_t *__restrict__ done, int32_t *__restrict__ cow_count, int32_t *status) {
+    int32_t *__restrict__ rc, int P, int32_t *__restrict__ free_top, KvBufs wb, int fast,
+    int32_t *__restrict__ cow_count, int32_t *status) {
   __shared__ int32_t a[kMaxN], cnt[kMaxN], tail_old[kMaxN], tail_new[kMaxN];
   __shared__ int32_t tile[kKvTileInts];
   __shared__ uint8_t colu[kKvTileInts];  // column of the tile holds one block in every row
   __shared__ int2 negl[kKvTileInts];     // (block, decrement); later the tail hash table
-  __shared__ int gcnt[kKvBlock];
   __shared__ int red[kKvBlock / kWave];
   __shared__ int sFlags, sValid, sLast, sNeg;
   const int b = blockIdx.x, tid = threadIdx.x;
   const int row0 = b * N;
   const int tail_partial = tail_mod != 0;
+  int32_t *__restrict__ cow_src = wb.cow_src;
   if (tid == 0) {
     sFlags = 0;
     sValid = 1;
+  }
+  // the call counter is only read here (the pop kernel advances it); its parity selects
+  // this call's bitmap and group counts
+  const int C = *wb.ctr;
+  uint32_t *__restrict__ bitmap = wb.bitmap2 + (C & 1) * wb.nwp;
+  int32_t *__restrict__ gcount = wb.gcount2 + (C & 1) * wb.ngp;
+  if (b == 0 && tid == 0) {
+    wb.scal[0] = *free_top;
+    wb.scal[3] = C;
   }
   // the ancestor row is read whether or not the prompt resampled, so both loads overlap
   const int res = resampled[b] != 0;
@@ -101,6 +118,7 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
   if (do_exchange) {
     for (int i = tid; i < N; i += kKvBlock) atomicAdd(&cnt[a[i]], 1);
     const int W = max(1, min(nb_old, kKvTileInts / N));
+    const int nseg = (N + kSeg - 1) / kSeg;
     for (int s0 = 0; s0 < nb_old; s0 += W) {
       const int w = min(W, nb_old - s0), nw = N * w;
       for (int e0 = tid; e0 < nw; e0 += kKvBlock * kStage) {
@@ -118,29 +136,66 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
           if (e < nw) tile[j * W + s] = v[k];
         }
       }
-      for (int s = tid; s < w; s += kKvBlock) colu[s] = 1;
       if (tid == 0) sNeg = 0;
+      if (nseg > 1)
+        for (int s = tid; s < w; s += kKvBlock) colu[s] = 1;
       __syncthreads();
-      for (int e = tid; e < nw; e += kKvBlock) {
-        const int j = e / w, s = e - j * w;
-        if (j > 0 && tile[j * W + s] != tile[(j - 1) * W + s]) colu[s] = 0;
-      }
-      __syncthreads();
-      // a uniform column keeps its block: the sum of (c_j - 1) over all rows is 0
-      for (int e = tid; e < nw; e += kKvBlock) {
-        const int j = e / w, s = e - j * w;
-        if (colu[s]) continue;
-        const int32_t blk = tile[j * W + s];
-        if (j > 0 && tile[(j - 1) * W + s] == blk) continue;  // not the head of its run
-        int delta = 0;
-        for (int jj = j; jj < N && tile[jj * W + s] == blk; ++jj) delta += cnt[jj] - 1;
-        if (delta == 0) continue;
-        if (blk < 0 || blk >= P) {
-          atomicOr(&sFlags, SMCSD_ST_BAD_INPUT);
-          continue;
+      if (nseg > 1) {
+        // columns of more than one segment: flag the uniform ones (a block shared by every
+        // row keeps its count, the sum of (c_j - 1) over all rows being 0)
+        for (int e = tid; e < nw; e += kKvBlock) {
+          const int j = e / w, s = e - j * w;
+          if (j > 0 && tile[j * W + s] != tile[(j - 1) * W + s]) colu[s] = 0;
         }
-        if (delta > 0) atomicAdd(&rc[blk], delta);
-        else negl[atomicAdd(&sNeg, 1)] = make_int2(blk, delta);
+        __syncthreads();
+      }
+      // one thread per (column, segment of kSeg rows): gather the new tables, then give
+      // each run of equal blocks down the segment one refcount change, the sum of (c_j - 1)
+      // over the run.  Increments are issued at once; decrements are listed for after
+      // them (a run split over segments gets one change per piece: every piece that
+      // increments still lands before every piece that decrements).
+      for (int it = tid; it < w * nseg; it += kKvBlock) {
+        const int sg = it / w, s = it - sg * w;
+        const int j0 = sg * kSeg, j1 = min(N, j0 + kSeg);
+        int32_t v[kSeg];
+        int d[kSeg];
+#pragma unroll
+        for (int k = 0; k < kSeg; ++k) {
+          const int j = min(j0 + k, N - 1);
+          v[k] = tile[j * W + s];
+          d[k] = cnt[j] - 1;
+        }
+        const bool is_tail = tail_partial && s0 + s == tail_slot;
+#pragma unroll
+        for (int k = 0; k < kSeg; ++k) {
+          const int i = j0 + k;
+          if (i < j1) {
+            const int32_t nv = tile[a[i] * W + s];
+            if (nv != v[k]) T[(row0 + i) * M_cap + s0 + s] = nv;
+            if (is_tail) tail_old[i] = v[k];
+          }
+        }
+        if (nseg > 1 && colu[s]) continue;
+        int32_t blk = v[0];
+        int acc = 0;
+        auto flush = [&]() {
+          if (acc == 0) return;
+          if (blk < 0 || blk >= P) atomicOr(&sFlags, SMCSD_ST_BAD_INPUT);
+          else if (acc > 0) atomicAdd(&rc[blk], acc);
+          else negl[atomicAdd(&sNeg, 1)] = make_int2(blk, acc);
+        };
+#pragma unroll
+        for (int k = 0; k < kSeg; ++k) {
+          if (j0 + k < j1) {
+            if (v[k] != blk) {
+              flush();
+              blk = v[k];
+              acc = 0;
+            }
+            acc += d[k];
+          }
+        }
+        flush();
       }
       wait_memory();  // increments performed before any decrement
       __syncthreads();
@@ -157,14 +212,10 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
         for (int k = 0; k < kNegBatch; ++k) old[k] = q[k].y ? atomicAdd(&rc[q[k].x], q[k].y) : 1;
 #pragma unroll
         for (int k = 0; k < kNegBatch; ++k)
-          if (q[k].y && old[k] + q[k].y == 0) atomicOr(&bitmap[q[k].x >> 5], 1u << (q[k].x & 31));
-      }
-      if (tail_partial && tail_slot >= s0 && tail_slot < s0 + w)
-        for (int j = tid; j < N; j += kKvBlock) tail_old[j] = tile[j * W + (tail_slot - s0)];
-      for (int e = tid; e < nw; e += kKvBlock) {
-        const int i = e / w, s = e - i * w;
-        const int32_t v = tile[a[i] * W + s];
-        if (v != tile[i * W + s]) T[(row0 + i) * M_cap + s0 + s] = v;
+          if (q[k].y && old[k] + q[k].y == 0) {
+            atomicOr(&bitmap[q[k].x >> 5], 1u << (q[k].x & 31));
+            atomicAdd(&gcount[q[k].x / kKvGroupBlocks], 1);
+          }
       }
       __syncthreads();
     }
@@ -215,10 +266,13 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
   __syncthreads();
   if (tid == 0 && sFlags) atomicOr(status, sFlags);
 
-  // ---- the last workgroup to arrive ranks the freed blocks and lays out the pops
+  if (fast) return;
+
+  // ---- many sequences: the last workgroup to arrive forms the group rank bases and lays
+  // out the pops for k_kv_pop
   __threadfence();
   __syncthreads();
-  if (tid == 0) sLast = atomicAdd(done, 1) == B - 1;
+  if (tid == 0) sLast = atomicAdd(wb.done, 1) == B - 1;
   __syncthreads();
   if (!sLast) return;
   __threadfence();
@@ -229,143 +283,269 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
   const int g0 = min(S, tid * sper), g1 = min(S, g0 + sper);
   int mycow = 0;
   for (int g = g0; g < g1; ++g) mycow += cow_src[g] != 0;
-
-  // freed blocks per group of kKvGroupWords bitmap words: wave w sums the groups
-  // congruent to w mod 4, one 16-byte load per lane per group (the bitmap region is
-  // padded to 64 words, so a load that starts below nwords stays inside it)
-  const int nwords = (P + 31) / 32;
-  const int ngroups = (nwords + kKvGroupWords - 1) / kKvGroupWords;
-  const int lane = tid % kWave, wave = tid / kWave;
-  const uint4 *bm4 = reinterpret_cast<const uint4 *>(bitmap);
   int F = 0;
-  for (int r0 = 0; r0 < ngroups; r0 += kKvBlock) {
-    const int ng = min(kKvBlock, ngroups - r0);
-    for (int k0 = wave; k0 < ng; k0 += 8 * (kKvBlock / kWave)) {
-      int c[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int gi = k0 + k * (kKvBlock / kWave);
-        const int w4 = (r0 + gi) * kKvGroupWords + lane * 4;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (gi < ng && w4 < nwords) v = bm4[w4 / 4];
-        c[k] = __popc(v.x) + __popc(v.y) + __popc(v.z) + __popc(v.w);
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        int x = c[k];
-        for (int m = kWave / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
-        const int gi = k0 + k * (kKvBlock / kWave);
-        if (lane == 0 && gi < ng) gcnt[gi] = x;
-      }
-    }
-    __syncthreads();
+  for (int r0 = 0; r0 < wb.ngroups; r0 += kKvBlock) {
+    const int q = r0 + tid;
     int tot;
-    const int ex = kv_scan(tid < ng ? gcnt[tid] : 0, red, &tot);
-    if (tid < ng) gbase[r0 + tid] = F + ex;
+    const int ex = kv_scan(q < wb.ngroups ? gcount[q] : 0, red, &tot);
+    if (q < wb.ngroups) wb.gbase[q] = F + ex;
     F += tot;
   }
 
   // pop layout: sequence g owns pop indices [g*nfresh + cow_excl[g], ... + cow_g + nfresh);
   // pop k < F takes the freed block of ascending rank k, recorded in popmap for the pop
   // kernel, and pop k >= F the old stack entry at top + F - 1 - k
-  int C;
-  int ci = kv_scan(mycow, red, &C);
+  int Ctot;
+  int ci = kv_scan(mycow, red, &Ctot);
   const int64_t avail = (int64_t)top + F;
   int ok_cow = 0;  // copy-on-writes whose pop falls inside the stack
   for (int g = g0; g < g1; ++g) {
     const int f = cow_src[g] != 0;
-    cow_excl[g] = ci;
+    wb.cow_excl[g] = ci;
     const int64_t k0 = (int64_t)g * nfresh + ci;
     ok_cow += f && k0 < avail;
-    for (int64_t k = k0; k < k0 + f + nfresh && k < F; ++k) popmap[k] = g;
+    for (int64_t k = k0; k < k0 + f + nfresh && k < F; ++k) wb.popmap[k] = g;
     ci += f;
   }
   int ncow_ok;
   kv_scan(ok_cow, red, &ncow_ok);
   if (tid == 0) {
-    const int64_t npops = (int64_t)S * nfresh + C;
-    scal[0] = top;
-    scal[1] = F;
-    scal[2] = (int32_t)min(npops, (int64_t)INT32_MAX);
+    const int64_t npops = (int64_t)S * nfresh + Ctot;
+    wb.scal[1] = F;
+    wb.scal[2] = (int32_t)min(npops, (int64_t)INT32_MAX);
     const int64_t nt = avail - npops;
     *free_top = (int32_t)(nt > 0 ? nt : 0);
     *cow_count = ncow_ok;
-    *done = 0;
+    *wb.done = 0;
   }
 }
 
-// Workgroups [0, ngroups): one thread per freed-bitmap word; the rest: one thread per
-// sequence.  A sequence's copy-on-write (tail slot) pops first, then its fresh slots.
+// Clear the bitmap and group counts of the other parity (used by the previous call) and,
+// from workgroup 0, advance the call counter.
+__device__ __forceinline__ void kv_clear_other(const KvBufs &wb, int C) {
+  uint32_t *ob = wb.bitmap2 + ((C + 1) & 1) * wb.nwp;
+  int32_t *og = wb.gcount2 + ((C + 1) & 1) * wb.ngp;
+  const int stride = gridDim.x * kKvBlock;
+  for (int i = blockIdx.x * kKvBlock + threadIdx.x; i < wb.nwords; i += stride) ob[i] = 0u;
+  for (int i = blockIdx.x * kKvBlock + threadIdx.x; i < wb.ngroups; i += stride) og[i] = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *wb.ctr = C + 1;
+}
+
+// Pops of one sequence (one thread per sequence): its copy-on-write (tail slot) pops
+// first, then its fresh slots; pop k takes the freed block of rank k when k < F (written
+// by the bitmap-word threads) and otherwise the old stack entry at top + F - 1 - k.
+__device__ __forceinline__ int kv_sequence_pops(int g, int32_t cs, int ce, int nfresh, int F,
+                                                int64_t avail, int32_t *__restrict__ T, int M_cap,
+                                                int nb_old, int tail_slot, int tail_mod,
+                                                int32_t *__restrict__ rc, int P,
+                                                const int32_t *__restrict__ free_list,
+                                                int32_t *__restrict__ cow) {
+  int flags = 0;
+  int64_t k = (int64_t)g * nfresh + ce;
+  for (int st = cs ? -1 : 0; st < nfresh; ++st, ++k) {
+    if (k >= avail) {
+      flags |= SMCSD_ST_NOSPACE;
+      continue;
+    }
+    int32_t d = -1;
+    if (k >= F) {  // from the old stack
+      const int64_t pos = avail - 1 - k;
+      d = pos < P ? free_list[pos] : -1;
+      if (d < 0 || d >= P) {
+        flags |= SMCSD_ST_BAD_INPUT;
+        continue;
+      }
+    }
+    if (st < 0) {
+      atomicSub(&rc[cs - 1], 1);
+      cow[3 * ce + 0] = cs - 1;
+      cow[3 * ce + 2] = tail_mod;
+    }
+    if (d >= 0) {
+      rc[d] = 1;
+      T[(int64_t)g * M_cap + (st < 0 ? tail_slot : nb_old + st)] = d;
+      if (st < 0) cow[3 * ce + 1] = d;
+    }
+  }
+  return flags;
+}
+
+// A freed block d of ascending rank r: stack position top + F - 1 - r (pushed in
+// descending id order); if pop r is requested (r < npops) it also fills that pop's slot
+// of sequence g, whose pops start at start_g and begin with a copy-on-write when f = 1.
+__device__ __forceinline__ void kv_place_freed(int32_t d, int64_t r, int64_t avail, int P,
+                                               int32_t *__restrict__ free_list, int &flags) {
+  const int64_t pos = avail - 1 - r;
+  if (pos >= 0 && pos < P) free_list[pos] = d;
+  else flags |= SMCSD_ST_BAD_INPUT;
+}
+__device__ __forceinline__ void kv_fill_pop(int32_t d, int g, int st, int ce, int32_t *__restrict__ T,
+                                            int M_cap, int nb_old, int tail_slot,
+                                            int32_t *__restrict__ rc, int32_t *__restrict__ cow) {
+  rc[d] = 1;
+  T[(int64_t)g * M_cap + (st < 0 ? tail_slot : nb_old + st)] = d;
+  if (st < 0) cow[3 * ce + 1] = d;
+}
+
+// Many-sequence path.  Workgroups [0, ngroups): one thread per word of this call's bitmap;
+// the rest: one thread per sequence.  Uses the layout the last k_kv workgroup wrote.
 __global__ __launch_bounds__(kKvBlock) void k_kv_pop(
-    int S, int ngroups, int nwords, int32_t *__restrict__ T, int M_cap, int nb_old, int nb_new,
-    int tail_slot, int tail_mod, int32_t *__restrict__ rc, int P, int32_t *__restrict__ free_list,
-    uint32_t *__restrict__ bitmap, const int32_t *__restrict__ cow_src,
-    const int32_t *__restrict__ cow_excl, const int32_t *__restrict__ gbase,
-    const int32_t *__restrict__ popmap, const int32_t *__restrict__ scal,
+    int S, int32_t *__restrict__ T, int M_cap, int nb_old, int nb_new, int tail_slot,
+    int tail_mod, int32_t *__restrict__ rc, int P, int32_t *__restrict__ free_list, KvBufs wb,
     int32_t *__restrict__ cow, int32_t *status) {
+  __shared__ int32_t sList[kKvGroupBlocks];  // this group's freed block ids, ascending
   __shared__ int red[kKvBlock / kWave];
   const int tid = threadIdx.x;
   const int nfresh = nb_new - nb_old;
-  const int F = scal[1], npops = scal[2];
-  const int64_t avail = (int64_t)scal[0] + F;
+  const int C = wb.scal[3];
+  const int F = wb.scal[1], npops = wb.scal[2];
+  const int64_t avail = (int64_t)wb.scal[0] + F;
+  const uint32_t *bitmap = wb.bitmap2 + (C & 1) * wb.nwp;
   int flags = 0;
-  if ((int)blockIdx.x < ngroups) {
-    // the freed block of ascending rank r goes to stack position top + F - 1 - r (pushed
-    // in descending id order); if pop r is requested it also fills that pop's slot
+  if ((int)blockIdx.x < wb.ngroups) {
     const int gi = blockIdx.x;
     const int w = gi * kKvGroupWords + tid;
-    uint32_t bits = w < nwords ? bitmap[w] : 0u;
-    const int base = gbase[gi];
+    uint32_t bits = w < wb.nwords ? bitmap[w] : 0u;
+    const int base = wb.gbase[gi];
     int tot;
-    int r = base + kv_scan(__popc(bits), red, &tot);
-    if (bits) bitmap[w] = 0u;
-    for (; bits; bits &= bits - 1, ++r) {
-      const int32_t d = w * 32 + __ffs(bits) - 1;
-      const int64_t pos = avail - 1 - r;
-      if (pos >= 0 && pos < P) free_list[pos] = d;
-      else flags |= SMCSD_ST_BAD_INPUT;
+    int j = kv_scan(__popc(bits), red, &tot);
+    for (; bits; bits &= bits - 1, ++j) sList[j] = w * 32 + __ffs(bits) - 1;
+    __syncthreads();
+    for (int i = tid; i < tot; i += kKvBlock) {
+      const int32_t d = sList[i];
+      const int64_t r = (int64_t)base + i;
+      kv_place_freed(d, r, avail, P, free_list, flags);
       if (r < npops) {
-        const int g = popmap[r];
-        const int f = cow_src[g] != 0, ce = cow_excl[g];
+        const int g = wb.popmap[r];
+        const int f = wb.cow_src[g] != 0, ce = wb.cow_excl[g];
         const int st = (int)(r - ((int64_t)g * nfresh + ce)) - f;
-        rc[d] = 1;
-        T[(int64_t)g * M_cap + (st < 0 ? tail_slot : nb_old + st)] = d;
-        if (st < 0) cow[3 * ce + 1] = d;
+        if (st >= -f && st < nfresh) kv_fill_pop(d, g, st, ce, T, M_cap, nb_old, tail_slot, rc, cow);
       }
     }
   } else {
-    const int g = (blockIdx.x - ngroups) * kKvBlock + tid;
-    if (g < S) {
-      const int32_t cs = cow_src[g];
-      const int ce = cow_excl[g];
-      int64_t k = (int64_t)g * nfresh + ce;
-      for (int st = cs ? -1 : 0; st < nfresh; ++st, ++k) {
-        if (k >= avail) {
-          flags |= SMCSD_ST_NOSPACE;
-          continue;
+    const int g = (blockIdx.x - wb.ngroups) * kKvBlock + tid;
+    if (g < S)
+      flags |= kv_sequence_pops(g, wb.cow_src[g], wb.cow_excl[g], nfresh, F, avail, T, M_cap,
+                                nb_old, tail_slot, tail_mod, rc, P, free_list, cow);
+  }
+  kv_clear_other(wb, C);
+  if (flags) atomicOr(status, flags);
+}
+
+// One-pass path (S <= kKvFastSeqMax, ngroups <= kKvFastGroupMax): every workgroup forms the
+// group-count prefix and the copy-on-write prefix itself, then workgroups [0, ngroups)
+// place the freed blocks of their bitmap words and the rest make the sequences' pops.
+constexpr int kGPer = kKvFastGroupMax / kKvBlock;
+constexpr int kSPer = kKvFastSeqMax / kKvBlock;
+
+__global__ __launch_bounds__(kKvBlock) void k_kv_pop_fast(
+    int S, int32_t *__restrict__ T, int M_cap, int nb_old, int nb_new, int tail_slot,
+    int tail_mod, int32_t *__restrict__ rc, int P, int32_t *__restrict__ free_list,
+    int32_t *__restrict__ free_top, KvBufs wb, int32_t *__restrict__ cow,
+    int32_t *__restrict__ cow_count, int32_t *status) {
+  __shared__ int32_t sSrc[kKvFastSeqMax];  // copy-on-write source + 1 per sequence
+  __shared__ int32_t sEx[kKvFastSeqMax];   // exclusive prefix of the copy-on-write flags
+  __shared__ int32_t sList[kKvGroupBlocks];  // this group's freed block ids, ascending
+  __shared__ int red[kKvBlock / kWave];
+  const int tid = threadIdx.x;
+  const int gi = blockIdx.x;
+  const bool word_wg = gi < wb.ngroups;
+  const int nfresh = nb_new - nb_old;
+
+  // one round of loads: scalars, this group's word in both bitmaps, both parities of the
+  // group counts, this thread's run of copy-on-write sources
+  const int C = wb.scal[3], top = wb.scal[0];
+  const int w = gi * kKvGroupWords + tid;
+  uint32_t wb0 = 0u, wb1 = 0u;
+  if (word_wg && w < wb.nwords) {
+    wb0 = wb.bitmap2[w];
+    wb1 = wb.bitmap2[wb.nwp + w];
+  }
+  int gc0[kGPer], gc1[kGPer];
+#pragma unroll
+  for (int k = 0; k < kGPer; ++k) {
+    const int q = tid + k * kKvBlock;
+    gc0[k] = q < wb.ngroups ? wb.gcount2[q] : 0;
+    gc1[k] = q < wb.ngroups ? wb.gcount2[wb.ngp + q] : 0;
+  }
+  const int sper = (S + kKvBlock - 1) / kKvBlock;
+  const int g0 = min(S, tid * sper), g1 = min(S, g0 + sper);
+  int cs[kSPer];
+#pragma unroll
+  for (int k = 0; k < kSPer; ++k) cs[k] = g0 + k < g1 ? wb.cow_src[g0 + k] : 0;
+
+  const int par = C & 1;
+  const uint32_t bits0 = par ? wb1 : wb0;
+  int Fpart = 0, below = 0, mycow = 0;
+#pragma unroll
+  for (int k = 0; k < kGPer; ++k) {
+    const int v = par ? gc1[k] : gc0[k];
+    Fpart += v;
+    if (tid + k * kKvBlock < gi) below += v;
+  }
+#pragma unroll
+  for (int k = 0; k < kSPer; ++k) mycow += cs[k] != 0;
+  int F, base, Ctot;
+  kv_scan(Fpart, red, &F);
+  kv_scan(below, red, &base);
+  int ci = kv_scan(mycow, red, &Ctot);
+#pragma unroll
+  for (int k = 0; k < kSPer; ++k) {
+    if (g0 + k < g1) {
+      sSrc[g0 + k] = cs[k];
+      sEx[g0 + k] = ci;
+    }
+    ci += cs[k] != 0;
+  }
+  const int64_t avail = (int64_t)top + F;
+  const int64_t npops = (int64_t)S * nfresh + Ctot;
+  __syncthreads();
+
+  int flags = 0;
+  if (word_wg) {
+    // the group's freed ids in ascending order into LDS (freed blocks cluster in low ids,
+    // so a word can hold many), then one thread per freed block
+    uint32_t bits = bits0;
+    int tot;
+    int j = kv_scan(__popc(bits), red, &tot);
+    for (; bits; bits &= bits - 1, ++j) sList[j] = w * 32 + __ffs(bits) - 1;
+    __syncthreads();
+    for (int i = tid; i < tot; i += kKvBlock) {
+      const int32_t d = sList[i];
+      const int64_t r = (int64_t)base + i;
+      kv_place_freed(d, r, avail, P, free_list, flags);
+      if (r < npops) {
+        // the owner of pop r: the last sequence whose first pop index is <= r
+        int lo = 0, hi = S - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if ((int64_t)mid * nfresh + sEx[mid] <= r) lo = mid;
+          else hi = mid - 1;
         }
-        int32_t d = -1;
-        if (k >= F) {  // from the old stack
-          const int64_t pos = avail - 1 - k;
-          d = pos < P ? free_list[pos] : -1;
-          if (d < 0 || d >= P) {
-            flags |= SMCSD_ST_BAD_INPUT;
-            continue;
-          }
-        }
-        if (st < 0) {
-          atomicSub(&rc[cs - 1], 1);
-          cow[3 * ce + 0] = cs - 1;
-          cow[3 * ce + 2] = tail_mod;
-        }
-        if (d >= 0) {
-          rc[d] = 1;
-          T[(int64_t)g * M_cap + (st < 0 ? tail_slot : nb_old + st)] = d;
-          if (st < 0) cow[3 * ce + 1] = d;
-        }
+        const int ce = sEx[lo], f = sSrc[lo] != 0;
+        const int st = (int)(r - ((int64_t)lo * nfresh + ce)) - f;
+        if (st >= -f && st < nfresh) kv_fill_pop(d, lo, st, ce, T, M_cap, nb_old, tail_slot, rc, cow);
       }
     }
+    if (gi == 0) {
+      // copy-on-writes whose pop falls inside the stack, and the new top
+      int ok = 0;
+      for (int g = g0; g < g1; ++g) ok += sSrc[g] != 0 && (int64_t)g * nfresh + sEx[g] < avail;
+      int ncow_ok;
+      kv_scan(ok, red, &ncow_ok);
+      if (tid == 0) {
+        const int64_t nt = avail - npops;
+        *free_top = (int32_t)(nt > 0 ? nt : 0);
+        *cow_count = ncow_ok;
+      }
+    }
+  } else {
+    const int g = (gi - wb.ngroups) * kKvBlock + tid;
+    if (g < S)
+      flags |= kv_sequence_pops(g, sSrc[g], sEx[g], nfresh, F, avail, T, M_cap, nb_old,
+                                tail_slot, tail_mod, rc, P, free_list, cow);
   }
+  kv_clear_other(wb, C);
   if (flags) atomicOr(status, flags);
 }
 
@@ -375,25 +555,35 @@ hipError_t launch_kv(const int32_t *anc, const int32_t *resampled, int B, int N,
                      int32_t *status, char *ws, hipStream_t stream) {
   const int S = B * N;
   const KvWs w = kv_ws_layout(S, P);
-  uint32_t *bitmap = reinterpret_cast<uint32_t *>(ws + w.bitmap);
-  int32_t *cow_src = reinterpret_cast<int32_t *>(ws + w.cow_src);
-  int32_t *cow_excl = reinterpret_cast<int32_t *>(ws + w.cow_excl);
-  int32_t *gbase = reinterpret_cast<int32_t *>(ws + w.gbase);
-  int32_t *popmap = reinterpret_cast<int32_t *>(ws + w.popmap);
-  int32_t *done = reinterpret_cast<int32_t *>(ws + w.done);
-  int32_t *scal = reinterpret_cast<int32_t *>(ws + w.scal);
+  KvBufs wb;
+  wb.bitmap2 = reinterpret_cast<uint32_t *>(ws + w.bitmap);
+  wb.gcount2 = reinterpret_cast<int32_t *>(ws + w.gcount);
+  wb.nwords = (int)w.nwords;
+  wb.ngroups = (int)w.ngroups;
+  wb.nwp = (int)w.nwp;
+  wb.ngp = (int)w.ngp;
+  wb.cow_src = reinterpret_cast<int32_t *>(ws + w.cow_src);
+  wb.cow_excl = reinterpret_cast<int32_t *>(ws + w.cow_excl);
+  wb.gbase = reinterpret_cast<int32_t *>(ws + w.gbase);
+  wb.popmap = reinterpret_cast<int32_t *>(ws + w.popmap);
+  wb.done = reinterpret_cast<int32_t *>(ws + w.done);
+  wb.ctr = reinterpret_cast<int32_t *>(ws + w.ctr);
+  wb.scal = reinterpret_cast<int32_t *>(ws + w.scal);
   const int nb_old = (int)ceil_div(L, bs);
   const int nb_new = (int)ceil_div(L + R, bs);
   const int tail_slot = (int)(L / bs), tail_mod = (int)(L % bs);
-  const int nwords = (int)ceil_div(P, 32);
-  const int ngroups = (int)ceil_div(nwords, kKvGroupWords);
+  const int fast = S <= kKvFastSeqMax && w.ngroups <= kKvFastGroupMax;
+  const unsigned grid2 = (unsigned)(w.ngroups + (S + kKvBlock - 1) / kKvBlock);
   hipLaunchKernelGGL(k_kv, dim3(B), dim3(kKvBlock), 0, stream, anc, resampled, B, N, tables, M_cap,
-                     nb_old, nb_new, tail_slot, tail_mod, rc, (int)P, free_top, bitmap, cow_src,
-                     cow_excl, gbase, popmap, scal, done, cow_count, status);
-  hipLaunchKernelGGL(k_kv_pop, dim3(ngroups + (S + kKvBlock - 1) / kKvBlock), dim3(kKvBlock), 0,
-                     stream, S, ngroups, nwords, tables, M_cap, nb_old, nb_new, tail_slot, tail_mod,
-                     rc, (int)P, free_list, bitmap, cow_src, cow_excl, gbase, popmap, scal, cow,
+                     nb_old, nb_new, tail_slot, tail_mod, rc, (int)P, free_top, wb, fast, cow_count,
                      status);
+  if (fast)
+    hipLaunchKernelGGL(k_kv_pop_fast, dim3(grid2), dim3(kKvBlock), 0, stream, S, tables, M_cap,
+                       nb_old, nb_new, tail_slot, tail_mod, rc, (int)P, free_list, free_top, wb, cow,
+                       cow_count, status);
+  else
+    hipLaunchKernelGGL(k_kv_pop, dim3(grid2), dim3(kKvBlock), 0, stream, S, tables, M_cap, nb_old,
+                       nb_new, tail_slot, tail_mod, rc, (int)P, free_list, wb, cow, status);
   return hipGetLastError();
 }
 

@@ -8,34 +8,51 @@
 
 namespace smcsd {
 
-constexpr int kKvGroupWords = 256;  // freed-bitmap words per pop-kernel workgroup
+constexpr int kKvGroupWords = 256;               // freed-bitmap words per pop-kernel workgroup
+constexpr int kKvGroupBlocks = 32 * kKvGroupWords;  // blocks per group (8192)
+// One-pass pop kernel (no last-workgroup step) limits: every workgroup holds the whole
+// copy-on-write prefix in LDS and reads every group count.
+constexpr int kKvFastSeqMax = 8192;
+constexpr int kKvFastGroupMax = 4096;
 
-// [freed bitmap uint32 x ceil(P/32), padded to 64 words]
-// [copy-on-write source + 1 (0 = none) int32 x S] [copy-on-write exclusive prefix int32 x S]
-// [bitmap group rank bases int32 x ceil(words/256)] [pop index -> sequence int32 x P]
-// [arrival counter] [top, F, pops requested]
-// The bitmap and the counter must be zero before a call and are zero after it.
+// Two freed-block bitmaps and two per-group freed counts, used alternately by successive
+// calls (parity of the call counter): a call sets bits in one pair and clears the other
+// pair, which the previous call used.
+//   [bitmap x2: uint32 x nwp each][group counts x2: int32 x ngp each]
+//   [copy-on-write source + 1 (0 = none) int32 x S]
+//   [copy-on-write exclusive prefix int32 x S][group rank bases int32 x ngroups]
+//   [pop index -> sequence int32 x P]            (these three: many-sequence path only)
+//   [arrival counter][call counter][scalars x 8]
+// The whole workspace must be zero before the first call; calls keep it consistent.
 struct KvWs {
-  size_t bitmap, cow_src, cow_excl, gbase, popmap, done, scal, total;
+  size_t bitmap, gcount, cow_src, cow_excl, gbase, popmap, done, ctr, scal, total;
+  int64_t nwords, ngroups, nwp, ngp;
 };
 inline KvWs kv_ws_layout(int64_t S, int64_t P) {
   KvWs w{};
-  const int64_t nwords = ceil_div(P, 32);
+  w.nwords = ceil_div(P, 32);
+  w.ngroups = ceil_div(w.nwords, kKvGroupWords);
+  w.nwp = ceil_div(w.nwords, 64) * 64;
+  w.ngp = ceil_div(w.ngroups, 64) * 64;
   size_t off = 0;
   w.bitmap = off;
-  off += align256(sizeof(uint32_t) * (size_t)nwords);
+  off += align256(sizeof(uint32_t) * 2 * (size_t)w.nwp);
+  w.gcount = off;
+  off += align256(sizeof(int32_t) * 2 * (size_t)w.ngp);
   w.cow_src = off;
   off += align256(sizeof(int32_t) * (size_t)S);
   w.cow_excl = off;
   off += align256(sizeof(int32_t) * (size_t)S);
   w.gbase = off;
-  off += align256(sizeof(int32_t) * (size_t)ceil_div(nwords, kKvGroupWords));
+  off += align256(sizeof(int32_t) * (size_t)w.ngroups);
   w.popmap = off;
   off += align256(sizeof(int32_t) * (size_t)P);
   w.done = off;
   off += align256(sizeof(int32_t));
+  w.ctr = off;
+  off += align256(sizeof(int32_t));
   w.scal = off;
-  off += align256(sizeof(int32_t) * 4);
+  off += align256(sizeof(int32_t) * 8);
   w.total = off;
   return w;
 }

@@ -74,9 +74,8 @@ __global__ __launch_bounds__(kStreamBlock) void k_lse_partials(RowMap rm, int ns
   using E = Elt<DT>;
   constexpr int EPV = E::kPerVec;
   __shared__ Lse lds[kStreamBlock / kWave];
-  __shared__ float sSlab[kStreamBlock / kWave][kSlabs];
+  __shared__ float sRed[(kStreamBlock / kWave) * (3 + kSlabs)];
   __shared__ float sSlabT[kStreamBlock][kSlabs + 1];  // per-thread slab sums (bonus tiles)
-  __shared__ float sTileMc;
   const int K = rm.K;
   const int R = 2 * K + 1;
   const int tid = threadIdx.x;
@@ -144,41 +143,29 @@ __global__ __launch_bounds__(kStreamBlock) void k_lse_partials(RowMap rm, int ns
         for (int u = 0; u < kSlabs; ++u) sSlabT[tid][u] = gs[u];
       }
     }
-    const float my_m = st.m, my_mc = st.mc;
-    st = lse_block_reduce<kStreamBlock>(st, c, lds);
-    if (tid == 0) part[((int64_t)g * R + slot) * chunks + ch] = make_float2(st.m, st.s);
-    if (bonus) {
-      // slab sums relative to the tile's m*c: this thread's sums rescaled, plus its head
-      // and tail elements, then summed over the workgroup
-      if (tid == 0) sTileMc = st.mc;
-      __syncthreads();
-      const float Mc = sTileMc;
-      const float f = my_m == kNegInf ? 0.0f : fast_exp2(my_mc - Mc);
+    if (!bonus) {
+      st = lse_block_reduce<kStreamBlock>(st, c, lds);
+      if (tid == 0) part[((int64_t)g * R + slot) * chunks + ch] = make_float2(st.m, st.s);
+    } else {
+      // slab sums relative to this thread's m*c (its head and tail elements included),
+      // carried through the same workgroup reduction as s
       float slab[kSlabs];
 #pragma unroll
-      for (int u = 0; u < kSlabs; ++u) slab[u] = sSlabT[tid][u] * f;
-      if (tid < head) slab[0] += fast_exp2(fmaf(xh, c, -Mc));
+      for (int u = 0; u < kSlabs; ++u) slab[u] = sSlabT[tid][u];
+      if (tid < head) slab[0] += fast_exp2(fmaf(xh, c, -st.mc));
       if (tid < e1 - a1) {
-        const float t = fast_exp2(fmaf(xt, c, -Mc));
-        const int st_slab = slab_of<DT>(a1 + tid, a0);
+        const float t = fast_exp2(fmaf(xt, c, -st.mc));
+        const int ts = slab_of<DT>(a1 + tid, a0);
 #pragma unroll
         for (int u = 0; u < kSlabs; ++u)
-          if (u == st_slab) slab[u] += t;
+          if (u == ts) slab[u] += t;
       }
-      const int lane = tid % kWave, wave = tid / kWave;
+      st = lse_block_reduce_with<kStreamBlock, kSlabs>(st, slab, c, sRed);
+      if (tid == 0) {
+        part[((int64_t)g * R + slot) * chunks + ch] = make_float2(st.m, st.s);
+        float *o = sub + ((int64_t)g * chunks + ch) * kSlabs;
 #pragma unroll
-      for (int u = 0; u < kSlabs; ++u) {
-        float v = slab[u];
-#pragma unroll
-        for (int m = kWave / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-        if (lane == 0) sSlab[wave][u] = v;
-      }
-      __syncthreads();
-      if (tid < kSlabs) {
-        float t = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kStreamBlock / kWave; ++w) t += sSlab[w][tid];
-        sub[((int64_t)g * chunks + ch) * kSlabs + tid] = t;
+        for (int u = 0; u < kSlabs; ++u) o[u] = slab[u];
       }
     }
     __syncthreads();

@@ -175,18 +175,24 @@ def test_resample_degenerate_weights():
     assert np.all(res.cpu().numpy() == 0)
 
 
+_KV_WS = {}
+
+
 def _kv_gpu(anc, res, B, N, T, bs, L, R, rc, fl, top):
+    """One smcsd_kv_reassign call on copies of the given state.  The workspace of a shape is
+    reused across calls (as a caller would), so successive calls alternate its buffers."""
     tables = torch.from_numpy(T.copy()).cuda()
     rcd = torch.from_numpy(rc.copy()).cuda()
     fld = torch.from_numpy(fl.copy()).cuda()
     topd = torch.tensor([top], dtype=torch.int32, device="cuda")
     cow, ncow, st = _i32(B * N, 3), _i32(1), _i32(1)
-    ws = sm.alloc_workspace(sm.OP_KV, B, N, P=rc.size)
+    key = (B, N, rc.size)
+    if key not in _KV_WS:
+        _KV_WS[key] = sm.alloc_workspace(sm.OP_KV, B, N, P=rc.size)
+    ws = _KV_WS[key]
     sm.kv_reassign(torch.from_numpy(anc).cuda(), torch.from_numpy(res).cuda(), B, N, tables, bs, L,
                    R, rcd, fld, topd, cow, ncow, st, ws)
     torch.cuda.synchronize()
-    nbits = 4 * ((rc.size + 31) // 32)
-    assert int(ws[:nbits].sum().cpu()) == 0    # the freed-block bitmap is left zeroed
     n = int(ncow.cpu()[0])
     return dict(tables=tables.cpu().numpy(), refcounts=rcd.cpu().numpy(),
                 free_list=fld.cpu().numpy(), free_top=int(topd.cpu()[0]), cow=cow.cpu().numpy()[:n],
