@@ -34,6 +34,7 @@ constexpr int kStage = 16;         // table loads in flight per thread while sta
 constexpr int kNegBatch = 4;       // decrements in flight per thread
 constexpr int kHash = 2 * kMaxN;   // open-addressing table of the tail blocks (load <= 1/2)
 constexpr int kSeg = 16;           // table rows one thread walks down a column
+constexpr int kPre = kKvTileInts / kKvBlock;  // first-tile entries each thread loads up front
 
 // Wait until every memory operation this wave issued (atomics included) has completed.
 __device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
@@ -56,6 +57,41 @@ __device__ __forceinline__ int kv_scan(int v, int *lds, int *total) {
   __syncthreads();
   *total = tot;
   return base + inc - v;
+}
+
+// Three scans over the workgroup in one pass: returns the exclusive prefix of v.z and
+// writes the totals of v.x, v.y, v.z.  lds holds 3 * (kKvBlock / kWave) ints and must not
+// be reused before the next barrier.
+__device__ __forceinline__ int kv_scan3(int3 v, int *lds, int3 *total) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  int3 inc = v;
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int ox = __shfl_up(inc.x, d, kWave), oy = __shfl_up(inc.y, d, kWave),
+              oz = __shfl_up(inc.z, d, kWave);
+    if (lane >= d) {
+      inc.x += ox;
+      inc.y += oy;
+      inc.z += oz;
+    }
+  }
+  constexpr int kW = kKvBlock / kWave;
+  if (lane == kWave - 1) {
+    lds[wave] = inc.x;
+    lds[kW + wave] = inc.y;
+    lds[2 * kW + wave] = inc.z;
+  }
+  __syncthreads();
+  int3 tot = make_int3(0, 0, 0);
+  int base = 0;
+  for (int w = 0; w < kW; ++w) {
+    tot.x += lds[w];
+    tot.y += lds[kW + w];
+    const int z = lds[2 * kW + w];
+    if (w < wave) base += z;
+    tot.z += z;
+  }
+  *total = tot;
+  return base + inc.z - v.z;
 }
 
 __device__ __forceinline__ int tail_hash(int32_t blk) {
@@ -97,7 +133,17 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
     wb.scal[0] = *free_top;
     wb.scal[3] = C;
   }
-  // the ancestor row is read whether or not the prompt resampled, so both loads overlap
+  // the ancestor row and the first column tile of the old tables are read whether or not
+  // the prompt resampled, so all of this workgroup's first loads overlap
+  const int W = max(1, min(nb_old, kKvTileInts / N));
+  const int w0 = min(W, nb_old), nw0 = N * w0;
+  int32_t pre[kPre];
+#pragma unroll
+  for (int k = 0; k < kPre; ++k) {
+    const int e = min(tid + k * kKvBlock, max(nw0 - 1, 0));
+    const int j = e / max(w0, 1), s = e - j * max(w0, 1);
+    pre[k] = nw0 > 0 ? T[(row0 + j) * M_cap + s] : 0;
+  }
   const int res = resampled[b] != 0;
   for (int i = tid; i < N; i += kKvBlock) {
     a[i] = anc[row0 + i];
@@ -117,11 +163,18 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
   // ---- phase 1: exchange (prompts that resampled)
   if (do_exchange) {
     for (int i = tid; i < N; i += kKvBlock) atomicAdd(&cnt[a[i]], 1);
-    const int W = max(1, min(nb_old, kKvTileInts / N));
     const int nseg = (N + kSeg - 1) / kSeg;
     for (int s0 = 0; s0 < nb_old; s0 += W) {
       const int w = min(W, nb_old - s0), nw = N * w;
-      for (int e0 = tid; e0 < nw; e0 += kKvBlock * kStage) {
+      if (s0 == 0) {
+#pragma unroll
+        for (int k = 0; k < kPre; ++k) {
+          const int e = tid + k * kKvBlock;
+          const int j = e / w, s = e - j * w;
+          if (e < nw) tile[j * W + s] = pre[k];
+        }
+      }
+      for (int e0 = tid; s0 > 0 && e0 < nw; e0 += kKvBlock * kStage) {
         int32_t v[kStage];
 #pragma unroll
         for (int k = 0; k < kStage; ++k) {
@@ -149,11 +202,11 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
         }
         __syncthreads();
       }
-      // one thread per (column, segment of kSeg rows): gather the new tables, then give
-      // each run of equal blocks down the segment one refcount change, the sum of (c_j - 1)
-      // over the run.  Increments are issued at once; decrements are listed for after
-      // them (a run split over segments gets one change per piece: every piece that
-      // increments still lands before every piece that decrements).
+      // one thread per (column, segment of kSeg rows): each run of equal blocks down the
+      // segment gets one refcount change, the sum of (c_j - 1) over the run.  Increments
+      // are issued at once; decrements are listed for after them (a run split over
+      // segments gets one change per piece: every piece that increments still lands
+      // before every piece that decrements).
       for (int it = tid; it < w * nseg; it += kKvBlock) {
         const int sg = it / w, s = it - sg * w;
         const int j0 = sg * kSeg, j1 = min(N, j0 + kSeg);
@@ -165,15 +218,10 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
           v[k] = tile[j * W + s];
           d[k] = cnt[j] - 1;
         }
-        const bool is_tail = tail_partial && s0 + s == tail_slot;
+        if (tail_partial && s0 + s == tail_slot) {
 #pragma unroll
-        for (int k = 0; k < kSeg; ++k) {
-          const int i = j0 + k;
-          if (i < j1) {
-            const int32_t nv = tile[a[i] * W + s];
-            if (nv != v[k]) T[(row0 + i) * M_cap + s0 + s] = nv;
-            if (is_tail) tail_old[i] = v[k];
-          }
+          for (int k = 0; k < kSeg; ++k)
+            if (j0 + k < j1) tail_old[j0 + k] = v[k];
         }
         if (nseg > 1 && colu[s]) continue;
         int32_t blk = v[0];
@@ -216,6 +264,20 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
             atomicOr(&bitmap[q[k].x >> 5], 1u << (q[k].x & 31));
             atomicAdd(&gcount[q[k].x / kKvGroupBlocks], 1);
           }
+      }
+      // the new tables (stores issued after the refcount waits, so nothing waits on them
+      // before the kernel ends)
+      for (int it = tid; it < w * nseg; it += kKvBlock) {
+        const int sg = it / w, s = it - sg * w;
+        const int j0 = sg * kSeg, j1 = min(N, j0 + kSeg);
+#pragma unroll
+        for (int k = 0; k < kSeg; ++k) {
+          const int i = j0 + k;
+          if (i < j1) {
+            const int32_t nv = tile[a[i] * W + s];
+            if (nv != tile[i * W + s]) T[(row0 + i) * M_cap + s0 + s] = nv;
+          }
+        }
       }
       __syncthreads();
     }
@@ -447,6 +509,7 @@ __global__ __launch_bounds__(kKvBlock) void k_kv_pop_fast(
   __shared__ int32_t sEx[kKvFastSeqMax];   // exclusive prefix of the copy-on-write flags
   __shared__ int32_t sList[kKvGroupBlocks];  // this group's freed block ids, ascending
   __shared__ int red[kKvBlock / kWave];
+  __shared__ int red3[3 * (kKvBlock / kWave)];
   const int tid = threadIdx.x;
   const int gi = blockIdx.x;
   const bool word_wg = gi < wb.ngroups;
@@ -485,10 +548,9 @@ __global__ __launch_bounds__(kKvBlock) void k_kv_pop_fast(
   }
 #pragma unroll
   for (int k = 0; k < kSPer; ++k) mycow += cs[k] != 0;
-  int F, base, Ctot;
-  kv_scan(Fpart, red, &F);
-  kv_scan(below, red, &base);
-  int ci = kv_scan(mycow, red, &Ctot);
+  int3 tot3;
+  int ci = kv_scan3(make_int3(Fpart, below, mycow), red3, &tot3);
+  const int F = tot3.x, base = tot3.y, Ctot = tot3.z;
 #pragma unroll
   for (int k = 0; k < kSPer; ++k) {
     if (g0 + k < g1) {
