@@ -1,0 +1,123 @@
+"""Distribution-level checks of the GPU path on a tiny vocabulary (V = 8, K = 2).
+
+The same construction as the oracle's law pins (prefix-dependent seeded logit tables,
+8^3 one-round continuations), run through the library instead of the oracle:
+
+* SMC-SD: one round over many independent prompts with N particles, resampling forced
+  (tau > 1), a uniformly chosen output particle -> the sampling-importance-resampling law
+  P_N, computed exactly by enumeration (SMC explainers, section 2: importance-weighted
+  resampling).  alpha = 1 and the power target alpha = 4.
+* SpS: rounds of the modified-rejection verify until three tokens are emitted -> the
+  target law (the speculative-sampling notes: the output follows the target exactly).
+
+Each GPU call draws its randomness from (seed, step, sequence index); the chi-square
+tests use p > 1e-4 on merged cells, like the oracle's pins.
+"""
+import numpy as np
+import pytest
+import torch
+
+import smc_verification_resampling_amd as sm
+from tests import test_oracle_laws as L
+
+pytestmark = pytest.mark.gpu
+
+V, K = L.V, L.K
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+
+
+def _i32(*shape):
+    return torch.zeros(shape, dtype=torch.int32, device="cuda")
+
+
+@pytest.mark.parametrize("N,alpha", [(4, 1.0), (3, 4.0)])
+def test_gpu_smc_round_follows_sir_law(N, alpha):
+    tgt, drf = L._tables(31337)
+    P, PI = L._sir_law(tgt, drf, N, alpha)
+    runs, seed = 60000, 11
+    rng = np.random.default_rng(seed)
+    S = runs * N
+    x1 = L._sample_rows(rng, np.repeat(L._softmax(drf[0][[0]]), S, 0))
+    x2 = L._sample_rows(rng, L._softmax(drf[1][x1]))
+    t_rows = np.stack([np.repeat(tgt[0][[0]], S, 0), tgt[1][x1], tgt[2][x1 * V + x2]], axis=1)
+    d_rows = np.stack([np.repeat(drf[0][[0]], S, 0), drf[1][x1]], axis=1)
+    toks = np.stack([x1, x2], axis=1).astype(np.int32)
+    t_d = torch.from_numpy(np.ascontiguousarray(t_rows, np.float32)).cuda()
+    d_d = torch.from_numpy(np.ascontiguousarray(d_rows, np.float32)).cuda()
+    x_d = torch.from_numpy(toks).cuda()
+    lw = torch.zeros(S, dtype=torch.float32, device="cuda")
+    out, st = _i32(S, K + 1), _i32(1)
+    ws = sm.alloc_workspace(sm.OP_VERIFY_SMC, runs, N, K, V)
+    sm.verify(t_d, d_d, x_d, runs, N, K, V, 1.0, alpha, sm.MODE_SMC, seed, 0, out, st, ws,
+              log_weights=lw)
+    anc, ess, res = _i32(runs, N), torch.zeros(runs, device="cuda"), _i32(runs)
+    sm.resample(lw.view(runs, N), runs, N, 2.0, seed, 0, anc, ess, res, st)   # tau > 1: always
+    torch.cuda.synchronize()
+    assert int(st.cpu()[0]) == 0
+    assert bool((res == 1).all())
+    y = out.cpu().numpy()
+    assert np.array_equal(y[:, :K], toks) and (y[:, K] >= 0).all() and (y[:, K] < V).all()
+    pick = rng.integers(0, N, runs)
+    g = np.arange(runs) * N + anc.cpu().numpy()[np.arange(runs), pick]
+    ys = y[g, 0] * 64 + y[g, 1] * 8 + y[g, 2]
+    counts = np.bincount(ys, minlength=V ** 3).astype(np.float64)
+    assert L._chi2_pvalue(counts, P) > 1e-4
+    assert np.abs(P - PI).sum() > 0.02     # the test can tell P_N from the target
+
+
+def test_gpu_sps_law_equals_target():
+    tgt, drf = L._tables(2024)
+    pi = L._target_law(tgt)
+    rng = np.random.default_rng(98)
+    runs = 60000
+    emitted = [[] for _ in range(runs)]
+    code = np.zeros(runs, np.int64)
+    length = np.zeros(runs, np.int64)
+    st = _i32(1)
+    rnd = 0
+    active = np.arange(runs)
+    while len(active):
+        len_at_start = length[active].copy()
+        for d in (0, 1, 2):
+            grp = active[len_at_start == d]
+            if not len(grp):
+                continue
+            c0 = code[grp]
+            x1 = L._sample_rows(rng, L._softmax(drf[d][c0]))
+            c1 = c0 * V + x1
+            x2 = L._sample_rows(rng, L._softmax(drf[d + 1][c1]))
+            c2 = c1 * V + x2
+            t_rows = np.stack([tgt[d][c0], tgt[d + 1][c1], tgt[d + 2][c2]], axis=1)
+            d_rows = np.stack([drf[d][c0], drf[d + 1][c1]], axis=1)
+            toks = np.stack([x1, x2], axis=1).astype(np.int32)
+            n = len(grp)
+            out, num = _i32(n, K + 1), _i32(n)
+            ws = sm.alloc_workspace(sm.OP_VERIFY_SPS, n, 1, K, V)
+            # distinct (step, index) per round and depth group: independent draws
+            sm.verify(torch.from_numpy(np.ascontiguousarray(t_rows, np.float32)).cuda(),
+                      torch.from_numpy(np.ascontiguousarray(d_rows, np.float32)).cuda(),
+                      torch.from_numpy(toks).cuda(), n, 1, K, V, 1.0, 1.0, sm.MODE_SPS, 77,
+                      rnd * 3 + d, out, st, ws, out_num_tokens=num)
+            o, nt = out.cpu().numpy(), num.cpu().numpy()
+            for j, r in enumerate(grp):
+                k = int(nt[j])
+                new = o[j, :k].tolist()
+                assert 1 <= k <= K + 1 and all(0 <= v < V for v in new)
+                emitted[r].extend(new)
+                for v in new:
+                    if length[r] < 3:
+                        code[r] = code[r] * V + v
+                        length[r] += 1
+        rnd += 1
+        active = np.array([r for r in active if length[r] < 3], dtype=np.int64)
+    assert int(st.cpu()[0]) == 0
+    ys = np.array([e[0] * 64 + e[1] * 8 + e[2] for e in emitted])
+    counts = np.bincount(ys, minlength=V ** 3).astype(np.float64)
+    assert L._chi2_pvalue(counts, pi) > 1e-4
