@@ -14,6 +14,9 @@ constexpr int kStreamUnroll = 8;
 constexpr int kChunkElemsBf16 = 16384;
 constexpr int kChunkElemsF32 = 8192;
 constexpr int kChunkElemsMin = kChunkElemsF32;  // workspace is sized for the smaller tile
+// Rows other than the bonus row are cut into tiles of kBigGroups chunks (128 KiB): fewer
+// workgroup reductions per byte.  Their partials use the first ceil(V / big chunk) slots.
+constexpr int kBigGroups = 4;
 
 constexpr int kMaxK = 32;
 constexpr int kMaxN = 1024;

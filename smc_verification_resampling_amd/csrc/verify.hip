@@ -65,10 +65,14 @@ __device__ __forceinline__ int slab_of(int64_t v, int64_t a0) {
   return v < a0 ? 0 : (int)min((int64_t)kSlabs - 1, (v - a0) / kSlabElems<DT>);
 }
 
+// Tiles: first the bonus rows in chunks of chunk_elems (one unrolled step each), then the
+// other rows in chunks of kBigGroups * chunk_elems.  Partials of row (g, slot) start at
+// part[(g * R + slot) * chunks].
 template <int DT>
 __global__ __launch_bounds__(kStreamBlock) void k_lse_partials(RowMap rm, int nseq, int V,
                                                                 int chunk_elems, int chunks,
-                                                                float c, float2 *__restrict__ part,
+                                                                int chunks_big, float c,
+                                                                float2 *__restrict__ part,
                                                                 float *__restrict__ sub,
                                                                 int64_t ntiles) {
   using E = Elt<DT>;
@@ -79,24 +83,29 @@ __global__ __launch_bounds__(kStreamBlock) void k_lse_partials(RowMap rm, int ns
   const int K = rm.K;
   const int R = 2 * K + 1;
   const int tid = threadIdx.x;
+  const int64_t ntiles_bonus = (int64_t)nseq * chunks;
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const int64_t row_id = t / chunks;
-    const int ch = (int)(t - row_id * chunks);
     // bonus rows first: their tiles do extra work, which then overlaps the stream of the
     // other rows instead of lengthening the kernel's tail
-    int g, slot;
-    if (row_id < nseq) {
-      g = (int)row_id;
+    int g, slot, ch;
+    int64_t ce;
+    if (t < ntiles_bonus) {
+      g = (int)(t / chunks);
+      ch = (int)(t - (int64_t)g * chunks);
       slot = K;
+      ce = chunk_elems;
     } else {
-      const int64_t r = row_id - nseq;
+      const int64_t u = t - ntiles_bonus;
+      const int64_t r = u / chunks_big;
+      ch = (int)(u - r * chunks_big);
       g = (int)(r / (2 * K));
       const int j = (int)(r - (int64_t)g * 2 * K);
       slot = j < K ? j : j + 1;
+      ce = (int64_t)chunk_elems * kBigGroups;
     }
     const char *row = rm.row(g, slot);
-    const int64_t e0 = (int64_t)ch * chunk_elems;
-    const int64_t e1 = min((int64_t)V, e0 + (int64_t)chunk_elems);
+    const int64_t e0 = (int64_t)ch * ce;
+    const int64_t e1 = min((int64_t)V, e0 + ce);
     const uintptr_t addr0 = (uintptr_t)(row + e0 * E::kBytes);
     int64_t head = (int64_t)((16 - (addr0 & 15)) & 15) / E::kBytes;
     if (head > e1 - e0) head = e1 - e0;
@@ -117,14 +126,14 @@ __global__ __launch_bounds__(kStreamBlock) void k_lse_partials(RowMap rm, int ns
       lse_update<1>(st, x, c);
     }
     // body: kStreamUnroll 16-byte vectors per lane in flight, then one max / rescale for
-    // the whole group of kStreamUnroll*EPV elements.  A tile is at most one such group.
+    // the whole group of kStreamUnroll*EPV elements.  A bonus tile is one such group.
     const bool bonus = slot == K;
     if (bonus) {
 #pragma unroll
       for (int u = 0; u < kSlabs; ++u) sSlabT[tid][u] = 0.0f;
     }
     const uint4 *vp = reinterpret_cast<const uint4 *>(row + a0 * E::kBytes);
-    for (int64_t v0 = 0; v0 < nvec; v0 += (int64_t)kStreamBlock * kStreamUnroll) {  // one pass
+    for (int64_t v0 = 0; v0 < nvec; v0 += (int64_t)kStreamBlock * kStreamUnroll) {
       uint4 buf[kStreamUnroll];
 #pragma unroll
       for (int u = 0; u < kStreamUnroll; ++u) {
@@ -379,7 +388,8 @@ static_assert(kSlabElems<SMCSD_DTYPE_BF16> + 16 <= 8 * kSmcFinalBlock * kSmcUnit
 template <int DT>
 __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
     RowMap rm, const int32_t *__restrict__ draft_tokens, int V, int chunk_elems, int chunks,
-    float c, float alpha, uint64_t seed, uint64_t step, const float2 *__restrict__ part,
+    int chunks_big, float c, float alpha, uint64_t seed, uint64_t step,
+    const float2 *__restrict__ part,
     const float *__restrict__ sub, float *__restrict__ lw, int32_t *__restrict__ out_tokens,
     int32_t *__restrict__ out_num,
     float *__restrict__ out_logp, float *__restrict__ out_logq, float *__restrict__ out_lse,
@@ -430,11 +440,12 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
   // row normalisers: chunk pairs combined in fp64 (row K also keeps its chunk terms)
   if (tid < R) {
     const float2 *p = (part_in_lds ? sPart : gpart) + tid * chunks;
+    const int n = tid == K ? chunks : chunks_big;
     float M = kNegInf;
-    for (int i = 0; i < chunks; ++i) M = fmaxf(M, p[i].x);
+    for (int i = 0; i < n; ++i) M = fmaxf(M, p[i].x);
     const float Mc = M == kNegInf ? 0.0f : __fmul_rn(M, c);
     double S = 0.0;
-    for (int i = 0; i < chunks; ++i) {
+    for (int i = 0; i < n; ++i) {
       const double t = chunk_term(p[i], c, Mc);
       if (tid == K) sTermK[i] = t;
       S += t;
@@ -556,7 +567,7 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
 // pair is (LSE*log2(e), 1).  ws_norm[g] = {Mc_p, inv_p, Mc_q, inv_q} for row pair k*.
 template <int DT>
 __global__ __launch_bounds__(kWave) void k_sps_decide(
-    RowMap rm, const int32_t *__restrict__ draft_tokens, int V, int chunks, float c,
+    RowMap rm, const int32_t *__restrict__ draft_tokens, int V, int chunks, int chunks_big, float c,
     uint64_t seed, uint64_t step, const float2 *__restrict__ part, const float *__restrict__ lse_in,
     int32_t *__restrict__ ws_kstar, float4 *__restrict__ ws_norm, int32_t *__restrict__ out_tokens,
     int32_t *__restrict__ out_num, float *__restrict__ out_logp, float *__restrict__ out_logq,
@@ -581,7 +592,7 @@ __global__ __launch_bounds__(kWave) void k_sps_decide(
       if (isnan(L2) || L2 == __builtin_inf()) atomicOr(&sFlags, SMCSD_ST_NAN_INPUT);
       else if (L2 == -__builtin_inf()) atomicOr(&sFlags, SMCSD_ST_EMPTY_ROW);
     } else {
-      const RowNorm rn = row_norm(part + ((int64_t)g * R + r) * chunks, chunks, c);
+      const RowNorm rn = row_norm(part + ((int64_t)g * R + r) * chunks, r == K ? chunks : chunks_big, c);
       sL2[r] = rn.L2;
       sS[r] = rn.S;
       sMc[r] = rn.Mc;
@@ -790,14 +801,16 @@ static hipError_t launch_verify_t(const VerifyArgs &a) {
   const VerifyWs w = verify_ws_layout(a.nseq, K, a.V, a.mode);
   float2 *part = reinterpret_cast<float2 *>(a.ws + w.part);
   float *sub = reinterpret_cast<float *>(a.ws + w.sub);
-  const int64_t ntiles = (int64_t)a.nseq * R * chunks;
+  const int chunks_big = (int)ceil_div(a.V, (int64_t)ce * kBigGroups);
+  const int64_t ntiles = (int64_t)a.nseq * (chunks + 2 * K * (int64_t)chunks_big);
   const unsigned grid = (unsigned)std::min<int64_t>(ntiles, (int64_t)1 << 30);
 
   if (a.mode == SMCSD_MODE_SMC) {
     hipLaunchKernelGGL(k_lse_partials<DT>, dim3(grid), dim3(kStreamBlock), 0, a.stream, rm, a.nseq,
-                       a.V, ce, chunks, a.c, part, sub, ntiles);
+                       a.V, ce, chunks, chunks_big, a.c, part, sub, ntiles);
     hipLaunchKernelGGL(k_smc_finalize<DT>, dim3(a.nseq), dim3(kSmcFinalBlock), 0, a.stream, rm,
-                       a.draft_tokens, a.V, ce, chunks, a.c, a.alpha, a.seed, a.step, part, sub,
+                       a.draft_tokens, a.V, ce, chunks, chunks_big, a.c, a.alpha, a.seed, a.step,
+                       part, sub,
                        a.log_weights, a.out_tokens, a.out_num_tokens, a.out_logp, a.out_logq,
                        a.out_lse, a.status);
     return hipGetLastError();
@@ -807,9 +820,10 @@ static hipError_t launch_verify_t(const VerifyArgs &a) {
   float2 *part2 = reinterpret_cast<float2 *>(a.ws + w.part2);
   if (!a.lse_in)
     hipLaunchKernelGGL(k_lse_partials<DT>, dim3(grid), dim3(kStreamBlock), 0, a.stream, rm, a.nseq,
-                       a.V, ce, chunks, a.c, part, sub, ntiles);
+                       a.V, ce, chunks, chunks_big, a.c, part, sub, ntiles);
   hipLaunchKernelGGL(k_sps_decide<DT>, dim3(a.nseq), dim3(kWave), 0, a.stream, rm, a.draft_tokens,
-                     a.V, chunks, a.c, a.seed, a.step, part, a.lse_in, kstar, norm, a.out_tokens,
+                     a.V, chunks, chunks_big, a.c, a.seed, a.step, part, a.lse_in, kstar, norm,
+                     a.out_tokens,
                      a.out_num_tokens, a.out_logp, a.out_logq, a.out_lse, a.status);
   const int64_t ntiles2 = (int64_t)a.nseq * chunks;
   hipLaunchKernelGGL(k_sps_residual<DT>, dim3((unsigned)std::min<int64_t>(ntiles2, (int64_t)1 << 30)),
