@@ -65,9 +65,9 @@ __device__ __forceinline__ int slab_of(int64_t v, int64_t a0) {
   return v < a0 ? 0 : (int)min((int64_t)kSlabs - 1, (v - a0) / kSlabElems<DT>);
 }
 
-// Tiles: first the bonus rows in chunks of chunk_elems (one unrolled step each), then the
-// other rows in chunks of kBigGroups * chunk_elems.  Partials of row (g, slot) start at
-// part[(g * R + slot) * chunks].
+// Tiles: first the rows other than the bonus row in chunks of kBigGroups * chunk_elems,
+// then the bonus rows in chunks of chunk_elems (one unrolled step each).  Partials of row
+// (g, slot) start at part[(g * R + slot) * chunks].
 template <int DT>
 __global__ __launch_bounds__(kStreamBlock) void k_lse_partials(RowMap rm, int nseq, int V,
                                                                 int chunk_elems, int chunks,
@@ -83,19 +83,20 @@ __global__ __launch_bounds__(kStreamBlock) void k_lse_partials(RowMap rm, int ns
   const int K = rm.K;
   const int R = 2 * K + 1;
   const int tid = threadIdx.x;
-  const int64_t ntiles_bonus = (int64_t)nseq * chunks;
+  const int64_t ntiles_big = ntiles - (int64_t)nseq * chunks;
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    // bonus rows first: their tiles do extra work, which then overlaps the stream of the
-    // other rows instead of lengthening the kernel's tail
+    // the big tiles of the other rows first, the bonus rows' one-step tiles last: small
+    // tiles even out the kernel's tail
     int g, slot, ch;
     int64_t ce;
-    if (t < ntiles_bonus) {
-      g = (int)(t / chunks);
-      ch = (int)(t - (int64_t)g * chunks);
+    if (t >= ntiles_big) {
+      const int64_t tb = t - ntiles_big;
+      g = (int)(tb / chunks);
+      ch = (int)(tb - (int64_t)g * chunks);
       slot = K;
       ce = chunk_elems;
     } else {
-      const int64_t u = t - ntiles_bonus;
+      const int64_t u = t;
       const int64_t r = u / chunks_big;
       ch = (int)(u - r * chunks_big);
       g = (int)(r / (2 * K));
