@@ -120,11 +120,91 @@ __global__ __launch_bounds__(kResBlock) void k_resample(float *__restrict__ lw, 
   for (int n = tid; n < N; n += kResBlock) lwb[n] = 0.0f;
 }
 
+// Up to 64 particles: one wave per prompt, four prompts per workgroup, everything in
+// registers and lane shuffles (no workgroup barriers).  Same arithmetic as k_resample:
+// fp64 weights relative to the max, ESS clamped to [1, N], strict threshold, systematic
+// positions (i + u0) / N against the normalised inclusive prefix.
+constexpr int kResWaves = 4;
+
+__global__ __launch_bounds__(kWave * kResWaves) void k_resample_wave(
+    float *__restrict__ lw, int B, int N, float tau, uint64_t seed, uint64_t step,
+    int32_t *__restrict__ anc, float *__restrict__ ess, int32_t *__restrict__ resampled,
+    int32_t *status) {
+  const int lane = threadIdx.x % kWave;
+  const int b = blockIdx.x * kResWaves + threadIdx.x / kWave;
+  if (b >= B) return;  // a whole wave: no barrier below
+  float *lwb = lw + (int64_t)b * N;
+  int32_t *ab = anc + (int64_t)b * N;
+  const bool act = lane < N;
+  const float x = act ? lwb[lane] : kNegInf;
+  int bad = act && isnan(x);
+  float m = act && !isnan(x) ? x : kNegInf;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    m = fmaxf(m, __shfl_xor(m, d, kWave));
+    bad |= __shfl_xor(bad, d, kWave);
+  }
+  if (bad || !isfinite(m)) {
+    if (act) ab[lane] = lane;
+    if (lane == 0) {
+      ess[b] = 0.0f;
+      resampled[b] = 0;
+      atomicOr(status, SMCSD_ST_DEGENERATE_WEIGHTS);
+    }
+    return;
+  }
+  const double w = act ? exp((double)x - (double)m) : 0.0;
+  double s1 = w, s2 = w * w;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    s1 += __shfl_xor(s1, d, kWave);
+    s2 += __shfl_xor(s2, d, kWave);
+  }
+  double e = s1 * s1 / s2;
+  if (e < 1.0) e = 1.0;
+  if (e > (double)N) e = (double)N;
+  const bool doit = e < (double)tau * (double)N;
+  if (lane == 0) {
+    ess[b] = (float)e;
+    resampled[b] = doit;
+  }
+  if (!doit) {
+    if (act) ab[lane] = lane;
+    return;
+  }
+  double cum = w;  // inclusive prefix over the lanes
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const double o = __shfl_up(cum, d, kWave);
+    if (lane >= d) cum += o;
+  }
+  const double tot = __shfl(cum, N - 1, kWave);
+  const double u0 = philox_uniform(seed, (uint32_t)b, step, 2u, 0);
+  const double pos = ((double)lane + u0) / (double)N;
+  // number of j with C_j <= pos (C non-decreasing) = first j with C_j > pos
+  int idx = 0;
+#pragma unroll
+  for (int stp = kWave / 2; stp >= 1; stp >>= 1) {
+    const int cand = idx + stp - 1;
+    const double cv = __shfl(cum, min(cand, N - 1), kWave);
+    if (cand < N && !(cv / tot > pos)) idx += stp;
+  }
+  if (act) {
+    ab[lane] = idx < N ? idx : N - 1;
+    lwb[lane] = 0.0f;
+  }
+}
+
 hipError_t launch_resample(float *lw, int B, int N, float tau, uint64_t seed, uint64_t step,
                            int32_t *anc, float *ess, int32_t *resampled, int32_t *status,
                            hipStream_t stream) {
-  hipLaunchKernelGGL(k_resample, dim3(B), dim3(kResBlock), 0, stream, lw, N, tau, seed, step, anc,
-                     ess, resampled, status);
+  if (N <= kWave)
+    hipLaunchKernelGGL(k_resample_wave, dim3((B + kResWaves - 1) / kResWaves),
+                       dim3(kWave * kResWaves), 0, stream, lw, B, N, tau, seed, step, anc, ess,
+                       resampled, status);
+  else
+    hipLaunchKernelGGL(k_resample, dim3(B), dim3(kResBlock), 0, stream, lw, N, tau, seed, step,
+                       anc, ess, resampled, status);
   return hipGetLastError();
 }
 

@@ -482,53 +482,53 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
   const char *brow = rm.row(g, K);
   int bonus = -1;
   if (isfinite(SK) && SK > 0.0) {
-    if (tid == 0) {
-      // the chunk, then the slab inside it, whose running sum first exceeds the target
-      // (if rounding leaves none, the last one with a positive sum)
+    if (tid < kWave) {
+      // wave 0: the chunk, then the slab inside it, whose running sum first exceeds the
+      // target (if rounding leaves none, the last chunk / last positive slab), each by a
+      // lane prefix sum and a ballot
+      const int lane = tid;
       double base = 0.0;
-      int ch = chunks - 1;
-      for (int i = 0; i < chunks; ++i) {
-        if (base + sTermK[i] > target) {
-          ch = i;
-          break;
+      int ch = -1;
+      for (int c0 = 0; c0 < chunks && ch < 0; c0 += kWave) {
+        const double t = c0 + lane < chunks ? sTermK[c0 + lane] : 0.0;
+        const double inc = wave_inclusive_scan(t);
+        const unsigned long long hit = __ballot(c0 + lane < chunks && base + inc > target);
+        if (hit) {
+          const int f = __ffsll(hit) - 1;
+          ch = c0 + f;
+          base += __shfl(inc - t, f, kWave);
+        } else {
+          base += __shfl(inc, kWave - 1, kWave);
         }
-        base += sTermK[i];
       }
-      if (ch == chunks - 1 && !(base > target)) {
-        // no crossing: restart the last chunk from its own prefix
-        base = 0.0;
-        for (int i = 0; i < chunks - 1; ++i) base += sTermK[i];
+      if (ch < 0) {  // no crossing: restart the last chunk from its own prefix
+        ch = chunks - 1;
+        double pre = 0.0;
+        for (int i = lane; i < chunks - 1; i += kWave) pre += sTermK[i];
+#pragma unroll
+        for (int d = kWave / 2; d >= 1; d >>= 1) pre += __shfl_xor(pre, d, kWave);
+        base = pre;
       }
       const float2 pk = (part_in_lds ? sPart : gpart)[K * chunks + ch];
       const double fk =
           pk.x == kNegInf ? 0.0 : (double)fast_exp2(__fmul_rn(pk.x, c) - sMc[K]);
       const float *sb = (sub_in_lds ? sSub : gsub) + ch * kSlabs;
-      int sl = -1, last = kSlabs - 1;
-      double base_last = base;
-      for (int u = 0; u < kSlabs; ++u) {
-        const double t = (double)sb[u] * fk;
-        if (base + t > target) {
-          sl = u;
-          break;
-        }
-        if (t > 0.0) {
-          last = u;
-          base_last = base;
-        }
-        base += t;
-      }
-      if (sl < 0) {
-        sl = last;
-        base = base_last;
-      }
+      const double ts = lane < kSlabs ? (double)sb[lane] * fk : 0.0;
+      const double incs = wave_inclusive_scan(ts);
+      const unsigned long long hit = __ballot(lane < kSlabs && base + incs > target);
+      const unsigned long long pos = __ballot(lane < kSlabs && ts > 0.0);
+      const int sl = hit ? __ffsll(hit) - 1 : (pos ? 63 - __clzll(pos) : kSlabs - 1);
+      base += __shfl(incs - ts, sl, kWave);
       // slab bounds: the vector body starts at the first 16-byte aligned element
       const int64_t e0 = (int64_t)ch * chunk_elems;
       const int64_t e1 = min((int64_t)V, e0 + (int64_t)chunk_elems);
       const uintptr_t addr0 = reinterpret_cast<uintptr_t>(brow + e0 * E::kBytes);
       const int64_t a0 = e0 + min((int64_t)(((16 - (addr0 & 15)) & 15) / E::kBytes), e1 - e0);
-      sLo = sl == 0 ? e0 : min(e1, a0 + (int64_t)sl * kSlabElems<DT>);
-      sHi = sl == kSlabs - 1 ? e1 : min(e1, a0 + (int64_t)(sl + 1) * kSlabElems<DT>);
-      sBase = base;
+      if (lane == 0) {
+        sLo = sl == 0 ? e0 : min(e1, a0 + (int64_t)sl * kSlabElems<DT>);
+        sHi = sl == kSlabs - 1 ? e1 : min(e1, a0 + (int64_t)(sl + 1) * kSlabElems<DT>);
+        sBase = base;
+      }
     }
     __syncthreads();
     const int64_t lo = sLo, hi = sHi;
