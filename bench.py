@@ -195,6 +195,7 @@ def main():
     achieved_gbs = bytes_per_verify / verify_avg_s / 1e9
     step_gbs = bytes_per_verify * steps_per_s / 1e9
 
+    sps = sps_timing(cfg, sets, args.steps) if cfg.sps else None
     ref = reference_kernels(args.probe_mib) if args.probe_mib > 0 else None
 
     cpu = None
@@ -225,6 +226,9 @@ def main():
             "algorithmic_bytes_per_step": bytes_per_verify,
             "step_hbm_gbs": round(step_gbs, 1),
             "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+            "sps_verify": sps,
+            "combined_ms_per_step": (round(ms_per_step + sps["us_per_call"] / 1e3, 5)
+                                     if sps else None),
             "status": st,
             "reference_kernels": ref,
         },
@@ -242,6 +246,46 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
+
+
+def sps_timing(cfg, sets, steps):
+    """The SpS modified-rejection verify on particle 0 of every prompt, on the same logits,
+    timed on its own (HIP events around a run of calls) after the SMC steps."""
+    import torch
+
+    import smc_verification_resampling_amd as sm
+
+    B, N, K, V = cfg.B, cfg.N, cfg.K, cfg.V
+    i32 = dict(dtype=torch.int32, device="cuda")
+    ws = sm.alloc_workspace(sm.OP_VERIFY_SPS, B, 1, K, V)
+    tok = torch.zeros((B, K + 1), **i32)
+    num = torch.zeros(B, **i32)
+    status = torch.zeros(1, **i32)
+    emitted = torch.zeros(B, dtype=torch.int64, device="cuda")
+
+    def call(t):
+        tgt, drf, toks = sets[t % cfg.n_sets]
+        sm.verify(tgt, drf, toks, B, 1, K, V, cfg.temperature, 1.0, sm.MODE_SPS, cfg.rng_seed,
+                  t, tok, status, ws, out_num_tokens=num, seq_step=N)
+
+    for t in range(5):
+        call(t)
+    n = max(1, min(steps, 200))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for t in range(n):
+        call(t)
+    ev[1].record()
+    torch.cuda.synchronize()
+    us = ev[0].elapsed_time(ev[1]) * 1e3 / n
+    for t in range(n):  # untimed: the number of tokens each call emits
+        call(t)
+        emitted += num
+    torch.cuda.synchronize()
+    return {"calls": n, "sequences": B, "us_per_call": round(us, 2),
+            "mean_emitted_tokens": round(float(emitted.sum()) / (n * B), 4),
+            "status": int(status.cpu()[0])}
 
 
 def reference_kernels(mib):
@@ -294,41 +338,52 @@ def cpu_baseline(cfg, sets, budget_s):
         return x.cpu().numpy()
 
     th, dh, xh = host(tgt[sel]), host(drf[sel]), toks[sel].cpu().numpy()
-    lw = np.zeros(nsamp, np.float32)
-    kv = synth.initial_kv(cfg)
-    T, rc, fl, top = kv["tables"], kv["refcounts"], kv["free_list"], int(kv["free_top"][0])
-    L = int(kv["seq_len"])
-    ident = np.tile(np.arange(N, dtype=np.int32), (B, 1))
-    o = oracle.kv_reassign(ident, np.zeros(B, np.int32), T, cfg.block_size, L, K + 1, rc, fl, top)
-    rng = np.random.default_rng(0)
-    t_verify = t_rest = 0.0
-    reps = 0
-    t_start = time.perf_counter()
-    while reps < 2 or time.perf_counter() - t_start < budget_s:
-        a = time.perf_counter()
-        v = oracle.verify_smc(th, dh, xh, float(np.float32(cfg.temperature)), cfg.alpha,
-                              cfg.rng_seed, reps, lw)
-        b = time.perf_counter()
-        lwfull = rng.normal(0, 2, (B, N)).astype(np.float32)
-        r = oracle.resample(lwfull, float(np.float32(cfg.tau)), cfg.rng_seed, reps)
-        L += K + 1
-        o = oracle.kv_reassign(r["ancestors"], r["resampled"], o["tables"], cfg.block_size, L,
-                               K + 1, o["refcounts"], o["free_list"], o["free_top"])
-        c = time.perf_counter()
-        t_verify += b - a
-        t_rest += c - b
-        reps += 1
-        if L + 2 * (K + 1) > cfg.M_cap * cfg.block_size:
-            break
-        del v
-    per_step = t_verify / reps * (S / nsamp) + t_rest / reps
+
+    def sample(seconds):
+        lw = np.zeros(nsamp, np.float32)
+        kv = synth.initial_kv(cfg)
+        T, rc, fl, top = kv["tables"], kv["refcounts"], kv["free_list"], int(kv["free_top"][0])
+        L = int(kv["seq_len"])
+        ident = np.tile(np.arange(N, dtype=np.int32), (B, 1))
+        o = oracle.kv_reassign(ident, np.zeros(B, np.int32), T, cfg.block_size, L, K + 1, rc, fl,
+                               top)
+        rng = np.random.default_rng(0)
+        t_verify = t_rest = 0.0
+        reps = 0
+        t_start = time.perf_counter()
+        while reps < 2 or time.perf_counter() - t_start < seconds:
+            a = time.perf_counter()
+            v = oracle.verify_smc(th, dh, xh, float(np.float32(cfg.temperature)), cfg.alpha,
+                                  cfg.rng_seed, reps, lw)
+            b = time.perf_counter()
+            lwfull = rng.normal(0, 2, (B, N)).astype(np.float32)
+            r = oracle.resample(lwfull, float(np.float32(cfg.tau)), cfg.rng_seed, reps)
+            L += K + 1
+            o = oracle.kv_reassign(r["ancestors"], r["resampled"], o["tables"], cfg.block_size,
+                                   L, K + 1, o["refcounts"], o["free_list"], o["free_top"])
+            c = time.perf_counter()
+            t_verify += b - a
+            t_rest += c - b
+            reps += 1
+            if L + 2 * (K + 1) > cfg.M_cap * cfg.block_size:
+                break
+            del v
+        return reps, t_verify / reps * (S / nsamp) + t_rest / reps
+
+    cores = oracle.max_threads()
+    reps, per_step = sample(budget_s)
+    oracle.set_threads(1)
+    reps1, per_step1 = sample(budget_s / 4)
+    oracle.set_threads(cores)
     return {
         "value": round(1.0 / per_step, 4),
         "unit": "steps/s",
-        "cores": oracle.max_threads(),
+        "cores": cores,
         "kind": "oracle",
         "sample": "%d reps: verify on %d of %d sequences (scaled x%d), resample + KV exchange on "
                   "all %d prompts; fp64 C, OpenMP over rows" % (reps, nsamp, S, S // nsamp, B),
+        "single_thread_value": round(1.0 / per_step1, 4),
+        "single_thread_reps": reps1,
     }
 
 

@@ -73,6 +73,8 @@ def configure(lib):
                                     P, P, P]
     lib.orc_kv_reassign.restype = ctypes.c_int
     lib.orc_max_threads.restype = ctypes.c_int
+    lib.orc_set_threads.argtypes = [ctypes.c_int]
+    lib.orc_set_threads.restype = None
     return lib
 
 
@@ -91,6 +93,11 @@ def _p(a: np.ndarray):
 
 def max_threads() -> int:
     return int(_load().orc_max_threads())
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads for the following oracle calls (the default is every core)."""
+    _load().orc_set_threads(int(n))
 
 
 def _logit_array(x: np.ndarray):
