@@ -35,14 +35,14 @@ EVENT_EVERY = 8
 # only for the kernel sources they were taken on: any change to them reports null.
 VERIFY_TRAFFIC = {
     "workload": "c3_batched",
-    "bytes": 1186973452,
+    "bytes": 1186198117,
     "sources": {
         "smc_verification_resampling_amd/csrc/verify.hip":
-            "34629128897adf60fec7ff53c2096437250a02be72dc381621783a072311ead8",
+            "26ab14ac3d0715f61ab74c81e5e78be038101425846004e026e2e8f779cdd988",
         "smc_verification_resampling_amd/csrc/device.hpp":
             "5f1a401af612b80cc49dc04b7dad254ea96512e328607395f475dfb4e5a87d97",
         "smc_verification_resampling_amd/csrc/internal.hpp":
-            "8b46bc541f48668ddae7afa3f53bf065074cc539857e0c0557c240be0e9ed8b5",
+            "b56b9debf43193fcffdf9819832cd74f12875a069f74ba74c23b033bdbf708d8",
     },
 }
 
