@@ -187,6 +187,12 @@ def main():
             reset()
             torch.cuda.synchronize()
     st = int(status.cpu()[0])
+    # KV occupancy at the end of the timed region: blocks off the free stack (the next
+    # round's reservation included) against every sequence holding its own copy
+    live = cfg.pool - int(top.cpu()[0])
+    unshared = S * -(-(state["L"] + K + 1) // cfg.block_size)
+    kv_occ = {"rounds_in_episode": chunks[-1], "context_tokens": state["L"], "live_blocks": live,
+              "unshared_blocks": unshared, "saving": round(1.0 - live / unshared, 4)}
     verify_ms = [e[0].elapsed_time(e[1]) for e in events if e is not None]
     verify_avg_s = float(np.mean(verify_ms)) / 1e3
     ms_per_step = t_total / args.steps * 1e3
@@ -226,6 +232,7 @@ def main():
             "algorithmic_bytes_per_step": bytes_per_verify,
             "step_hbm_gbs": round(step_gbs, 1),
             "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+            "kv_occupancy": kv_occ,
             "sps_verify": sps,
             "combined_ms_per_step": (round(ms_per_step + sps["us_per_call"] / 1e3, 5)
                                      if sps else None),

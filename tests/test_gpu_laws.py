@@ -121,3 +121,22 @@ def test_gpu_sps_law_equals_target():
     ys = np.array([e[0] * 64 + e[1] * 8 + e[2] for e in emitted])
     counts = np.bincount(ys, minlength=V ** 3).astype(np.float64)
     assert L._chi2_pvalue(counts, pi) > 1e-4
+
+
+def test_temperature_sweep_runs_and_reports_ranges(capsys):
+    """The temperature sweep (SpS tokens per round vs SMC-SD's K+1, ESS, resample rate) on
+    the tiny workload: every reported figure inside its range."""
+    import json
+
+    from smc_verification_resampling_amd import sweep
+
+    sweep.main(["--workload", "c1_tiny", "--temperatures", "0.7,1.3", "--rounds", "6",
+                "--sets", "2"])
+    lines = [json.loads(x) for x in capsys.readouterr().out.strip().splitlines()]
+    assert [d["temperature"] for d in lines] == [0.7, 1.3]
+    for d in lines:
+        assert d["status"] == 0
+        assert 1.0 <= d["sps_tokens_per_round"] <= d["K"] + 1
+        assert d["smc_tokens_per_round"] == d["K"] + 1
+        assert 0.0 < d["smc_mean_ess_fraction"] <= 1.0
+        assert 0.0 <= d["smc_resample_rate"] <= 1.0
