@@ -60,11 +60,14 @@ def configure(lib):
     lib.orc_row_lse.argtypes = [P, ctypes.c_int, i64, dbl, P]
     lib.orc_row_lse.restype = dbl
     lib.orc_verify_smc.argtypes = [P, P, ctypes.c_int, i64, ctypes.c_int, P, ctypes.c_int, P,
-                                   dbl, dbl, u64, u64, P, P, P, P, P, P, P, P, P]
+                                   dbl, dbl, u64, u64, P, P, P, P, P, P, P, P, P, P]
     lib.orc_verify_smc.restype = ctypes.c_int
     lib.orc_verify_sps.argtypes = [P, P, ctypes.c_int, i64, ctypes.c_int, P, ctypes.c_int, P,
                                    dbl, u64, u64, P, P, P, P, P, P, P, P]
     lib.orc_verify_sps.restype = ctypes.c_int
+    lib.orc_draft_sample.argtypes = [P, ctypes.c_int, i64, ctypes.c_int, P, ctypes.c_int, dbl,
+                                     u64, u64, P, P, P, P]
+    lib.orc_draft_sample.restype = ctypes.c_int
     lib.orc_resample.argtypes = [P, ctypes.c_int, ctypes.c_int, dbl, u64, u64,
                                  P, P, P, P, P, P, P]
     lib.orc_resample.restype = ctypes.c_int
@@ -133,15 +136,23 @@ def row_lse(row: np.ndarray, T: float = 1.0):
 
 
 # --------------------------------------------------------------------------- verify
-def verify_smc(target: np.ndarray, draft: np.ndarray, draft_tokens: np.ndarray, T: float,
-               alpha: float, seed: int, t: int, lw_in: np.ndarray,
-               rng_index: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
-    """SMC verify for nseq sequences.  target [nseq, K+1, V], draft [nseq, K, V]."""
+def verify_smc(target: np.ndarray, draft: Optional[np.ndarray], draft_tokens: np.ndarray,
+               T: float, alpha: float, seed: int, t: int, lw_in: np.ndarray,
+               rng_index: Optional[np.ndarray] = None,
+               logq_in: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """SMC verify for nseq sequences.  target [nseq, K+1, V], draft [nseq, K, V]; with
+    logq_in [nseq, K] (the draft's log-probabilities of its tokens) the draft rows are not
+    read and draft may be None."""
     tg, code = _logit_array(target)
     nseq, K1, V = tg.shape
     K = K1 - 1
-    dr, code2 = _logit_array(draft.reshape(nseq, K, V))
-    assert code == code2
+    if logq_in is None:
+        dr, code2 = _logit_array(draft.reshape(nseq, K, V))
+        assert code == code2
+        lq_in = None
+    else:
+        dr = np.zeros(1, np.float32)
+        lq_in = np.ascontiguousarray(logq_in, dtype=np.float64).reshape(nseq, K)
     tok = np.ascontiguousarray(draft_tokens, dtype=np.int32).reshape(nseq, K)
     idx = np.arange(nseq, dtype=np.int64) if rng_index is None else \
         np.ascontiguousarray(rng_index, dtype=np.int64)
@@ -157,10 +168,27 @@ def verify_smc(target: np.ndarray, draft: np.ndarray, draft_tokens: np.ndarray, 
     }
     logq_buf = np.zeros((nseq, max(K, 1)), np.float64)
     _load().orc_verify_smc(_p(tg), _p(dr), code, V, nseq, _p(idx), K, _p(tok), T, alpha, seed, t,
-                           _p(lw), _p(out["lw"]), _p(out["tokens"]), _p(out["logp"]),
+                           _p(lw), None if lq_in is None else _p(lq_in), _p(out["lw"]),
+                           _p(out["tokens"]), _p(out["logp"]),
                            _p(logq_buf), _p(out["lse"]), _p(out["u"]), _p(out["margin"]),
                            _p(out["status"]))
     out["logq"] = logq_buf[:, :K].copy()
+    out["status"] = int(out["status"][0])
+    return out
+
+
+def draft_sample(rows: np.ndarray, T: float, seed: int, t: int, pos: int,
+                 rng_index: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Draft-side sampler: one token per row from softmax(rows / T) and its log q.
+    rows [n, V]; the RNG stream index of row r is rng_index[r] (default r)."""
+    rw, code = _logit_array(rows)
+    n, V = rw.shape
+    idx = np.arange(n, dtype=np.int64) if rng_index is None else \
+        np.ascontiguousarray(rng_index, dtype=np.int64)
+    out = {"tokens": np.zeros(n, np.int32), "logq": np.zeros(n, np.float64),
+           "margin": np.zeros(n, np.float64), "status": np.zeros(1, np.int32)}
+    _load().orc_draft_sample(_p(rw), code, V, n, _p(idx), pos, T, seed, t, _p(out["tokens"]),
+                             _p(out["logq"]), _p(out["margin"]), _p(out["status"]))
     out["status"] = int(out["status"][0])
     return out
 

@@ -47,6 +47,7 @@
 #define ORC_TAG_RESAMPLE 2u
 #define ORC_TAG_SPS_ACCEPT 3u
 #define ORC_TAG_SPS_FINAL 4u
+#define ORC_TAG_DRAFT 5u
 
 int orc_version(void) { return 1; }
 
@@ -204,19 +205,24 @@ static int32_t inverse_cdf_row(const void *row, int dtype, int64_t V, double T, 
 /* ------------------------------------------------------------------------- */
 int orc_verify_smc(const void *tgt, const void *drf, int dtype, int64_t V, int nseq,
                    const int64_t *rng_index, int K, const int32_t *draft_tokens, double T,
-                   double alpha, uint64_t seed, uint64_t t, const double *lw_in, double *lw_out,
-                   int32_t *tokens, double *logp, double *logq, double *lse, double *bonus_u,
-                   double *margin, int32_t *status)
+                   double alpha, uint64_t seed, uint64_t t, const double *lw_in,
+                   const double *logq_in, double *lw_out, int32_t *tokens, double *logp,
+                   double *logq, double *lse, double *bonus_u, double *margin, int32_t *status)
 {
     const int R = 2 * K + 1;
     const int64_t nrows = (int64_t)nseq * R;
     int32_t st = 0;
 
-    /* Score: every row's log-normaliser (rows are independent) */
+    /* Score: every row's log-normaliser (rows are independent).  With logq_in (the
+       draft's log-probabilities emitted when it sampled) the draft rows are not read. */
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : st)
     for (int64_t r = 0; r < nrows; ++r) {
         int64_t s = r / R;
         int k = (int)(r % R);
+        if (k > K && logq_in) {
+            lse[r] = NAN;
+            continue;
+        }
         const void *row = k <= K ? row_ptr(tgt, dtype, s * (K + 1) + k, V)
                                  : row_ptr(drf, dtype, s * K + (k - K - 1), V);
         int32_t rst = 0;
@@ -231,9 +237,10 @@ int orc_verify_smc(const void *tgt, const void *drf, int dtype, int64_t V, int n
         for (int k = 0; k < K; ++k) {
             int32_t x = draft_tokens[(int64_t)s * K + k];
             const void *trow = row_ptr(tgt, dtype, (int64_t)s * (K + 1) + k, V);
-            const void *drow = row_ptr(drf, dtype, (int64_t)s * K + k, V);
             double lp = load_elem(trow, dtype, x) / T - L[k];
-            double lq = load_elem(drow, dtype, x) / T - L[K + 1 + k];
+            double lq = logq_in ? logq_in[(int64_t)s * K + k]
+                                : load_elem(row_ptr(drf, dtype, (int64_t)s * K + k, V), dtype, x) / T -
+                                      L[K + 1 + k];
             logp[(int64_t)s * (K + 1) + k] = lp;
             logq[(int64_t)s * K + k] = lq;
             tokens[(int64_t)s * (K + 1) + k] = x;
@@ -273,6 +280,39 @@ int orc_verify_smc(const void *tgt, const void *drf, int dtype, int64_t V, int n
 /* position.  margin_accept[s] = min |r_k - ratio_k| over the tests made;        */
 /* margin_final[s] = distance of u to the nearest bracketing (normalised) CDF.    */
 /* ------------------------------------------------------------------------- */
+/* ------------------------------------------------------------------------- */
+/* [SMC] Extend step, draft side: the draft model proposes each token from its  */
+/* own tempered distribution (core flow, "Extend").  One row per sequence at one */
+/* draft position pos: x = min{v : sum_{w<=v} softmax(z)_w > u} with z = l / T   */
+/* and u = U(seed; g, t, DRAFT | pos << 8) (a reading: inverse CDF in ascending  */
+/* id order, the same rule as the bonus token), and log q(x) = z_x - LSE(z), the */
+/* value the verify's reweighting needs, so the verify can skip the draft rows.  */
+/* margin[r] = distance from u to the nearest CDF boundary of the choice.       */
+/* ------------------------------------------------------------------------- */
+int orc_draft_sample(const void *rows, int dtype, int64_t V, int nrows, const int64_t *rng_index,
+                     int pos, double T, uint64_t seed, uint64_t t, int32_t *tokens, double *logq,
+                     double *margin, int32_t *status)
+{
+    int32_t st = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : st)
+    for (int r = 0; r < nrows; ++r) {
+        const void *row = row_ptr(rows, dtype, r, V);
+        int32_t rst = 0;
+        double L = orc_row_lse(row, dtype, V, T, &rst);
+        st |= rst;
+        double u = orc_uniform(seed, (uint32_t)rng_index[r], t,
+                               ORC_TAG_DRAFT | ((uint32_t)pos << 8), 0);
+        double m = 0.0;
+        int32_t x = -1;
+        if (isfinite(L)) x = inverse_cdf_row(row, dtype, V, T, L, u, &m);
+        tokens[r] = x;
+        logq[r] = x >= 0 ? load_elem(row, dtype, x) / T - L : NAN;
+        margin[r] = m;
+    }
+    *status |= st;
+    return 0;
+}
+
 int orc_verify_sps(const void *tgt, const void *drf, int dtype, int64_t V, int nseq,
                    const int64_t *rng_index, int K, const int32_t *draft_tokens, double T,
                    uint64_t seed, uint64_t t, int32_t *tokens, int32_t *num_tokens, double *logp,

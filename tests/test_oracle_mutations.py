@@ -15,6 +15,7 @@ import tempfile
 import pytest
 
 import oracle
+from tests import test_oracle_draft as dr
 from tests import test_oracle_kv as kv
 from tests import test_oracle_laws as laws
 from tests import test_oracle_resample as rs
@@ -70,8 +71,8 @@ CASES = [
      "double lp = load_elem(trow, dtype, x) - L[k];",
      [lambda: vf.test_verify_gather_and_weights_vs_log_softmax(O, "f32", 1.0)]),
     ("log q gathered from the target row",
-     "double lq = load_elem(drow, dtype, x) / T - L[K + 1 + k];",
-     "double lq = load_elem(trow, dtype, x) / T - L[K + 1 + k];",
+     "load_elem(row_ptr(drf, dtype, (int64_t)s * K + k, V), dtype, x) / T",
+     "load_elem(trow, dtype, x) / T",
      [lambda: vf.test_verify_gather_and_weights_vs_log_softmax(O, "f32", 1.0)]),
     ("bonus drawn from row K-1",
      "const void *brow = row_ptr(tgt, dtype, (int64_t)s * (K + 1) + K, V);",
@@ -112,6 +113,17 @@ CASES = [
      [lambda: laws.test_sps_law_equals_target(O)]),
     ("SMC weight uses q/p", "incr += alpha * lp - lq;", "incr += lq - alpha * lp;",
      [lambda: laws.test_smc_round_follows_sir_law(O, 4, 1.0)]),
+    ("draft uniform ignores the position", "ORC_TAG_DRAFT | ((uint32_t)pos << 8)", "ORC_TAG_DRAFT",
+     [lambda: dr.test_draft_sample_is_the_textbook_inverse_cdf(O, "f32", 1.0)]),
+    ("draft log q without the temperature",
+     "logq[r] = x >= 0 ? load_elem(row, dtype, x) / T - L : NAN;",
+     "logq[r] = x >= 0 ? load_elem(row, dtype, x) - L : NAN;",
+     [lambda: dr.test_draft_sample_is_the_textbook_inverse_cdf(O, "f32", 0.8)]),
+    ("draft log q of the wrong token", "logq[r] = x >= 0 ? load_elem(row, dtype, x) / T - L : NAN;",
+     "logq[r] = x >= 0 ? load_elem(row, dtype, x > 0 ? x - 1 : x) / T - L : NAN;",
+     [lambda: dr.test_draft_sample_is_the_textbook_inverse_cdf(O, "f32", 1.0)]),
+    ("verify reads the wrong precomputed log q", "logq_in[(int64_t)s * K + k]", "logq_in[(int64_t)s * K]",
+     [lambda: dr.test_verify_with_draft_logq_equals_reading_the_draft_rows(O)]),
 ]
 
 
