@@ -72,6 +72,9 @@ def _parse():
     ap.add_argument("--workload", default="c3_batched")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--draft-logq", action="store_true",
+                    help="draft tokens and their log q from smcsd_draft_sample (untimed, part of "
+                         "the Extend step); the timed verify takes them and skips the draft rows")
     ap.add_argument("--probe-mib", type=int, default=1024,
                     help="size of the reference copy / read kernels (0 = skip)")
     return ap.parse_args()
@@ -101,7 +104,10 @@ def main():
     sets = []
     for s in range(cfg.n_sets):
         t, d = synth.make_logit_set(cfg, s, dev, base)
-        sets.append((t, d, synth.sample_draft_tokens(cfg, d, s)))
+        sets.append((t, d, synth.sample_draft_tokens(cfg, d, s), None))
+    draft_info = None
+    if args.draft_logq:
+        sets, draft_info = draft_side(cfg, sets)
 
     i32 = dict(dtype=torch.int32, device=dev)
     f32 = dict(dtype=torch.float32, device=dev)
@@ -144,12 +150,12 @@ def main():
     max_rounds = cfg.iters
 
     def step(t, ev=None):
-        tgt, drf, toks = sets[t % cfg.n_sets]
+        tgt, drf, toks, lq_in = sets[t % cfg.n_sets]
         if ev is not None:
             ev[0].record()
-        sm.verify(tgt, drf, toks, B, N, K, V, cfg.temperature, cfg.alpha, sm.MODE_SMC, seed, t,
-                  tokens, status, ws_v, log_weights=lw, out_num_tokens=num, out_logp=logp,
-                  out_logq=logq)
+        sm.verify(tgt, None if lq_in is not None else drf, toks, B, N, K, V, cfg.temperature,
+                  cfg.alpha, sm.MODE_SMC, seed, t, tokens, status, ws_v, log_weights=lw,
+                  out_num_tokens=num, out_logp=logp, out_logq=logq, logq_in=lq_in)
         if ev is not None:
             ev[1].record()
         sm.resample(lw.view(B, N), B, N, cfg.tau, seed, t, anc, ess, resampled, status)
@@ -198,6 +204,8 @@ def main():
     ms_per_step = t_total / args.steps * 1e3
     steps_per_s = args.steps / t_total
     bytes_per_verify = cfg.logit_bytes_per_step
+    if args.draft_logq:  # the K draft rows are not read
+        bytes_per_verify = bytes_per_verify * (K + 1) // (2 * K + 1)
     achieved_gbs = bytes_per_verify / verify_avg_s / 1e9
     step_gbs = bytes_per_verify * steps_per_s / 1e9
 
@@ -222,12 +230,14 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": "%s: B=%d prompts x N=%d particles, K=%d, V=%d, %s logits (%s), T=%g, "
+            "workload": "%s%s: B=%d prompts x N=%d particles, K=%d, V=%d, %s logits (%s), T=%g, "
                         "alpha=%g, tau=%g, ctx %d in %d-token blocks%s" % (
-                            cfg.name, B, N, K, V, cfg.dtype, cfg.target_kind, cfg.temperature,
-                            cfg.alpha, cfg.tau, cfg.ctx0, cfg.block_size,
-                            ", shared prefix" if cfg.shared_prefix else ""),
-            "step": "smcsd_verify + smcsd_resample + smcsd_kv_reassign",
+                            cfg.name, "+draft_logq" if args.draft_logq else "", B, N, K, V,
+                            cfg.dtype, cfg.target_kind, cfg.temperature, cfg.alpha, cfg.tau,
+                            cfg.ctx0, cfg.block_size, ", shared prefix" if cfg.shared_prefix else ""),
+            "step": "smcsd_verify%s + smcsd_resample + smcsd_kv_reassign" % (
+                " (logq_in: target rows only)" if args.draft_logq else ""),
+            "draft_sample": draft_info,
             "logit_sets": cfg.n_sets,
             "algorithmic_bytes_per_step": bytes_per_verify,
             "step_hbm_gbs": round(step_gbs, 1),
@@ -246,13 +256,55 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-            "traffic": verify_traffic(cfg.name),
+            "traffic": verify_traffic(cfg.name + ("+draft_logq" if args.draft_logq else "")),
             "avg_launch_us": round(verify_avg_s * 1e6, 2),
             "launches_timed": len(verify_ms),
         },
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
+
+
+def draft_side(cfg, sets):
+    """Draft tokens and their log q for every logit set from smcsd_draft_sample, one draft
+    position per call (as the Extend step would call it), untimed in the step; the cost
+    of one position call over the whole batch is timed here with HIP events."""
+    import torch
+
+    import smc_verification_resampling_amd as sm
+
+    S, K, V = cfg.S, cfg.K, cfg.V
+    ws = sm.alloc_workspace(sm.OP_DRAFT, S, 1, 0, V)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = []
+    for s, (tgt, drf, _, _) in enumerate(sets):
+        toks = torch.zeros((S, K), dtype=torch.int32, device="cuda")
+        lq = torch.zeros((S, K), dtype=torch.float32, device="cuda")
+        flat = drf.reshape(-1)
+        for k in range(K):
+            tk = torch.zeros(S, dtype=torch.int32, device="cuda")
+            lk = torch.zeros(S, dtype=torch.float32, device="cuda")
+            sm.draft_sample(flat[k * V:], S, V, cfg.temperature, cfg.rng_seed, s, k, tk, st, ws,
+                            out_logq=lk, row_stride=K * V)
+            toks[:, k] = tk
+            lq[:, k] = lk
+        out.append((tgt, drf, toks, lq))
+    tk = torch.zeros(S, dtype=torch.int32, device="cuda")
+    lk = torch.zeros(S, dtype=torch.float32, device="cuda")
+    flat = sets[0][1].reshape(-1)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    reps = 50
+    torch.cuda.synchronize()
+    ev[0].record()
+    for r in range(reps):
+        sm.draft_sample(flat[(r % K) * V:], S, V, cfg.temperature, cfg.rng_seed, 99, r % K, tk, st,
+                        ws, out_logq=lk, row_stride=K * V)
+    ev[1].record()
+    torch.cuda.synchronize()
+    us = ev[0].elapsed_time(ev[1]) * 1e3 / reps
+    elt = 2 if cfg.dtype == "bf16" else 4
+    return out, {"us_per_position_call": round(us, 2), "rows_per_call": S,
+                 "GBps": round(S * V * elt / (us * 1e-6) / 1e9, 1), "status": int(st.cpu()[0])}
 
 
 def sps_timing(cfg, sets, steps):
@@ -271,7 +323,7 @@ def sps_timing(cfg, sets, steps):
     emitted = torch.zeros(B, dtype=torch.int64, device="cuda")
 
     def call(t):
-        tgt, drf, toks = sets[t % cfg.n_sets]
+        tgt, drf, toks, _ = sets[t % cfg.n_sets]
         sm.verify(tgt, drf, toks, B, 1, K, V, cfg.temperature, 1.0, sm.MODE_SPS, cfg.rng_seed,
                   t, tok, status, ws, out_num_tokens=num, seq_step=N)
 
@@ -335,7 +387,7 @@ def cpu_baseline(cfg, sets, budget_s):
 
     B, N, K, S = cfg.B, cfg.N, cfg.K, cfg.S
     nsamp = min(S, 32)
-    tgt, drf, toks = sets[0]
+    tgt, drf, toks, _ = sets[0]
     sel = torch.arange(nsamp, device=tgt.device)
 
     def host(x):

@@ -33,7 +33,8 @@
  * key = (seed low, seed high) and counter = (stream index, step low, step high, tag);
  * a uniform is (word >> 8) * 2^-24.  Tags: 1 bonus token (index = sequence g),
  * 2 resampling offset (index = prompt b), 3 | (k/4) << 8 SpS acceptance of draft k
- * (word k mod 4), 4 SpS final token.  Results depend only on (inputs, seed, step):
+ * (word k mod 4), 4 SpS final token, 5 | pos << 8 draft token at draft position pos
+ * (index = row).  Results depend only on (inputs, seed, step):
  * runs are bit-reproducible and resumable.
  */
 #ifndef SMCSD_H
@@ -46,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SMCSD_VERSION 1
+#define SMCSD_VERSION 2
 
 /* logits element type */
 #define SMCSD_DTYPE_F32 0
@@ -74,6 +75,7 @@ extern "C" {
 #define SMCSD_OP_VERIFY_SMC 0
 #define SMCSD_OP_VERIFY_SPS 1
 #define SMCSD_OP_KV 2
+#define SMCSD_OP_DRAFT 3
 
 /* Library version (SMCSD_VERSION). */
 int smcsd_version(void);
@@ -85,6 +87,7 @@ const char *smcsd_status_string(int code);
  * Device workspace bytes for one call.  Workspaces are caller-owned device buffers whose
  * start must be 256-byte aligned (SMCSD_EWORKSPACE otherwise).
  *   SMCSD_OP_VERIFY_SMC / _SPS: B, N, K, V as passed to smcsd_verify (P ignored).
+ *   SMCSD_OP_DRAFT: B = number of rows, N = 1, V as passed to smcsd_draft_sample.
  *   SMCSD_OP_KV: B, N and the pool size P (K, V ignored).  The KV workspace must be
  *   zero-filled before its first use and then passed, unmodified, to every later call
  *   with the same B, N and P: calls keep its contents consistent (it alternates two
@@ -127,6 +130,11 @@ size_t smcsd_workspace_bytes(int op, int B, int N, int K, int V, int64_t P);
  * out_num_tokens[g] = k*+1 (K+1 if all accepted); out_logp[g][K] = target
  * log-probability of the drawn token at its position; log_weights is not touched.
  * If lse_in is given (SpS mode only) the LSE pass is skipped and lse_in is used.
+ * If logq_in is given (SMC mode only) [src, K] fp32 - the draft's log-probabilities of
+ * its own tokens, as smcsd_draft_sample emits them while drafting - the draft rows are
+ * not read at all (draft_logits may be NULL): logq_k = logq_in[src][k], and the LSE
+ * pass covers only the K+1 target rows (out_lse's draft entries are NaN).  The bytes
+ * read per sequence fall from (2K+1)V to (K+1)V.
  *
  * Outputs (indexed by g): out_tokens [B*N, K+1] int32 (required); out_num_tokens
  * [B*N], out_logp [B*N, K+1], out_logq [B*N, K], out_lse [B*N, 2K+1] (target rows
@@ -138,9 +146,31 @@ size_t smcsd_workspace_bytes(int op, int B, int N, int K, int V, int64_t P);
 int smcsd_verify(const void *target_logits, const void *draft_logits, int dtype,
                  int64_t row_stride, int seq_step, const int32_t *draft_tokens, int B, int N,
                  int K, int V, float temperature, float alpha, int mode, uint64_t seed,
-                 uint64_t step, const float *lse_in, float *log_weights, int32_t *out_tokens,
-                 int32_t *out_num_tokens, float *out_logp, float *out_logq, float *out_lse,
-                 int32_t *status, void *workspace, size_t workspace_bytes, void *stream);
+                 uint64_t step, const float *lse_in, const float *logq_in, float *log_weights,
+                 int32_t *out_tokens, int32_t *out_num_tokens, float *out_logp, float *out_logq,
+                 float *out_lse, int32_t *status, void *workspace, size_t workspace_bytes,
+                 void *stream);
+
+/*
+ * smcsd_draft_sample - the draft side of the Extend step at one draft position: each
+ * of n rows (one sequence's draft logits at position pos) draws its token from its own
+ * tempered distribution and also yields that token's log-probability, which is what
+ * the verify's reweighting needs from the draft (SMC explainers, methodology "core
+ * flow": the draft model extends every particle by K tokens).  The draw is a reading:
+ * x = min{v : sum_{w<=v} softmax(z)_w > u}, z = logit / temperature,
+ * u = U(seed; r, step, 5 | pos << 8) for row r; out_logq[r] = z_x - LSE(z) (fp32
+ * accumulation, as in smcsd_verify).  Passing these values as smcsd_verify's logq_in
+ * lets the verify skip the draft rows.
+ * Layout: draft_logits + r * row_stride (element units), V valid elements per row,
+ * dtype bf16 or fp32, element-aligned.  out_tokens [n] int32 (-1 for a row with no
+ * finite logit, which also sets EMPTY_ROW), out_logq [n] fp32 (nullable).
+ * Limits: 1 <= V <= 2^24, 0 <= pos < 2^24, temperature finite > 0.  n = 0 is a
+ * no-op.  workspace: smcsd_workspace_bytes(SMCSD_OP_DRAFT, n, 1, 0, V, 0).
+ */
+int smcsd_draft_sample(const void *draft_logits, int dtype, int64_t row_stride, int n, int V,
+                       float temperature, uint64_t seed, uint64_t step, int pos,
+                       int32_t *out_tokens, float *out_logq, int32_t *status, void *workspace,
+                       size_t workspace_bytes, void *stream);
 
 /*
  * smcsd_resample - ESS and resampling per prompt (the Resample step: compute the

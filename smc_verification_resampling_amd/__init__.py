@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libsmcsd.so")
 
 DTYPE_F32, DTYPE_BF16 = 0, 1
 MODE_SMC, MODE_SPS = 0, 1
-OP_VERIFY_SMC, OP_VERIFY_SPS, OP_KV = 0, 1, 2
+OP_VERIFY_SMC, OP_VERIFY_SPS, OP_KV, OP_DRAFT = 0, 1, 2, 3
 
 ST_NAN_INPUT = 1
 ST_EMPTY_ROW = 2
@@ -28,7 +28,7 @@ ST_DEGENERATE_WEIGHTS = 8
 ST_BAD_INPUT = 16
 
 EXPORTED = ("smcsd_version", "smcsd_status_string", "smcsd_workspace_bytes", "smcsd_verify",
-            "smcsd_resample", "smcsd_kv_reassign", "smcsd_philox4x32_10")
+            "smcsd_draft_sample", "smcsd_resample", "smcsd_kv_reassign", "smcsd_philox4x32_10")
 
 _DT = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
 
@@ -56,8 +56,10 @@ def load_library(path: str = LIB_PATH):
     lib.smcsd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i64]
     lib.smcsd_workspace_bytes.restype = sz
     lib.smcsd_verify.argtypes = [P, P, i32, i64, i32, P, i32, i32, i32, i32, f32, f32, i32, u64,
-                                 u64, P, P, P, P, P, P, P, P, P, sz, P]
+                                 u64, P, P, P, P, P, P, P, P, P, P, sz, P]
     lib.smcsd_verify.restype = i32
+    lib.smcsd_draft_sample.argtypes = [P, i32, i64, i32, i32, f32, u64, u64, i32, P, P, P, P, sz, P]
+    lib.smcsd_draft_sample.restype = i32
     lib.smcsd_resample.argtypes = [P, i32, i32, f32, u64, u64, P, P, P, P, P]
     lib.smcsd_resample.restype = i32
     lib.smcsd_kv_reassign.argtypes = [P, P, i32, i32, P, i32, i32, i64, i32, P, P, P, i64, P, P,
@@ -125,8 +127,9 @@ def verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: Op
            step: int, out_tokens: torch.Tensor, status: torch.Tensor, workspace: torch.Tensor,
            log_weights: Optional[torch.Tensor] = None, out_num_tokens=None, out_logp=None,
            out_logq=None, out_lse=None, lse_in=None, seq_step: int = 1,
-           row_stride: Optional[int] = None, stream=None) -> None:
-    """smcsd_verify.  target [*, K+1, row_stride], draft [*, K, row_stride] (bf16 or fp32)."""
+           row_stride: Optional[int] = None, stream=None, logq_in=None) -> None:
+    """smcsd_verify.  target [*, K+1, row_stride], draft [*, K, row_stride] (bf16 or fp32).
+    With logq_in [*, K] fp32 (the draft's log q of its tokens) draft may be None."""
     if target.dtype not in _DT:
         raise SmcsdError("logits must be bfloat16 or float32")
     rs = V if row_stride is None else int(row_stride)
@@ -134,13 +137,14 @@ def verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: Op
     nsrc = (S - 1) * seq_step + 1 if S > 0 else 0
     tp = _dev(target, "target", target.dtype, nsrc * (K + 1) * rs - (rs - V) if S else 0)
     dp = _dev(draft, "draft", target.dtype, nsrc * K * rs - (rs - V) if S and K else 0) \
-        if K > 0 else None
+        if K > 0 and (draft is not None or logq_in is None) else None
     xp = _dev(draft_tokens, "draft_tokens", torch.int32, nsrc * K) if K > 0 else None
     lw = _dev(log_weights, "log_weights", torch.float32, S)
     rc = _L().smcsd_verify(
         tp, dp, _DT[target.dtype], rs, seq_step, xp, B, N, K, V, float(temperature), float(alpha),
         mode, int(seed) & (2**64 - 1), int(step) & (2**64 - 1),
-        _dev(lse_in, "lse_in", torch.float32, nsrc * (2 * K + 1)), lw,
+        _dev(lse_in, "lse_in", torch.float32, nsrc * (2 * K + 1)),
+        _dev(logq_in, "logq_in", torch.float32, nsrc * K), lw,
         _dev(out_tokens, "out_tokens", torch.int32, S * (K + 1)),
         _dev(out_num_tokens, "out_num_tokens", torch.int32, S),
         _dev(out_logp, "out_logp", torch.float32, S * (K + 1)),
@@ -149,6 +153,23 @@ def verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: Op
         _dev(status, "status", torch.int32, 1),
         _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
     _check(rc, "smcsd_verify")
+
+
+def draft_sample(draft: torch.Tensor, n: int, V: int, temperature: float, seed: int, step: int,
+                 pos: int, out_tokens: torch.Tensor, status: torch.Tensor, workspace: torch.Tensor,
+                 out_logq: Optional[torch.Tensor] = None, row_stride: Optional[int] = None,
+                 stream=None) -> None:
+    """smcsd_draft_sample.  draft [n, row_stride] (bf16 or fp32) at one draft position."""
+    if draft.dtype not in _DT:
+        raise SmcsdError("logits must be bfloat16 or float32")
+    rs = V if row_stride is None else int(row_stride)
+    rc = _L().smcsd_draft_sample(
+        _dev(draft, "draft", draft.dtype, n * rs - (rs - V) if n else 0), _DT[draft.dtype], rs, n,
+        V, float(temperature), int(seed) & (2**64 - 1), int(step) & (2**64 - 1), int(pos),
+        _dev(out_tokens, "out_tokens", torch.int32, n),
+        _dev(out_logq, "out_logq", torch.float32, n), _dev(status, "status", torch.int32, 1),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
+    _check(rc, "smcsd_draft_sample")
 
 
 def resample(log_weights: torch.Tensor, B: int, N: int, tau: float, seed: int, step: int,

@@ -45,6 +45,10 @@ size_t smcsd_workspace_bytes(int op, int B, int N, int K, int V, int64_t P) {
     if (K < 0 || K > kMaxK || V < 1 || V > kMaxV) return 0;
     return verify_ws_layout(S, K, V, op == SMCSD_OP_VERIFY_SPS ? 1 : 0).total;
   }
+  if (op == SMCSD_OP_DRAFT) {
+    if (V < 1 || V > kMaxV) return 0;
+    return verify_ws_layout(S, 0, V, 0).total;
+  }
   if (op == SMCSD_OP_KV) {
     if (P < 1) return 0;
     return kv_ws_layout(S, P).total;
@@ -55,9 +59,10 @@ size_t smcsd_workspace_bytes(int op, int B, int N, int K, int V, int64_t P) {
 int smcsd_verify(const void *target_logits, const void *draft_logits, int dtype,
                  int64_t row_stride, int seq_step, const int32_t *draft_tokens, int B, int N,
                  int K, int V, float temperature, float alpha, int mode, uint64_t seed,
-                 uint64_t step, const float *lse_in, float *log_weights, int32_t *out_tokens,
-                 int32_t *out_num_tokens, float *out_logp, float *out_logq, float *out_lse,
-                 int32_t *status, void *workspace, size_t workspace_bytes, void *stream) {
+                 uint64_t step, const float *lse_in, const float *logq_in, float *log_weights,
+                 int32_t *out_tokens, int32_t *out_num_tokens, float *out_logp, float *out_logq,
+                 float *out_lse, int32_t *status, void *workspace, size_t workspace_bytes,
+                 void *stream) {
   if (dtype != SMCSD_DTYPE_F32 && dtype != SMCSD_DTYPE_BF16) return SMCSD_EDTYPE;
   if (mode != SMCSD_MODE_SMC && mode != SMCSD_MODE_SPS) return SMCSD_EINVAL;
   if (B < 0 || N < 0 || K < 0 || K > kMaxK || V < 1 || V > kMaxV || seq_step < 1)
@@ -70,7 +75,9 @@ int smcsd_verify(const void *target_logits, const void *draft_logits, int dtype,
   if (S > INT32_MAX / 2) return SMCSD_EINVAL;
   const size_t esz = dtype == SMCSD_DTYPE_BF16 ? 2 : 4;
   if (!target_logits || !aligned(target_logits, esz)) return SMCSD_EINVAL;
-  if (K > 0 && (!draft_logits || !aligned(draft_logits, esz) || !draft_tokens)) return SMCSD_EINVAL;
+  if (logq_in && mode != SMCSD_MODE_SMC) return SMCSD_EINVAL;
+  if (K > 0 && (!draft_tokens || (!logq_in && (!draft_logits || !aligned(draft_logits, esz)))))
+    return SMCSD_EINVAL;
   if (!out_tokens || !status) return SMCSD_EINVAL;
   if (mode == SMCSD_MODE_SMC && (!log_weights || lse_in)) return SMCSD_EINVAL;
   const size_t need = verify_ws_layout(S, K, V, mode == SMCSD_MODE_SPS ? 1 : 0).total;
@@ -92,6 +99,8 @@ int smcsd_verify(const void *target_logits, const void *draft_logits, int dtype,
   a.seed = seed;
   a.step = step;
   a.lse_in = lse_in;
+  a.logq_in = logq_in;
+  a.bonus_tag = 1u;
   a.log_weights = log_weights;
   a.out_tokens = out_tokens;
   a.out_num_tokens = out_num_tokens;
@@ -101,6 +110,45 @@ int smcsd_verify(const void *target_logits, const void *draft_logits, int dtype,
   a.status = status;
   a.ws = static_cast<char *>(workspace);
   a.stream = as_stream(stream);
+  return hip_rc(launch_verify(a));
+}
+
+int smcsd_draft_sample(const void *draft_logits, int dtype, int64_t row_stride, int n, int V,
+                       float temperature, uint64_t seed, uint64_t step, int pos,
+                       int32_t *out_tokens, float *out_logq, int32_t *status, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+  if (dtype != SMCSD_DTYPE_F32 && dtype != SMCSD_DTYPE_BF16) return SMCSD_EDTYPE;
+  if (n < 0 || V < 1 || V > kMaxV || row_stride < V || pos < 0 || pos >= (1 << 24))
+    return SMCSD_EINVAL;
+  if (!(temperature > 0.0f) || !std::isfinite(temperature)) return SMCSD_EINVAL;
+  if (n == 0) return SMCSD_OK;
+  const size_t esz = dtype == SMCSD_DTYPE_BF16 ? 2 : 4;
+  if (!draft_logits || !aligned(draft_logits, esz) || !out_tokens || !status) return SMCSD_EINVAL;
+  const size_t need = verify_ws_layout(n, 0, V, 0).total;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) return SMCSD_EWORKSPACE;
+  // the row-K draw of a verify with K = 0 over the draft rows, with the draft's RNG tag
+  VerifyArgs a{};
+  a.tgt = draft_logits;
+  a.drf = nullptr;
+  a.dtype = dtype;
+  a.row_stride = row_stride;
+  a.seq_step = 1;
+  a.draft_tokens = nullptr;
+  a.nseq = n;
+  a.K = 0;
+  a.V = V;
+  a.c = (float)(1.4426950408889634073599246810018921 / (double)temperature);
+  a.alpha = 1.0f;
+  a.mode = SMCSD_MODE_SMC;
+  a.seed = seed;
+  a.step = step;
+  a.log_weights = nullptr;
+  a.out_tokens = out_tokens;
+  a.out_logp = out_logq;
+  a.status = status;
+  a.ws = static_cast<char *>(workspace);
+  a.stream = as_stream(stream);
+  a.bonus_tag = 5u | ((uint32_t)pos << 8);
   return hip_rc(launch_verify(a));
 }
 

@@ -67,6 +67,8 @@ struct VerifyArgs {
   int mode;
   uint64_t seed, step;
   const float *lse_in;
+  const float *logq_in;
+  uint32_t bonus_tag;  // RNG tag of the row-K draw: 1 (bonus token) or 5 | pos << 8 (draft)
   float *log_weights;
   int32_t *out_tokens, *out_num_tokens;
   float *out_logp, *out_logq, *out_lse;

@@ -65,13 +65,15 @@ __device__ __forceinline__ int slab_of(int64_t v, int64_t a0) {
   return v < a0 ? 0 : (int)min((int64_t)kSlabs - 1, (v - a0) / kSlabElems<DT>);
 }
 
-// Tiles: first the rows other than the bonus row in chunks of kBigGroups * chunk_elems,
-// then the bonus rows in chunks of chunk_elems (one unrolled step each).  Partials of row
-// (g, slot) start at part[(g * R + slot) * chunks].
+// Tiles: first the rows other than the bonus row (nb_per_seq per sequence: the K target
+// rows, then the K draft rows unless the draft's log q is given) in chunks of
+// kBigGroups * chunk_elems, then the bonus rows in chunks of chunk_elems (one unrolled
+// step each).  Partials of row (g, slot) start at part[(g * R + slot) * chunks].
 template <int DT>
 __global__ __launch_bounds__(kStreamBlock) void k_lse_partials(RowMap rm, int nseq, int V,
                                                                 int chunk_elems, int chunks,
-                                                                int chunks_big, float c,
+                                                                int chunks_big, int nb_per_seq,
+                                                                float c,
                                                                 float2 *__restrict__ part,
                                                                 float *__restrict__ sub,
                                                                 int64_t ntiles) {
@@ -96,11 +98,12 @@ __global__ __launch_bounds__(kStreamBlock) void k_lse_partials(RowMap rm, int ns
       slot = K;
       ce = chunk_elems;
     } else {
+      // nb_per_seq = 2K (target rows 0..K-1, then draft rows) or K (target rows only)
       const int64_t u = t;
       const int64_t r = u / chunks_big;
       ch = (int)(u - r * chunks_big);
-      g = (int)(r / (2 * K));
-      const int j = (int)(r - (int64_t)g * 2 * K);
+      g = (int)(r / nb_per_seq);
+      const int j = (int)(r - (int64_t)g * nb_per_seq);
       slot = j < K ? j : j + 1;
       ce = (int64_t)chunk_elems * kBigGroups;
     }
@@ -389,8 +392,8 @@ static_assert(kSlabElems<SMCSD_DTYPE_BF16> + 16 <= 8 * kSmcFinalBlock * kSmcUnit
 template <int DT>
 __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
     RowMap rm, const int32_t *__restrict__ draft_tokens, int V, int chunk_elems, int chunks,
-    int chunks_big, float c, float alpha, uint64_t seed, uint64_t step,
-    const float2 *__restrict__ part,
+    int chunks_big, float c, float alpha, uint64_t seed, uint64_t step, uint32_t bonus_tag,
+    const float2 *__restrict__ part, const float *__restrict__ logq_in,
     const float *__restrict__ sub, float *__restrict__ lw, int32_t *__restrict__ out_tokens,
     int32_t *__restrict__ out_num,
     float *__restrict__ out_logp, float *__restrict__ out_logq, float *__restrict__ out_lse,
@@ -412,7 +415,7 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
   __shared__ float sPickLogit;
   __shared__ int sFlags;
   if (tid == 0) sFlags = 0;
-  const float lw_old = tid == 0 ? lw[g] : 0.0f;  // loaded early: used only at the end
+  const float lw_old = tid == 0 && lw ? lw[g] : 0.0f;  // loaded early: used only at the end
 
   // One round of loads up front: the draft tokens, this sequence's chunk pairs (staged
   // in LDS), then the draft-token logits.
@@ -420,10 +423,12 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
   int32_t x = 0;
   float xv = 0.0f;
   int slot = 0;
+  float lq_given = 0.0f;
   if (tid < 2 * K) {
     const int k = tid < K ? tid : tid - K;
     slot = tid < K ? k : K + 1 + k;
     x = draft_tokens[src * K + k];
+    if (logq_in && tid >= K) lq_given = logq_in[src * K + k];
   }
   const int npart = R * chunks;
   const bool part_in_lds = npart <= kMaxPartLds;
@@ -435,11 +440,12 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
   const float *gsub = sub + (int64_t)g * nsub;
   if (sub_in_lds)
     for (int i = tid; i < nsub; i += kSmcFinalBlock) sSub[i] = gsub[i];
-  if (tid < 2 * K && x >= 0 && x < V) xv = E::load(rm.row(g, slot), x);
+  if (tid < (logq_in ? K : 2 * K) && x >= 0 && x < V) xv = E::load(rm.row(g, slot), x);
   __syncthreads();
 
-  // row normalisers: chunk pairs combined in fp64 (row K also keeps its chunk terms)
-  if (tid < R) {
+  // row normalisers: chunk pairs combined in fp64 (row K also keeps its chunk terms);
+  // the draft rows only when their log q is not given
+  if (tid < (logq_in ? K + 1 : R)) {
     const float2 *p = (part_in_lds ? sPart : gpart) + tid * chunks;
     const int n = tid == K ? chunks : chunks_big;
     float M = kNegInf;
@@ -465,6 +471,7 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
     const int k = tid < K ? tid : tid - K;
     double lp = __builtin_nan("");
     if (x < 0 || x >= V) atomicOr(&sFlags, SMCSD_ST_BAD_INPUT);
+    else if (logq_in && tid >= K) lp = (double)lq_given;
     else lp = ((double)xv * (double)c - sL2[slot]) * kLn2;
     if (tid < K) {
       sLogp[k] = lp;
@@ -477,7 +484,7 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
   // Bonus: u = U(seed; g, step, BONUS); first v whose running sum of 2^(x*c - Mc_K)
   // exceeds u * S_K (the unnormalised CDF; the common factor 2^Mc_K cancels).
   const double SK = sS[K];
-  const double u = philox_uniform(seed, (uint32_t)g, step, 1u, 0);
+  const double u = philox_uniform(seed, (uint32_t)g, step, bonus_tag, 0);
   const double target = u * SK;
   const char *brow = rm.row(g, K);
   int bonus = -1;
@@ -548,12 +555,13 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
     if (out_logp) out_logp[(int64_t)g * (K + 1) + tid] = (float)sLogp[tid];
     if (out_logq) out_logq[(int64_t)g * K + tid] = (float)sLogq[tid];
   }
-  if (out_lse && tid < R) out_lse[(int64_t)g * R + tid] = (float)(sL2[tid] * kLn2);
+  if (out_lse && tid < R)
+    out_lse[(int64_t)g * R + tid] = logq_in && tid > K ? __builtin_nanf("") : (float)(sL2[tid] * kLn2);
   if (tid == 0) {
     double incr = 0.0;
     for (int k = 0; k < K; ++k) incr += (double)alpha * sLogp[k] - sLogq[k];
     incr += ((double)alpha - 1.0) * lpK;
-    lw[g] = (float)((double)lw_old + incr);
+    if (lw) lw[g] = (float)((double)lw_old + incr);
     tok[K] = bonus;
     if (out_num) out_num[g] = K + 1;
     if (out_logp) out_logp[(int64_t)g * (K + 1) + K] = (float)lpK;
@@ -803,15 +811,16 @@ static hipError_t launch_verify_t(const VerifyArgs &a) {
   float2 *part = reinterpret_cast<float2 *>(a.ws + w.part);
   float *sub = reinterpret_cast<float *>(a.ws + w.sub);
   const int chunks_big = (int)ceil_div(a.V, (int64_t)ce * kBigGroups);
-  const int64_t ntiles = (int64_t)a.nseq * (chunks + 2 * K * (int64_t)chunks_big);
+  const int nb_per_seq = a.logq_in ? K : 2 * K;
+  const int64_t ntiles = (int64_t)a.nseq * (chunks + (int64_t)nb_per_seq * chunks_big);
   const unsigned grid = (unsigned)std::min<int64_t>(ntiles, (int64_t)1 << 30);
 
   if (a.mode == SMCSD_MODE_SMC) {
     hipLaunchKernelGGL(k_lse_partials<DT>, dim3(grid), dim3(kStreamBlock), 0, a.stream, rm, a.nseq,
-                       a.V, ce, chunks, chunks_big, a.c, part, sub, ntiles);
+                       a.V, ce, chunks, chunks_big, nb_per_seq, a.c, part, sub, ntiles);
     hipLaunchKernelGGL(k_smc_finalize<DT>, dim3(a.nseq), dim3(kSmcFinalBlock), 0, a.stream, rm,
                        a.draft_tokens, a.V, ce, chunks, chunks_big, a.c, a.alpha, a.seed, a.step,
-                       part, sub,
+                       a.bonus_tag, part, a.logq_in, sub,
                        a.log_weights, a.out_tokens, a.out_num_tokens, a.out_logp, a.out_logq,
                        a.out_lse, a.status);
     return hipGetLastError();
@@ -821,7 +830,7 @@ static hipError_t launch_verify_t(const VerifyArgs &a) {
   float2 *part2 = reinterpret_cast<float2 *>(a.ws + w.part2);
   if (!a.lse_in)
     hipLaunchKernelGGL(k_lse_partials<DT>, dim3(grid), dim3(kStreamBlock), 0, a.stream, rm, a.nseq,
-                       a.V, ce, chunks, chunks_big, a.c, part, sub, ntiles);
+                       a.V, ce, chunks, chunks_big, nb_per_seq, a.c, part, sub, ntiles);
   hipLaunchKernelGGL(k_sps_decide<DT>, dim3(a.nseq), dim3(kWave), 0, a.stream, rm, a.draft_tokens,
                      a.V, chunks, chunks_big, a.c, a.seed, a.step, part, a.lse_in, kstar, norm,
                      a.out_tokens,

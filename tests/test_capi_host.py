@@ -45,7 +45,7 @@ def test_gfx950_code_object_present(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.smcsd_version() == 1
+    assert lib.smcsd_version() == 2
     assert sm.status_string(0) == "ok"
     assert "workspace" in sm.status_string(-4)
     assert "pool" in sm.status_string(sm.ST_NOSPACE)
@@ -58,18 +58,19 @@ def test_workspace_sizes(lib):
     assert sm.workspace_bytes(sm.OP_KV, 32, 16, 0, 0, 145920) >= 145920 // 8
     assert sm.workspace_bytes(sm.OP_VERIFY_SMC, 1, 1, 33, 10) == 0   # K above the limit
     assert sm.workspace_bytes(sm.OP_KV, 1, 1, 0, 0, 0) == 0
+    assert sm.workspace_bytes(sm.OP_DRAFT, 512, 1, 0, 128256) >= 512 * 16 * 8
 
 
 def _verify_rc(lib, **kw):
     a = dict(tgt=ctypes.c_void_p(0x1000), drf=ctypes.c_void_p(0x1000), dtype=1, rs=64, step=1,
              tok=ctypes.c_void_p(0x1000), B=1, N=1, K=1, V=64, T=1.0, alpha=1.0, mode=0, lse=None,
              lw=ctypes.c_void_p(0x1000), out=ctypes.c_void_p(0x1000), st=ctypes.c_void_p(0x1000),
-             ws=ctypes.c_void_p(0x1000), wsb=1 << 20)
+             ws=ctypes.c_void_p(0x1000), wsb=1 << 20, logq=None)
     a.update(kw)
     return lib.smcsd_verify(a["tgt"], a["drf"], a["dtype"], a["rs"], a["step"], a["tok"], a["B"],
                             a["N"], a["K"], a["V"], a["T"], a["alpha"], a["mode"], 0, 0, a["lse"],
-                            a["lw"], a["out"], None, None, None, None, a["st"], a["ws"], a["wsb"],
-                            None)
+                            a["logq"], a["lw"], a["out"], None, None, None, None, a["st"], a["ws"],
+                            a["wsb"], None)
 
 
 def test_verify_host_validation(lib):
@@ -87,6 +88,31 @@ def test_verify_host_validation(lib):
     assert _verify_rc(lib, ws=ctypes.c_void_p(0x1010)) == -4    # workspace not 256-byte aligned
     assert _verify_rc(lib, mode=3) == -1
     assert _verify_rc(lib, B=0) == 0                            # empty batch: nothing enqueued
+    p = ctypes.c_void_p(0x1000)
+    assert _verify_rc(lib, mode=1, logq=p) == -1                # the draft's log q: SMC mode only
+    assert _verify_rc(lib, drf=None, logq=p, B=0) == 0          # draft rows not needed with it
+
+
+def test_draft_sample_host_validation(lib):
+    p = ctypes.c_void_p(0x1000)
+
+    def rc(**kw):
+        a = dict(d=p, dtype=1, rs=64, n=4, V=64, T=1.0, pos=0, out=p, lq=p, st=p, ws=p,
+                 wsb=1 << 20)
+        a.update(kw)
+        return lib.smcsd_draft_sample(a["d"], a["dtype"], a["rs"], a["n"], a["V"], a["T"], 0, 0,
+                                      a["pos"], a["out"], a["lq"], a["st"], a["ws"], a["wsb"],
+                                      None)
+    assert rc(dtype=5) == -2
+    assert rc(V=0) == -1
+    assert rc(rs=10) == -1
+    assert rc(T=0.0) == -1
+    assert rc(pos=-1) == -1 and rc(pos=1 << 24) == -1
+    assert rc(d=None) == -1
+    assert rc(out=None) == -1
+    assert rc(wsb=8) == -4
+    assert rc(ws=ctypes.c_void_p(0x1010)) == -4
+    assert rc(n=0) == 0
 
 
 def test_resample_and_kv_host_validation(lib):
