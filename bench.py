@@ -35,14 +35,14 @@ EVENT_EVERY = 8
 # only for the kernel sources they were taken on: any change to them reports null.
 VERIFY_TRAFFIC = {
     "workload": "c3_batched",
-    "bytes": 1186198117,
+    "bytes": 1186194364,
     "sources": {
         "smc_verification_resampling_amd/csrc/verify.hip":
-            "26ab14ac3d0715f61ab74c81e5e78be038101425846004e026e2e8f779cdd988",
+            "3add99d70b2a46559019b2d4e6edb57c8286a6d888bfcaa85fac691a931dd50b",
         "smc_verification_resampling_amd/csrc/device.hpp":
             "5f1a401af612b80cc49dc04b7dad254ea96512e328607395f475dfb4e5a87d97",
         "smc_verification_resampling_amd/csrc/internal.hpp":
-            "b56b9debf43193fcffdf9819832cd74f12875a069f74ba74c23b033bdbf708d8",
+            "03e0ad22e11f6b98eef10d8bdeb8daba2f6d6d27f4f867e813af03e7e469eb79",
     },
 }
 
