@@ -33,6 +33,10 @@ TAG_BONUS = 1
 TAG_RESAMPLE = 2
 TAG_SPS_ACCEPT = 3
 TAG_SPS_FINAL = 4
+TAG_DRAFT = 5
+TAG_RACE = 6
+
+BONUS_RULES = {"cdf": 0, "race": 1}
 
 _lock = threading.Lock()
 _lib = None
@@ -60,7 +64,8 @@ def configure(lib):
     lib.orc_row_lse.argtypes = [P, ctypes.c_int, i64, dbl, P]
     lib.orc_row_lse.restype = dbl
     lib.orc_verify_smc.argtypes = [P, P, ctypes.c_int, i64, ctypes.c_int, P, ctypes.c_int, P,
-                                   dbl, dbl, u64, u64, P, P, P, P, P, P, P, P, P, P]
+                                   dbl, dbl, u64, u64, P, P, ctypes.c_int, P, P, P, P, P, P, P,
+                                   P]
     lib.orc_verify_smc.restype = ctypes.c_int
     lib.orc_verify_sps.argtypes = [P, P, ctypes.c_int, i64, ctypes.c_int, P, ctypes.c_int, P,
                                    dbl, u64, u64, P, P, P, P, P, P, P, P]
@@ -68,6 +73,10 @@ def configure(lib):
     lib.orc_draft_sample.argtypes = [P, ctypes.c_int, i64, ctypes.c_int, P, ctypes.c_int, dbl,
                                      u64, u64, P, P, P, P]
     lib.orc_draft_sample.restype = ctypes.c_int
+    lib.orc_race_clock.argtypes = [u64, ctypes.c_uint32, u64, i64]
+    lib.orc_race_clock.restype = dbl
+    lib.orc_race_sample.argtypes = [P, ctypes.c_int, i64, ctypes.c_int, P, dbl, u64, u64, P, P]
+    lib.orc_race_sample.restype = ctypes.c_int
     lib.orc_resample.argtypes = [P, ctypes.c_int, ctypes.c_int, dbl, u64, u64,
                                  P, P, P, P, P, P, P]
     lib.orc_resample.restype = ctypes.c_int
@@ -139,10 +148,11 @@ def row_lse(row: np.ndarray, T: float = 1.0):
 def verify_smc(target: np.ndarray, draft: Optional[np.ndarray], draft_tokens: np.ndarray,
                T: float, alpha: float, seed: int, t: int, lw_in: np.ndarray,
                rng_index: Optional[np.ndarray] = None,
-               logq_in: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+               logq_in: Optional[np.ndarray] = None, bonus: str = "cdf") -> Dict[str, np.ndarray]:
     """SMC verify for nseq sequences.  target [nseq, K+1, V], draft [nseq, K, V]; with
     logq_in [nseq, K] (the draft's log-probabilities of its tokens) the draft rows are not
-    read and draft may be None."""
+    read and draft may be None.  bonus: "cdf" (inverse CDF) or "race" (exponential race);
+    with "race", margin is the gap between the two largest race keys."""
     tg, code = _logit_array(target)
     nseq, K1, V = tg.shape
     K = K1 - 1
@@ -168,7 +178,8 @@ def verify_smc(target: np.ndarray, draft: Optional[np.ndarray], draft_tokens: np
     }
     logq_buf = np.zeros((nseq, max(K, 1)), np.float64)
     _load().orc_verify_smc(_p(tg), _p(dr), code, V, nseq, _p(idx), K, _p(tok), T, alpha, seed, t,
-                           _p(lw), None if lq_in is None else _p(lq_in), _p(out["lw"]),
+                           _p(lw), None if lq_in is None else _p(lq_in), BONUS_RULES[bonus],
+                           _p(out["lw"]),
                            _p(out["tokens"]), _p(out["logp"]),
                            _p(logq_buf), _p(out["lse"]), _p(out["u"]), _p(out["margin"]),
                            _p(out["status"]))
@@ -190,6 +201,25 @@ def draft_sample(rows: np.ndarray, T: float, seed: int, t: int, pos: int,
     _load().orc_draft_sample(_p(rw), code, V, n, _p(idx), pos, T, seed, t, _p(out["tokens"]),
                              _p(out["logq"]), _p(out["margin"]), _p(out["status"]))
     out["status"] = int(out["status"][0])
+    return out
+
+
+def race_clock(seed: int, index: int, t: int, v: int) -> float:
+    """E_v = -ln u_v, the exponential clock of token v in stream (seed; index, t)."""
+    return float(_load().orc_race_clock(seed, index, t, v))
+
+
+def race_sample(rows: np.ndarray, T: float, seed: int, t: int,
+                rng_index: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Exponential-race draw, one token per row from softmax(rows / T).  rows [n, V];
+    margin = gap between the two largest keys z_v - ln E_v."""
+    rw, code = _logit_array(rows)
+    n, V = rw.shape
+    idx = np.arange(n, dtype=np.int64) if rng_index is None else \
+        np.ascontiguousarray(rng_index, dtype=np.int64)
+    out = {"tokens": np.zeros(n, np.int32), "margin": np.zeros(n, np.float64)}
+    _load().orc_race_sample(_p(rw), code, V, n, _p(idx), T, seed, t, _p(out["tokens"]),
+                            _p(out["margin"]))
     return out
 
 

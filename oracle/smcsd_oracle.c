@@ -19,6 +19,9 @@
  *          loop) and section 4.2 Modified Rejection Sampling.
  *   [Philox] Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as
  *          1, 2, 3", SC'11 - the Philox4x32 bijection with 10 rounds.
+ *   [ERSD] "Speculative Sampling via Exponential Races" (paper summary page):
+ *          key design, the exponential race - only the race as a sampling rule is
+ *          used here (the one-pass bonus variant), not ERSD's verify.
  *
  * The pages leave several steps open (the weight formula beyond "target/draft
  * ratio", the ESS formula, the resampling scheme, the RNG, the block-table rules).
@@ -48,6 +51,11 @@
 #define ORC_TAG_SPS_ACCEPT 3u
 #define ORC_TAG_SPS_FINAL 4u
 #define ORC_TAG_DRAFT 5u
+#define ORC_TAG_RACE 6u
+
+/* bonus-token rules of the SMC verify */
+#define ORC_BONUS_CDF 0
+#define ORC_BONUS_RACE 1
 
 int orc_version(void) { return 1; }
 
@@ -190,11 +198,71 @@ static int32_t inverse_cdf_row(const void *row, int dtype, int64_t V, double T, 
 }
 
 /* ------------------------------------------------------------------------- */
+/* [ERSD] key design: an exponential race.  Every token v starts an independent */
+/* exponential clock of rate p_v; the first to finish, argmin_v E_v / p_v with    */
+/* E_v ~ Exp(1), is a draw from p (the minimum of independent exponentials is     */
+/* attained at v with probability p_v / sum_w p_w).  With p_v proportional to    */
+/* exp(z_v) the rule reads argmax_v (z_v - ln E_v): no normaliser is needed, so   */
+/* one pass over the row decides it.                                              */
+/* The clock of token v (a reading; the pages fix no generator): word v mod 4 of  */
+/* the Philox block with counter (index, t low, t high, RACE | (v div 4) << 8);   */
+/* u_v = (floor(w / 2^9) + 1/2) * 2^-23, strictly inside (0, 1) and exact in fp32; */
+/* E_v = -ln u_v.                                                                 */
+/* ------------------------------------------------------------------------- */
+double orc_race_clock(uint64_t seed, uint32_t index, uint64_t t, int64_t v)
+{
+    uint32_t ctr[4] = {index, (uint32_t)t, (uint32_t)(t >> 32),
+                       ORC_TAG_RACE | ((uint32_t)(v >> 2) << 8)};
+    uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t out[4];
+    orc_philox4x32_10(ctr, key, out);
+    double u = ((double)(out[v & 3] >> 9) + 0.5) / 8388608.0;
+    return -log(u);
+}
+
+/* The race over one row: the token with the largest z_v - ln E_v among the finite
+ * z_v (a -inf logit never finishes; NaN is reported by the row's LSE).  Equal keys
+ * go to the smaller id.  *margin receives the gap between the two largest keys
+ * (+inf with a single finite logit); -1 if no logit is finite. */
+static int32_t race_row(const void *row, int dtype, int64_t V, double T, uint64_t seed,
+                        uint32_t index, uint64_t t, double *margin)
+{
+    double best = -INFINITY, second = -INFINITY;
+    int32_t arg = -1;
+    for (int64_t v = 0; v < V; ++v) {
+        double z = load_elem(row, dtype, v) / T;
+        if (!(z > -INFINITY) || isnan(z)) continue;
+        double key = z - log(orc_race_clock(seed, index, t, v));
+        if (key > best) {
+            second = best;
+            best = key;
+            arg = (int32_t)v;
+        } else if (key > second) {
+            second = key;
+        }
+    }
+    *margin = arg < 0 ? 0.0 : best - second;
+    return arg;
+}
+
+/* The race for nrows rows (rows [nrows, V]); rng_index[r] is row r's stream. */
+int orc_race_sample(const void *rows, int dtype, int64_t V, int nrows, const int64_t *rng_index,
+                    double T, uint64_t seed, uint64_t t, int32_t *tokens, double *margin)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < nrows; ++r)
+        tokens[r] = race_row(row_ptr(rows, dtype, r, V), dtype, V, T, seed,
+                             (uint32_t)rng_index[r], t, &margin[r]);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
 /* [SMC] One verify round for nseq sequences (SMC mode).                       */
 /*   Score:    LSE of the K+1 target rows and the K draft rows (tempered).       */
 /*   Gather:   logp_k = z^t_k[x_k] - LSE^t_k,  logq_k = z^d_k[x_k] - LSE^d_k.    */
 /*   Bonus:    one extra token per sequence from the target row K by inverse    */
-/*             CDF with u = U(seed; g, t, BONUS); logp_K = its log-probability.  */
+/*             CDF with u = U(seed; g, t, BONUS) (bonus_rule CDF), or by the      */
+/*             exponential race above (bonus_rule RACE); logp_K = its log-prob.   */
 /*   Reweight: lw += sum_{k<K} (alpha*logp_k - logq_k) + (alpha-1)*logp_K.       */
 /*             alpha = 1 gives the plain target/draft ratio; the bonus is drawn  */
 /*             from the target, so it contributes (alpha-1)*logp_K (power mode). */
@@ -206,7 +274,8 @@ static int32_t inverse_cdf_row(const void *row, int dtype, int64_t V, double T, 
 int orc_verify_smc(const void *tgt, const void *drf, int dtype, int64_t V, int nseq,
                    const int64_t *rng_index, int K, const int32_t *draft_tokens, double T,
                    double alpha, uint64_t seed, uint64_t t, const double *lw_in,
-                   const double *logq_in, double *lw_out, int32_t *tokens, double *logp,
+                   const double *logq_in, int bonus_rule, double *lw_out, int32_t *tokens,
+                   double *logp,
                    double *logq, double *lse, double *bonus_u, double *margin, int32_t *status)
 {
     const int R = 2 * K + 1;
@@ -253,7 +322,10 @@ int orc_verify_smc(const void *tgt, const void *drf, int dtype, int64_t V, int n
         int32_t bonus = -1;
         double lpK = NAN;
         if (isfinite(L[K])) {
-            bonus = inverse_cdf_row(brow, dtype, V, T, L[K], u, &m);
+            if (bonus_rule == ORC_BONUS_RACE)
+                bonus = race_row(brow, dtype, V, T, seed, (uint32_t)rng_index[s], t, &m);
+            else
+                bonus = inverse_cdf_row(brow, dtype, V, T, L[K], u, &m);
             lpK = load_elem(brow, dtype, bonus) / T - L[K];
         }
         tokens[(int64_t)s * (K + 1) + K] = bonus;

@@ -18,6 +18,7 @@ import oracle
 from tests import test_oracle_draft as dr
 from tests import test_oracle_kv as kv
 from tests import test_oracle_laws as laws
+from tests import test_oracle_race as race
 from tests import test_oracle_resample as rs
 from tests import test_oracle_rng as rng_t
 from tests import test_oracle_verify as vf
@@ -122,6 +123,16 @@ CASES = [
     ("draft log q of the wrong token", "logq[r] = x >= 0 ? load_elem(row, dtype, x) / T - L : NAN;",
      "logq[r] = x >= 0 ? load_elem(row, dtype, x > 0 ? x - 1 : x) / T - L : NAN;",
      [lambda: dr.test_draft_sample_is_the_textbook_inverse_cdf(O, "f32", 1.0)]),
+    ("race key adds the log clock", "double key = z - log(orc_race_clock(", "double key = z + log(orc_race_clock(",
+     [lambda: race.test_race_law_chi_square(O, 1.0)]),
+    ("race key without the temperature", "double key = z - log(orc_race_clock(",
+     "double key = z * T - log(orc_race_clock(", [lambda: race.test_race_law_chi_square(O, 0.7)]),
+    ("race clocks share one Philox word", "(double)(out[v & 3] >> 9)", "(double)(out[0] >> 9)",
+     [lambda: race.test_race_clocks_are_exponential_and_uncorrelated(O)]),
+    ("race clocks repeat every block", "ORC_TAG_RACE | ((uint32_t)(v >> 2) << 8)", "ORC_TAG_RACE",
+     [lambda: race.test_race_clocks_are_exponential_and_uncorrelated(O)]),
+    ("verify ignores the race rule", "if (bonus_rule == ORC_BONUS_RACE)", "if (0)",
+     [lambda: race.test_verify_race_bonus_is_the_race_and_reweights(O, 1.0)]),
     ("verify reads the wrong precomputed log q", "logq_in[(int64_t)s * K + k]", "logq_in[(int64_t)s * K]",
      [lambda: dr.test_verify_with_draft_logq_equals_reading_the_draft_rows(O)]),
 ]
