@@ -75,6 +75,9 @@ def _parse():
     ap.add_argument("--draft-logq", action="store_true",
                     help="draft tokens and their log q from smcsd_draft_sample (untimed, part of "
                          "the Extend step); the timed verify takes them and skips the draft rows")
+    ap.add_argument("--race-bonus", action="store_true",
+                    help="SMCSD_MODE_SMC_RACE: the bonus token by an exponential race inside the "
+                         "LSE pass instead of the inverse CDF with its one-slab re-read")
     ap.add_argument("--probe-mib", type=int, default=1024,
                     help="size of the reference copy / read kernels (0 = skip)")
     return ap.parse_args()
@@ -106,6 +109,8 @@ def main():
         t, d = synth.make_logit_set(cfg, s, dev, base)
         sets.append((t, d, synth.sample_draft_tokens(cfg, d, s), None))
     draft_info = None
+    mode = sm.MODE_SMC_RACE if args.race_bonus else sm.MODE_SMC
+    variant = ("+draft_logq" if args.draft_logq else "") + ("+race_bonus" if args.race_bonus else "")
     if args.draft_logq:
         sets, draft_info = draft_side(cfg, sets)
 
@@ -154,7 +159,7 @@ def main():
         if ev is not None:
             ev[0].record()
         sm.verify(tgt, None if lq_in is not None else drf, toks, B, N, K, V, cfg.temperature,
-                  cfg.alpha, sm.MODE_SMC, seed, t, tokens, status, ws_v, log_weights=lw,
+                  cfg.alpha, mode, seed, t, tokens, status, ws_v, log_weights=lw,
                   out_num_tokens=num, out_logp=logp, out_logq=logq, logq_in=lq_in)
         if ev is not None:
             ev[1].record()
@@ -214,7 +219,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, sets, args.cpu_seconds)
+        cpu = cpu_baseline(cfg, sets, args.cpu_seconds, "race" if args.race_bonus else "cdf")
 
     out = {
         "metric": "SMC verify+resample steps/s; HBM GB/s % of peak (V=128256,N=16,K=4,B=32)",
@@ -232,11 +237,12 @@ def main():
         "config": {
             "workload": "%s%s: B=%d prompts x N=%d particles, K=%d, V=%d, %s logits (%s), T=%g, "
                         "alpha=%g, tau=%g, ctx %d in %d-token blocks%s" % (
-                            cfg.name, "+draft_logq" if args.draft_logq else "", B, N, K, V,
+                            cfg.name, variant, B, N, K, V,
                             cfg.dtype, cfg.target_kind, cfg.temperature, cfg.alpha, cfg.tau,
                             cfg.ctx0, cfg.block_size, ", shared prefix" if cfg.shared_prefix else ""),
-            "step": "smcsd_verify%s + smcsd_resample + smcsd_kv_reassign" % (
-                " (logq_in: target rows only)" if args.draft_logq else ""),
+            "step": "smcsd_verify%s%s + smcsd_resample + smcsd_kv_reassign" % (
+                " (logq_in: target rows only)" if args.draft_logq else "",
+                " (race-mode bonus)" if args.race_bonus else ""),
             "draft_sample": draft_info,
             "logit_sets": cfg.n_sets,
             "algorithmic_bytes_per_step": bytes_per_verify,
@@ -256,7 +262,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-            "traffic": verify_traffic(cfg.name + ("+draft_logq" if args.draft_logq else "")),
+            "traffic": verify_traffic(cfg.name + variant),
             "avg_launch_us": round(verify_avg_s * 1e6, 2),
             "launches_timed": len(verify_ms),
         },
@@ -376,7 +382,7 @@ def reference_kernels(mib):
             "read_sum_GBps": round(n / sum_s / 1e9, 1)}
 
 
-def cpu_baseline(cfg, sets, budget_s):
+def cpu_baseline(cfg, sets, budget_s, bonus="cdf"):
     """The oracle as it stands, on a bounded sample: verify on a subset of sequences (scaled
     to the full batch), resample and KV exchange on the whole batch."""
     import numpy as np
@@ -413,7 +419,7 @@ def cpu_baseline(cfg, sets, budget_s):
         while reps < 2 or time.perf_counter() - t_start < seconds:
             a = time.perf_counter()
             v = oracle.verify_smc(th, dh, xh, float(np.float32(cfg.temperature)), cfg.alpha,
-                                  cfg.rng_seed, reps, lw)
+                                  cfg.rng_seed, reps, lw, bonus=bonus)
             b = time.perf_counter()
             lwfull = rng.normal(0, 2, (B, N)).astype(np.float32)
             r = oracle.resample(lwfull, float(np.float32(cfg.tau)), cfg.rng_seed, reps)
@@ -439,8 +445,9 @@ def cpu_baseline(cfg, sets, budget_s):
         "unit": "steps/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": "%d reps: verify on %d of %d sequences (scaled x%d), resample + KV exchange on "
-                  "all %d prompts; fp64 C, OpenMP over rows" % (reps, nsamp, S, S // nsamp, B),
+        "sample": "%d reps: verify (%s bonus) on %d of %d sequences (scaled x%d), resample + KV "
+                  "exchange on all %d prompts; fp64 C, OpenMP over rows" % (
+                      reps, bonus, nsamp, S, S // nsamp, B),
         "single_thread_value": round(1.0 / per_step1, 4),
         "single_thread_reps": reps1,
     }

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SMCSD_VERSION 2
+#define SMCSD_VERSION 3
 
 /* logits element type */
 #define SMCSD_DTYPE_F32 0
@@ -56,6 +56,7 @@ extern "C" {
 /* verify mode */
 #define SMCSD_MODE_SMC 0
 #define SMCSD_MODE_SPS 1
+#define SMCSD_MODE_SMC_RACE 2 /* SMC mode, bonus token by an exponential race */
 
 /* host return codes */
 #define SMCSD_OK 0
@@ -129,8 +130,16 @@ size_t smcsd_workspace_bytes(int op, int B, int N, int K, int V, int64_t P);
  * out_tokens[g] = accepted drafts then the drawn token, padded with -1;
  * out_num_tokens[g] = k*+1 (K+1 if all accepted); out_logp[g][K] = target
  * log-probability of the drawn token at its position; log_weights is not touched.
+ * SMC race mode: SMC mode with the bonus drawn by an exponential race (the
+ * exponential-races summary page, key design: token v finishes at E_v / p_v with
+ * E_v ~ Exp(1), and the first to finish is a draw from p):
+ *   bonus = argmax_v (z^t_K[v] - ln E_v),  E_v = -ln u_v,
+ *   u_v = (floor(w / 2^9) + 1/2) * 2^-23,  w = word (v mod 4) of the Philox block with
+ *   counter (g, step low, step high, 6 | (v div 4) << 8) and key (seed low, seed high);
+ * equal keys go to the smaller v.  The keys are evaluated in fp32 during the LSE pass,
+ * so the bonus row is read once; everything else is as in SMC mode.
  * If lse_in is given (SpS mode only) the LSE pass is skipped and lse_in is used.
- * If logq_in is given (SMC mode only) [src, K] fp32 - the draft's log-probabilities of
+ * If logq_in is given (SMC or SMC race mode) [src, K] fp32 - the draft's log-probabilities of
  * its own tokens, as smcsd_draft_sample emits them while drafting - the draft rows are
  * not read at all (draft_logits may be NULL): logq_k = logq_in[src][k], and the LSE
  * pass covers only the K+1 target rows (out_lse's draft entries are NaN).  The bytes
@@ -139,9 +148,10 @@ size_t smcsd_workspace_bytes(int op, int B, int N, int K, int V, int64_t P);
  * Outputs (indexed by g): out_tokens [B*N, K+1] int32 (required); out_num_tokens
  * [B*N], out_logp [B*N, K+1], out_logq [B*N, K], out_lse [B*N, 2K+1] (target rows
  * 0..K then draft rows 0..K-1), all nullable.  log_weights [B*N] fp32 in/out
- * (required in SMC mode).
+ * (required in the SMC modes).
  * Limits: 0 <= K <= 32, 1 <= V <= 2^24, temperature finite > 0, alpha finite.
- * B*N = 0 is a no-op.  workspace: smcsd_workspace_bytes(SMCSD_OP_VERIFY_*, ...).
+ * B*N = 0 is a no-op.  workspace: smcsd_workspace_bytes(SMCSD_OP_VERIFY_SMC, ...) for
+ * the SMC modes, SMCSD_OP_VERIFY_SPS for SpS.
  */
 int smcsd_verify(const void *target_logits, const void *draft_logits, int dtype,
                  int64_t row_stride, int seq_step, const int32_t *draft_tokens, int B, int N,

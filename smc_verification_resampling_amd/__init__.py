@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsmcsd.so")
 
 DTYPE_F32, DTYPE_BF16 = 0, 1
-MODE_SMC, MODE_SPS = 0, 1
+MODE_SMC, MODE_SPS, MODE_SMC_RACE = 0, 1, 2  # MODE_SMC_RACE: SMC with the exponential-race bonus
 OP_VERIFY_SMC, OP_VERIFY_SPS, OP_KV, OP_DRAFT = 0, 1, 2, 3
 
 ST_NAN_INPUT = 1

@@ -64,7 +64,9 @@ int smcsd_verify(const void *target_logits, const void *draft_logits, int dtype,
                  float *out_lse, int32_t *status, void *workspace, size_t workspace_bytes,
                  void *stream) {
   if (dtype != SMCSD_DTYPE_F32 && dtype != SMCSD_DTYPE_BF16) return SMCSD_EDTYPE;
-  if (mode != SMCSD_MODE_SMC && mode != SMCSD_MODE_SPS) return SMCSD_EINVAL;
+  if (mode != SMCSD_MODE_SMC && mode != SMCSD_MODE_SPS && mode != SMCSD_MODE_SMC_RACE)
+    return SMCSD_EINVAL;
+  const bool smc = mode != SMCSD_MODE_SPS;
   if (B < 0 || N < 0 || K < 0 || K > kMaxK || V < 1 || V > kMaxV || seq_step < 1)
     return SMCSD_EINVAL;
   if (row_stride < V) return SMCSD_EINVAL;
@@ -75,11 +77,11 @@ int smcsd_verify(const void *target_logits, const void *draft_logits, int dtype,
   if (S > INT32_MAX / 2) return SMCSD_EINVAL;
   const size_t esz = dtype == SMCSD_DTYPE_BF16 ? 2 : 4;
   if (!target_logits || !aligned(target_logits, esz)) return SMCSD_EINVAL;
-  if (logq_in && mode != SMCSD_MODE_SMC) return SMCSD_EINVAL;
+  if (logq_in && !smc) return SMCSD_EINVAL;
   if (K > 0 && (!draft_tokens || (!logq_in && (!draft_logits || !aligned(draft_logits, esz)))))
     return SMCSD_EINVAL;
   if (!out_tokens || !status) return SMCSD_EINVAL;
-  if (mode == SMCSD_MODE_SMC && (!log_weights || lse_in)) return SMCSD_EINVAL;
+  if (smc && (!log_weights || lse_in)) return SMCSD_EINVAL;
   const size_t need = verify_ws_layout(S, K, V, mode == SMCSD_MODE_SPS ? 1 : 0).total;
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) return SMCSD_EWORKSPACE;
 

@@ -22,12 +22,15 @@ constexpr double kLog2e = 1.442695040888963407359924681001892137;
 // new counter is (hi(w2*M1) ^ w1 ^ k0, lo(w2*M1), hi(w0*M0) ^ w3 ^ k1, lo(w0*M0)).
 // The key advances by the two Weyl increments after every round.
 // ---------------------------------------------------------------------------------
+// Each 64-bit product is one v_mad_u64_u32 (both halves at once) instead of a mul_lo and
+// a mul_hi.
 __device__ __forceinline__ void philox_block(uint32_t c[4], uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint32_t w0 = c[0], w2 = c[2];
-    const uint32_t lo0 = w0 * 0xD2511F53u, hi0 = __umulhi(w0, 0xD2511F53u);
-    const uint32_t lo1 = w2 * 0xCD9E8D57u, hi1 = __umulhi(w2, 0xCD9E8D57u);
+    const uint64_t p0 = (uint64_t)c[0] * 0xD2511F53u;
+    const uint64_t p1 = (uint64_t)c[2] * 0xCD9E8D57u;
+    const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
+    const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
     c[0] = hi1 ^ c[1] ^ k0;
     c[1] = lo1;
     c[2] = hi0 ^ c[3] ^ k1;

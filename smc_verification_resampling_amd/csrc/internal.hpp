@@ -31,9 +31,10 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 constexpr int kSlabs = kStreamUnroll;
 
 // Verify workspace: [row partials float2 x nseq*(2K+1)*chunks][bonus slab sums float x nseq*chunks*kSlabs]
+//                   [bonus race winners int2 x nseq*chunks]
 //                   [kstar int32 x nseq][L2 pair double2 x nseq][residual partials float2 x nseq*chunks]
 struct VerifyWs {
-  size_t part, sub, kstar, l2, part2, total;
+  size_t part, sub, race, kstar, l2, part2, total;
 };
 inline VerifyWs verify_ws_layout(int64_t nseq, int K, int V, int mode) {
   VerifyWs w{};
@@ -43,6 +44,8 @@ inline VerifyWs verify_ws_layout(int64_t nseq, int K, int V, int mode) {
   off += align256(sizeof(float) * 2 * (size_t)(nseq * (2 * K + 1) * chunks));
   w.sub = off;
   off += align256(sizeof(float) * (size_t)(nseq * chunks * kSlabs));
+  w.race = off;
+  off += align256(sizeof(int32_t) * 2 * (size_t)(nseq * chunks));
   if (mode == 1) {
     w.kstar = off;
     off += align256(sizeof(int32_t) * (size_t)nseq);

@@ -17,6 +17,11 @@
 //                    token by inverse CDF (selects the chunk from the pairs and the slab
 //                    from the slab sums, re-reads only that slab) and updates the
 //                    log-weight.
+//   race mode        the bonus row's tiles also run an exponential race (exponential-races
+//                    summary page, key design) over their elements and keep the winner;
+//                    the finalize takes the best of the tiles' winners and reads only the
+//                    winner's logit: no slab sums and no re-read, for one Philox block per
+//                    four vocabulary entries and two logarithms per entry.
 //   k_sps_decide / k_sps_residual / k_sps_final
 //                    SpS: acceptance tests from the gathered log-probabilities, one pass
 //                    over the residual max(0, p - q) (or p_K) of the single row pair that is
@@ -49,6 +54,100 @@ __device__ __forceinline__ double chunk_term(float2 p, float c, float Mc) {
 }
 
 // ---------------------------------------------------------------------------------
+// Exponential race (bonus row in race mode)
+// ---------------------------------------------------------------------------------
+// Token v's clock: word v mod 4 of the Philox block with counter (g, step low, step high,
+// kTagRace | (v div 4) << 8); u_v = (floor(w / 2^9) + 1/2) * 2^-23 is exact in fp32 and
+// lies in (0, 1); E_v = -ln u_v.  The key x_v*c - log2(-log2 u_v) equals
+// log2(e) * (z_v - ln E_v) less a constant shared by every v, so the largest key is the
+// race's winner, argmin E_v / p_v.  Both logarithms see normal arguments only
+// (u_v >= 2^-24, -log2 u_v >= 2^-24 * log2(e)).  Equal keys go to the smaller id; a -inf
+// logit has key -inf and a NaN logit a NaN key, which never wins (the row's LSE reports
+// the NaN).
+constexpr uint32_t kTagRace = 6u;
+
+struct RaceBest {
+  float key;
+  int idx;
+};
+
+__device__ __forceinline__ RaceBest race_init() { return RaceBest{kNegInf, INT_MAX}; }
+
+// Merge of two candidates (largest key, then smallest id), branch-free.
+__device__ __forceinline__ void race_take(RaceBest &b, float key, int idx) {
+  const bool take = (key > b.key) | ((key == b.key) & (idx < b.idx));
+  b.key = take ? key : b.key;
+  b.idx = take ? idx : b.idx;
+}
+
+// A thread's own elements arrive in increasing id order: a strictly larger key wins and
+// an equal key keeps the earlier (smaller) id.
+__device__ __forceinline__ void race_next(RaceBest &b, float key, int idx) {
+  const bool take = key > b.key;
+  b.key = take ? key : b.key;
+  b.idx = take ? idx : b.idx;
+}
+
+__device__ __forceinline__ float race_key(float x, float c, uint32_t w) {
+  const float u = fmaf((float)(w >> 9), 0x1p-23f, 0x1p-24f);
+  const float e2 = -__builtin_amdgcn_logf(u);
+  return fmaf(x, c, -__builtin_amdgcn_logf(e2));
+}
+
+__device__ __forceinline__ void race_block(uint64_t seed, int g, uint64_t step, int v4,
+                                           uint32_t w[4]) {
+  w[0] = (uint32_t)g;
+  w[1] = (uint32_t)step;
+  w[2] = (uint32_t)(step >> 32);
+  w[3] = kTagRace | ((uint32_t)v4 << 8);
+  philox_block(w, (uint32_t)seed, (uint32_t)(seed >> 32));
+}
+
+// One element v on its own (head, tail, or a vector that does not start at a multiple of 4);
+// every call of a thread has a larger v than its previous calls
+__device__ __forceinline__ void race_one(RaceBest &b, float x, float c, uint64_t seed, int g,
+                                         uint64_t step, int v) {
+  uint32_t w[4];
+  race_block(seed, g, step, v >> 2, w);
+  const int j = v & 3;
+  const uint32_t wj = j == 0 ? w[0] : j == 1 ? w[1] : j == 2 ? w[2] : w[3];
+  race_next(b, race_key(x, c, wj), v);
+}
+
+// The elements of one 16-byte vector starting at v, a multiple of 4 (unpacked here from the
+// raw vector: the raw form is half the registers of the widened one for bf16)
+template <int DT>
+__device__ __forceinline__ void race_vec(RaceBest &b, const uint4 &raw, float c, uint64_t seed, int g,
+                                         uint64_t step, int v) {
+  constexpr int NV = Elt<DT>::kPerVec;
+  float x[NV];
+  Elt<DT>::unpack(raw, x);
+#pragma unroll
+  for (int q = 0; q < NV / 4; ++q) {
+    uint32_t w[4];
+    race_block(seed, g, step, (v >> 2) + q, w);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) race_next(b, race_key(x[4 * q + j], c, w[j]), v + 4 * q + j);
+  }
+}
+
+// Workgroup argmax of (key, -idx); the result is valid in thread 0.
+template <int BLOCK>
+__device__ __forceinline__ RaceBest race_block_reduce(RaceBest b, RaceBest *lds) {
+#pragma unroll
+  for (int mask = 1; mask < kWave; mask <<= 1)
+    race_take(b, __shfl_xor(b.key, mask, kWave), __shfl_xor(b.idx, mask, kWave));
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  if (lane == 0) lds[wave] = b;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int w = 1; w < BLOCK / kWave; ++w) race_take(b, lds[w].key, lds[w].idx);
+  }
+  return b;
+}
+
+// ---------------------------------------------------------------------------------
 // Streaming LSE pass
 // ---------------------------------------------------------------------------------
 // Elements of one slab: the kStreamBlock vectors a workgroup loads in one unrolled step.
@@ -69,17 +168,23 @@ __device__ __forceinline__ int slab_of(int64_t v, int64_t a0) {
 // rows, then the K draft rows unless the draft's log q is given) in chunks of
 // kBigGroups * chunk_elems, then the bonus rows in chunks of chunk_elems (one unrolled
 // step each).  Partials of row (g, slot) start at part[(g * R + slot) * chunks].
-template <int DT>
+// RACE: the bonus tiles write the winner of their race to race[g * chunks + ch] as
+// (key bits, id) instead of slab sums.
+template <int DT, bool RACE>
 __global__ __launch_bounds__(kStreamBlock) void k_lse_partials(RowMap rm, int nseq, int V,
                                                                 int chunk_elems, int chunks,
                                                                 int chunks_big, int nb_per_seq,
                                                                 float c,
                                                                 float2 *__restrict__ part,
                                                                 float *__restrict__ sub,
-                                                                int64_t ntiles) {
+                                                                int64_t ntiles, uint64_t seed,
+                                                                uint64_t step,
+                                                                int2 *__restrict__ race) {
   using E = Elt<DT>;
   constexpr int EPV = E::kPerVec;
   __shared__ Lse lds[kStreamBlock / kWave];
+  __shared__ RaceBest sRace[kStreamBlock / kWave];
+  __shared__ RaceBest sRaceT[RACE ? kStreamBlock : 1];
   __shared__ float sRed[(kStreamBlock / kWave) * (3 + kSlabs)];
   __shared__ float sSlabT[kStreamBlock][kSlabs + 1];  // per-thread slab sums (bonus tiles)
   const int K = rm.K;
@@ -88,18 +193,28 @@ __global__ __launch_bounds__(kStreamBlock) void k_lse_partials(RowMap rm, int ns
   const int64_t ntiles_big = ntiles - (int64_t)nseq * chunks;
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
     // the big tiles of the other rows first, the bonus rows' one-step tiles last: small
-    // tiles even out the kernel's tail
+    // tiles even out the kernel's tail.  In race mode the bonus tiles are ALU-heavy and are
+    // spread evenly among the big tiles instead, so their arithmetic overlaps the others'
+    // streaming: tile t is a bonus tile when floor(t * nB / ntiles) steps up at t.
+    int64_t tt = t;
+    bool isb = t >= ntiles_big;
+    if (RACE) {
+      const int64_t nB = ntiles - ntiles_big;
+      const int64_t kb = t * nB / ntiles, kb1 = (t + 1) * nB / ntiles;
+      isb = kb1 > kb;
+      tt = isb ? ntiles_big + kb : t - kb;
+    }
     int g, slot, ch;
     int64_t ce;
-    if (t >= ntiles_big) {
-      const int64_t tb = t - ntiles_big;
+    if (isb) {
+      const int64_t tb = tt - ntiles_big;
       g = (int)(tb / chunks);
       ch = (int)(tb - (int64_t)g * chunks);
       slot = K;
       ce = chunk_elems;
     } else {
       // nb_per_seq = 2K (target rows 0..K-1, then draft rows) or K (target rows only)
-      const int64_t u = t;
+      const int64_t u = tt;
       const int64_t r = u / chunks_big;
       ch = (int)(u - r * chunks_big);
       g = (int)(r / nb_per_seq);
@@ -118,11 +233,14 @@ __global__ __launch_bounds__(kStreamBlock) void k_lse_partials(RowMap rm, int ns
     const int64_t a1 = a0 + nvec * EPV;
 
     Lse st = lse_init();
+    const bool bonus = slot == K;
+    RaceBest rb = race_init();
     float xh = kNegInf, xt = kNegInf;
     if (tid < head) {
       xh = E::load(row, e0 + tid);
       const float x[1] = {xh};
       lse_update<1>(st, x, c);
+      if (RACE && bonus) race_one(rb, xh, c, seed, g, step, (int)(e0 + tid));
     }
     if (tid < e1 - a1) {
       xt = E::load(row, a1 + tid);
@@ -131,8 +249,7 @@ __global__ __launch_bounds__(kStreamBlock) void k_lse_partials(RowMap rm, int ns
     }
     // body: kStreamUnroll 16-byte vectors per lane in flight, then one max / rescale for
     // the whole group of kStreamUnroll*EPV elements.  A bonus tile is one such group.
-    const bool bonus = slot == K;
-    if (bonus) {
+    if (!RACE && bonus) {
 #pragma unroll
       for (int u = 0; u < kSlabs; ++u) sSlabT[tid][u] = 0.0f;
     }
@@ -144,6 +261,15 @@ __global__ __launch_bounds__(kStreamBlock) void k_lse_partials(RowMap rm, int ns
         const int64_t v = v0 + u * kStreamBlock + tid;
         buf[u] = v < nvec ? load_stream(vp + v) : NegInfVec<DT>::get();
       }
+      if (RACE && bonus && (a0 & 3) == 0) {
+#pragma unroll
+        for (int u = 0; u < kStreamUnroll; ++u) {
+          const int64_t v = v0 + u * kStreamBlock + tid;
+          if (v < nvec) race_vec<DT>(rb, buf[u], c, seed, g, step, (int)(a0 + v * EPV));
+        }
+        sRaceT[tid] = rb;  // parked: no race registers held across the LSE update
+      }
+
       float x[kStreamUnroll * EPV];
 #pragma unroll
       for (int u = 0; u < kStreamUnroll; ++u) E::unpack(buf[u], x + u * EPV);
@@ -151,12 +277,28 @@ __global__ __launch_bounds__(kStreamBlock) void k_lse_partials(RowMap rm, int ns
       lse_update_g<kStreamUnroll * EPV, EPV>(st, x, c, gs);
       // bonus tiles park this thread's slab sums in LDS (no registers held across the
       // workgroup reduction)
-      if (bonus) {
+      if (!RACE && bonus) {
 #pragma unroll
         for (int u = 0; u < kSlabs; ++u) sSlabT[tid][u] = gs[u];
       }
     }
-    if (!bonus) {
+    if (RACE && bonus && (a0 & 3) == 0 && nvec > 0) rb = sRaceT[tid];
+    if (RACE && bonus && (a0 & 3) != 0) {
+      // vectors that do not start at a multiple of 4 (a row start that is not 16-byte
+      // aligned): the body's elements one at a time, read again
+      for (int v = (int)a0 + tid; v < (int)a1; v += kStreamBlock) race_one(rb, E::load(row, v), c, seed, g, step, v);
+    }
+    // the tail last (a thread races its elements in increasing id order), read again
+    // rather than held in a register across the body
+    if (RACE && bonus && tid < e1 - a1) race_one(rb, E::load(row, a1 + tid), c, seed, g, step, (int)(a1 + tid));
+    if (RACE && bonus) {
+      st = lse_block_reduce<kStreamBlock>(st, c, lds);
+      rb = race_block_reduce<kStreamBlock>(rb, sRace);
+      if (tid == 0) {
+        part[((int64_t)g * R + slot) * chunks + ch] = make_float2(st.m, st.s);
+        race[(int64_t)g * chunks + ch] = make_int2(__float_as_int(rb.key), rb.idx);
+      }
+    } else if (!bonus) {
       st = lse_block_reduce<kStreamBlock>(st, c, lds);
       if (tid == 0) part[((int64_t)g * R + slot) * chunks + ch] = make_float2(st.m, st.s);
     } else {
@@ -389,12 +531,13 @@ static_assert(kSlabElems<SMCSD_DTYPE_BF16> + 16 <= 8 * kSmcFinalBlock * kSmcUnit
                   kSlabElems<SMCSD_DTYPE_F32> + 16 <= 8 * kSmcFinalBlock * kSmcUnits,
               "the finalize workgroup must cover one slab");
 
-template <int DT>
+template <int DT, bool RACE>
 __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
     RowMap rm, const int32_t *__restrict__ draft_tokens, int V, int chunk_elems, int chunks,
     int chunks_big, float c, float alpha, uint64_t seed, uint64_t step, uint32_t bonus_tag,
     const float2 *__restrict__ part, const float *__restrict__ logq_in,
-    const float *__restrict__ sub, float *__restrict__ lw, int32_t *__restrict__ out_tokens,
+    const float *__restrict__ sub, const int2 *__restrict__ race, float *__restrict__ lw,
+    int32_t *__restrict__ out_tokens,
     int32_t *__restrict__ out_num,
     float *__restrict__ out_logp, float *__restrict__ out_logq, float *__restrict__ out_lse,
     int32_t *status) {
@@ -438,7 +581,7 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
   const int nsub = chunks * kSlabs;
   const bool sub_in_lds = nsub <= kMaxSubLds;
   const float *gsub = sub + (int64_t)g * nsub;
-  if (sub_in_lds)
+  if (!RACE && sub_in_lds)
     for (int i = tid; i < nsub; i += kSmcFinalBlock) sSub[i] = gsub[i];
   if (tid < (logq_in ? K : 2 * K) && x >= 0 && x < V) xv = E::load(rm.row(g, slot), x);
   __syncthreads();
@@ -488,7 +631,25 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
   const double target = u * SK;
   const char *brow = rm.row(g, K);
   int bonus = -1;
-  if (isfinite(SK) && SK > 0.0) {
+  float race_logit = 0.0f;
+  if (RACE) {
+    // race mode: the best of the tiles' winners (largest key, then smallest id); only
+    // thread 0 uses the result
+    if (isfinite(SK) && SK > 0.0 && tid < kWave) {
+      RaceBest b = race_init();
+      for (int i = tid; i < chunks; i += kWave) {
+        const int2 r = race[(int64_t)g * chunks + i];
+        race_take(b, __int_as_float(r.x), r.y);
+      }
+#pragma unroll
+      for (int mask = 1; mask < kWave; mask <<= 1)
+        race_take(b, __shfl_xor(b.key, mask, kWave), __shfl_xor(b.idx, mask, kWave));
+      if (tid == 0 && b.key > kNegInf && b.idx >= 0 && b.idx < V) {
+        bonus = b.idx;
+        race_logit = E::load(brow, b.idx);
+      }
+    }
+  } else if (isfinite(SK) && SK > 0.0) {
     if (tid < kWave) {
       // wave 0: the chunk, then the slab inside it, whose running sum first exceeds the
       // target (if rounding leaves none, the last chunk / last positive slab), each by a
@@ -548,7 +709,7 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
   }
 
   double lpK = __builtin_nan("");
-  if (bonus >= 0) lpK = ((double)sPickLogit * (double)c - sL2[K]) * kLn2;
+  if (bonus >= 0) lpK = ((double)(RACE ? race_logit : sPickLogit) * (double)c - sL2[K]) * kLn2;
   int32_t *tok = out_tokens + (int64_t)g * (K + 1);
   if (tid < K) {
     tok[tid] = sTok[tid];
@@ -810,17 +971,30 @@ static hipError_t launch_verify_t(const VerifyArgs &a) {
   const VerifyWs w = verify_ws_layout(a.nseq, K, a.V, a.mode);
   float2 *part = reinterpret_cast<float2 *>(a.ws + w.part);
   float *sub = reinterpret_cast<float *>(a.ws + w.sub);
+  int2 *race = reinterpret_cast<int2 *>(a.ws + w.race);
   const int chunks_big = (int)ceil_div(a.V, (int64_t)ce * kBigGroups);
   const int nb_per_seq = a.logq_in ? K : 2 * K;
   const int64_t ntiles = (int64_t)a.nseq * (chunks + (int64_t)nb_per_seq * chunks_big);
   const unsigned grid = (unsigned)std::min<int64_t>(ntiles, (int64_t)1 << 30);
 
   if (a.mode == SMCSD_MODE_SMC) {
-    hipLaunchKernelGGL(k_lse_partials<DT>, dim3(grid), dim3(kStreamBlock), 0, a.stream, rm, a.nseq,
-                       a.V, ce, chunks, chunks_big, nb_per_seq, a.c, part, sub, ntiles);
-    hipLaunchKernelGGL(k_smc_finalize<DT>, dim3(a.nseq), dim3(kSmcFinalBlock), 0, a.stream, rm,
-                       a.draft_tokens, a.V, ce, chunks, chunks_big, a.c, a.alpha, a.seed, a.step,
-                       a.bonus_tag, part, a.logq_in, sub,
+    hipLaunchKernelGGL((k_lse_partials<DT, false>), dim3(grid), dim3(kStreamBlock), 0, a.stream, rm,
+                       a.nseq, a.V, ce, chunks, chunks_big, nb_per_seq, a.c, part, sub, ntiles,
+                       a.seed, a.step, race);
+    hipLaunchKernelGGL((k_smc_finalize<DT, false>), dim3(a.nseq), dim3(kSmcFinalBlock), 0, a.stream,
+                       rm, a.draft_tokens, a.V, ce, chunks, chunks_big, a.c, a.alpha, a.seed, a.step,
+                       a.bonus_tag, part, a.logq_in, sub, race,
+                       a.log_weights, a.out_tokens, a.out_num_tokens, a.out_logp, a.out_logq,
+                       a.out_lse, a.status);
+    return hipGetLastError();
+  }
+  if (a.mode == SMCSD_MODE_SMC_RACE) {
+    hipLaunchKernelGGL((k_lse_partials<DT, true>), dim3(grid), dim3(kStreamBlock), 0, a.stream, rm,
+                       a.nseq, a.V, ce, chunks, chunks_big, nb_per_seq, a.c, part, sub, ntiles,
+                       a.seed, a.step, race);
+    hipLaunchKernelGGL((k_smc_finalize<DT, true>), dim3(a.nseq), dim3(kSmcFinalBlock), 0, a.stream,
+                       rm, a.draft_tokens, a.V, ce, chunks, chunks_big, a.c, a.alpha, a.seed, a.step,
+                       a.bonus_tag, part, a.logq_in, sub, race,
                        a.log_weights, a.out_tokens, a.out_num_tokens, a.out_logp, a.out_logq,
                        a.out_lse, a.status);
     return hipGetLastError();
@@ -829,8 +1003,9 @@ static hipError_t launch_verify_t(const VerifyArgs &a) {
   float4 *norm = reinterpret_cast<float4 *>(a.ws + w.l2);
   float2 *part2 = reinterpret_cast<float2 *>(a.ws + w.part2);
   if (!a.lse_in)
-    hipLaunchKernelGGL(k_lse_partials<DT>, dim3(grid), dim3(kStreamBlock), 0, a.stream, rm, a.nseq,
-                       a.V, ce, chunks, chunks_big, nb_per_seq, a.c, part, sub, ntiles);
+    hipLaunchKernelGGL((k_lse_partials<DT, false>), dim3(grid), dim3(kStreamBlock), 0, a.stream, rm,
+                       a.nseq, a.V, ce, chunks, chunks_big, nb_per_seq, a.c, part, sub, ntiles,
+                       a.seed, a.step, race);
   hipLaunchKernelGGL(k_sps_decide<DT>, dim3(a.nseq), dim3(kWave), 0, a.stream, rm, a.draft_tokens,
                      a.V, chunks, chunks_big, a.c, a.seed, a.step, part, a.lse_in, kstar, norm,
                      a.out_tokens,

@@ -45,7 +45,7 @@ def test_gfx950_code_object_present(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.smcsd_version() == 2
+    assert lib.smcsd_version() == 3
     assert sm.status_string(0) == "ok"
     assert "workspace" in sm.status_string(-4)
     assert "pool" in sm.status_string(sm.ST_NOSPACE)
@@ -87,10 +87,14 @@ def test_verify_host_validation(lib):
     assert _verify_rc(lib, ws=None) == -4
     assert _verify_rc(lib, ws=ctypes.c_void_p(0x1010)) == -4    # workspace not 256-byte aligned
     assert _verify_rc(lib, mode=3) == -1
+    assert _verify_rc(lib, mode=2, lw=None) == -1              # the race mode is an SMC mode
+    assert _verify_rc(lib, mode=2, lse=ctypes.c_void_p(0x1000)) == -1
+    assert _verify_rc(lib, mode=2, wsb=16) == -4
     assert _verify_rc(lib, B=0) == 0                            # empty batch: nothing enqueued
     p = ctypes.c_void_p(0x1000)
     assert _verify_rc(lib, mode=1, logq=p) == -1                # the draft's log q: SMC mode only
     assert _verify_rc(lib, drf=None, logq=p, B=0) == 0          # draft rows not needed with it
+    assert _verify_rc(lib, drf=None, logq=p, B=0, mode=2) == 0
 
 
 def test_draft_sample_host_validation(lib):

@@ -6,7 +6,8 @@ The same construction as the oracle's law pins (prefix-dependent seeded logit ta
 * SMC-SD: one round over many independent prompts with N particles, resampling forced
   (tau > 1), a uniformly chosen output particle -> the sampling-importance-resampling law
   P_N, computed exactly by enumeration (SMC explainers, section 2: importance-weighted
-  resampling).  alpha = 1 and the power target alpha = 4.
+  resampling).  alpha = 1 and the power target alpha = 4; the bonus drawn by inverse CDF
+  and by the exponential race.
 * SpS: rounds of the modified-rejection verify until three tokens are emitted -> the
   target law (the speculative-sampling notes: the output follows the target exactly).
 
@@ -37,8 +38,9 @@ def _i32(*shape):
     return torch.zeros(shape, dtype=torch.int32, device="cuda")
 
 
+@pytest.mark.parametrize("mode", [sm.MODE_SMC, sm.MODE_SMC_RACE], ids=["cdf_bonus", "race_bonus"])
 @pytest.mark.parametrize("N,alpha", [(4, 1.0), (3, 4.0)])
-def test_gpu_smc_round_follows_sir_law(N, alpha):
+def test_gpu_smc_round_follows_sir_law(N, alpha, mode):
     tgt, drf = L._tables(31337)
     P, PI = L._sir_law(tgt, drf, N, alpha)
     runs, seed = 60000, 11
@@ -55,7 +57,7 @@ def test_gpu_smc_round_follows_sir_law(N, alpha):
     lw = torch.zeros(S, dtype=torch.float32, device="cuda")
     out, st = _i32(S, K + 1), _i32(1)
     ws = sm.alloc_workspace(sm.OP_VERIFY_SMC, runs, N, K, V)
-    sm.verify(t_d, d_d, x_d, runs, N, K, V, 1.0, alpha, sm.MODE_SMC, seed, 0, out, st, ws,
+    sm.verify(t_d, d_d, x_d, runs, N, K, V, 1.0, alpha, mode, seed, 0, out, st, ws,
               log_weights=lw)
     anc, ess, res = _i32(runs, N), torch.zeros(runs, device="cuda"), _i32(runs)
     sm.resample(lw.view(runs, N), runs, N, 2.0, seed, 0, anc, ess, res, st)   # tau > 1: always
