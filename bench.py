@@ -78,6 +78,9 @@ def _parse():
     ap.add_argument("--race-bonus", action="store_true",
                     help="SMCSD_MODE_SMC_RACE: the bonus token by an exponential race inside the "
                          "LSE pass instead of the inverse CDF with its one-slab re-read")
+    ap.add_argument("--separate-kv", action="store_true",
+                    help="time smcsd_resample and smcsd_kv_reassign as two calls instead of the "
+                         "fused smcsd_resample_kv_reassign (same results)")
     ap.add_argument("--probe-mib", type=int, default=1024,
                     help="size of the reference copy / read kernels (0 = skip)")
     return ap.parse_args()
@@ -163,9 +166,14 @@ def main():
                   out_num_tokens=num, out_logp=logp, out_logq=logq, logq_in=lq_in)
         if ev is not None:
             ev[1].record()
-        sm.resample(lw.view(B, N), B, N, cfg.tau, seed, t, anc, ess, resampled, status)
         state["L"] += K + 1
-        kv_call(anc, resampled)
+        if args.separate_kv:
+            sm.resample(lw.view(B, N), B, N, cfg.tau, seed, t, anc, ess, resampled, status)
+            kv_call(anc, resampled)
+        else:
+            sm.resample_kv_reassign(lw.view(B, N), B, N, cfg.tau, seed, t, anc, ess, resampled,
+                                    tables, cfg.block_size, state["L"], K + 1, rc, fl, top, cow,
+                                    ncow, status, ws_kv)
 
     reset()
     for t in range(args.warmup):
@@ -240,9 +248,11 @@ def main():
                             cfg.name, variant, B, N, K, V,
                             cfg.dtype, cfg.target_kind, cfg.temperature, cfg.alpha, cfg.tau,
                             cfg.ctx0, cfg.block_size, ", shared prefix" if cfg.shared_prefix else ""),
-            "step": "smcsd_verify%s%s + smcsd_resample + smcsd_kv_reassign" % (
+            "step": "smcsd_verify%s%s + %s" % (
                 " (logq_in: target rows only)" if args.draft_logq else "",
-                " (race-mode bonus)" if args.race_bonus else ""),
+                " (race-mode bonus)" if args.race_bonus else "",
+                "smcsd_resample + smcsd_kv_reassign" if args.separate_kv else
+                "smcsd_resample_kv_reassign (smcsd_resample + smcsd_kv_reassign in one launch fewer)"),
             "draft_sample": draft_info,
             "logit_sets": cfg.n_sets,
             "algorithmic_bytes_per_step": bytes_per_verify,

@@ -242,6 +242,27 @@ int smcsd_kv_reassign(const int32_t *ancestors, const int32_t *resampled, int B,
                       int32_t *status, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * smcsd_resample_kv_reassign - smcsd_resample followed by smcsd_kv_reassign, in one
+ * launch fewer: the Resample step of the round (SMC explainers, methodology "core
+ * flow") and the KV pointer exchange that follows it ("system optimisation design":
+ * KV cache) run in the same per-prompt workgroup, which takes its prompt's ancestors
+ * from on-chip memory.  Arguments, layouts, limits, outputs and status bits are those
+ * of the two calls: log_weights [B, N] in/out, ancestors [B, N], ess [B] and
+ * resampled [B] are written exactly as smcsd_resample writes them (the same bits), and
+ * the block tables, refcounts, free stack and copy-on-write list end exactly as
+ * smcsd_kv_reassign leaves them given those ancestors.  Limits: those of both calls
+ * (1 <= N <= 1024, tau finite).  workspace: smcsd_workspace_bytes(SMCSD_OP_KV, B, N, 0,
+ * 0, P), shared with smcsd_kv_reassign (the two may alternate on one workspace).
+ */
+int smcsd_resample_kv_reassign(float *log_weights, int B, int N, float tau, uint64_t seed,
+                               uint64_t step, int32_t *ancestors, float *ess, int32_t *resampled,
+                               int32_t *block_tables, int M_cap, int block_size, int64_t seq_len,
+                               int reserve_tokens, int32_t *refcounts, int32_t *free_list,
+                               int32_t *free_top, int64_t P, int32_t *cow, int32_t *cow_count,
+                               int32_t *status, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/*
  * smcsd_philox4x32_10 - the library's device Philox4x32-10 block function (SC'11),
  * exposed so its bit-exactness can be checked: out[i] = Philox(counters[i],
  * keys[i]) for i < n.  counters [n, 4], keys [n, 2], out [n, 4] uint32 device arrays.

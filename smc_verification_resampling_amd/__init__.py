@@ -28,7 +28,8 @@ ST_DEGENERATE_WEIGHTS = 8
 ST_BAD_INPUT = 16
 
 EXPORTED = ("smcsd_version", "smcsd_status_string", "smcsd_workspace_bytes", "smcsd_verify",
-            "smcsd_draft_sample", "smcsd_resample", "smcsd_kv_reassign", "smcsd_philox4x32_10")
+            "smcsd_draft_sample", "smcsd_resample", "smcsd_kv_reassign",
+            "smcsd_resample_kv_reassign", "smcsd_philox4x32_10")
 
 _DT = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
 
@@ -65,6 +66,9 @@ def load_library(path: str = LIB_PATH):
     lib.smcsd_kv_reassign.argtypes = [P, P, i32, i32, P, i32, i32, i64, i32, P, P, P, i64, P, P,
                                       P, P, sz, P]
     lib.smcsd_kv_reassign.restype = i32
+    lib.smcsd_resample_kv_reassign.argtypes = [P, i32, i32, f32, u64, u64, P, P, P, P, i32, i32, i64,
+                                               i32, P, P, P, i64, P, P, P, P, sz, P]
+    lib.smcsd_resample_kv_reassign.restype = i32
     lib.smcsd_philox4x32_10.argtypes = [P, P, i32, P, P]
     lib.smcsd_philox4x32_10.restype = i32
     if path == LIB_PATH:
@@ -204,6 +208,32 @@ def kv_reassign(ancestors: torch.Tensor, resampled: torch.Tensor, B: int, N: int
         _dev(cow_count, "cow_count", torch.int32, 1), _dev(status, "status", torch.int32, 1),
         _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
     _check(rc, "smcsd_kv_reassign")
+
+
+def resample_kv_reassign(log_weights: torch.Tensor, B: int, N: int, tau: float, seed: int,
+                         step: int, ancestors: torch.Tensor, ess: torch.Tensor,
+                         resampled: torch.Tensor, block_tables: torch.Tensor, block_size: int,
+                         seq_len: int, reserve_tokens: int, refcounts: torch.Tensor,
+                         free_list: torch.Tensor, free_top: torch.Tensor, cow: torch.Tensor,
+                         cow_count: torch.Tensor, status: torch.Tensor, workspace: torch.Tensor,
+                         stream=None) -> None:
+    """smcsd_resample_kv_reassign: resample then kv_reassign in one launch fewer."""
+    if block_tables.dim() != 2 or block_tables.shape[0] != B * N:
+        raise SmcsdError("block_tables must be [B*N, M_cap]")
+    M_cap = block_tables.shape[1]
+    P = refcounts.numel()
+    rc = _L().smcsd_resample_kv_reassign(
+        _dev(log_weights, "log_weights", torch.float32, B * N), B, N, float(tau),
+        int(seed) & (2**64 - 1), int(step) & (2**64 - 1),
+        _dev(ancestors, "ancestors", torch.int32, B * N), _dev(ess, "ess", torch.float32, B),
+        _dev(resampled, "resampled", torch.int32, B),
+        _dev(block_tables, "block_tables", torch.int32), M_cap, block_size, int(seq_len),
+        reserve_tokens, _dev(refcounts, "refcounts", torch.int32),
+        _dev(free_list, "free_list", torch.int32, P), _dev(free_top, "free_top", torch.int32, 1), P,
+        _dev(cow, "cow", torch.int32, 3 * B * N), _dev(cow_count, "cow_count", torch.int32, 1),
+        _dev(status, "status", torch.int32, 1), _dev(workspace, "workspace", torch.uint8),
+        workspace.numel(), _stream(stream))
+    _check(rc, "smcsd_resample_kv_reassign")
 
 
 def philox4x32_10(counters: torch.Tensor, keys: torch.Tensor, out: torch.Tensor, stream=None):

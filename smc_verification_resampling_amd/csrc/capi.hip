@@ -164,25 +164,60 @@ int smcsd_resample(float *log_weights, int B, int N, float tau, uint64_t seed, u
                                 status, as_stream(stream)));
 }
 
+// Host checks of a KV reassign call (SMCSD_OK to go ahead, 1 for an empty batch).
+static int kv_check(int B, int N, const int32_t *block_tables, int M_cap, int block_size,
+                    int64_t seq_len, int reserve_tokens, const int32_t *refcounts,
+                    const int32_t *free_list, const int32_t *free_top, int64_t P, const int32_t *cow,
+                    const int32_t *cow_count, const int32_t *status, const void *workspace,
+                    size_t workspace_bytes) {
+  if (B < 0 || N < 1 || N > kMaxN || M_cap < 1 || block_size < 1 || seq_len < 0 ||
+      reserve_tokens < 0 || P < 1 || P > INT32_MAX)
+    return SMCSD_EINVAL;
+  if (ceil_div(seq_len + reserve_tokens, block_size) > M_cap) return SMCSD_EINVAL;
+  if (B == 0) return 1;
+  if ((int64_t)B * N * M_cap >= INT32_MAX) return SMCSD_EINVAL;  // 32-bit table indexing
+  if (!block_tables || !refcounts || !free_list || !free_top || !cow || !cow_count || !status)
+    return SMCSD_EINVAL;
+  const size_t need = kv_ws_layout((int64_t)B * N, P).total;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) return SMCSD_EWORKSPACE;
+  return SMCSD_OK;
+}
+
 int smcsd_kv_reassign(const int32_t *ancestors, const int32_t *resampled, int B, int N,
                       int32_t *block_tables, int M_cap, int block_size, int64_t seq_len,
                       int reserve_tokens, int32_t *refcounts, int32_t *free_list,
                       int32_t *free_top, int64_t P, int32_t *cow, int32_t *cow_count,
                       int32_t *status, void *workspace, size_t workspace_bytes, void *stream) {
-  if (B < 0 || N < 1 || N > kMaxN || M_cap < 1 || block_size < 1 || seq_len < 0 ||
-      reserve_tokens < 0 || P < 1 || P > INT32_MAX)
-    return SMCSD_EINVAL;
-  if (ceil_div(seq_len + reserve_tokens, block_size) > M_cap) return SMCSD_EINVAL;
-  if (B == 0) return SMCSD_OK;
-  if ((int64_t)B * N * M_cap >= INT32_MAX) return SMCSD_EINVAL;  // 32-bit table indexing
-  if (!ancestors || !resampled || !block_tables || !refcounts || !free_list || !free_top || !cow ||
-      !cow_count || !status)
-    return SMCSD_EINVAL;
-  const size_t need = kv_ws_layout((int64_t)B * N, P).total;
-  if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) return SMCSD_EWORKSPACE;
-  return hip_rc(launch_kv(ancestors, resampled, B, N, block_tables, M_cap, block_size, seq_len,
-                          reserve_tokens, refcounts, free_list, free_top, P, cow, cow_count, status,
-                          static_cast<char *>(workspace), as_stream(stream)));
+  const int chk = kv_check(B, N, block_tables, M_cap, block_size, seq_len, reserve_tokens,
+                           refcounts, free_list, free_top, P, cow, cow_count, status, workspace,
+                           workspace_bytes);
+  if (chk == 1) return SMCSD_OK;
+  if (chk != SMCSD_OK) return chk;
+  if (!ancestors || !resampled) return SMCSD_EINVAL;
+  const FusedResample none{};
+  return hip_rc(launch_kv(ancestors, resampled, none, B, N, block_tables, M_cap, block_size,
+                          seq_len, reserve_tokens, refcounts, free_list, free_top, P, cow,
+                          cow_count, status, static_cast<char *>(workspace), as_stream(stream)));
+}
+
+int smcsd_resample_kv_reassign(float *log_weights, int B, int N, float tau, uint64_t seed,
+                               uint64_t step, int32_t *ancestors, float *ess, int32_t *resampled,
+                               int32_t *block_tables, int M_cap, int block_size, int64_t seq_len,
+                               int reserve_tokens, int32_t *refcounts, int32_t *free_list,
+                               int32_t *free_top, int64_t P, int32_t *cow, int32_t *cow_count,
+                               int32_t *status, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+  if (!std::isfinite(tau)) return SMCSD_EINVAL;
+  const int chk = kv_check(B, N, block_tables, M_cap, block_size, seq_len, reserve_tokens,
+                           refcounts, free_list, free_top, P, cow, cow_count, status, workspace,
+                           workspace_bytes);
+  if (chk == 1) return SMCSD_OK;
+  if (chk != SMCSD_OK) return chk;
+  if (!log_weights || !ancestors || !ess || !resampled) return SMCSD_EINVAL;
+  const FusedResample fr{log_weights, tau, seed, step, ancestors, ess, resampled};
+  return hip_rc(launch_kv(nullptr, nullptr, fr, B, N, block_tables, M_cap, block_size, seq_len,
+                          reserve_tokens, refcounts, free_list, free_top, P, cow, cow_count,
+                          status, static_cast<char *>(workspace), as_stream(stream)));
 }
 
 int smcsd_philox4x32_10(const uint32_t *counters, const uint32_t *keys, int n, uint32_t *out,

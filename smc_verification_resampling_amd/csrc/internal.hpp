@@ -86,10 +86,21 @@ hipError_t launch_resample(float *lw, int B, int N, float tau, uint64_t seed, ui
                            int32_t *anc, float *ess, int32_t *resampled, int32_t *status,
                            hipStream_t stream);
 
-hipError_t launch_kv(const int32_t *anc, const int32_t *resampled, int B, int N, int32_t *tables,
-                     int M_cap, int bs, int64_t L, int R, int32_t *rc, int32_t *free_list,
-                     int32_t *free_top, int64_t P, int32_t *cow, int32_t *cow_count,
-                     int32_t *status, char *ws, hipStream_t stream);
+// The Resample step run inside the KV exchange kernel (lw == nullptr: not fused; the
+// ancestors and decisions then come from anc / resampled).
+struct FusedResample {
+  float *lw;
+  float tau;
+  uint64_t seed, step;
+  int32_t *anc;
+  float *ess;
+  int32_t *res;
+};
+
+hipError_t launch_kv(const int32_t *anc, const int32_t *resampled, const FusedResample &fr, int B,
+                     int N, int32_t *tables, int M_cap, int bs, int64_t L, int R, int32_t *rc,
+                     int32_t *free_list, int32_t *free_top, int64_t P, int32_t *cow,
+                     int32_t *cow_count, int32_t *status, char *ws, hipStream_t stream);
 
 hipError_t launch_philox(const uint32_t *ctr, const uint32_t *key, int n, uint32_t *out,
                          hipStream_t stream);

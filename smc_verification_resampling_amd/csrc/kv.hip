@@ -25,6 +25,7 @@
 #include "device.hpp"
 #include "internal.hpp"
 #include "kv_layout.hpp"
+#include "resample.hpp"
 
 namespace smcsd {
 
@@ -105,11 +106,16 @@ struct KvBufs {
   int32_t *cow_src, *cow_excl, *gbase, *popmap, *done, *ctr, *scal;
 };
 
+static_assert(kKvBlock == kResBlock, "the fused resample runs on the KV workgroup");
+
+// fr.lw != nullptr: the Resample step is fused in - each workgroup first resamples its
+// prompt (the same device code as smcsd_resample, so the same bits) and takes the
+// ancestors from LDS; anc / resampled are then unused.
 __global__ __launch_bounds__(kKvBlock) void k_kv(
-    const int32_t *__restrict__ anc, const int32_t *__restrict__ resampled, int B, int N,
-    int32_t *__restrict__ T, int M_cap, int nb_old, int nb_new, int tail_slot, int tail_mod,
-    int32_t *__restrict__ rc, int P, int32_t *__restrict__ free_top, KvBufs wb, int fast,
-    int32_t *__restrict__ cow_count, int32_t *status) {
+    const int32_t *__restrict__ anc, const int32_t *__restrict__ resampled, FusedResample fr,
+    int B, int N, int32_t *__restrict__ T, int M_cap, int nb_old, int nb_new, int tail_slot,
+    int tail_mod, int32_t *__restrict__ rc, int P, int32_t *__restrict__ free_top, KvBufs wb,
+    int fast, int32_t *__restrict__ cow_count, int32_t *status) {
   __shared__ int32_t a[kMaxN], cnt[kMaxN], tail_old[kMaxN], tail_new[kMaxN];
   __shared__ int32_t tile[kKvTileInts];
   __shared__ uint8_t colu[kKvTileInts];  // column of the tile holds one block in every row
@@ -144,12 +150,32 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
     const int j = e / max(w0, 1), s = e - j * max(w0, 1);
     pre[k] = nw0 > 0 ? T[(row0 + j) * M_cap + s] : 0;
   }
-  const int res = resampled[b] != 0;
-  for (int i = tid; i < N; i += kKvBlock) {
-    a[i] = anc[row0 + i];
-    cnt[i] = 0;
+  int res;
+  if (fr.lw) {
+    __shared__ ResampleLds sResL;
+    __shared__ int sRes;
+    if (N <= kWave) {
+      if (tid < kWave) {
+        const int d = resample_prompt_wave(fr.lw + row0, N, fr.tau, fr.seed, b, fr.step,
+                                           fr.anc + row0, fr.ess + b, fr.res + b, status, a);
+        if (tid == 0) sRes = d;
+      }
+    } else {
+      const int d = resample_prompt_block(fr.lw + row0, N, fr.tau, fr.seed, b, fr.step,
+                                          fr.anc + row0, fr.ess + b, fr.res + b, status, a, sResL);
+      if (tid == 0) sRes = d;
+    }
+    for (int i = tid; i < N; i += kKvBlock) cnt[i] = 0;
+    __syncthreads();
+    res = sRes;
+  } else {
+    res = resampled[b] != 0;
+    for (int i = tid; i < N; i += kKvBlock) {
+      a[i] = anc[row0 + i];
+      cnt[i] = 0;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   for (int i = tid; i < N; i += kKvBlock) {
     const int32_t x = res ? a[i] : i;
     const int ok = x >= 0 && x < N;
@@ -611,10 +637,10 @@ __global__ __launch_bounds__(kKvBlock) void k_kv_pop_fast(
   if (flags) atomicOr(status, flags);
 }
 
-hipError_t launch_kv(const int32_t *anc, const int32_t *resampled, int B, int N, int32_t *tables,
-                     int M_cap, int bs, int64_t L, int R, int32_t *rc, int32_t *free_list,
-                     int32_t *free_top, int64_t P, int32_t *cow, int32_t *cow_count,
-                     int32_t *status, char *ws, hipStream_t stream) {
+hipError_t launch_kv(const int32_t *anc, const int32_t *resampled, const FusedResample &fr, int B,
+                     int N, int32_t *tables, int M_cap, int bs, int64_t L, int R, int32_t *rc,
+                     int32_t *free_list, int32_t *free_top, int64_t P, int32_t *cow,
+                     int32_t *cow_count, int32_t *status, char *ws, hipStream_t stream) {
   const int S = B * N;
   const KvWs w = kv_ws_layout(S, P);
   KvBufs wb;
@@ -636,7 +662,7 @@ hipError_t launch_kv(const int32_t *anc, const int32_t *resampled, int B, int N,
   const int tail_slot = (int)(L / bs), tail_mod = (int)(L % bs);
   const int fast = S <= kKvFastSeqMax && w.ngroups <= kKvFastGroupMax;
   const unsigned grid2 = (unsigned)(w.ngroups + (S + kKvBlock - 1) / kKvBlock);
-  hipLaunchKernelGGL(k_kv, dim3(B), dim3(kKvBlock), 0, stream, anc, resampled, B, N, tables, M_cap,
+  hipLaunchKernelGGL(k_kv, dim3(B), dim3(kKvBlock), 0, stream, anc, resampled, fr, B, N, tables, M_cap,
                      nb_old, nb_new, tail_slot, tail_mod, rc, (int)P, free_top, wb, fast, cow_count,
                      status);
   if (fast)

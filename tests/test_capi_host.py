@@ -97,6 +97,26 @@ def test_verify_host_validation(lib):
     assert _verify_rc(lib, drf=None, logq=p, B=0, mode=2) == 0
 
 
+def test_resample_kv_reassign_host_validation(lib):
+    p = ctypes.c_void_p(0x1000)
+
+    def rc(**kw):
+        a = dict(lw=p, B=2, N=4, tau=0.5, anc=p, ess=p, res=p, T=p, M=8, bs=4, L=0, R=1, rc=p,
+                 fl=p, top=p, P=64, cow=p, ncow=p, st=p, ws=p, wsb=1 << 20)
+        a.update(kw)
+        return lib.smcsd_resample_kv_reassign(a["lw"], a["B"], a["N"], a["tau"], 0, 0, a["anc"],
+                                              a["ess"], a["res"], a["T"], a["M"], a["bs"], a["L"],
+                                              a["R"], a["rc"], a["fl"], a["top"], a["P"], a["cow"],
+                                              a["ncow"], a["st"], a["ws"], a["wsb"], None)
+    assert rc(tau=float("nan")) == -1
+    assert rc(N=0) == -1 and rc(N=1025) == -1
+    assert rc(L=30, R=8) == -1                                   # beyond M_cap slots
+    assert rc(lw=None) == -1 and rc(anc=None) == -1 and rc(ess=None) == -1 and rc(res=None) == -1
+    assert rc(T=None) == -1 and rc(top=None) == -1
+    assert rc(wsb=16) == -4 and rc(ws=ctypes.c_void_p(0x1010)) == -4
+    assert rc(B=0) == 0                                          # empty batch: nothing enqueued
+
+
 def test_draft_sample_host_validation(lib):
     p = ctypes.c_void_p(0x1000)
 

@@ -1,0 +1,141 @@
+"""smcsd_resample_kv_reassign against smcsd_resample followed by smcsd_kv_reassign.
+
+Two copies of the same state run the same rounds, one through the fused entry point and
+one through the two separate calls; every output must be bit-identical after every
+round: ancestors, ESS, decisions, reset log-weights, block tables, refcounts, free stack,
+copy-on-write list and status.  Covers the one-wave resample (N <= 64) and the workgroup
+resample (N > 64), shared and unshared prefixes, prompts with degenerate (NaN) weights,
+the many-sequence KV path, and the two forms alternating on one workspace.  The first
+round of each case is also checked against the oracle.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import smc_verification_resampling_amd as sm
+from workloads import configs as C
+from workloads import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+
+
+def _i32(*shape):
+    return torch.zeros(shape, dtype=torch.int32, device="cuda")
+
+
+class _State:
+    def __init__(self, kv, B, N, P):
+        self.tables = torch.from_numpy(kv["tables"].copy()).cuda()
+        self.rc = torch.from_numpy(kv["refcounts"].copy()).cuda()
+        self.fl = torch.from_numpy(kv["free_list"].copy()).cuda()
+        self.top = torch.from_numpy(kv["free_top"].copy()).cuda()
+        self.cow, self.ncow, self.st = _i32(B * N, 3), _i32(1), _i32(1)
+        self.anc, self.res = _i32(B, N), _i32(B)
+        self.ess = torch.zeros(B, device="cuda")
+        self.ws = sm.alloc_workspace(sm.OP_KV, B, N, P=P)
+
+    def snapshot(self, lw):
+        n = int(self.ncow.cpu()[0])
+        return dict(anc=self.anc.cpu().numpy(), res=self.res.cpu().numpy(),
+                    ess=self.ess.cpu().numpy(), lw=lw.cpu().numpy(),
+                    tables=self.tables.cpu().numpy(), rc=self.rc.cpu().numpy(),
+                    top=int(self.top.cpu()[0]), fl=self.fl.cpu().numpy(), cow=self.cow.cpu().numpy()[:n],
+                    ncow=n, st=int(self.st.cpu()[0]))
+
+
+def _equal(a, b):
+    top = a["top"]
+    for k in ("anc", "res", "ess", "lw", "tables", "rc", "cow"):
+        # NaN log-weights of a degenerate prompt stay NaN on both sides
+        if not np.array_equal(a[k], b[k], equal_nan=a[k].dtype.kind == "f"):
+            return k
+    for k in ("top", "ncow", "st"):
+        if a[k] != b[k]:
+            return k
+    if not np.array_equal(a["fl"][:top], b["fl"][:top]):
+        return "fl"
+    return None
+
+
+@pytest.mark.parametrize("B,N,shared", [(3, 16, True), (2, 5, False), (2, 128, True),
+                                        (40, 256, False)])
+def test_fused_equals_separate_calls(B, N, shared):
+    bs, K, ctx0, rounds = 4, 2, 10, 6
+    R = K + 1
+    cfg = C.C1.scaled(B=B, N=N, K=K, ctx0=ctx0, block_size=bs, shared_prefix=shared, iters=rounds)
+    kv = synth.initial_kv(cfg)
+    P = kv["refcounts"].size
+    A, F = _State(kv, B, N, P), _State(kv, B, N, P)
+    ident = torch.arange(N, dtype=torch.int32, device="cuda").repeat(B, 1)
+    zero = _i32(B)
+    L = ctx0
+    for s in (A, F):
+        sm.kv_reassign(ident, zero, B, N, s.tables, bs, L, R, s.rc, s.fl, s.top, s.cow, s.ncow, s.st,
+                       s.ws)
+    g = torch.Generator(device="cuda").manual_seed(B * 1000 + N)
+    lw_a = torch.zeros(B * N, device="cuda")
+    lw_f = torch.zeros(B * N, device="cuda")
+    tau = 0.6
+    for r in range(rounds):
+        L += R
+        inc = torch.randn(B * N, generator=g, device="cuda") * (0.3 + r)
+        if r == 2:
+            inc[:N] = float("nan")            # prompt 0: degenerate weights this round
+        lw_a += inc
+        lw_f += inc
+        lw_in = lw_a.cpu().numpy().copy()
+        tables_in, rc_in = A.tables.cpu().numpy(), A.rc.cpu().numpy()
+        fl_in, top_in = A.fl.cpu().numpy(), int(A.top.cpu()[0])
+        sm.resample(lw_a.view(B, N), B, N, tau, 77, r, A.anc, A.ess, A.res, A.st)
+        sm.kv_reassign(A.anc, A.res, B, N, A.tables, bs, L, R, A.rc, A.fl, A.top, A.cow, A.ncow,
+                       A.st, A.ws)
+        if r % 3 == 1:   # F's workspace also serves the separate calls between fused ones
+            sm.resample(lw_f.view(B, N), B, N, tau, 77, r, F.anc, F.ess, F.res, F.st)
+            sm.kv_reassign(F.anc, F.res, B, N, F.tables, bs, L, R, F.rc, F.fl, F.top, F.cow,
+                           F.ncow, F.st, F.ws)
+        else:
+            sm.resample_kv_reassign(lw_f.view(B, N), B, N, tau, 77, r, F.anc, F.ess, F.res,
+                                    F.tables, bs, L, R, F.rc, F.fl, F.top, F.cow, F.ncow, F.st,
+                                    F.ws)
+        torch.cuda.synchronize()
+        a, f = A.snapshot(lw_a), F.snapshot(lw_f)
+        bad = _equal(a, f)
+        assert bad is None, (r, bad)
+        if r == 0:
+            o = oracle.resample(lw_in.reshape(B, N), float(np.float32(tau)), 77, r)
+            assert np.array_equal(f["anc"], o["ancestors"]) and np.array_equal(f["res"], o["resampled"])
+            ok = oracle.kv_reassign(o["ancestors"], o["resampled"], tables_in, bs, L, R, rc_in, fl_in,
+                                    top_in)
+            assert np.array_equal(f["tables"], ok["tables"]) and f["top"] == ok["free_top"]
+    if N <= 64:
+        assert (a["res"] == 1).any()          # the rounds did resample
+    assert a["st"] & sm.ST_DEGENERATE_WEIGHTS
+
+
+def test_fused_rejects_what_either_call_rejects():
+    B, N, P = 2, 4, 64
+    lw = torch.zeros(B * N, device="cuda")
+    anc, res, ess = _i32(B, N), _i32(B), torch.zeros(B, device="cuda")
+    tables = torch.full((B * N, 8), -1, dtype=torch.int32, device="cuda")
+    rc, fl, top = _i32(P), _i32(P), _i32(1)
+    cow, ncow, st = _i32(B * N, 3), _i32(1), _i32(1)
+    ws = sm.alloc_workspace(sm.OP_KV, B, N, P=P)
+    with pytest.raises(sm.SmcsdError):
+        sm.resample_kv_reassign(lw, B, N, float("nan"), 1, 0, anc, ess, res, tables, 4, 0, 1, rc, fl,
+                                top, cow, ncow, st, ws)
+    with pytest.raises(sm.SmcsdError):      # reservation beyond M_cap
+        sm.resample_kv_reassign(lw, B, N, 0.5, 1, 0, anc, ess, res, tables, 4, 30, 8, rc, fl, top,
+                                cow, ncow, st, ws)
+    with pytest.raises(sm.SmcsdError):      # workspace too small
+        sm.resample_kv_reassign(lw, B, N, 0.5, 1, 0, anc, ess, res, tables, 4, 0, 1, rc, fl, top,
+                                cow, ncow, st, ws[:64])
