@@ -68,6 +68,20 @@ def test_draft_sample_matches_oracle(dtype, V, T, pos):
     assert np.all((tok >= 0) & (tok < V))
 
 
+def test_draft_sample_maximum_vocabulary():
+    """V = 2^24 rows (1024 one-step tiles per row): tokens and log q against the oracle."""
+    V, n = 1 << 24, 3
+    g = torch.Generator(device="cuda").manual_seed(99)
+    rows = (torch.randn((n, V), generator=g, device="cuda") * 1.5).to(torch.bfloat16)
+    tok, lq, st = _gpu_draft(rows, V, 0.7, 5, 8, 2)
+    assert st == 0
+    o = oracle.draft_sample(_host(rows), float(np.float32(0.7)), 5, 8, 2)
+    flagged = o["margin"] < MARGIN
+    assert np.array_equal(tok[~flagged], o["tokens"][~flagged])
+    same = tok == o["tokens"]
+    assert np.all(np.abs(lq[same] - o["logq"][same]) <= 1e-5 * np.maximum(1.0, np.abs(o["logq"][same])))
+
+
 def test_draft_sample_masked_one_hot_and_empty_rows():
     V = 20000
     rows = torch.full((4, V), float("-inf"), device="cuda")

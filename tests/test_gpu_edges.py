@@ -30,14 +30,15 @@ def _f32(*shape):
     return torch.zeros(shape, dtype=torch.float32, device="cuda")
 
 
-def _verify_case(target, draft, toks, K, V, T, alpha, seed, step, lw0, row_stride=None):
+def _verify_case(target, draft, toks, K, V, T, alpha, seed, step, lw0, row_stride=None,
+                 mode=sm.MODE_SMC):
     """One SMC verify on the GPU vs the oracle; returns (gpu dict, oracle dict)."""
     S = toks.shape[0]
     out = dict(tokens=_i32(S, K + 1), num=_i32(S), logp=_f32(S, K + 1), logq=_f32(S, max(K, 1)),
                lse=_f32(S, 2 * K + 1), status=_i32(1))
     lw = torch.tensor(lw0, dtype=torch.float32, device="cuda")
     ws = sm.alloc_workspace(sm.OP_VERIFY_SMC, S, 1, K, V)
-    sm.verify(target, draft, toks, S, 1, K, V, T, alpha, sm.MODE_SMC, seed, step, out["tokens"],
+    sm.verify(target, draft, toks, S, 1, K, V, T, alpha, mode, seed, step, out["tokens"],
               out["status"], ws, log_weights=lw, out_num_tokens=out["num"], out_logp=out["logp"],
               out_logq=out["logq"], out_lse=out["lse"], row_stride=row_stride)
     torch.cuda.synchronize()
@@ -47,17 +48,18 @@ def _verify_case(target, draft, toks, K, V, T, alpha, seed, step, lw0, row_strid
         np.zeros((S, 0, V), th.dtype)
     o = oracle.verify_smc(np.ascontiguousarray(th), np.ascontiguousarray(dh),
                           toks.cpu().numpy(), float(np.float32(T)), float(np.float32(alpha)), seed,
-                          step, np.asarray(lw0, np.float32))
+                          step, np.asarray(lw0, np.float32),
+                          bonus="race" if mode == sm.MODE_SMC_RACE else "cdf")
     g = {k: v.cpu().numpy() for k, v in out.items()}
     g["lw"] = lw.cpu().numpy()
     return g, o
 
 
-def _assert_verify_parity(g, o, K):
+def _assert_verify_parity(g, o, K, margin=H.MARGIN):
     assert int(g["status"][0]) == o["status"]
     assert np.array_equal(g["tokens"][:, :K], o["tokens"][:, :K])
     for i in range(len(o["lw"])):
-        if o["margin"][i] >= H.MARGIN:
+        if o["margin"][i] >= margin:
             assert g["tokens"][i, K] == o["tokens"][i, K], (i, o["margin"][i])
             assert abs(g["lw"][i] - o["lw"][i]) <= H.TOL_LW
     fin = np.isfinite(o["lse"])
@@ -333,6 +335,23 @@ def test_many_chunks_per_sequence():
     toks = torch.randint(0, V, (S, K), generator=g, device="cuda", dtype=torch.int32)
     gg, o = _verify_case(tgt, drf.contiguous(), toks, K, V, 0.8, 1.0, 5, 6, np.zeros(S))
     _assert_verify_parity(gg, o, K)
+
+
+@pytest.mark.parametrize("dtype,mode", [("bf16", sm.MODE_SMC), ("f32", sm.MODE_SMC),
+                                        ("bf16", sm.MODE_SMC_RACE)])
+def test_maximum_vocabulary(dtype, mode):
+    """V = 2^24, the largest vocabulary the library takes: 1024 (bf16) or 2048 (fp32) chunks
+    per row, so the finalize's chunk terms fill their LDS array and the slab sums are read in
+    place; in race mode the clock counters reach (v div 4) = 2^22 - 1."""
+    S, K, V = 2, 1, 1 << 24
+    g = torch.Generator(device="cuda").manual_seed(24)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tgt = (torch.randn((S, K + 1, V), generator=g, device="cuda") * 1.5).to(dt)
+    drf = (torch.randn((S, K, V), generator=g, device="cuda") * 1.5).to(dt)
+    toks = torch.tensor([[V - 1], [12345]], dtype=torch.int32, device="cuda")
+    gg, o = _verify_case(tgt, drf, toks, K, V, 0.9, 2.0, 13, 4, np.array([0.0, -1.0]), mode=mode)
+    _assert_verify_parity(gg, o, K, margin=1e-4 if mode == sm.MODE_SMC_RACE else H.MARGIN)
+    assert np.all((gg["tokens"][:, K] >= 0) & (gg["tokens"][:, K] < V))
 
 
 @pytest.mark.parametrize("L,R", [(12, 0), (8, 4), (10, 2), (9, 0)])
