@@ -35,14 +35,14 @@ EVENT_EVERY = 8
 # only for the kernel sources they were taken on: any change to them reports null.
 VERIFY_TRAFFIC = {
     "workload": "c3_batched",
-    "bytes": 1186194364,
+    "bytes": 1186176667,
     "sources": {
         "smc_verification_resampling_amd/csrc/verify.hip":
-            "3add99d70b2a46559019b2d4e6edb57c8286a6d888bfcaa85fac691a931dd50b",
+            "9addd32b66f2c36c80b54895e0e836f5adf44f1228051be02a47003128bfa975",
         "smc_verification_resampling_amd/csrc/device.hpp":
-            "5f1a401af612b80cc49dc04b7dad254ea96512e328607395f475dfb4e5a87d97",
+            "4edde2c3edddba0bcfb398a012d90b9a18224f38e37bd532b4ecce58691e1159",
         "smc_verification_resampling_amd/csrc/internal.hpp":
-            "03e0ad22e11f6b98eef10d8bdeb8daba2f6d6d27f4f867e813af03e7e469eb79",
+            "4beeaced470350a87cc377eb863c14b8a32fc382d92e8c2b0f371a6093494092",
     },
 }
 

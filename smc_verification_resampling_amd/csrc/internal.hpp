@@ -20,7 +20,7 @@ constexpr int kBigGroups = 4;
 
 constexpr int kMaxK = 32;
 constexpr int kMaxN = 1024;
-constexpr int kMaxV = 1 << 24;  // finalize keeps one fp64 term per vocabulary chunk in LDS
+constexpr int kMaxV = 1 << 24;  // largest vocabulary taken (and tested); ids fit every index type used
 
 inline int chunk_elems(int dtype) { return dtype == 1 ? kChunkElemsBf16 : kChunkElemsF32; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

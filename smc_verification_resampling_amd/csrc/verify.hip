@@ -14,8 +14,8 @@
 //                    so the bonus draw re-reads one slab instead of a whole chunk.
 //   k_smc_finalize   grid = sequences.  Combines the chunk pairs in fp64 into each row's
 //                    normaliser, gathers the draft-token log-probabilities, draws the bonus
-//                    token by inverse CDF (selects the chunk from the pairs and the slab
-//                    from the slab sums, re-reads only that slab) and updates the
+//                    token by inverse CDF (selects the slab from the slab sums of all the
+//                    row's chunks in one scan, re-reads only that slab) and updates the
 //                    log-weight.
 //   race mode        the bonus row's tiles also run an exponential race (exponential-races
 //                    summary page, key design) over their elements and keep the winner;
@@ -521,7 +521,6 @@ struct ExpRow {
 // ---------------------------------------------------------------------------------
 // SMC finalize: one workgroup per sequence
 // ---------------------------------------------------------------------------------
-constexpr int kMaxChunks = kMaxV / kChunkElemsF32;
 constexpr int kMaxPartLds = 1024;  // chunk pairs of one sequence staged in LDS (else read in place)
 constexpr int kMaxSubLds = 1024;   // bonus slab sums of one sequence staged in LDS
 // units per thread for the finalize's one-slab re-read: a slab plus a head or tail of
@@ -548,7 +547,6 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
   __shared__ double sS[2 * kMaxK + 1], sL2[2 * kMaxK + 1];
   __shared__ double sLogp[kMaxK + 1], sLogq[kMaxK + 1];
   __shared__ int32_t sTok[kMaxK + 1];
-  __shared__ double sTermK[kMaxChunks];
   __shared__ float2 sPart[kMaxPartLds];
   __shared__ float sSub[kMaxSubLds];
   __shared__ double sScan[kSmcFinalBlock / kWave];
@@ -586,7 +584,7 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
   if (tid < (logq_in ? K : 2 * K) && x >= 0 && x < V) xv = E::load(rm.row(g, slot), x);
   __syncthreads();
 
-  // row normalisers: chunk pairs combined in fp64 (row K also keeps its chunk terms);
+  // row normalisers: chunk pairs combined in fp64;
   // the draft rows only when their log q is not given
   if (tid < (logq_in ? K + 1 : R)) {
     const float2 *p = (part_in_lds ? sPart : gpart) + tid * chunks;
@@ -595,11 +593,7 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
     for (int i = 0; i < n; ++i) M = fmaxf(M, p[i].x);
     const float Mc = M == kNegInf ? 0.0f : __fmul_rn(M, c);
     double S = 0.0;
-    for (int i = 0; i < n; ++i) {
-      const double t = chunk_term(p[i], c, Mc);
-      if (tid == K) sTermK[i] = t;
-      S += t;
-    }
+    for (int i = 0; i < n; ++i) S += chunk_term(p[i], c, Mc);
     sMc[tid] = Mc;
     sS[tid] = S;
     sL2[tid] = (double)Mc + log2(S);
@@ -651,42 +645,44 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
     }
   } else if (isfinite(SK) && SK > 0.0) {
     if (tid < kWave) {
-      // wave 0: the chunk, then the slab inside it, whose running sum first exceeds the
-      // target (if rounding leaves none, the last chunk / last positive slab), each by a
-      // lane prefix sum and a ballot
+      // wave 0: the slab whose running sum first exceeds the target, over all slabs of the
+      // row in order (chunk-major), by lane prefix sums and a ballot per 64 slabs; a slab's
+      // term is its sum rescaled from its chunk's reference to the row's.  If rounding
+      // leaves no crossing, the last slab with a positive term.
       const int lane = tid;
-      double base = 0.0;
-      int ch = -1;
-      for (int c0 = 0; c0 < chunks && ch < 0; c0 += kWave) {
-        const double t = c0 + lane < chunks ? sTermK[c0 + lane] : 0.0;
+      const float *sb = sub_in_lds ? sSub : gsub;
+      const float2 *pk = (part_in_lds ? sPart : gpart) + K * chunks;
+      const int nsl = chunks * kSlabs;
+      double base = 0.0, base_last = 0.0;
+      int sel = -1, last = -1;
+      for (int j0 = 0; j0 < nsl && sel < 0; j0 += kWave) {
+        const int j = j0 + lane;
+        double t = 0.0;
+        if (j < nsl) {
+          const float2 p = pk[j / kSlabs];
+          if (p.x != kNegInf) t = (double)sb[j] * (double)fast_exp2(__fmul_rn(p.x, c) - sMc[K]);
+        }
         const double inc = wave_inclusive_scan(t);
-        const unsigned long long hit = __ballot(c0 + lane < chunks && base + inc > target);
+        const unsigned long long hit = __ballot(j < nsl && base + inc > target);
+        const unsigned long long pos = __ballot(j < nsl && t > 0.0);
+        if (pos) {
+          const int f = 63 - __clzll(pos);
+          last = j0 + f;
+          base_last = base + __shfl(inc - t, f, kWave);
+        }
         if (hit) {
           const int f = __ffsll(hit) - 1;
-          ch = c0 + f;
+          sel = j0 + f;
           base += __shfl(inc - t, f, kWave);
         } else {
           base += __shfl(inc, kWave - 1, kWave);
         }
       }
-      if (ch < 0) {  // no crossing: restart the last chunk from its own prefix
-        ch = chunks - 1;
-        double pre = 0.0;
-        for (int i = lane; i < chunks - 1; i += kWave) pre += sTermK[i];
-#pragma unroll
-        for (int d = kWave / 2; d >= 1; d >>= 1) pre += __shfl_xor(pre, d, kWave);
-        base = pre;
+      if (sel < 0) {
+        sel = last >= 0 ? last : nsl - 1;
+        base = last >= 0 ? base_last : base;
       }
-      const float2 pk = (part_in_lds ? sPart : gpart)[K * chunks + ch];
-      const double fk =
-          pk.x == kNegInf ? 0.0 : (double)fast_exp2(__fmul_rn(pk.x, c) - sMc[K]);
-      const float *sb = (sub_in_lds ? sSub : gsub) + ch * kSlabs;
-      const double ts = lane < kSlabs ? (double)sb[lane] * fk : 0.0;
-      const double incs = wave_inclusive_scan(ts);
-      const unsigned long long hit = __ballot(lane < kSlabs && base + incs > target);
-      const unsigned long long pos = __ballot(lane < kSlabs && ts > 0.0);
-      const int sl = hit ? __ffsll(hit) - 1 : (pos ? 63 - __clzll(pos) : kSlabs - 1);
-      base += __shfl(incs - ts, sl, kWave);
+      const int ch = sel / kSlabs, sl = sel - ch * kSlabs;
       // slab bounds: the vector body starts at the first 16-byte aligned element
       const int64_t e0 = (int64_t)ch * chunk_elems;
       const int64_t e1 = min((int64_t)V, e0 + (int64_t)chunk_elems);
