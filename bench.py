@@ -27,7 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-EVENT_EVERY = 8
+EVENT_EVERY = 16
 
 # HBM bytes per smcsd_verify call (k_lse_partials + k_smc_finalize) on c3_batched, from two
 # rocprofv3 passes (FETCH_SIZE, WRITE_SIZE) scaled by the same counters on a 1 GiB device

@@ -139,6 +139,10 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
     wb.scal[0] = *free_top;
     wb.scal[3] = C;
   }
+  // fused resample: the prompt's log-weights are loaded before anything else (loads
+  // complete in order, so the resample below then waits for them alone, not for the table
+  // prefetch)
+  const float lw0 = fr.lw && N <= kWave && tid < N ? fr.lw[row0 + tid] : 0.0f;
   // the ancestor row and the first column tile of the old tables are read whether or not
   // the prompt resampled, so all of this workgroup's first loads overlap
   const int W = max(1, min(nb_old, kKvTileInts / N));
@@ -156,7 +160,7 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
     __shared__ int sRes;
     if (N <= kWave) {
       if (tid < kWave) {
-        const int d = resample_prompt_wave(fr.lw + row0, N, fr.tau, fr.seed, b, fr.step,
+        const int d = resample_prompt_wave(lw0, fr.lw + row0, N, fr.tau, fr.seed, b, fr.step,
                                            fr.anc + row0, fr.ess + b, fr.res + b, status, a);
         if (tid == 0) sRes = d;
       }

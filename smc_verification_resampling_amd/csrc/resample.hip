@@ -27,8 +27,11 @@ __global__ __launch_bounds__(kWave * kResWaves) void k_resample_wave(
     int32_t *status) {
   const int b = blockIdx.x * kResWaves + threadIdx.x / kWave;
   if (b >= B) return;  // a whole wave: no barrier below
-  resample_prompt_wave(lw + (int64_t)b * N, N, tau, seed, b, step, anc + (int64_t)b * N, ess + b,
-                       resampled + b, status, nullptr);
+  const int lane = threadIdx.x % kWave;
+  float *lwb = lw + (int64_t)b * N;
+  const float x = lane < N ? lwb[lane] : 0.0f;
+  resample_prompt_wave(x, lwb, N, tau, seed, b, step, anc + (int64_t)b * N, ess + b, resampled + b,
+                       status, nullptr);
 }
 
 hipError_t launch_resample(float *lw, int B, int N, float tau, uint64_t seed, uint64_t step,

@@ -20,15 +20,16 @@ namespace smcsd {
 constexpr int kResBlock = 256;
 
 // By one wave, N <= kWave: everything in registers and lane shuffles.  Every lane of the
-// wave calls it; lanes >= N idle.  Outputs of prompt b: ab[N] ancestors, *essb, *resb, the
-// reset of lwb; sa (nullable) gets the ancestors too.  Returns the decision (every lane).
-__device__ __forceinline__ int resample_prompt_wave(float *__restrict__ lwb, int N, float tau,
-                                                    uint64_t seed, int b, uint64_t step,
+// wave calls it with x = lwb[lane] already loaded (any value for lanes >= N, which idle), so
+// a caller can issue that load early.  Outputs of prompt b: ab[N] ancestors, *essb, *resb,
+// the reset of lwb; sa (nullable) gets the ancestors too.  Returns the decision (every lane).
+__device__ __forceinline__ int resample_prompt_wave(float x_in, float *__restrict__ lwb, int N,
+                                                    float tau, uint64_t seed, int b, uint64_t step,
                                                     int32_t *__restrict__ ab, float *essb,
                                                     int32_t *resb, int32_t *status, int32_t *sa) {
   const int lane = threadIdx.x % kWave;
   const bool act = lane < N;
-  const float x = act ? lwb[lane] : kNegInf;
+  const float x = act ? x_in : kNegInf;
   int bad = act && isnan(x);
   float m = act && !isnan(x) ? x : kNegInf;
 #pragma unroll
