@@ -90,7 +90,7 @@ def main():
     args = _parse()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the verify / resample / KV path shards by prompt "
-              "with no exchange, and this build runs on a single MI355X (got --gpus %d)"
+              "with no exchange, so one GPU's figure is the one measured (got --gpus %d)"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
 
