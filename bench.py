@@ -35,10 +35,10 @@ EVENT_EVERY = 16
 # only for the kernel sources they were taken on: any change to them reports null.
 VERIFY_TRAFFIC = {
     "workload": "c3_batched",
-    "bytes": 1186176667,
+    "bytes": 1186197273,
     "sources": {
         "smc_verification_resampling_amd/csrc/verify.hip":
-            "9addd32b66f2c36c80b54895e0e836f5adf44f1228051be02a47003128bfa975",
+            "e8fe52deeba4395302cab76af9b1cc424bacb029a6e3c5d319dd55d534a66742",
         "smc_verification_resampling_amd/csrc/device.hpp":
             "4edde2c3edddba0bcfb398a012d90b9a18224f38e37bd532b4ecce58691e1159",
         "smc_verification_resampling_amd/csrc/internal.hpp":

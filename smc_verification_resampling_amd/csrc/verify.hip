@@ -164,12 +164,19 @@ __device__ __forceinline__ int slab_of(int64_t v, int64_t a0) {
   return v < a0 ? 0 : (int)min((int64_t)kSlabs - 1, (v - a0) / kSlabElems<DT>);
 }
 
-// Tiles: first the rows other than the bonus row (nb_per_seq per sequence: the K target
-// rows, then the K draft rows unless the draft's log q is given) in chunks of
-// kBigGroups * chunk_elems, then the bonus rows in chunks of chunk_elems (one unrolled
-// step each).  Partials of row (g, slot) start at part[(g * R + slot) * chunks].
+// Tiles: the rows other than the bonus row (nb_per_seq per sequence: the K target rows,
+// then the K draft rows unless the draft's log q is given) in chunks of
+// kBigGroups * chunk_elems, and the bonus rows in chunks of chunk_elems (one unrolled step
+// each), in the order described at the tile loop.  Tile indices below ntiles_big are big
+// tiles, the rest bonus tiles.  Partials of row (g, slot) start at
+// part[(g * R + slot) * chunks].
 // RACE: the bonus tiles write the winner of their race to race[g * chunks + ch] as
 // (key bits, id) instead of slab sums.
+// Bonus tiles held back to the end of the LSE pass (inverse-CDF mode): about half of one
+// full set of resident workgroups (5 per CU on 256 CUs); measured at C3 and C5 against
+// 0, 160, 320, 1280 and 2560.
+constexpr int kTailBonusTiles = 640;
+
 template <int DT, bool RACE>
 __global__ __launch_bounds__(kStreamBlock) void k_lse_partials(RowMap rm, int nseq, int V,
                                                                 int chunk_elems, int chunks,
@@ -191,18 +198,23 @@ __global__ __launch_bounds__(kStreamBlock) void k_lse_partials(RowMap rm, int ns
   const int R = 2 * K + 1;
   const int tid = threadIdx.x;
   const int64_t ntiles_big = ntiles - (int64_t)nseq * chunks;
+  // Tile order: the bonus rows' one-step tiles spread evenly among the big tiles (tile t
+  // is a bonus tile when floor(t * nB1 / n1) steps up at t), except the last M, which run
+  // at the very end: small tiles even out the kernel's tail.  In race mode the bonus tiles
+  // are ALU-heavy and none is held back, so all their arithmetic overlaps the streaming.
+  const int64_t nB = ntiles - ntiles_big;
+  const int64_t M = min(nB, (int64_t)(RACE ? 0 : kTailBonusTiles));
+  const int64_t n1 = ntiles - M, nB1 = nB - M;
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    // the big tiles of the other rows first, the bonus rows' one-step tiles last: small
-    // tiles even out the kernel's tail.  In race mode the bonus tiles are ALU-heavy and are
-    // spread evenly among the big tiles instead, so their arithmetic overlaps the others'
-    // streaming: tile t is a bonus tile when floor(t * nB / ntiles) steps up at t.
-    int64_t tt = t;
-    bool isb = t >= ntiles_big;
-    if (RACE) {
-      const int64_t nB = ntiles - ntiles_big;
-      const int64_t kb = t * nB / ntiles, kb1 = (t + 1) * nB / ntiles;
+    int64_t tt;
+    bool isb;
+    if (t < n1) {
+      const int64_t kb = t * nB1 / n1, kb1 = (t + 1) * nB1 / n1;
       isb = kb1 > kb;
       tt = isb ? ntiles_big + kb : t - kb;
+    } else {
+      isb = true;
+      tt = ntiles_big + nB1 + (t - n1);
     }
     int g, slot, ch;
     int64_t ce;
