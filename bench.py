@@ -40,7 +40,7 @@ VERIFY_TRAFFIC = {
         "smc_verification_resampling_amd/csrc/verify.hip":
             "e8fe52deeba4395302cab76af9b1cc424bacb029a6e3c5d319dd55d534a66742",
         "smc_verification_resampling_amd/csrc/device.hpp":
-            "4edde2c3edddba0bcfb398a012d90b9a18224f38e37bd532b4ecce58691e1159",
+            "bef1fbbb27e6c6f8f8a934f045b612c44afb16b9277e83a74e1d3a4e06dd55cd",
         "smc_verification_resampling_amd/csrc/internal.hpp":
             "4beeaced470350a87cc377eb863c14b8a32fc382d92e8c2b0f371a6093494092",
     },

@@ -301,24 +301,4 @@ __device__ __forceinline__ T block_sum(T v, T *lds) {
   return tot;
 }
 
-// Sum (or count) of p[lo, hi) with kBatch loads in flight per thread: every load of a
-// batch is issued at a clamped in-bounds index and masked afterwards, so the compiler emits
-// straight-line loads instead of a branch and a wait per element.  Needs hi > lo or no call.
-template <int kBatch, typename T, typename Acc, typename Fn>
-__device__ __forceinline__ Acc batched_reduce(const T *p, int64_t lo, int64_t hi, Acc acc, Fn f) {
-  for (int64_t b = lo; b < hi; b += kBatch) {
-    T v[kBatch];
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) v[i] = p[min(b + i, hi - 1)];
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i)
-      if (b + i < hi) acc = f(acc, v[i]);
-  }
-  return acc;
-}
-
-__device__ __forceinline__ void flag(int32_t *status, int32_t bits) {
-  if (bits) atomicOr(status, bits);
-}
-
 }  // namespace smcsd
