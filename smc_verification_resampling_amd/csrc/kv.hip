@@ -11,8 +11,10 @@
 //     increments are performed (waited for, then a barrier) before any decrement, so a
 //     block that stays referenced never reaches 0, and the decrement that brings a count
 //     to 0 marks the block in a freed bitmap and counts it in its group of 8192 ids,
-//     exactly once.  Then the gathered tables and the copy-on-write decision for the
-//     partial tail.
+//     exactly once.  With at most 16 particles one thread holds a whole column; it issues
+//     the column's increments and then its decrements with no wait, since one thread's
+//     atomics on an address take effect in program order.  Then the gathered tables and
+//     the copy-on-write decision for the partial tail.
 //   * k_kv_pop_fast (up to 8192 sequences), one thread per bitmap word and one per
 //     sequence: every workgroup first forms the group-count prefix and the copy-on-write
 //     prefix itself; a freed block's rank in ascending id order fixes its stack position
@@ -35,7 +37,8 @@ constexpr int kStage = 16;         // table loads in flight per thread while sta
 constexpr int kNegBatch = 4;       // decrements in flight per thread
 constexpr int kHash = 2 * kMaxN;   // open-addressing table of the tail blocks (load <= 1/2)
 constexpr int kSeg = 16;           // table rows one thread walks down a column
-constexpr int kPre = kKvTileInts / kKvBlock;  // first-tile entries each thread loads up front
+// first-tile entries each prefetching thread loads up front (enough for three waves)
+constexpr int kPre = (kKvTileInts + kKvBlock - kWave - 1) / (kKvBlock - kWave);
 
 // Wait until every memory operation this wave issued (atomics included) has completed.
 __device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
@@ -139,20 +142,26 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
     wb.scal[0] = *free_top;
     wb.scal[3] = C;
   }
-  // fused resample: the prompt's log-weights are loaded before anything else (loads
-  // complete in order, so the resample below then waits for them alone, not for the table
-  // prefetch)
-  const float lw0 = fr.lw && N <= kWave && tid < N ? fr.lw[row0 + tid] : 0.0f;
   // the ancestor row and the first column tile of the old tables are read whether or not
-  // the prompt resampled, so all of this workgroup's first loads overlap
+  // the prompt resampled, so all of this workgroup's first loads overlap.  With the fused
+  // one-wave resample, wave 0 loads only the prompt's log-weights and the other waves take
+  // its share of the tile: the load counter is per wave, so wave 0's resample then waits
+  // for its own load alone while the tile is still arriving.
+  const bool split = fr.lw && N <= kWave;
+  const float lw0 = split && tid < N ? fr.lw[row0 + tid] : 0.0f;
+  const int pthr = split ? kKvBlock - kWave : kKvBlock;  // threads that prefetch
+  const int pid = split ? tid - kWave : tid;              // this one's index among them
   const int W = max(1, min(nb_old, kKvTileInts / N));
   const int w0 = min(W, nb_old), nw0 = N * w0;
   int32_t pre[kPre];
 #pragma unroll
   for (int k = 0; k < kPre; ++k) {
-    const int e = min(tid + k * kKvBlock, max(nw0 - 1, 0));
-    const int j = e / max(w0, 1), s = e - j * max(w0, 1);
-    pre[k] = nw0 > 0 ? T[(row0 + j) * M_cap + s] : 0;
+    const int e = pid + k * pthr;
+    pre[k] = 0;
+    if (pid >= 0 && e < nw0) {
+      const int j = e / w0, s = e - j * w0;
+      pre[k] = T[(row0 + j) * M_cap + s];
+    }
   }
   int res;
   if (fr.lw) {
@@ -199,9 +208,9 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
       if (s0 == 0) {
 #pragma unroll
         for (int k = 0; k < kPre; ++k) {
-          const int e = tid + k * kKvBlock;
+          const int e = pid + k * pthr;
           const int j = e / w, s = e - j * w;
-          if (e < nw) tile[j * W + s] = pre[k];
+          if (pid >= 0 && e < nw) tile[j * W + s] = pre[k];
         }
       }
       for (int e0 = tid; s0 > 0 && e0 < nw; e0 += kKvBlock * kStage) {
@@ -254,6 +263,37 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
             if (j0 + k < j1) tail_old[j0 + k] = v[k];
         }
         if (nseg > 1 && colu[s]) continue;
+        if (nseg == 1) {
+          // the whole column is in this thread, and a thread's atomics on one address take
+          // effect in program order: its increments, then at once its decrements, leave no
+          // block at a transient 0 and need no wait between them.  accs[k] is the change of
+          // the run that ends at row k (0 elsewhere).
+          int accs[kSeg], olds[kSeg];
+          int run = 0;
+#pragma unroll
+          for (int k = 0; k < kSeg; ++k) {
+            run += k < N ? d[k] : 0;
+            const bool end = k < N && (k == N - 1 || (k + 1 < kSeg && v[k + 1] != v[k]));
+            accs[k] = end ? run : 0;
+            if (end) run = 0;
+            if (accs[k] != 0 && (v[k] < 0 || v[k] >= P)) {
+              atomicOr(&sFlags, SMCSD_ST_BAD_INPUT);
+              accs[k] = 0;
+            }
+          }
+#pragma unroll
+          for (int k = 0; k < kSeg; ++k)
+            if (accs[k] > 0) atomicAdd(&rc[v[k]], accs[k]);
+#pragma unroll
+          for (int k = 0; k < kSeg; ++k) olds[k] = accs[k] < 0 ? atomicAdd(&rc[v[k]], accs[k]) : 1;
+#pragma unroll
+          for (int k = 0; k < kSeg; ++k)
+            if (accs[k] < 0 && olds[k] + accs[k] == 0) {
+              atomicOr(&bitmap[v[k] >> 5], 1u << (v[k] & 31));
+              atomicAdd(&gcount[v[k] / kKvGroupBlocks], 1);
+            }
+          continue;
+        }
         int32_t blk = v[0];
         int acc = 0;
         auto flush = [&]() {
@@ -275,7 +315,7 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
         }
         flush();
       }
-      wait_memory();  // increments performed before any decrement
+      if (nseg > 1) wait_memory();  // increments performed before any decrement
       __syncthreads();
       const int nneg = sNeg;
       for (int l0 = tid; l0 < nneg; l0 += kKvBlock * kNegBatch) {
