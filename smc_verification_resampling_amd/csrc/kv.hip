@@ -206,11 +206,12 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
     for (int s0 = 0; s0 < nb_old; s0 += W) {
       const int w = min(W, nb_old - s0), nw = N * w;
       if (s0 == 0) {
+        // the first tile is W columns wide (W = min(nb_old, kKvTileInts / N) = w), so entry
+        // e = j * w + s sits at tile[e]: no division on this path
 #pragma unroll
         for (int k = 0; k < kPre; ++k) {
           const int e = pid + k * pthr;
-          const int j = e / w, s = e - j * w;
-          if (pid >= 0 && e < nw) tile[j * W + s] = pre[k];
+          if (pid >= 0 && e < nw) tile[e] = pre[k];
         }
       }
       for (int e0 = tid; s0 > 0 && e0 < nw; e0 += kKvBlock * kStage) {
