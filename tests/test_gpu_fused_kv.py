@@ -3,8 +3,8 @@
 Two copies of the same state run the same rounds, one through the fused entry point and
 one through the two separate calls; every output must be bit-identical after every
 round: ancestors, ESS, decisions, reset log-weights, block tables, refcounts, free stack,
-copy-on-write list and status.  Covers the one-wave resample (N <= 64) and the workgroup
-resample (N > 64), shared and unshared prefixes, prompts with degenerate (NaN) weights,
+copy-on-write list and status.  Covers the one-wave resample (N <= 64: one column segment
+for N <= 16, several above) and the workgroup resample (N > 64), shared and unshared prefixes, prompts with degenerate (NaN) weights,
 the many-sequence KV path, and the two forms alternating on one workspace.  The first
 round of each case is also checked against the oracle.
 """
@@ -67,8 +67,8 @@ def _equal(a, b):
     return None
 
 
-@pytest.mark.parametrize("B,N,shared", [(3, 16, True), (2, 5, False), (2, 128, True),
-                                        (40, 256, False)])
+@pytest.mark.parametrize("B,N,shared", [(3, 16, True), (2, 5, False), (3, 40, True), (2, 64, False),
+                                        (2, 128, True), (40, 256, False)])
 def test_fused_equals_separate_calls(B, N, shared):
     bs, K, ctx0, rounds = 4, 2, 10, 6
     R = K + 1

@@ -155,3 +155,31 @@ def test_race_masked_one_hot_empty_and_nan_rows():
                sm.MODE_SMC_RACE)
     assert got["status"] & sm.ST_NAN_INPUT
     assert got["tokens"][4, K] == -1
+
+
+def test_race_mode_with_the_drafts_log_q():
+    """Race mode with logq_in (the draft rows not read) against race mode reading them:
+    same tokens, log-weights within rounding (the tile order differs between the two)."""
+    g = torch.Generator(device="cuda").manual_seed(31)
+    B, N, K, V, T = 2, 16, 4, 70001, 0.8
+    S = B * N
+    tgt = (torch.randn((S, K + 1, V), generator=g, device="cuda") * 2).to(torch.bfloat16)
+    drf = (tgt[:, :K].float() + torch.randn((S, K, V), generator=g, device="cuda")).to(torch.bfloat16)
+    toks = torch.randint(0, V, (S, K), generator=g, device="cuda", dtype=torch.int32)
+    ref = oracle.verify_smc(_host(tgt), _host(drf), toks.cpu().numpy(), float(np.float32(T)), 1.0,
+                            6, 2, np.zeros(S), bonus="race")
+    lq = torch.from_numpy(ref["logq"].astype(np.float32)).cuda()
+    outs = []
+    for use in (False, True):
+        lw = torch.zeros(S, device="cuda")
+        out, st = _i32(S, K + 1), _i32(1)
+        ws = sm.alloc_workspace(sm.OP_VERIFY_SMC, B, N, K, V)
+        sm.verify(tgt, None if use else drf, toks, B, N, K, V, T, 1.0, sm.MODE_SMC_RACE, 6, 2, out,
+                  st, ws, log_weights=lw, logq_in=lq if use else None)
+        torch.cuda.synchronize()
+        assert int(st.cpu()[0]) == 0
+        outs.append((out.cpu().numpy(), lw.cpu().numpy()))
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.max(np.abs(outs[0][1] - outs[1][1])) < 1e-4
+    flagged = ref["margin"] < MARGIN
+    assert np.array_equal(outs[1][0][~flagged], ref["tokens"][~flagged])
