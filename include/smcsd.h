@@ -34,8 +34,9 @@
  * a uniform is (word >> 8) * 2^-24.  Tags: 1 bonus token (index = sequence g),
  * 2 resampling offset (index = prompt b), 3 | (k/4) << 8 SpS acceptance of draft k
  * (word k mod 4), 4 SpS final token, 5 | pos << 8 draft token at draft position pos
- * (index = row).  Results depend only on (inputs, seed, step):
- * runs are bit-reproducible and resumable.
+ * (index = row), 6 | (v/4) << 8 the race-mode clock of vocabulary entry v (word v mod 4,
+ * index = sequence g; that clock uses (floor(word / 2^9) + 1/2) * 2^-23).  Results depend only
+ * on (inputs, seed, step): runs are bit-reproducible and resumable.
  */
 #ifndef SMCSD_H
 #define SMCSD_H
