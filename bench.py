@@ -38,7 +38,7 @@ VERIFY_TRAFFIC = {
     "bytes": 1186197273,
     "sources": {
         "smc_verification_resampling_amd/csrc/verify.hip":
-            "e8fe52deeba4395302cab76af9b1cc424bacb029a6e3c5d319dd55d534a66742",
+            "dde3d0177d8e2356258941afc1593407614ad0fa43bf47be4558b290b8e4df6e",
         "smc_verification_resampling_amd/csrc/device.hpp":
             "bef1fbbb27e6c6f8f8a934f045b612c44afb16b9277e83a74e1d3a4e06dd55cd",
         "smc_verification_resampling_amd/csrc/internal.hpp":

@@ -821,10 +821,7 @@ __global__ __launch_bounds__(kWave) void k_sps_decide(
 }
 
 // Residual element values, identical in the pass and in the re-read.
-template <int DT>
-__device__ __forceinline__ float sps_p(const char *row, int64_t v, float c, float Mc, float inv) {
-  return fast_exp2(fmaf(Elt<DT>::load(row, v), c, -Mc)) * inv;
-}
+constexpr int kResidBatch = 32;
 
 template <int DT>
 __global__ __launch_bounds__(kStreamBlock) void k_sps_residual(
@@ -843,10 +840,25 @@ __global__ __launch_bounds__(kStreamBlock) void k_sps_residual(
     const int64_t e0 = (int64_t)ch * chunk_elems;
     const int64_t e1 = min((int64_t)V, e0 + (int64_t)chunk_elems);
     float srho = 0.0f, sp = 0.0f;
-    for (int64_t v = e0 + tid; v < e1; v += kStreamBlock) {
-      const float p = sps_p<DT>(prow, v, c, nm.x, nm.y);
-      sp += p;
-      if (qrow) srho += fmaxf(p - sps_p<DT>(qrow, v, c, nm.z, nm.w), 0.0f);
+    // kResidBatch strided elements per thread per pass, every load issued before the first
+    // use (the two rows may differ in alignment, so the loads are scalar); the sums run in
+    // the same element order as a one-at-a-time loop
+    for (int64_t v0 = e0 + tid; v0 < e1; v0 += (int64_t)kStreamBlock * kResidBatch) {
+      float xp[kResidBatch], xq[kResidBatch];
+#pragma unroll
+      for (int u = 0; u < kResidBatch; ++u) {
+        const int64_t v = min(v0 + (int64_t)u * kStreamBlock, e1 - 1);  // clamped: in bounds
+        xp[u] = Elt<DT>::load(prow, v);
+        xq[u] = qrow ? Elt<DT>::load(qrow, v) : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < kResidBatch; ++u) {
+        if (v0 + (int64_t)u * kStreamBlock < e1) {
+          const float p = fast_exp2(fmaf(xp[u], c, -nm.x)) * nm.y;
+          sp += p;
+          if (qrow) srho += fmaxf(p - fast_exp2(fmaf(xq[u], c, -nm.z)) * nm.w, 0.0f);
+        }
+      }
     }
     srho = block_sum<float, kStreamBlock>(srho, red);
     sp = block_sum<float, kStreamBlock>(sp, red);
