@@ -4,7 +4,7 @@ Argument marshalling only: every step of the path runs in the library's HIP kern
 Tensors must be device (HIP) tensors; this module checks placement, dtype, contiguity
 and sizes so that no host pointer or short buffer reaches a kernel, passes raw pointers
 and the current torch stream, and turns negative return codes into ``SmcsdError``.
-There is no fallback: if the library is not built, importing a call raises.
+There is no fallback: if the library is not built, every call raises.
 """
 from __future__ import annotations
 
@@ -133,7 +133,9 @@ def verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: Op
            out_logq=None, out_lse=None, lse_in=None, seq_step: int = 1,
            row_stride: Optional[int] = None, stream=None, logq_in=None) -> None:
     """smcsd_verify.  target [*, K+1, row_stride], draft [*, K, row_stride] (bf16 or fp32).
-    With logq_in [*, K] fp32 (the draft's log q of its tokens) draft may be None."""
+    mode: MODE_SMC (bonus by inverse CDF), MODE_SMC_RACE (bonus by the exponential race)
+    or MODE_SPS.  With logq_in [*, K] fp32 (the draft's log q of its tokens; SMC modes)
+    draft may be None."""
     if target.dtype not in _DT:
         raise SmcsdError("logits must be bfloat16 or float32")
     rs = V if row_stride is None else int(row_stride)
