@@ -460,7 +460,20 @@ def cpu_baseline(cfg, sets, budget_s, bonus="cdf"):
                       reps, bonus, nsamp, S, S // nsamp, B),
         "single_thread_value": round(1.0 / per_step1, 4),
         "single_thread_reps": reps1,
+        "cpu_model": _cpu_model(),
+        "host_cpus": os.cpu_count(),
     }
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 if __name__ == "__main__":
