@@ -140,6 +140,15 @@ def test_philox_bit_exact_against_oracle():
     assert np.array_equal(got, ref)
 
 
+def test_philox_known_answer_vectors_on_device():
+    from tests.test_oracle_rng import load_kat
+    ctr, key, ref = load_kat()
+    out = _i32(len(ctr), 4)
+    sm.philox4x32_10(torch.from_numpy(ctr.view(np.int32)).cuda(),
+                     torch.from_numpy(key.view(np.int32)).cuda(), out)
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), ref)
+
+
 @pytest.mark.parametrize("N", [1, 2, 3, 64, 1000, 1024])
 def test_resample_particle_counts(N):
     B = 7

@@ -82,10 +82,12 @@ CASES = [
     ("uniform loses its top bit", "(double)(out[word & 3] >> 8)", "(double)(out[word & 3] >> 9)",
      [lambda: rng_t.test_uniform_chi_square(O)]),
     ("Philox key bump uses the wrong Weyl constant", "k0 += weyl0;", "k0 += weyl1;",
-     [lambda: rng_t.test_philox_matches_rocrand_block_function(O)] if NEEDS_PROBE else []),
+     [lambda: rng_t.test_philox_known_answer_vectors(O)]
+     + ([lambda: rng_t.test_philox_matches_rocrand_block_function(O)] if NEEDS_PROBE else [])),
     ("Philox round mixes the wrong high half", "uint32_t n0 = hi1 ^ c1 ^ k0;",
      "uint32_t n0 = hi0 ^ c1 ^ k0;",
-     [lambda: rng_t.test_philox_matches_rocrand_block_function(O)] if NEEDS_PROBE else []),
+     [lambda: rng_t.test_philox_known_answer_vectors(O)]
+     + ([lambda: rng_t.test_philox_matches_rocrand_block_function(O)] if NEEDS_PROBE else [])),
     ("counter words t_hi and tag swapped",
      "uint32_t ctr[4] = {index, (uint32_t)t, (uint32_t)(t >> 32), tag};",
      "uint32_t ctr[4] = {index, (uint32_t)t, tag, (uint32_t)(t >> 32)};",
