@@ -97,6 +97,20 @@ __device__ __forceinline__ uint4 load_stream(const uint4 *p) {
   return make_uint4(r.x, r.y, r.z, r.w);
 }
 
+// The same streaming load through a buffer resource: the resource holds a wave-uniform
+// base and size, the lane supplies a 32-bit byte offset and the instruction a uniform one,
+// so a group of loads needs no per-lane 64-bit address arithmetic.  Offsets past the
+// resource's size would read zeros (no fault); callers keep every offset inside it.
+constexpr int kBufRsrcWord3 = 0x00020000;  // raw (untyped) buffer, 32-bit data format
+constexpr int kBufNonTemporal = 2;         // cache-policy operand: nt
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(const void *base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, kBufRsrcWord3);
+}
+__device__ __forceinline__ uint4 load_stream(__amdgpu_buffer_rsrc_t rs, int lane_off, int uni_off) {
+  const u32x4_t r = __builtin_amdgcn_raw_buffer_load_b128(rs, lane_off, uni_off, kBufNonTemporal);
+  return make_uint4(r.x, r.y, r.z, r.w);
+}
+
 // -inf in every element of a 16-byte vector (fills the lanes past a row's end)
 template <int DT> struct NegInfVec;
 template <> struct NegInfVec<SMCSD_DTYPE_F32> {

@@ -266,12 +266,21 @@ __global__ __launch_bounds__(kStreamBlock) void k_lse_partials(RowMap rm, int ns
       for (int u = 0; u < kSlabs; ++u) sSlabT[tid][u] = 0.0f;
     }
     const uint4 *vp = reinterpret_cast<const uint4 *>(row + a0 * E::kBytes);
-    for (int64_t v0 = 0; v0 < nvec; v0 += (int64_t)kStreamBlock * kStreamUnroll) {
+    constexpr int64_t kGroupVecs = (int64_t)kStreamBlock * kStreamUnroll;
+    for (int64_t v0 = 0; v0 < nvec; v0 += kGroupVecs) {
       uint4 buf[kStreamUnroll];
+      if (v0 + kGroupVecs <= nvec) {
+        // a whole group: no per-load bounds test or -inf fill, and buffer loads whose
+        // offsets (lane, then load) stay inside the group's kGroupVecs * 16 bytes
+        const __amdgpu_buffer_rsrc_t rs = stream_rsrc(vp + v0, (int)(kGroupVecs * 16));
 #pragma unroll
-      for (int u = 0; u < kStreamUnroll; ++u) {
-        const int64_t v = v0 + u * kStreamBlock + tid;
-        buf[u] = v < nvec ? load_stream(vp + v) : NegInfVec<DT>::get();
+        for (int u = 0; u < kStreamUnroll; ++u) buf[u] = load_stream(rs, tid * 16, u * kStreamBlock * 16);
+      } else {
+#pragma unroll
+        for (int u = 0; u < kStreamUnroll; ++u) {
+          const int64_t v = v0 + u * kStreamBlock + tid;
+          buf[u] = v < nvec ? load_stream(vp + v) : NegInfVec<DT>::get();
+        }
       }
       if (RACE && bonus && (a0 & 3) == 0) {
 #pragma unroll
