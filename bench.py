@@ -35,12 +35,12 @@ EVENT_EVERY = 16
 # only for the kernel sources they were taken on: any change to them reports null.
 VERIFY_TRAFFIC = {
     "workload": "c3_batched",
-    "bytes": 1186197273,
+    "bytes": 1186198308,
     "sources": {
         "smc_verification_resampling_amd/csrc/verify.hip":
-            "dde3d0177d8e2356258941afc1593407614ad0fa43bf47be4558b290b8e4df6e",
+            "b738127307c8a3fd278318af9c7adee375abe11803cb494e3f6a77a0d609b5e9",
         "smc_verification_resampling_amd/csrc/device.hpp":
-            "bef1fbbb27e6c6f8f8a934f045b612c44afb16b9277e83a74e1d3a4e06dd55cd",
+            "e0711ab8add5e1eb90bd6f0e5f4aead04257c662e1daba0188a7e7dcf3c5508c",
         "smc_verification_resampling_amd/csrc/internal.hpp":
             "4beeaced470350a87cc377eb863c14b8a32fc382d92e8c2b0f371a6093494092",
     },
