@@ -358,12 +358,17 @@ struct RowNorm {
   int flags;
 };
 
+// p points to LDS or to global memory; a caller passes a pointer of one known kind (not a
+// select between the two), so the loads are LDS or global loads, not flat ones, and the
+// unrolled loops keep several in flight.
 __device__ __forceinline__ RowNorm row_norm(const float2 *p, int chunks, float c) {
   float M = kNegInf;
+#pragma unroll 8
   for (int i = 0; i < chunks; ++i) M = fmaxf(M, p[i].x);
   RowNorm r{};
   r.Mc = M == kNegInf ? 0.0f : __fmul_rn(M, c);
   double S = 0.0;
+#pragma unroll 8
   for (int i = 0; i < chunks; ++i) S += chunk_term(p[i], c, r.Mc);
   r.S = S;
   r.L2 = (double)r.Mc + log2(S);
@@ -579,49 +584,66 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
   if (tid == 0) sFlags = 0;
   const float lw_old = tid == 0 && lw ? lw[g] : 0.0f;  // loaded early: used only at the end
 
-  // One round of loads up front: the draft tokens, this sequence's chunk pairs (staged
-  // in LDS), then the draft-token logits.
+  // One round of loads, all issued before any is used: the draft tokens (and a given log
+  // q), this sequence's chunk pairs and slab sums into registers, the draft-token logits
+  // as soon as the tokens are in, then the LDS staging.  The token and logit loads are
+  // made by every lane at clamped, valid addresses (no divergent branch around a load, so
+  // each use waits for its own load only); the register staging has uniform bounds.
+  constexpr int kPartPer = kMaxPartLds / kSmcFinalBlock;
+  constexpr int kSubPer = kMaxSubLds / kSmcFinalBlock;
   const int64_t src = (int64_t)g * rm.seq_step;
+  const bool tok_lane = tid < 2 * K;
+  const int kk = tok_lane ? (tid < K ? tid : tid - K) : 0;
+  const int slot = tid < K ? kk : K + 1 + kk;
   int32_t x = 0;
-  float xv = 0.0f;
-  int slot = 0;
   float lq_given = 0.0f;
-  if (tid < 2 * K) {
-    const int k = tid < K ? tid : tid - K;
-    slot = tid < K ? k : K + 1 + k;
-    x = draft_tokens[src * K + k];
-    if (logq_in && tid >= K) lq_given = logq_in[src * K + k];
+  if (K > 0) {
+    x = draft_tokens[src * K + kk];
+    if (logq_in) lq_given = logq_in[src * K + kk];
   }
   const int npart = R * chunks;
   const bool part_in_lds = npart <= kMaxPartLds;
   const float2 *gpart = part + (int64_t)g * npart;
-  if (part_in_lds)
-    for (int i = tid; i < npart; i += kSmcFinalBlock) sPart[i] = gpart[i];
+  float2 pr[kPartPer];
+  if (part_in_lds) {
+#pragma unroll
+    for (int j = 0; j < kPartPer; ++j)
+      if (j * kSmcFinalBlock < npart) pr[j] = gpart[min(tid + j * kSmcFinalBlock, npart - 1)];
+  }
   const int nsub = chunks * kSlabs;
   const bool sub_in_lds = nsub <= kMaxSubLds;
   const float *gsub = sub + (int64_t)g * nsub;
-  if (!RACE && sub_in_lds)
-    for (int i = tid; i < nsub; i += kSmcFinalBlock) sSub[i] = gsub[i];
-  if (tid < (logq_in ? K : 2 * K) && x >= 0 && x < V) xv = E::load(rm.row(g, slot), x);
+  float sr[kSubPer];
+  if (!RACE && sub_in_lds) {
+#pragma unroll
+    for (int j = 0; j < kSubPer; ++j)
+      if (j * kSmcFinalBlock < nsub) sr[j] = gsub[min(tid + j * kSmcFinalBlock, nsub - 1)];
+  }
+  const bool xv_lane = tid < (logq_in ? K : 2 * K) && x >= 0 && x < V;
+  const float xv_raw = E::load(rm.row(g, xv_lane ? slot : 0), xv_lane ? x : 0);
+  if (part_in_lds) {
+#pragma unroll
+    for (int j = 0; j < kPartPer; ++j)
+      if (tid + j * kSmcFinalBlock < npart) sPart[tid + j * kSmcFinalBlock] = pr[j];
+  }
+  if (!RACE && sub_in_lds) {
+#pragma unroll
+    for (int j = 0; j < kSubPer; ++j)
+      if (tid + j * kSmcFinalBlock < nsub) sSub[tid + j * kSmcFinalBlock] = sr[j];
+  }
   __syncthreads();
+  const float xv = xv_lane ? xv_raw : 0.0f;
 
   // row normalisers: chunk pairs combined in fp64;
   // the draft rows only when their log q is not given
   if (tid < (logq_in ? K + 1 : R)) {
-    const float2 *p = (part_in_lds ? sPart : gpart) + tid * chunks;
     const int n = tid == K ? chunks : chunks_big;
-    float M = kNegInf;
-    for (int i = 0; i < n; ++i) M = fmaxf(M, p[i].x);
-    const float Mc = M == kNegInf ? 0.0f : __fmul_rn(M, c);
-    double S = 0.0;
-    for (int i = 0; i < n; ++i) S += chunk_term(p[i], c, Mc);
-    sMc[tid] = Mc;
-    sS[tid] = S;
-    sL2[tid] = (double)Mc + log2(S);
-    int fl = 0;
-    if (isnan(S) || isinf(S)) fl |= SMCSD_ST_NAN_INPUT;
-    else if (M == kNegInf) fl |= SMCSD_ST_EMPTY_ROW;
-    if (fl) atomicOr(&sFlags, fl);
+    const RowNorm rn = part_in_lds ? row_norm(sPart + tid * chunks, n, c)
+                                   : row_norm(gpart + tid * chunks, n, c);
+    sMc[tid] = rn.Mc;
+    sS[tid] = rn.S;
+    sL2[tid] = rn.L2;
+    if (rn.flags) atomicOr(&sFlags, rn.flags);
   }
   __syncthreads();
 
@@ -671,34 +693,38 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
       // term is its sum rescaled from its chunk's reference to the row's.  If rounding
       // leaves no crossing, the last slab with a positive term.
       const int lane = tid;
-      const float *sb = sub_in_lds ? sSub : gsub;
-      const float2 *pk = (part_in_lds ? sPart : gpart) + K * chunks;
       const int nsl = chunks * kSlabs;
+      const float McK = sMc[K];
       double base = 0.0, base_last = 0.0;
       int sel = -1, last = -1;
-      for (int j0 = 0; j0 < nsl && sel < 0; j0 += kWave) {
-        const int j = j0 + lane;
-        double t = 0.0;
-        if (j < nsl) {
-          const float2 p = pk[j / kSlabs];
-          if (p.x != kNegInf) t = (double)sb[j] * (double)fast_exp2(__fmul_rn(p.x, c) - sMc[K]);
+      // sb / pk both in LDS or both in global memory (never a select between the two)
+      auto scan = [&](const float *sb, const float2 *pk) {
+        for (int j0 = 0; j0 < nsl && sel < 0; j0 += kWave) {
+          const int j = j0 + lane;
+          double t = 0.0;
+          if (j < nsl) {
+            const float2 p = pk[j / kSlabs];
+            if (p.x != kNegInf) t = (double)sb[j] * (double)fast_exp2(__fmul_rn(p.x, c) - McK);
+          }
+          const double inc = wave_inclusive_scan(t);
+          const unsigned long long hit = __ballot(j < nsl && base + inc > target);
+          const unsigned long long pos = __ballot(j < nsl && t > 0.0);
+          if (pos) {
+            const int f = 63 - __clzll(pos);
+            last = j0 + f;
+            base_last = base + __shfl(inc - t, f, kWave);
+          }
+          if (hit) {
+            const int f = __ffsll(hit) - 1;
+            sel = j0 + f;
+            base += __shfl(inc - t, f, kWave);
+          } else {
+            base += __shfl(inc, kWave - 1, kWave);
+          }
         }
-        const double inc = wave_inclusive_scan(t);
-        const unsigned long long hit = __ballot(j < nsl && base + inc > target);
-        const unsigned long long pos = __ballot(j < nsl && t > 0.0);
-        if (pos) {
-          const int f = 63 - __clzll(pos);
-          last = j0 + f;
-          base_last = base + __shfl(inc - t, f, kWave);
-        }
-        if (hit) {
-          const int f = __ffsll(hit) - 1;
-          sel = j0 + f;
-          base += __shfl(inc - t, f, kWave);
-        } else {
-          base += __shfl(inc, kWave - 1, kWave);
-        }
-      }
+      };
+      if (part_in_lds && sub_in_lds) scan(sSub, sPart + K * chunks);
+      else scan(gsub, gpart + K * chunks);
       if (sel < 0) {
         sel = last >= 0 ? last : nsl - 1;
         base = last >= 0 ? base_last : base;
