@@ -35,10 +35,10 @@ EVENT_EVERY = 16
 # only for the kernel sources they were taken on: any change to them reports null.
 VERIFY_TRAFFIC = {
     "workload": "c3_batched",
-    "bytes": 1186315125,
+    "bytes": 1186314875,
     "sources": {
         "smc_verification_resampling_amd/csrc/verify.hip":
-            "8611836162a21d6460a48549b23b511f5adcde46add3f3e1c4deff9d1e8b8445",
+            "15d1adb3d89571ca412581be3c3e19d977e2f4bedd14ba77a162bab8b0fa4843",
         "smc_verification_resampling_amd/csrc/device.hpp":
             "e0711ab8add5e1eb90bd6f0e5f4aead04257c662e1daba0188a7e7dcf3c5508c",
         "smc_verification_resampling_amd/csrc/internal.hpp":

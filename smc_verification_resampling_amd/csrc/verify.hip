@@ -1015,6 +1015,38 @@ __global__ void k_philox(const uint32_t *__restrict__ ctr, const uint32_t *__res
 // ---------------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------------
+// Occupancy of the inverse-CDF LSE pass.  Its registers allow 5 workgroups (20 waves) per
+// CU; measured on the MI355X, 4 stream faster whenever rows span several tiles (B = 32,
+// N = 16, K = 4, V = 128256 bf16: verify call 186 -> 183 us; B = 8, N = 128, K = 5,
+// V = 152064: 517 -> 506 us; B = 16, N = 64, K = 8, fp32: 1325 -> 1316 us), while 3 per CU
+// is no better than 5 and 2 is 20 % slower.  The race mode (ALU-heavy bonus tiles) and a
+// launch of bonus tiles only (K = 0: the draft sampler) are faster at 5 and keep it.  The
+// limit is set through LDS: the launch asks for dynamic LDS, which the kernel never
+// touches, so that each workgroup holds just over a fifth of the CU's 160 KiB.
+constexpr size_t kLdsPerCu = 160 * 1024;
+constexpr int kLseWgPerCu = 4;
+
+struct LdsPad {
+  hipError_t err;
+  size_t bytes;
+};
+
+// Taken once per element type (a thread-safe static): the kernel's static LDS is fixed at
+// build time.
+template <int DT>
+static hipError_t lse_occupancy_pad(size_t *pad) {
+  static const LdsPad p = [] {
+    hipFuncAttributes fa{};
+    const hipError_t e =
+        hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(&k_lse_partials<DT, false>));
+    if (e != hipSuccess) return LdsPad{e, 0};
+    const size_t per_wg = kLdsPerCu / (kLseWgPerCu + 1) + 1;
+    return LdsPad{hipSuccess, per_wg > fa.sharedSizeBytes ? per_wg - fa.sharedSizeBytes : 0};
+  }();
+  *pad = p.bytes;
+  return p.err;
+}
+
 template <int DT>
 static hipError_t launch_verify_t(const VerifyArgs &a) {
   const int esz = Elt<DT>::kBytes;
@@ -1031,9 +1063,14 @@ static hipError_t launch_verify_t(const VerifyArgs &a) {
   const int nb_per_seq = a.logq_in ? K : 2 * K;
   const int64_t ntiles = (int64_t)a.nseq * (chunks + (int64_t)nb_per_seq * chunks_big);
   const unsigned grid = (unsigned)std::min<int64_t>(ntiles, (int64_t)1 << 30);
+  size_t pad = 0;
+  if (K > 0 && a.mode != SMCSD_MODE_SMC_RACE) {
+    const hipError_t e = lse_occupancy_pad<DT>(&pad);
+    if (e != hipSuccess) return e;
+  }
 
   if (a.mode == SMCSD_MODE_SMC) {
-    hipLaunchKernelGGL((k_lse_partials<DT, false>), dim3(grid), dim3(kStreamBlock), 0, a.stream, rm,
+    hipLaunchKernelGGL((k_lse_partials<DT, false>), dim3(grid), dim3(kStreamBlock), pad, a.stream, rm,
                        a.nseq, a.V, ce, chunks, chunks_big, nb_per_seq, a.c, part, sub, ntiles,
                        a.seed, a.step, race);
     hipLaunchKernelGGL((k_smc_finalize<DT, false>), dim3(a.nseq), dim3(kSmcFinalBlock), 0, a.stream,
@@ -1058,7 +1095,7 @@ static hipError_t launch_verify_t(const VerifyArgs &a) {
   float4 *norm = reinterpret_cast<float4 *>(a.ws + w.l2);
   float2 *part2 = reinterpret_cast<float2 *>(a.ws + w.part2);
   if (!a.lse_in)
-    hipLaunchKernelGGL((k_lse_partials<DT, false>), dim3(grid), dim3(kStreamBlock), 0, a.stream, rm,
+    hipLaunchKernelGGL((k_lse_partials<DT, false>), dim3(grid), dim3(kStreamBlock), pad, a.stream, rm,
                        a.nseq, a.V, ce, chunks, chunks_big, nb_per_seq, a.c, part, sub, ntiles,
                        a.seed, a.step, race);
   hipLaunchKernelGGL(k_sps_decide<DT>, dim3(a.nseq), dim3(kWave), 0, a.stream, rm, a.draft_tokens,
