@@ -17,7 +17,10 @@
  *
  * Conventions for every entry point
  *   - Array arguments are DEVICE pointers owned by the caller; the library allocates
- *     nothing, keeps no state between calls and never synchronises the stream.
+ *     nothing, keeps no state between calls and never synchronises the stream.  (The
+ *     one value it keeps is a constant of the build: the streaming kernel's static LDS
+ *     size, read once from the runtime to size the unused dynamic LDS that holds that
+ *     kernel to four workgroups per compute unit.)
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All work is
  *     enqueued on it, in call order.
  *   - Host-detectable argument errors return a negative code before anything is
