@@ -35,14 +35,14 @@ EVENT_EVERY = 16
 # only for the kernel sources they were taken on: any change to them reports null.
 VERIFY_TRAFFIC = {
     "workload": "c3_batched",
-    "bytes": 1186314875,
+    "bytes": 1186574561,
     "sources": {
         "smc_verification_resampling_amd/csrc/verify.hip":
-            "15d1adb3d89571ca412581be3c3e19d977e2f4bedd14ba77a162bab8b0fa4843",
+            "cd3fab6e0d4ab1bd39b55cd1ed84189d15b1360dd57e1cb4908c9619d4c42345",
         "smc_verification_resampling_amd/csrc/device.hpp":
             "e0711ab8add5e1eb90bd6f0e5f4aead04257c662e1daba0188a7e7dcf3c5508c",
         "smc_verification_resampling_amd/csrc/internal.hpp":
-            "4beeaced470350a87cc377eb863c14b8a32fc382d92e8c2b0f371a6093494092",
+            "eee11a3a5c7749718f84f1f816eacb03cc128d53658a1fa7ca6bf5564dac0731",
     },
 }
 

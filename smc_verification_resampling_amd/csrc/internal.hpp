@@ -14,9 +14,24 @@ constexpr int kStreamUnroll = 8;
 constexpr int kChunkElemsBf16 = 16384;
 constexpr int kChunkElemsF32 = 8192;
 constexpr int kChunkElemsMin = kChunkElemsF32;  // workspace is sized for the smaller tile
-// Rows other than the bonus row are cut into tiles of kBigGroups chunks (128 KiB): fewer
-// workgroup reductions per byte.  Their partials use the first ceil(V / big chunk) slots.
-constexpr int kBigGroups = 4;
+// Rows other than the bonus row are cut into big tiles: fewer workgroup reductions per
+// byte.  Their partials use the first ceil(V / big tile) slots.  Inverse-CDF and SpS
+// passes: kBigTileElems elements (64 KiB of bf16, 128 KiB of fp32: about four tiles per row
+// of a 128K vocabulary).  Measured on the MI355X with that pass at 4 workgroups per CU:
+// bf16 rows stream fastest in 64 KiB tiles (B = 32, N = 16, K = 4, V = 128256: 4,955
+// against 4,923 steps/s for 128 KiB; 256 KiB 4,760), fp32 rows in 128 KiB tiles
+// (B = 16, N = 64, K = 8: 719 against 712 steps/s for 64 KiB).  Race mode keeps 128 KiB
+// for both dtypes: its ALU-heavy bonus tiles, spread among the big tiles, ran 7 % slower
+// among 64 KiB bf16 tiles (4,541 against 4,894 steps/s at the B = 32 shape).
+constexpr int kBigTileElems = 32768;
+constexpr int kRaceBigTileBytes = 128 * 1024;
+constexpr int big_tile_elems(int elt_bytes, bool race) {
+  return race ? kRaceBigTileBytes / elt_bytes : kBigTileElems;
+}
+static_assert(kBigTileElems % kChunkElemsBf16 == 0 && kBigTileElems % kChunkElemsF32 == 0 &&
+                  (kRaceBigTileBytes / 2) % kChunkElemsBf16 == 0 &&
+                  (kRaceBigTileBytes / 4) % kChunkElemsF32 == 0,
+              "a big tile is a whole number of unrolled steps for both dtypes");
 
 constexpr int kMaxK = 32;
 constexpr int kMaxN = 1024;

@@ -165,8 +165,9 @@ __device__ __forceinline__ int slab_of(int64_t v, int64_t a0) {
 }
 
 // Tiles: the rows other than the bonus row (nb_per_seq per sequence: the K target rows,
-// then the K draft rows unless the draft's log q is given) in chunks of
-// kBigGroups * chunk_elems, and the bonus rows in chunks of chunk_elems (one unrolled step
+// then the K draft rows unless the draft's log q is given) in big tiles of
+// big_tile_elems(element bytes, RACE), and the bonus rows in chunks of chunk_elems (one
+// unrolled step
 // each), in the order described at the tile loop.  Tile indices below ntiles_big are big
 // tiles, the rest bonus tiles.  Partials of row (g, slot) start at
 // part[(g * R + slot) * chunks].
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(kStreamBlock) void k_lse_partials(RowMap rm, int ns
       g = (int)(r / nb_per_seq);
       const int j = (int)(r - (int64_t)g * nb_per_seq);
       slot = j < K ? j : j + 1;
-      ce = (int64_t)chunk_elems * kBigGroups;
+      ce = big_tile_elems(E::kBytes, RACE);
     }
     const char *row = rm.row(g, slot);
     const int64_t e0 = (int64_t)ch * ce;
@@ -1059,7 +1060,7 @@ static hipError_t launch_verify_t(const VerifyArgs &a) {
   float2 *part = reinterpret_cast<float2 *>(a.ws + w.part);
   float *sub = reinterpret_cast<float *>(a.ws + w.sub);
   int2 *race = reinterpret_cast<int2 *>(a.ws + w.race);
-  const int chunks_big = (int)ceil_div(a.V, (int64_t)ce * kBigGroups);
+  const int chunks_big = (int)ceil_div(a.V, big_tile_elems(esz, a.mode == SMCSD_MODE_SMC_RACE));
   const int nb_per_seq = a.logq_in ? K : 2 * K;
   const int64_t ntiles = (int64_t)a.nseq * (chunks + (int64_t)nb_per_seq * chunks_big);
   const unsigned grid = (unsigned)std::min<int64_t>(ntiles, (int64_t)1 << 30);

@@ -70,12 +70,16 @@ def _assert_verify_parity(g, o, K, margin=H.MARGIN):
                                          ("bf16", 1, 0), ("f32", 5, 0), ("bf16", 16385, 1),
                                          ("f32", 8193, 0), ("bf16", 32768, 0),
                                          ("bf16", 65536, 0), ("bf16", 65535, 0), ("bf16", 65537, 5),
-                                         ("f32", 16384, 0), ("f32", 16383, 1)])
+                                         ("f32", 16384, 0), ("f32", 16383, 1),
+                                         ("bf16", 32767, 0), ("bf16", 32769, 3),
+                                         ("f32", 32768, 0), ("f32", 32767, 0), ("f32", 32769, 1),
+                                         ("f32", 65537, 0)])
 def test_ragged_and_misaligned_rows(dtype, V, pad):
     """Rows whose length or stride is not a multiple of the 16-byte vector (so rows start
     misaligned), single-element rows, and tiles split one element past a boundary; rows
     made only of whole load groups (8 vectors per lane over the workgroup) and rows one
-    element short of or past them."""
+    element short of or past them; rows of exactly one or two big tiles (32768 elements)
+    and one element short of or past them."""
     K, S = 3, 5
     rs = V + pad
     g = torch.Generator(device="cuda").manual_seed(V * 7 + pad)

@@ -115,7 +115,11 @@ def test_race_verify_full_c3_shape_sampled():
     assert _check(sub, o, K) <= 2
 
 
-def test_race_mode_equals_smc_mode_apart_from_the_bonus():
+def test_race_mode_matches_smc_mode_apart_from_the_bonus():
+    """Race and inverse-CDF modes on the same inputs: the bonus row is cut into the same
+    tiles in both, so its normaliser is bit-equal; the other rows are cut into larger big
+    tiles in race mode, so their normalisers, the gathered log-probabilities and the
+    log-weights agree to rounding (checked ten times tighter than the oracle bar)."""
     g = torch.Generator(device="cuda").manual_seed(4)
     B, N, K, V = 2, 16, 4, 50000
     S = B * N
@@ -127,9 +131,11 @@ def test_race_mode_equals_smc_mode_apart_from_the_bonus():
     b = _run(tgt, drf, toks, B, N, K, V, 0.9, 1.0, 3, 8, lw0, sm.MODE_SMC_RACE)
     assert a["status"] == 0 and b["status"] == 0
     assert np.array_equal(a["tokens"][:, :K], b["tokens"][:, :K])
-    assert np.array_equal(a["lse"], b["lse"])
-    assert np.array_equal(a["logp"][:, :K], b["logp"][:, :K])
-    assert np.array_equal(a["lw"], b["lw"])         # alpha = 1: the bonus adds nothing
+    lse_a, lse_b = a["lse"].reshape(S, 2 * K + 1), b["lse"].reshape(S, 2 * K + 1)
+    assert np.array_equal(lse_a[:, K], lse_b[:, K])
+    assert np.all(np.abs(lse_a - lse_b) <= 1e-6 * np.abs(lse_a))
+    assert np.max(np.abs(a["logp"][:, :K] - b["logp"][:, :K])) <= 1e-6 * max(1.0, np.max(np.abs(a["logp"][:, :K])))
+    assert np.max(np.abs(a["lw"] - b["lw"])) <= 1e-5  # alpha = 1: the bonus adds nothing
     assert (a["tokens"][:, K] != b["tokens"][:, K]).any()
 
 
