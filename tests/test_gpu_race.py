@@ -70,7 +70,8 @@ def _check(got, o, K):
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("V,pad,T,alpha", [(40000, 0, 0.8, 1.0), (40000, 3, 1.3, 4.0),
-                                           (8193, 1, 1.0, 1.0), (5, 0, 1.0, 2.0)])
+                                           (8193, 1, 1.0, 1.0), (5, 0, 1.0, 2.0),
+                                           (65537, 0, 1.0, 1.0), (32769, 2, 0.9, 1.0)])
 def test_race_verify_matches_oracle(dtype, V, pad, T, alpha):
     g = torch.Generator(device="cuda").manual_seed(V + pad)
     B, N, K = 4, 12, 2
