@@ -113,21 +113,29 @@ static_assert(kKvBlock == kResBlock, "the fused resample runs on the KV workgrou
 
 // fr.lw != nullptr: the Resample step is fused in - each workgroup first resamples its
 // prompt (the same device code as smcsd_resample, so the same bits) and takes the
-// ancestors from LDS; anc / resampled are then unused.
+// ancestors from LDS; anc / resampled are then unused.  Only with parts == 1.
+// parts > 1: a prompt's old table columns are split over `parts` workgroups (blockIdx.x =
+// prompt * parts + part), `span` columns each; a block id sits in one column only, so the
+// refcount changes of different columns are independent.  The workgroup whose columns hold
+// the partial tail (part 0 when there is none) makes the prompt's copy-on-write decision.
 __global__ __launch_bounds__(kKvBlock) void k_kv(
     const int32_t *__restrict__ anc, const int32_t *__restrict__ resampled, FusedResample fr,
-    int B, int N, int32_t *__restrict__ T, int M_cap, int nb_old, int nb_new, int tail_slot,
-    int tail_mod, int32_t *__restrict__ rc, int P, int32_t *__restrict__ free_top, KvBufs wb,
-    int fast, int32_t *__restrict__ cow_count, int32_t *status) {
+    int B, int N, int parts, int span, int32_t *__restrict__ T, int M_cap, int nb_old,
+    int nb_new, int tail_slot, int tail_mod, int32_t *__restrict__ rc, int P,
+    int32_t *__restrict__ free_top, KvBufs wb, int fast, int32_t *__restrict__ cow_count,
+    int32_t *status) {
   __shared__ int32_t a[kMaxN], cnt[kMaxN], tail_old[kMaxN], tail_new[kMaxN];
   __shared__ int32_t tile[kKvTileInts];
   __shared__ uint8_t colu[kKvTileInts];  // column of the tile holds one block in every row
   __shared__ int2 negl[kKvTileInts];     // (block, decrement); later the tail hash table
   __shared__ int red[kKvBlock / kWave];
   __shared__ int sFlags, sValid, sLast, sNeg;
-  const int b = blockIdx.x, tid = threadIdx.x;
+  const int b = blockIdx.x / parts, part = blockIdx.x - b * parts, tid = threadIdx.x;
   const int row0 = b * N;
   const int tail_partial = tail_mod != 0;
+  const int c_begin = min(nb_old, part * span), c_end = min(nb_old, c_begin + span);
+  const bool tail_owner =
+      tail_partial ? tail_slot >= c_begin && tail_slot < c_end : part == 0;
   int32_t *__restrict__ cow_src = wb.cow_src;
   if (tid == 0) {
     sFlags = 0;
@@ -138,7 +146,7 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
   const int C = *wb.ctr;
   uint32_t *__restrict__ bitmap = wb.bitmap2 + (C & 1) * wb.nwp;
   int32_t *__restrict__ gcount = wb.gcount2 + (C & 1) * wb.ngp;
-  if (b == 0 && tid == 0) {
+  if (blockIdx.x == 0 && tid == 0) {
     wb.scal[0] = *free_top;
     wb.scal[3] = C;
   }
@@ -151,8 +159,8 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
   const float lw0 = split && tid < N ? fr.lw[row0 + tid] : 0.0f;
   const int pthr = split ? kKvBlock - kWave : kKvBlock;  // threads that prefetch
   const int pid = split ? tid - kWave : tid;              // this one's index among them
-  const int W = max(1, min(nb_old, kKvTileInts / N));
-  const int w0 = min(W, nb_old), nw0 = N * w0;
+  const int W = max(1, min(c_end - c_begin, kKvTileInts / N));
+  const int w0 = min(W, c_end - c_begin), nw0 = N * w0;
   int32_t pre[kPre];
 #pragma unroll
   for (int k = 0; k < kPre; ++k) {
@@ -160,7 +168,7 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
     pre[k] = 0;
     if (pid >= 0 && e < nw0) {
       const int j = e / w0, s = e - j * w0;
-      pre[k] = T[(row0 + j) * M_cap + s];
+      pre[k] = T[(row0 + j) * M_cap + c_begin + s];
     }
   }
   int res;
@@ -203,18 +211,18 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
   if (do_exchange) {
     for (int i = tid; i < N; i += kKvBlock) atomicAdd(&cnt[a[i]], 1);
     const int nseg = (N + kSeg - 1) / kSeg;
-    for (int s0 = 0; s0 < nb_old; s0 += W) {
-      const int w = min(W, nb_old - s0), nw = N * w;
-      if (s0 == 0) {
-        // the first tile is W columns wide (W = min(nb_old, kKvTileInts / N) = w), so entry
-        // e = j * w + s sits at tile[e]: no division on this path
+    for (int s0 = c_begin; s0 < c_end; s0 += W) {
+      const int w = min(W, c_end - s0), nw = N * w;
+      if (s0 == c_begin) {
+        // the first tile is W columns wide (W = min(c_end - c_begin, kKvTileInts / N) = w),
+        // so entry e = j * w + s sits at tile[e]: no division on this path
 #pragma unroll
         for (int k = 0; k < kPre; ++k) {
           const int e = pid + k * pthr;
           if (pid >= 0 && e < nw) tile[e] = pre[k];
         }
       }
-      for (int e0 = tid; s0 > 0 && e0 < nw; e0 += kKvBlock * kStage) {
+      for (int e0 = tid; s0 > c_begin && e0 < nw; e0 += kKvBlock * kStage) {
         int32_t v[kStage];
 #pragma unroll
         for (int k = 0; k < kStage; ++k) {
@@ -352,9 +360,9 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
       }
       __syncthreads();
     }
-    if (tail_partial)
+    if (tail_partial && tail_owner)
       for (int i = tid; i < N; i += kKvBlock) tail_new[i] = tail_old[a[i]];
-  } else if (tail_partial) {
+  } else if (tail_partial && tail_owner) {
     for (int i = tid; i < N; i += kKvBlock) tail_new[i] = T[(row0 + i) * M_cap + tail_slot];
   }
   __syncthreads();
@@ -364,7 +372,7 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
   // block comes from an LDS hash table keyed by block id.
   int32_t *hkey = reinterpret_cast<int32_t *>(negl);
   int32_t *hmax = hkey + kHash;
-  if (tail_partial) {
+  if (tail_partial && tail_owner) {
     for (int h = tid; h < kHash; h += kKvBlock) {
       hkey[h] = -1;
       hmax[h] = -1;
@@ -384,7 +392,7 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
     }
     __syncthreads();
   }
-  for (int i = tid; i < N; i += kKvBlock) {
+  for (int i = tid; tail_owner && i < N; i += kKvBlock) {
     int32_t src = 0;
     if (tail_partial) {
       const int32_t blk = tail_new[i];
@@ -405,7 +413,7 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
   // out the pops for k_kv_pop
   __threadfence();
   __syncthreads();
-  if (tid == 0) sLast = atomicAdd(wb.done, 1) == B - 1;
+  if (tid == 0) sLast = atomicAdd(wb.done, 1) == (int)gridDim.x - 1;
   __syncthreads();
   if (!sLast) return;
   __threadfence();
@@ -707,9 +715,26 @@ hipError_t launch_kv(const int32_t *anc, const int32_t *resampled, const FusedRe
   const int tail_slot = (int)(L / bs), tail_mod = (int)(L % bs);
   const int fast = S <= kKvFastSeqMax && w.ngroups <= kKvFastGroupMax;
   const unsigned grid2 = (unsigned)(w.ngroups + (S + kKvBlock - 1) / kKvBlock);
-  hipLaunchKernelGGL(k_kv, dim3(B), dim3(kKvBlock), 0, stream, anc, resampled, fr, B, N, tables, M_cap,
-                     nb_old, nb_new, tail_slot, tail_mod, rc, (int)P, free_top, wb, fast, cow_count,
-                     status);
+  // A prompt whose old table spans more than one column tile is split over one workgroup
+  // per tile.  Measured on the MI355X: B = 8, N = 128 with ~330 blocks per sequence spent
+  // 91 us in one workgroup per prompt.  The resample then runs as its own kernel first (the
+  // same device code, so the same bits): the parts of a prompt cannot share one resample,
+  // and the resample resets the log-weights the other parts would still be reading.
+  const int wcap = std::max(1, kKvTileInts / N);
+  const int parts = (int64_t)N * nb_old > kKvTileInts ? (int)ceil_div(nb_old, wcap) : 1;
+  const int span = parts > 1 ? wcap : std::max(nb_old, 1);
+  FusedResample frk = fr;
+  if (fr.lw && parts > 1) {
+    const hipError_t e = launch_resample(fr.lw, B, N, fr.tau, fr.seed, fr.step, fr.anc, fr.ess,
+                                         fr.res, status, stream);
+    if (e != hipSuccess) return e;
+    anc = fr.anc;
+    resampled = fr.res;
+    frk = FusedResample{};
+  }
+  hipLaunchKernelGGL(k_kv, dim3((unsigned)((int64_t)B * parts)), dim3(kKvBlock), 0, stream, anc,
+                     resampled, frk, B, N, parts, span, tables, M_cap, nb_old, nb_new, tail_slot,
+                     tail_mod, rc, (int)P, free_top, wb, fast, cow_count, status);
   if (fast)
     hipLaunchKernelGGL(k_kv_pop_fast, dim3(grid2), dim3(kKvBlock), 0, stream, S, tables, M_cap,
                        nb_old, nb_new, tail_slot, tail_mod, rc, (int)P, free_list, free_top, wb, cow,
