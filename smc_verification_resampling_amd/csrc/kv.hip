@@ -715,14 +715,18 @@ hipError_t launch_kv(const int32_t *anc, const int32_t *resampled, const FusedRe
   const int tail_slot = (int)(L / bs), tail_mod = (int)(L % bs);
   const int fast = S <= kKvFastSeqMax && w.ngroups <= kKvFastGroupMax;
   const unsigned grid2 = (unsigned)(w.ngroups + (S + kKvBlock - 1) / kKvBlock);
-  // A prompt whose old table spans more than one column tile is split over one workgroup
-  // per tile.  Measured on the MI355X: B = 8, N = 128 with ~330 blocks per sequence spent
-  // 91 us in one workgroup per prompt.  The resample then runs as its own kernel first (the
-  // same device code, so the same bits): the parts of a prompt cannot share one resample,
-  // and the resample resets the log-weights the other parts would still be reading.
+  // A prompt whose old table spans more than one column tile is split over workgroups of
+  // a quarter tile's columns each.  Measured on the MI355X: B = 8, N = 128 with ~330 blocks
+  // per sequence spent 91 us in one workgroup per prompt, 31 us with one per tile and 26 us
+  // with one per quarter tile.  The resample then runs as its own kernel first (the same
+  // device code, so the same bits): the parts of a prompt cannot share one resample, and
+  // the resample resets the log-weights the other parts would still be reading.  Tables of
+  // one tile keep one workgroup and the fused resample (B = 32, N = 16, 285 blocks: 2 or 4
+  // parts plus the resample kernel were 1.5-2 us slower per step).
   const int wcap = std::max(1, kKvTileInts / N);
-  const int parts = (int64_t)N * nb_old > kKvTileInts ? (int)ceil_div(nb_old, wcap) : 1;
-  const int span = parts > 1 ? wcap : std::max(nb_old, 1);
+  const int parts =
+      (int64_t)N * nb_old > kKvTileInts ? (int)ceil_div(nb_old, std::max(1, wcap / 4)) : 1;
+  const int span = parts > 1 ? std::max(1, wcap / 4) : std::max(nb_old, 1);
   FusedResample frk = fr;
   if (fr.lw && parts > 1) {
     const hipError_t e = launch_resample(fr.lw, B, N, fr.tau, fr.seed, fr.step, fr.anc, fr.ess,
