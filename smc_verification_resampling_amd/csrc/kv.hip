@@ -111,13 +111,24 @@ struct KvBufs {
 
 static_assert(kKvBlock == kResBlock, "the fused resample runs on the KV workgroup");
 
+// Log-weights of resampled prompts that the pop kernel resets (lw == nullptr: none), when
+// the fused resample ran in several workgroups per prompt.
+struct LwReset {
+  float *lw;
+  const int32_t *res;
+  int N;
+};
+
 // fr.lw != nullptr: the Resample step is fused in - each workgroup first resamples its
 // prompt (the same device code as smcsd_resample, so the same bits) and takes the
-// ancestors from LDS; anc / resampled are then unused.  Only with parts == 1.
+// ancestors from LDS; anc / resampled are then unused.
 // parts > 1: a prompt's old table columns are split over `parts` workgroups (blockIdx.x =
 // prompt * parts + part), `span` columns each; a block id sits in one column only, so the
 // refcount changes of different columns are independent.  The workgroup whose columns hold
 // the partial tail (part 0 when there is none) makes the prompt's copy-on-write decision.
+// With the resample fused in, every part resamples the prompt (the same bits), part 0
+// writes the ancestors, ESS and decision, and the log-weights of resampled prompts are
+// reset by the pop kernel, after every part has read them.
 __global__ __launch_bounds__(kKvBlock) void k_kv(
     const int32_t *__restrict__ anc, const int32_t *__restrict__ resampled, FusedResample fr,
     int B, int N, int parts, int span, int32_t *__restrict__ T, int M_cap, int nb_old,
@@ -178,12 +189,14 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
     if (N <= kWave) {
       if (tid < kWave) {
         const int d = resample_prompt_wave(lw0, fr.lw + row0, N, fr.tau, fr.seed, b, fr.step,
-                                           fr.anc + row0, fr.ess + b, fr.res + b, status, a);
+                                           fr.anc + row0, fr.ess + b, fr.res + b, status, a,
+                                           part == 0, parts == 1);
         if (tid == 0) sRes = d;
       }
     } else {
       const int d = resample_prompt_block(fr.lw + row0, N, fr.tau, fr.seed, b, fr.step,
-                                          fr.anc + row0, fr.ess + b, fr.res + b, status, a, sResL);
+                                          fr.anc + row0, fr.ess + b, fr.res + b, status, a, sResL,
+                                          part == 0, parts == 1);
       if (tid == 0) sRes = d;
     }
     for (int i = tid; i < N; i += kKvBlock) cnt[i] = 0;
@@ -533,7 +546,7 @@ __device__ __forceinline__ void kv_fill_pop(int32_t d, int g, int st, int ce, in
 __global__ __launch_bounds__(kKvBlock) void k_kv_pop(
     int S, int32_t *__restrict__ T, int M_cap, int nb_old, int nb_new, int tail_slot,
     int tail_mod, int32_t *__restrict__ rc, int P, int32_t *__restrict__ free_list, KvBufs wb,
-    int32_t *__restrict__ cow, int32_t *status) {
+    int32_t *__restrict__ cow, int32_t *status, LwReset lr) {
   __shared__ int32_t sList[kKvGroupBlocks];  // this group's freed block ids, ascending
   __shared__ int red[kKvBlock / kWave];
   const int tid = threadIdx.x;
@@ -565,9 +578,11 @@ __global__ __launch_bounds__(kKvBlock) void k_kv_pop(
     }
   } else {
     const int g = (blockIdx.x - wb.ngroups) * kKvBlock + tid;
-    if (g < S)
+    if (g < S) {
       flags |= kv_sequence_pops(g, wb.cow_src[g], wb.cow_excl[g], nfresh, F, avail, T, M_cap,
                                 nb_old, tail_slot, tail_mod, rc, P, free_list, cow);
+      if (lr.lw && lr.res[g / lr.N]) lr.lw[g] = 0.0f;
+    }
   }
   kv_clear_other(wb, C);
   if (flags) atomicOr(status, flags);
@@ -583,7 +598,7 @@ __global__ __launch_bounds__(kKvBlock) void k_kv_pop_fast(
     int S, int32_t *__restrict__ T, int M_cap, int nb_old, int nb_new, int tail_slot,
     int tail_mod, int32_t *__restrict__ rc, int P, int32_t *__restrict__ free_list,
     int32_t *__restrict__ free_top, KvBufs wb, int32_t *__restrict__ cow,
-    int32_t *__restrict__ cow_count, int32_t *status) {
+    int32_t *__restrict__ cow_count, int32_t *status, LwReset lr) {
   __shared__ int32_t sSrc[kKvFastSeqMax];  // copy-on-write source + 1 per sequence
   __shared__ int32_t sEx[kKvFastSeqMax];   // exclusive prefix of the copy-on-write flags
   __shared__ int32_t sList[kKvGroupBlocks];  // this group's freed block ids, ascending
@@ -682,9 +697,11 @@ __global__ __launch_bounds__(kKvBlock) void k_kv_pop_fast(
     }
   } else {
     const int g = (gi - wb.ngroups) * kKvBlock + tid;
-    if (g < S)
+    if (g < S) {
       flags |= kv_sequence_pops(g, sSrc[g], sEx[g], nfresh, F, avail, T, M_cap, nb_old,
                                 tail_slot, tail_mod, rc, P, free_list, cow);
+      if (lr.lw && lr.res[g / lr.N]) lr.lw[g] = 0.0f;
+    }
   }
   kv_clear_other(wb, C);
   if (flags) atomicOr(status, flags);
@@ -718,34 +735,23 @@ hipError_t launch_kv(const int32_t *anc, const int32_t *resampled, const FusedRe
   // A prompt whose old table spans more than one column tile is split over workgroups of
   // a quarter tile's columns each.  Measured on the MI355X: B = 8, N = 128 with ~330 blocks
   // per sequence spent 91 us in one workgroup per prompt, 31 us with one per tile and 26 us
-  // with one per quarter tile.  The resample then runs as its own kernel first (the same
-  // device code, so the same bits): the parts of a prompt cannot share one resample, and
-  // the resample resets the log-weights the other parts would still be reading.  Tables of
-  // one tile keep one workgroup and the fused resample (B = 32, N = 16, 285 blocks: 2 or 4
-  // parts plus the resample kernel were 1.5-2 us slower per step).
+  // with one per quarter tile.  With the resample fused in, each part resamples the prompt
+  // and the pop kernel resets the log-weights.
   const int wcap = std::max(1, kKvTileInts / N);
   const int parts =
       (int64_t)N * nb_old > kKvTileInts ? (int)ceil_div(nb_old, std::max(1, wcap / 4)) : 1;
   const int span = parts > 1 ? std::max(1, wcap / 4) : std::max(nb_old, 1);
-  FusedResample frk = fr;
-  if (fr.lw && parts > 1) {
-    const hipError_t e = launch_resample(fr.lw, B, N, fr.tau, fr.seed, fr.step, fr.anc, fr.ess,
-                                         fr.res, status, stream);
-    if (e != hipSuccess) return e;
-    anc = fr.anc;
-    resampled = fr.res;
-    frk = FusedResample{};
-  }
+  const LwReset lr = fr.lw && parts > 1 ? LwReset{fr.lw, fr.res, N} : LwReset{nullptr, nullptr, 1};
   hipLaunchKernelGGL(k_kv, dim3((unsigned)((int64_t)B * parts)), dim3(kKvBlock), 0, stream, anc,
-                     resampled, frk, B, N, parts, span, tables, M_cap, nb_old, nb_new, tail_slot,
+                     resampled, fr, B, N, parts, span, tables, M_cap, nb_old, nb_new, tail_slot,
                      tail_mod, rc, (int)P, free_top, wb, fast, cow_count, status);
   if (fast)
     hipLaunchKernelGGL(k_kv_pop_fast, dim3(grid2), dim3(kKvBlock), 0, stream, S, tables, M_cap,
                        nb_old, nb_new, tail_slot, tail_mod, rc, (int)P, free_list, free_top, wb, cow,
-                       cow_count, status);
+                       cow_count, status, lr);
   else
     hipLaunchKernelGGL(k_kv_pop, dim3(grid2), dim3(kKvBlock), 0, stream, S, tables, M_cap, nb_old,
-                       nb_new, tail_slot, tail_mod, rc, (int)P, free_list, wb, cow, status);
+                       nb_new, tail_slot, tail_mod, rc, (int)P, free_list, wb, cow, status, lr);
   return hipGetLastError();
 }
 

@@ -14,7 +14,7 @@ __global__ __launch_bounds__(kResBlock) void k_resample(float *__restrict__ lw, 
   __shared__ ResampleLds L;
   const int b = blockIdx.x;
   resample_prompt_block(lw + (int64_t)b * N, N, tau, seed, b, step, anc + (int64_t)b * N, ess + b,
-                        resampled + b, status, nullptr, L);
+                        resampled + b, status, nullptr, L, true, true);
 }
 
 // Up to 64 particles: one wave per prompt, four prompts per workgroup, no workgroup
@@ -31,7 +31,7 @@ __global__ __launch_bounds__(kWave * kResWaves) void k_resample_wave(
   float *lwb = lw + (int64_t)b * N;
   const float x = lane < N ? lwb[lane] : 0.0f;
   resample_prompt_wave(x, lwb, N, tau, seed, b, step, anc + (int64_t)b * N, ess + b, resampled + b,
-                       status, nullptr);
+                       status, nullptr, true, true);
 }
 
 hipError_t launch_resample(float *lw, int B, int N, float tau, uint64_t seed, uint64_t step,

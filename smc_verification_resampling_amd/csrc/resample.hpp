@@ -21,12 +21,16 @@ constexpr int kResBlock = 256;
 
 // By one wave, N <= kWave: everything in registers and lane shuffles.  Every lane of the
 // wave calls it with x = lwb[lane] already loaded (any value for lanes >= N, which idle), so
-// a caller can issue that load early.  Outputs of prompt b: ab[N] ancestors, *essb, *resb,
-// the reset of lwb; sa (nullable) gets the ancestors too.  Returns the decision (every lane).
+// a caller can issue that load early.  Outputs of prompt b: ab[N] ancestors, *essb, *resb
+// and the status flag (only when out), the reset of lwb (only when reset); sa (nullable)
+// gets the ancestors too.  Returns the decision (every lane).  Several workgroups may
+// resample one prompt (the same bits in each) when one of them writes the outputs and none
+// resets lwb while another may still read it.
 __device__ __forceinline__ int resample_prompt_wave(float x_in, float *__restrict__ lwb, int N,
                                                     float tau, uint64_t seed, int b, uint64_t step,
                                                     int32_t *__restrict__ ab, float *essb,
-                                                    int32_t *resb, int32_t *status, int32_t *sa) {
+                                                    int32_t *resb, int32_t *status, int32_t *sa,
+                                                    bool out, bool reset) {
   const int lane = threadIdx.x % kWave;
   const bool act = lane < N;
   const float x = act ? x_in : kNegInf;
@@ -39,10 +43,10 @@ __device__ __forceinline__ int resample_prompt_wave(float x_in, float *__restric
   }
   if (bad || !isfinite(m)) {
     if (act) {
-      ab[lane] = lane;
+      if (out) ab[lane] = lane;
       if (sa) sa[lane] = lane;
     }
-    if (lane == 0) {
+    if (lane == 0 && out) {
       *essb = 0.0f;
       *resb = 0;
       atomicOr(status, SMCSD_ST_DEGENERATE_WEIGHTS);
@@ -60,13 +64,13 @@ __device__ __forceinline__ int resample_prompt_wave(float x_in, float *__restric
   if (e < 1.0) e = 1.0;
   if (e > (double)N) e = (double)N;
   const bool doit = e < (double)tau * (double)N;
-  if (lane == 0) {
+  if (lane == 0 && out) {
     *essb = (float)e;
     *resb = doit;
   }
   if (!doit) {
     if (act) {
-      ab[lane] = lane;
+      if (out) ab[lane] = lane;
       if (sa) sa[lane] = lane;
     }
     return 0;
@@ -90,9 +94,9 @@ __device__ __forceinline__ int resample_prompt_wave(float x_in, float *__restric
   }
   if (act) {
     const int a = idx < N ? idx : N - 1;
-    ab[lane] = a;
+    if (out) ab[lane] = a;
     if (sa) sa[lane] = a;
-    lwb[lane] = 0.0f;
+    if (reset) lwb[lane] = 0.0f;
   }
   return 1;
 }
@@ -109,12 +113,12 @@ struct ResampleLds {
 // By a whole kResBlock-thread workgroup (every thread calls it), N <= kMaxN: the weights
 // staged in LDS in fp64, the inclusive prefix by contiguous per-thread segments plus a
 // workgroup scan, every particle's ancestor by binary search over the prefix.  Same
-// outputs and return value as resample_prompt_wave.
+// outputs, flags and return value as resample_prompt_wave.
 __device__ __forceinline__ int resample_prompt_block(float *__restrict__ lwb, int N, float tau,
                                                      uint64_t seed, int b, uint64_t step,
                                                      int32_t *__restrict__ ab, float *essb,
                                                      int32_t *resb, int32_t *status, int32_t *sa,
-                                                     ResampleLds &L) {
+                                                     ResampleLds &L, bool out, bool reset) {
   const int tid = threadIdx.x;
   const int lane = tid % kWave, wave = tid / kWave;
 
@@ -146,10 +150,10 @@ __device__ __forceinline__ int resample_prompt_block(float *__restrict__ lwb, in
 
   if (bad || !isfinite(m)) {
     for (int n = tid; n < N; n += kResBlock) {
-      ab[n] = n;
+      if (out) ab[n] = n;
       if (sa) sa[n] = n;
     }
-    if (tid == 0) {
+    if (tid == 0 && out) {
       *essb = 0.0f;
       *resb = 0;
       atomicOr(status, SMCSD_ST_DEGENERATE_WEIGHTS);
@@ -170,14 +174,16 @@ __device__ __forceinline__ int resample_prompt_block(float *__restrict__ lwb, in
   if (e < 1.0) e = 1.0;
   if (e > (double)N) e = (double)N;
   if (tid == 0) {
-    *essb = (float)e;
     L.decision = e < (double)tau * (double)N;
-    *resb = L.decision;
+    if (out) {
+      *essb = (float)e;
+      *resb = L.decision;
+    }
   }
   __syncthreads();
   if (!L.decision) {
     for (int n = tid; n < N; n += kResBlock) {
-      ab[n] = n;
+      if (out) ab[n] = n;
       if (sa) sa[n] = n;
     }
     return 0;
@@ -207,10 +213,11 @@ __device__ __forceinline__ int resample_prompt_block(float *__restrict__ lwb, in
       else lo = mid + 1;
     }
     const int a = lo < N ? lo : N - 1;
-    ab[i] = a;
+    if (out) ab[i] = a;
     if (sa) sa[i] = a;
   }
-  for (int n = tid; n < N; n += kResBlock) lwb[n] = 0.0f;
+  if (reset)
+    for (int n = tid; n < N; n += kResBlock) lwb[n] = 0.0f;
   return 1;
 }
 
