@@ -70,7 +70,22 @@ def _equal(a, b):
 @pytest.mark.parametrize("B,N,shared", [(3, 16, True), (2, 5, False), (3, 40, True), (2, 64, False),
                                         (2, 128, True), (40, 256, False)])
 def test_fused_equals_separate_calls(B, N, shared):
-    bs, K, ctx0, rounds = 4, 2, 10, 6
+    _fused_vs_separate(B, N, shared, bs=4, ctx0=10)
+
+
+@pytest.mark.parametrize("B,N,shared,bs,ctx0", [(3, 128, True, 4, 300), (2, 64, False, 2, 300),
+                                                (2, 16, True, 1, 600), (1, 1024, False, 4, 40),
+                                                (2, 40, True, 3, 700)])
+def test_fused_equals_separate_calls_split_tables(B, N, shared, bs, ctx0):
+    """Tables of more than one 32 KiB column tile per prompt (N * blocks > 8192): the exchange
+    runs in several workgroups per prompt, each resampling the prompt itself, and the pop
+    kernel resets the log-weights; every output must equal the two separate calls'."""
+    assert N * (ctx0 // bs) > 8192
+    _fused_vs_separate(B, N, shared, bs=bs, ctx0=ctx0)
+
+
+def _fused_vs_separate(B, N, shared, bs, ctx0):
+    K, rounds = 2, 6
     R = K + 1
     cfg = C.C1.scaled(B=B, N=N, K=K, ctx0=ctx0, block_size=bs, shared_prefix=shared, iters=rounds)
     kv = synth.initial_kv(cfg)
