@@ -75,11 +75,12 @@ def test_fused_equals_separate_calls(B, N, shared):
 
 @pytest.mark.parametrize("B,N,shared,bs,ctx0", [(3, 128, True, 4, 300), (2, 64, False, 2, 300),
                                                 (2, 16, True, 1, 600), (1, 1024, False, 4, 40),
-                                                (2, 40, True, 3, 700)])
+                                                (2, 40, True, 3, 700), (40, 256, False, 4, 160)])
 def test_fused_equals_separate_calls_split_tables(B, N, shared, bs, ctx0):
     """Tables of more than one 32 KiB column tile per prompt (N * blocks > 8192): the exchange
     runs in several workgroups per prompt, each resampling the prompt itself, and the pop
-    kernel resets the log-weights; every output must equal the two separate calls'."""
+    kernel resets the log-weights; every output must equal the two separate calls'.  The last
+    case also takes the many-sequence pop path (B * N > 8192)."""
     assert N * (ctx0 // bs) > 8192
     _fused_vs_separate(B, N, shared, bs=bs, ctx0=ctx0)
 
