@@ -35,10 +35,10 @@ EVENT_EVERY = 16
 # only for the kernel sources they were taken on: any change to them reports null.
 VERIFY_TRAFFIC = {
     "workload": "c3_batched",
-    "bytes": 1186574561,
+    "bytes": 1186573509,
     "sources": {
         "smc_verification_resampling_amd/csrc/verify.hip":
-            "cd3fab6e0d4ab1bd39b55cd1ed84189d15b1360dd57e1cb4908c9619d4c42345",
+            "da2ebf9c595b8052a2d1f25a8985e36056aa2ba328ccef31cfde3191a72b98a0",
         "smc_verification_resampling_amd/csrc/device.hpp":
             "e0711ab8add5e1eb90bd6f0e5f4aead04257c662e1daba0188a7e7dcf3c5508c",
         "smc_verification_resampling_amd/csrc/internal.hpp":

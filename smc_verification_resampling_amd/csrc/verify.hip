@@ -958,27 +958,63 @@ __global__ __launch_bounds__(kSpsFinalBlock) void k_sps_final(
   const char *prow = rm.row(g, kstar);
   const char *qrow = kstar < K ? rm.row(g, K + 1 + kstar) : nullptr;
   const float2 *p2 = part2 + (int64_t)g * chunks;
-  double Rt = 0.0, Pt = 0.0;
-  for (int i = 0; i < chunks; ++i) {
-    Rt += (double)p2[i].x;
-    Pt += (double)p2[i].y;
-  }
-  const bool use_rho = qrow != nullptr && Rt > 0.0;
-  const double total = use_rho ? Rt : Pt;
+  __shared__ double sTot, sBase;
+  __shared__ int sUse, sCh;
   const double u = philox_uniform(seed, (uint32_t)g, step, 4u, 0);
+  if (tid < kWave) {
+    // wave 0, one lane per chunk: the residual and target totals, then the first chunk
+    // whose running sum exceeds u * total, by lane prefix sums and one ballot per 64
+    // chunks.  Both passes add the same values in the same order (scan within 64 chunks,
+    // then block by block), so the running sum ends exactly at the total and, as u < 1,
+    // some chunk crosses.
+    double rt = 0.0, pt = 0.0;
+    for (int j0 = 0; j0 < chunks; j0 += kWave) {
+      const int j = j0 + tid;
+      const float2 v = j < chunks ? p2[j] : make_float2(0.0f, 0.0f);
+      rt += __shfl(wave_inclusive_scan((double)v.x), kWave - 1, kWave);
+      pt += __shfl(wave_inclusive_scan((double)v.y), kWave - 1, kWave);
+    }
+    const bool use_rho = qrow != nullptr && rt > 0.0;
+    const double total = use_rho ? rt : pt;
+    const double target = u * total;
+    double base = 0.0;
+    int ch = -1;
+    if (isfinite(total) && total > 0.0) {
+      for (int j0 = 0; j0 < chunks && ch < 0; j0 += kWave) {
+        const int j = j0 + tid;
+        const float2 v = j < chunks ? p2[j] : make_float2(0.0f, 0.0f);
+        const double t = use_rho ? (double)v.x : (double)v.y;
+        const double inc = wave_inclusive_scan(t);
+        const unsigned long long hit = __ballot(j < chunks && base + inc > target);
+        if (hit) {
+          const int f = __ffsll(hit) - 1;
+          ch = j0 + f;
+          base += __shfl(inc - t, f, kWave);
+        } else {
+          base += __shfl(inc, kWave - 1, kWave);
+        }
+      }
+      if (ch < 0) {  // not reached (see above); kept as the last chunk from its start
+        ch = chunks - 1;
+        const float2 v = p2[ch];
+        base -= use_rho ? (double)v.x : (double)v.y;
+      }
+    }
+    if (tid == 0) {
+      sTot = total;
+      sUse = use_rho;
+      sCh = ch;
+      sBase = base;
+    }
+  }
+  __syncthreads();
+  const double total = sTot;
+  const bool use_rho = sUse != 0;
   const double target = u * total;
   int tok = -1;
   if (isfinite(total) && total > 0.0) {
-    double base = 0.0;
-    int ch = chunks - 1;
-    for (int i = 0; i < chunks; ++i) {
-      const double si = use_rho ? (double)p2[i].x : (double)p2[i].y;
-      if (base + si > target) {
-        ch = i;
-        break;
-      }
-      base += si;
-    }
+    const int ch = sCh;
+    const double base = sBase;
     const int64_t e0 = (int64_t)ch * chunk_elems;
     const int64_t e1 = min((int64_t)V, e0 + (int64_t)chunk_elems);
     const ResidRow<DT> fn{prow, qrow, c, nm.x, nm.y, nm.z, nm.w, use_rho};
