@@ -277,6 +277,35 @@ __device__ __forceinline__ Lse lse_block_reduce_with(Lse st, float (&v)[NS], flo
 // ---------------------------------------------------------------------------------
 // scans and sums
 // ---------------------------------------------------------------------------------
+// fp64 values moved across lanes by DPP, as two 32-bit halves; lanes whose source is
+// outside the pattern, or whose row is not in ROW_MASK, read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_d(double v) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(unsigned)b, CTRL, ROW_MASK, 0xf, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(unsigned)(b >> 32), CTRL, ROW_MASK, 0xf, true);
+  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
+}
+// Inclusive scan over the 64 lanes: shifts of 1, 2, 4 and 8 lanes within each row of 16,
+// then the last lane of row 0 (and of row 2) added to row 1 (and row 3), then lane 31 added
+// to rows 2 and 3.
+__device__ __forceinline__ double wave_inclusive_scan(double v) {
+  v += dpp_d<0x111, 0xf>(v);  // row_shr:1
+  v += dpp_d<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_d<0x114, 0xf>(v);  // row_shr:4
+  v += dpp_d<0x118, 0xf>(v);  // row_shr:8
+  v += dpp_d<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_d<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+// The sum over the 64 lanes, in every lane: the scan's last lane, read as a uniform value.
+__device__ __forceinline__ double wave_sum(double v) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(wave_inclusive_scan(v));
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)b, kWave - 1);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(b >> 32), kWave - 1);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_inclusive_scan(T v) {
   const int lane = threadIdx.x % kWave;

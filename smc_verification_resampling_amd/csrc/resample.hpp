@@ -54,12 +54,7 @@ __device__ __forceinline__ int resample_prompt_wave(float x_in, float *__restric
     return 0;
   }
   const double w = act ? exp((double)x - (double)m) : 0.0;
-  double s1 = w, s2 = w * w;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    s1 += __shfl_xor(s1, d, kWave);
-    s2 += __shfl_xor(s2, d, kWave);
-  }
+  const double s1 = wave_sum(w), s2 = wave_sum(w * w);
   double e = s1 * s1 / s2;
   if (e < 1.0) e = 1.0;
   if (e > (double)N) e = (double)N;
@@ -75,12 +70,7 @@ __device__ __forceinline__ int resample_prompt_wave(float x_in, float *__restric
     }
     return 0;
   }
-  double cum = w;  // inclusive prefix over the lanes
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const double o = __shfl_up(cum, d, kWave);
-    if (lane >= d) cum += o;
-  }
+  const double cum = wave_inclusive_scan(w);  // inclusive prefix over the lanes
   const double tot = __shfl(cum, N - 1, kWave);
   const double u0 = philox_uniform(seed, (uint32_t)b, step, 2u, 0);
   const double pos = ((double)lane + u0) / (double)N;
