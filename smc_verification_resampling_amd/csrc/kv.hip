@@ -125,13 +125,16 @@ struct LwReset {
 // parts > 1: a prompt's old table columns are split over `parts` workgroups (blockIdx.x =
 // prompt * parts + part), `span` columns each; a block id sits in one column only, so the
 // refcount changes of different columns are independent.  The workgroup whose columns hold
-// the partial tail (part 0 when there is none) makes the prompt's copy-on-write decision.
+// the partial tail (part 0 when there is none) makes the prompt's copy-on-write decision;
+// with tail_alone that is the last part, which holds the tail column only, so the decision
+// runs beside the other parts' columns instead of after a full part's.
 // With the resample fused in, every part resamples the prompt (the same bits), part 0
 // writes the ancestors, ESS and decision, and the log-weights of resampled prompts are
 // reset by the pop kernel, after every part has read them.
 __global__ __launch_bounds__(kKvBlock) void k_kv(
     const int32_t *__restrict__ anc, const int32_t *__restrict__ resampled, FusedResample fr,
-    int B, int N, int parts, int span, int32_t *__restrict__ T, int M_cap, int nb_old,
+    int B, int N, int parts, int span, int tail_alone, int32_t *__restrict__ T, int M_cap,
+    int nb_old,
     int nb_new, int tail_slot, int tail_mod, int32_t *__restrict__ rc, int P,
     int32_t *__restrict__ free_top, KvBufs wb, int fast, int32_t *__restrict__ cow_count,
     int32_t *status) {
@@ -144,7 +147,10 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
   const int b = blockIdx.x / parts, part = blockIdx.x - b * parts, tid = threadIdx.x;
   const int row0 = b * N;
   const int tail_partial = tail_mod != 0;
-  const int c_begin = min(nb_old, part * span), c_end = min(nb_old, c_begin + span);
+  const bool tail_part = tail_alone && part == parts - 1;
+  const int body_end = tail_alone ? nb_old - 1 : nb_old;
+  const int c_begin = tail_part ? nb_old - 1 : min(body_end, part * span);
+  const int c_end = tail_part ? nb_old : min(body_end, c_begin + span);
   const bool tail_owner =
       tail_partial ? tail_slot >= c_begin && tail_slot < c_end : part == 0;
   int32_t *__restrict__ cow_src = wb.cow_src;
@@ -738,13 +744,16 @@ hipError_t launch_kv(const int32_t *anc, const int32_t *resampled, const FusedRe
   // with one per quarter tile.  With the resample fused in, each part resamples the prompt
   // and the pop kernel resets the log-weights.
   const int wcap = std::max(1, kKvTileInts / N);
-  const int parts =
-      (int64_t)N * nb_old > kKvTileInts ? (int)ceil_div(nb_old, std::max(1, wcap / 4)) : 1;
-  const int span = parts > 1 ? std::max(1, wcap / 4) : std::max(nb_old, 1);
+  // With a partial tail the tail column gets a part of its own: its workgroup also makes the
+  // copy-on-write decision (B = 8, N = 128: that part was the last to finish).
+  const bool split = (int64_t)N * nb_old > kKvTileInts;  // then nb_old > 8
+  const int tail_alone = split && tail_mod != 0;
+  const int span = split ? std::max(1, wcap / 4) : std::max(nb_old, 1);
+  const int parts = split ? (int)ceil_div(nb_old - tail_alone, span) + tail_alone : 1;
   const LwReset lr = fr.lw && parts > 1 ? LwReset{fr.lw, fr.res, N} : LwReset{nullptr, nullptr, 1};
   hipLaunchKernelGGL(k_kv, dim3((unsigned)((int64_t)B * parts)), dim3(kKvBlock), 0, stream, anc,
-                     resampled, fr, B, N, parts, span, tables, M_cap, nb_old, nb_new, tail_slot,
-                     tail_mod, rc, (int)P, free_top, wb, fast, cow_count, status);
+                     resampled, fr, B, N, parts, span, tail_alone, tables, M_cap, nb_old, nb_new,
+                     tail_slot, tail_mod, rc, (int)P, free_top, wb, fast, cow_count, status);
   if (fast)
     hipLaunchKernelGGL(k_kv_pop_fast, dim3(grid2), dim3(kKvBlock), 0, stream, S, tables, M_cap,
                        nb_old, nb_new, tail_slot, tail_mod, rc, (int)P, free_list, free_top, wb, cow,
