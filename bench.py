@@ -35,12 +35,12 @@ EVENT_EVERY = 16
 # only for the kernel sources they were taken on: any change to them reports null.
 VERIFY_TRAFFIC = {
     "workload": "c3_batched",
-    "bytes": 1186551278,
+    "bytes": 1186544688,
     "sources": {
         "smc_verification_resampling_amd/csrc/verify.hip":
             "da2ebf9c595b8052a2d1f25a8985e36056aa2ba328ccef31cfde3191a72b98a0",
         "smc_verification_resampling_amd/csrc/device.hpp":
-            "9521d659a830b8a9b0ace8dbdb29a4018caf9f1f925bbb5db9d2a03b0eee2bf0",
+            "052e9639476c02ca5093ff5435e86d38bb86ed9e9cd9eac50112402c4a58b14d",
         "smc_verification_resampling_amd/csrc/internal.hpp":
             "eee11a3a5c7749718f84f1f816eacb03cc128d53658a1fa7ca6bf5564dac0731",
     },

@@ -298,6 +298,21 @@ __device__ __forceinline__ double wave_inclusive_scan(double v) {
   v += dpp_d<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
   return v;
 }
+// The same scan for 32-bit integers: one DPP move per step (integer sums are exact, so the
+// result does not depend on the order of the additions).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xf, true);
+}
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v += dpp_i<0x111, 0xf>(v);  // row_shr:1
+  v += dpp_i<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_i<0x114, 0xf>(v);  // row_shr:4
+  v += dpp_i<0x118, 0xf>(v);  // row_shr:8
+  v += dpp_i<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_i<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
 // The sum over the 64 lanes, in every lane: the scan's last lane, read as a uniform value.
 __device__ __forceinline__ double wave_sum(double v) {
   const unsigned long long b = (unsigned long long)__double_as_longlong(wave_inclusive_scan(v));

@@ -46,11 +46,7 @@ __device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
 // Exclusive scan over the 256 threads of the workgroup; *total gets the sum.
 __device__ __forceinline__ int kv_scan(int v, int *lds, int *total) {
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  int inc = v;
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int o = __shfl_up(inc, d, kWave);
-    if (lane >= d) inc += o;
-  }
+  const int inc = wave_inclusive_scan(v);
   if (lane == kWave - 1) lds[wave] = inc;
   __syncthreads();
   int base = 0, tot = 0;
@@ -68,16 +64,8 @@ __device__ __forceinline__ int kv_scan(int v, int *lds, int *total) {
 // be reused before the next barrier.
 __device__ __forceinline__ int kv_scan3(int3 v, int *lds, int3 *total) {
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  int3 inc = v;
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int ox = __shfl_up(inc.x, d, kWave), oy = __shfl_up(inc.y, d, kWave),
-              oz = __shfl_up(inc.z, d, kWave);
-    if (lane >= d) {
-      inc.x += ox;
-      inc.y += oy;
-      inc.z += oz;
-    }
-  }
+  const int3 inc = make_int3(wave_inclusive_scan(v.x), wave_inclusive_scan(v.y),
+                             wave_inclusive_scan(v.z));
   constexpr int kW = kKvBlock / kWave;
   if (lane == kWave - 1) {
     lds[wave] = inc.x;
