@@ -9,11 +9,13 @@ bonus token, weight update), smcsd_resample (ESS, systematic resampling), smcsd_
 logit sets (4.7 GB, far above the 256 MB last-level cache) are generated untimed and step t
 uses set t mod 4.
 
-Prints one JSON line.  `roofline` covers the dominant work: the smcsd_verify call of one
-step in eight of the timed region is bracketed by HIP events on the stream it is launched
-on, and its algorithmic bytes (B*N*(2K+1)*V*2 logit bytes) are divided by the average
-duration.  `cpu_baseline` times the
-CPU oracle on a bounded sample of the same workload and scales it to steps/s.
+Prints one JSON line.  Before the W warm-up steps the bench runs whole steps, untimed, for
+--settle-ms (after any idle period this GPU runs the path ~10 % slower for ~20 ms while its
+clocks settle); the W warm-up steps then start a fresh episode that the timed steps continue.
+`roofline` covers the dominant work, the smcsd_verify call: its algorithmic bytes
+(B*N*(2K+1)*V*elt logit bytes) over its average duration from back-to-back calls between one
+pair of HIP events on its stream, right after the timed region.  `cpu_baseline` times the CPU
+oracle on a bounded sample of the same workload and scales it to steps/s.
 """
 from __future__ import annotations
 
@@ -69,9 +71,13 @@ def _parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c3_batched")
+    ap.add_argument("--workload", default="c3_batched",
+                    help="c1_tiny | c2_single_prompt | c3_batched | c4_wide_particle | c5_power")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="untimed steps run for this long before the warm-up steps: after any "
+                         "idle period the MI355X runs this path ~10%% slower for ~20 ms")
     ap.add_argument("--draft-logq", action="store_true",
                     help="draft tokens and their log q from smcsd_draft_sample (untimed, part of "
                          "the Extend step); the timed verify takes them and skips the draft rows")
@@ -81,6 +87,10 @@ def _parse():
     ap.add_argument("--separate-kv", action="store_true",
                     help="time smcsd_resample and smcsd_kv_reassign as two calls instead of the "
                          "fused smcsd_resample_kv_reassign (same results)")
+    ap.add_argument("--graph", action="store_true",
+                    help="record each run of timed steps in a HIP graph (untimed) and time its "
+                         "replay: the same launches with the same arguments, without the host's "
+                         "per-launch cost (for the launch-bound small workloads)")
     ap.add_argument("--probe-mib", type=int, default=1024,
                     help="size of the reference copy / read kernels (0 = skip)")
     return ap.parse_args()
@@ -104,8 +114,8 @@ def main():
     dev = "cuda"
     torch.cuda.init()
     B, N, K, V, S = cfg.B, cfg.N, cfg.K, cfg.V, cfg.S
-    print("[bench] generating %d logit sets of %.2f GB" % (cfg.n_sets, cfg.logit_bytes_per_step / 1e9),
-          file=sys.stderr, flush=True)
+    print("[bench] %s: generating %d logit sets of %.4g GB" % (
+        cfg.name, cfg.n_sets, cfg.logit_bytes_per_step / 1e9), file=sys.stderr, flush=True)
     base = synth.zipf_base(cfg, dev) if cfg.target_kind == "zipf" else None
     sets = []
     for s in range(cfg.n_sets):
@@ -121,17 +131,20 @@ def main():
     f32 = dict(dtype=torch.float32, device=dev)
     lw = torch.zeros(S, **f32)
     kv = synth.initial_kv(cfg)
-    tables = torch.from_numpy(kv["tables"]).to(dev)
-    rc = torch.from_numpy(kv["refcounts"]).to(dev)
-    fl = torch.from_numpy(kv["free_list"]).to(dev)
-    top = torch.from_numpy(kv["free_top"]).to(dev)
+    # the episode's start state stays resident: a restart is device-to-device copies, so the
+    # GPU never waits on the host between the warm-up and the timed steps
+    kv0 = {k: torch.from_numpy(kv[k]).to(dev) for k in ("tables", "refcounts", "free_list",
+                                                        "free_top")}
+    tables, rc, fl, top = (kv0[k].clone() for k in ("tables", "refcounts", "free_list", "free_top"))
+    ident = torch.arange(N, **i32).repeat(B, 1)
+    no_res = torch.zeros(B, **i32)
     L0 = int(kv["seq_len"])
     ws_v = sm.alloc_workspace(sm.OP_VERIFY_SMC, B, N, K, V)
     ws_kv = sm.alloc_workspace(sm.OP_KV, B, N, P=cfg.pool)
     tokens = torch.zeros((S, K + 1), **i32)
     num = torch.zeros(S, **i32)
     logp = torch.zeros((S, K + 1), **f32)
-    logq = torch.zeros((S, K), **f32)
+    logq = torch.zeros((S, max(K, 1)), **f32)
     status = torch.zeros(1, **i32)
     anc = torch.zeros((B, N), **i32)
     ess = torch.zeros(B, **f32)
@@ -139,25 +152,28 @@ def main():
     cow = torch.zeros((S, 3), **i32)
     ncow = torch.zeros(1, **i32)
     seed = cfg.rng_seed
-    state = {"L": L0}
+    state = {"L": L0, "round": 0, "t": 0}
 
     def kv_call(a, r):
         sm.kv_reassign(a, r, B, N, tables, cfg.block_size, state["L"], K + 1, rc, fl, top, cow, ncow,
                        status, ws_kv)
 
     def reset():
+        """Restart the episode (enqueued on the stream; no host synchronisation)."""
         lw.zero_()
-        tables.copy_(torch.from_numpy(kv["tables"]))
-        rc.copy_(torch.from_numpy(kv["refcounts"]))
-        fl.copy_(torch.from_numpy(kv["free_list"]))
-        top.copy_(torch.from_numpy(kv["free_top"]))
+        tables.copy_(kv0["tables"])
+        rc.copy_(kv0["refcounts"])
+        fl.copy_(kv0["free_list"])
+        top.copy_(kv0["free_top"])
         state["L"] = L0
-        kv_call(torch.arange(N, **i32).repeat(B, 1), torch.zeros(B, **i32))
+        state["round"] = 0
+        kv_call(ident, no_res)
 
-    # the block pool holds M_cap slots per sequence: restart the episode before it fills
+    # the block pool holds M_cap slots per sequence: an episode is at most cfg.iters rounds
     max_rounds = cfg.iters
 
-    def step(t, ev=None):
+    def step(ev=None):
+        t = state["t"]
         tgt, drf, toks, lq_in = sets[t % cfg.n_sets]
         if ev is not None:
             ev[0].record()
@@ -174,53 +190,108 @@ def main():
             sm.resample_kv_reassign(lw.view(B, N), B, N, cfg.tau, seed, t, anc, ess, resampled,
                                     tables, cfg.block_size, state["L"], K + 1, rc, fl, top, cow,
                                     ncow, status, ws_kv)
+        state["t"] += 1
+        state["round"] += 1
 
-    reset()
-    for t in range(args.warmup):
-        if t and t % max_rounds == 0:
+    def steps_in_episode(n):
+        """Steps that fit before the episode's end, restarting it first if it is full."""
+        if state["round"] >= max_rounds:
             reset()
-        step(t)
-    torch.cuda.synchronize()
+        return min(n, max_rounds - state["round"])
+
+    # settle: after an idle period this GPU's clocks take ~20 ms of load to settle (the verify
+    # call runs ~10 % slower meanwhile); run whole steps, untimed, for settle_ms first
     reset()
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_ms / 1e3:
+        n = steps_in_episode(50)
+        for _ in range(n):
+            step()
+        settle_steps += n
+        torch.cuda.synchronize()
+    # warm-up: the W steps just before the timed region, from a fresh episode that the timed
+    # steps then continue
+    reset()
+    done_w = 0
+    while done_w < args.warmup:
+        n = steps_in_episode(args.warmup - done_w)
+        for _ in range(n):
+            step()
+        done_w += n
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` steps (episode restarts are pure state resets, outside it)
-    # HIP events bracket the verify call on one step in EVENT_EVERY: each recorded event
-    # costs a few microseconds of stream time, so bracketing every step would slow it
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              if i % EVENT_EVERY == 0 else None for i in range(args.steps)]
+    # timed region: exactly `steps` steps; an episode restart (device copies) between runs of
+    # steps is outside the clock.  HIP events bracket the verify call of one step in
+    # EVENT_EVERY (not a run's first step): each recorded event costs a few microseconds
+    events = []
     chunks = []
     t_total = 0.0
     done = 0
     while done < args.steps:
-        n = min(max_rounds, args.steps - done)
+        n = steps_in_episode(args.steps - done)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               if (not args.graph and i > 0 and (done + i) % EVENT_EVERY == 0) else None
+               for i in range(n)]
+        graph = None
+        if args.graph:
+            # record the run's steps (nothing executes during capture), then replay them once
+            saved = dict(state)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for i in range(n):
+                    step()
+            state.update(saved)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(n):
-            step(done + i, events[done + i])
+        if graph is not None:
+            graph.replay()
+        else:
+            for i in range(n):
+                step(evs[i])
         torch.cuda.synchronize()
         t_total += time.perf_counter() - t0
+        if graph is not None:
+            for i in range(n):  # the host-side counters the replay advanced
+                state["t"] += 1
+                state["round"] += 1
+                state["L"] += K + 1
+            del graph
+        events += [e for e in evs if e is not None]
         done += n
         chunks.append(n)
-        if done < args.steps:
-            reset()
-            torch.cuda.synchronize()
     st = int(status.cpu()[0])
     # KV occupancy at the end of the timed region: blocks off the free stack (the next
     # round's reservation included) against every sequence holding its own copy
     live = cfg.pool - int(top.cpu()[0])
     unshared = S * -(-(state["L"] + K + 1) // cfg.block_size)
-    kv_occ = {"rounds_in_episode": chunks[-1], "context_tokens": state["L"], "live_blocks": live,
-              "unshared_blocks": unshared, "saving": round(1.0 - live / unshared, 4)}
-    verify_ms = [e[0].elapsed_time(e[1]) for e in events if e is not None]
-    verify_avg_s = float(np.mean(verify_ms)) / 1e3
+    kv_occ = {"rounds_in_episode": state["round"], "context_tokens": state["L"],
+              "live_blocks": live, "unshared_blocks": unshared,
+              "saving": round(1.0 - live / unshared, 4)}
+    in_region_us = [e[0].elapsed_time(e[1]) * 1e3 for e in events]
     ms_per_step = t_total / args.steps * 1e3
     steps_per_s = args.steps / t_total
     bytes_per_verify = cfg.logit_bytes_per_step
     if args.draft_logq:  # the K draft rows are not read
         bytes_per_verify = bytes_per_verify * (K + 1) // (2 * K + 1)
-    achieved_gbs = bytes_per_verify / verify_avg_s / 1e9
     step_gbs = bytes_per_verify * steps_per_s / 1e9
+
+    # roofline: the verify call's average duration over back-to-back calls between one event
+    # pair, right after the timed region (the GPU still under load), independent of --steps
+    verify_reps = max(50, min(200, args.steps))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    tgt0, drf0, toks0, lq0 = sets[0]
+    ev[0].record()
+    for i in range(verify_reps):
+        tgt, drf, toks, lq_in = sets[i % cfg.n_sets]
+        sm.verify(tgt, None if lq_in is not None else drf, toks, B, N, K, V, cfg.temperature,
+                  cfg.alpha, mode, seed, state["t"] + i, tokens, status, ws_v, log_weights=lw,
+                  out_num_tokens=num, out_logp=logp, out_logq=logq, logq_in=lq_in)
+    ev[1].record()
+    torch.cuda.synchronize()
+    verify_avg_s = ev[0].elapsed_time(ev[1]) / 1e3 / verify_reps
+    achieved_gbs = bytes_per_verify / verify_avg_s / 1e9
 
     sps = sps_timing(cfg, sets, args.steps) if cfg.sps else None
     ref = reference_kernels(args.probe_mib) if args.probe_mib > 0 else None
@@ -240,6 +311,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
+        # the arithmetic type of the path (fp32 accumulation); the logits' storage type is
+        # config.logits_dtype
         "dtype": "f32",
         "data": "synthetic",
         "config": {
@@ -248,11 +321,14 @@ def main():
                             cfg.name, variant, B, N, K, V,
                             cfg.dtype, cfg.target_kind, cfg.temperature, cfg.alpha, cfg.tau,
                             cfg.ctx0, cfg.block_size, ", shared prefix" if cfg.shared_prefix else ""),
-            "step": "smcsd_verify%s%s + %s" % (
+            "logits_dtype": cfg.dtype,
+            "step": "smcsd_verify%s%s + %s%s" % (
                 " (logq_in: target rows only)" if args.draft_logq else "",
                 " (race-mode bonus)" if args.race_bonus else "",
                 "smcsd_resample + smcsd_kv_reassign" if args.separate_kv else
-                "smcsd_resample_kv_reassign (smcsd_resample + smcsd_kv_reassign in one launch fewer)"),
+                "smcsd_resample_kv_reassign (smcsd_resample + smcsd_kv_reassign in one launch fewer)",
+                "; timed as HIP graph replays" if args.graph else ""),
+            "settle": {"ms": args.settle_ms, "steps": settle_steps},
             "draft_sample": draft_info,
             "logit_sets": cfg.n_sets,
             "algorithmic_bytes_per_step": bytes_per_verify,
@@ -274,7 +350,10 @@ def main():
             "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
             "traffic": verify_traffic(cfg.name + variant),
             "avg_launch_us": round(verify_avg_s * 1e6, 2),
-            "launches_timed": len(verify_ms),
+            "launches_timed": verify_reps,
+            "timing": "back-to-back verify calls between one event pair after the timed region",
+            "in_region_median_us": round(float(np.median(in_region_us)), 2) if in_region_us else None,
+            "in_region_launches": len(in_region_us),
         },
         "cpu_baseline": cpu,
     }
