@@ -20,7 +20,8 @@
  *     nothing, keeps no state between calls and never synchronises the stream.  (The
  *     one value it keeps is a constant of the build: the streaming kernel's static LDS
  *     size, read once from the runtime to size the unused dynamic LDS that holds that
- *     kernel to four workgroups per compute unit.)
+ *     kernel to four workgroups per compute unit.  smcsd_verify_static, for callers that
+ *     cannot allocate, uses a scratch array inside the library instead of a workspace.)
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All work is
  *     enqueued on it, in call order.
  *   - Host-detectable argument errors return a negative code before anything is
@@ -51,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SMCSD_VERSION 3
+#define SMCSD_VERSION 4
 
 /* logits element type */
 #define SMCSD_DTYPE_F32 0
@@ -68,6 +69,7 @@ extern "C" {
 #define SMCSD_EDTYPE (-2)
 #define SMCSD_EHIP (-3)
 #define SMCSD_EWORKSPACE (-4)
+#define SMCSD_ESCRATCH (-5) /* smcsd_verify_static: needs more than SMCSD_STATIC_SCRATCH_BYTES */
 
 /* device status bits (sticky, OR'ed into *status) */
 #define SMCSD_ST_NAN_INPUT 1          /* a NaN or +inf logit in a row that was read      */
@@ -164,6 +166,31 @@ int smcsd_verify(const void *target_logits, const void *draft_logits, int dtype,
                  int32_t *out_tokens, int32_t *out_num_tokens, float *out_logp, float *out_logq,
                  float *out_lse, int32_t *status, void *workspace, size_t workspace_bytes,
                  void *stream);
+
+/*
+ * smcsd_verify_static - smcsd_verify for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): no
+ * workspace argument; the kernels' scratch (per-tile (max, sum) partials, bonus slab sums,
+ * race winners, SpS residual partials) is a device array inside the library of
+ * SMCSD_STATIC_SCRATCH_BYTES, one copy per GPU, located on the first call on each device
+ * and held until the process ends.  Arguments, layouts, outputs, status bits and limits are
+ * those of smcsd_verify, whose results it reproduces bit for bit (the same kernels).
+ * Returns SMCSD_ESCRATCH, before anything is enqueued, when the call needs more scratch
+ * than the array holds, i.e. smcsd_workspace_bytes(SMCSD_OP_VERIFY_SMC or _SPS, B, N, K, V,
+ * 0) > SMCSD_STATIC_SCRATCH_BYTES (the five reference shapes need at most 3 MB); SMCSD_EHIP
+ * if the array cannot be located.  It allocates nothing and needs no clearing (each call
+ * writes every scratch entry before reading it), but every call on one GPU shares that
+ * GPU's array: calls that overlap in time on one GPU (two streams, two host threads) race,
+ * and the caller must serialise them.
+ */
+#define SMCSD_STATIC_SCRATCH_BYTES (4u << 20)
+int smcsd_verify_static(const void *target_logits, const void *draft_logits, int dtype,
+                        int64_t row_stride, int seq_step, const int32_t *draft_tokens, int B,
+                        int N, int K, int V, float temperature, float alpha, int mode,
+                        uint64_t seed, uint64_t step, const float *lse_in, const float *logq_in,
+                        float *log_weights, int32_t *out_tokens, int32_t *out_num_tokens,
+                        float *out_logp, float *out_logq, float *out_lse, int32_t *status,
+                        void *stream);
 
 /*
  * smcsd_draft_sample - the draft side of the Extend step at one draft position: each

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libsmcsd.so")
 DTYPE_F32, DTYPE_BF16 = 0, 1
 MODE_SMC, MODE_SPS, MODE_SMC_RACE = 0, 1, 2  # MODE_SMC_RACE: SMC with the exponential-race bonus
 OP_VERIFY_SMC, OP_VERIFY_SPS, OP_KV, OP_DRAFT = 0, 1, 2, 3
+STATIC_SCRATCH_BYTES = 4 << 20  # smcsd_verify_static's per-GPU scratch array
 
 ST_NAN_INPUT = 1
 ST_EMPTY_ROW = 2
@@ -28,7 +29,7 @@ ST_DEGENERATE_WEIGHTS = 8
 ST_BAD_INPUT = 16
 
 EXPORTED = ("smcsd_version", "smcsd_status_string", "smcsd_workspace_bytes", "smcsd_verify",
-            "smcsd_draft_sample", "smcsd_resample", "smcsd_kv_reassign",
+            "smcsd_verify_static", "smcsd_draft_sample", "smcsd_resample", "smcsd_kv_reassign",
             "smcsd_resample_kv_reassign", "smcsd_philox4x32_10")
 
 _DT = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
@@ -59,6 +60,9 @@ def load_library(path: str = LIB_PATH):
     lib.smcsd_verify.argtypes = [P, P, i32, i64, i32, P, i32, i32, i32, i32, f32, f32, i32, u64,
                                  u64, P, P, P, P, P, P, P, P, P, P, sz, P]
     lib.smcsd_verify.restype = i32
+    lib.smcsd_verify_static.argtypes = [P, P, i32, i64, i32, P, i32, i32, i32, i32, f32, f32, i32,
+                                        u64, u64, P, P, P, P, P, P, P, P, P, P]
+    lib.smcsd_verify_static.restype = i32
     lib.smcsd_draft_sample.argtypes = [P, i32, i64, i32, i32, f32, u64, u64, i32, P, P, P, P, sz, P]
     lib.smcsd_draft_sample.restype = i32
     lib.smcsd_resample.argtypes = [P, i32, i32, f32, u64, u64, P, P, P, P, P]
@@ -159,6 +163,40 @@ def verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: Op
         _dev(status, "status", torch.int32, 1),
         _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
     _check(rc, "smcsd_verify")
+
+
+def verify_static(target: torch.Tensor, draft: Optional[torch.Tensor],
+                  draft_tokens: Optional[torch.Tensor], B: int, N: int, K: int, V: int,
+                  temperature: float, alpha: float, mode: int, seed: int, step: int,
+                  out_tokens: torch.Tensor, status: torch.Tensor,
+                  log_weights: Optional[torch.Tensor] = None, out_num_tokens=None, out_logp=None,
+                  out_logq=None, out_lse=None, lse_in=None, seq_step: int = 1,
+                  row_stride: Optional[int] = None, stream=None, logq_in=None) -> None:
+    """smcsd_verify_static: smcsd_verify with the library's own per-GPU scratch array instead
+    of a workspace (for callers that cannot allocate); same arguments otherwise.  Calls that
+    overlap in time on one GPU race on that array."""
+    if target.dtype not in _DT:
+        raise SmcsdError("logits must be bfloat16 or float32")
+    rs = V if row_stride is None else int(row_stride)
+    S = B * N
+    nsrc = (S - 1) * seq_step + 1 if S > 0 else 0
+    tp = _dev(target, "target", target.dtype, nsrc * (K + 1) * rs - (rs - V) if S else 0)
+    dp = _dev(draft, "draft", target.dtype, nsrc * K * rs - (rs - V) if S and K else 0) \
+        if K > 0 and (draft is not None or logq_in is None) else None
+    xp = _dev(draft_tokens, "draft_tokens", torch.int32, nsrc * K) if K > 0 else None
+    lw = _dev(log_weights, "log_weights", torch.float32, S)
+    rc = _L().smcsd_verify_static(
+        tp, dp, _DT[target.dtype], rs, seq_step, xp, B, N, K, V, float(temperature), float(alpha),
+        mode, int(seed) & (2**64 - 1), int(step) & (2**64 - 1),
+        _dev(lse_in, "lse_in", torch.float32, nsrc * (2 * K + 1)),
+        _dev(logq_in, "logq_in", torch.float32, nsrc * K), lw,
+        _dev(out_tokens, "out_tokens", torch.int32, S * (K + 1)),
+        _dev(out_num_tokens, "out_num_tokens", torch.int32, S),
+        _dev(out_logp, "out_logp", torch.float32, S * (K + 1)),
+        _dev(out_logq, "out_logq", torch.float32, S * K),
+        _dev(out_lse, "out_lse", torch.float32, S * (2 * K + 1)),
+        _dev(status, "status", torch.int32, 1), _stream(stream))
+    _check(rc, "smcsd_verify_static")
 
 
 def draft_sample(draft: torch.Tensor, n: int, V: int, temperature: float, seed: int, step: int,

@@ -1,6 +1,7 @@
 // capi.hip - extern "C" entry points of libsmcsd.so: argument validation, dtype
 // dispatch and launch.  Declarations and the full contract are in include/smcsd.h.
 #include <cmath>
+#include <mutex>
 
 #include "../../include/smcsd.h"
 #include "internal.hpp"
@@ -29,6 +30,7 @@ const char *smcsd_status_string(int code) {
     case SMCSD_EDTYPE: return "unsupported dtype";
     case SMCSD_EHIP: return "HIP launch error";
     case SMCSD_EWORKSPACE: return "workspace too small or missing";
+    case SMCSD_ESCRATCH: return "call needs more scratch than the static array holds";
     case SMCSD_ST_NAN_INPUT: return "NaN or +inf logit";
     case SMCSD_ST_EMPTY_ROW: return "row with no finite logit";
     case SMCSD_ST_NOSPACE: return "block pool exhausted";
@@ -56,13 +58,42 @@ size_t smcsd_workspace_bytes(int op, int B, int N, int K, int V, int64_t P) {
   return 0;
 }
 
-int smcsd_verify(const void *target_logits, const void *draft_logits, int dtype,
-                 int64_t row_stride, int seq_step, const int32_t *draft_tokens, int B, int N,
-                 int K, int V, float temperature, float alpha, int mode, uint64_t seed,
-                 uint64_t step, const float *lse_in, const float *logq_in, float *log_weights,
-                 int32_t *out_tokens, int32_t *out_num_tokens, float *out_logp, float *out_logq,
-                 float *out_lse, int32_t *status, void *workspace, size_t workspace_bytes,
-                 void *stream) {
+}  // extern "C"
+
+namespace {
+
+// The verify's scratch for callers that cannot allocate: a file-scope device array, one copy
+// per GPU, held until the process ends.  Host code never uses the array's name as an
+// address: each device's copy is found once with hipGetSymbolAddress and kept.
+constexpr size_t kStaticScratchBytes = SMCSD_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of the array (looked up on its first use on that device).
+int static_scratch(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SMCSD_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SMCSD_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SMCSD_OK;
+}
+
+// smcsd_verify with the workspace either given (static_ws = false) or the library's array.
+int verify_impl(const void *target_logits, const void *draft_logits, int dtype,
+                int64_t row_stride, int seq_step, const int32_t *draft_tokens, int B, int N, int K,
+                int V, float temperature, float alpha, int mode, uint64_t seed, uint64_t step,
+                const float *lse_in, const float *logq_in, float *log_weights,
+                int32_t *out_tokens, int32_t *out_num_tokens, float *out_logp, float *out_logq,
+                float *out_lse, int32_t *status, void *workspace, size_t workspace_bytes,
+                bool static_ws, void *stream) {
   if (dtype != SMCSD_DTYPE_F32 && dtype != SMCSD_DTYPE_BF16) return SMCSD_EDTYPE;
   if (mode != SMCSD_MODE_SMC && mode != SMCSD_MODE_SPS && mode != SMCSD_MODE_SMC_RACE)
     return SMCSD_EINVAL;
@@ -83,6 +114,12 @@ int smcsd_verify(const void *target_logits, const void *draft_logits, int dtype,
   if (!out_tokens || !status) return SMCSD_EINVAL;
   if (smc && (!log_weights || lse_in)) return SMCSD_EINVAL;
   const size_t need = verify_ws_layout(S, K, V, mode == SMCSD_MODE_SPS ? 1 : 0).total;
+  if (static_ws) {
+    if (need > kStaticScratchBytes) return SMCSD_ESCRATCH;
+    const int rc = static_scratch(&workspace);
+    if (rc != SMCSD_OK) return rc;
+    workspace_bytes = kStaticScratchBytes;
+  }
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) return SMCSD_EWORKSPACE;
 
   VerifyArgs a{};
@@ -113,6 +150,36 @@ int smcsd_verify(const void *target_logits, const void *draft_logits, int dtype,
   a.ws = static_cast<char *>(workspace);
   a.stream = as_stream(stream);
   return hip_rc(launch_verify(a));
+}
+
+}  // namespace
+
+extern "C" {
+
+int smcsd_verify(const void *target_logits, const void *draft_logits, int dtype,
+                 int64_t row_stride, int seq_step, const int32_t *draft_tokens, int B, int N,
+                 int K, int V, float temperature, float alpha, int mode, uint64_t seed,
+                 uint64_t step, const float *lse_in, const float *logq_in, float *log_weights,
+                 int32_t *out_tokens, int32_t *out_num_tokens, float *out_logp, float *out_logq,
+                 float *out_lse, int32_t *status, void *workspace, size_t workspace_bytes,
+                 void *stream) {
+  return verify_impl(target_logits, draft_logits, dtype, row_stride, seq_step, draft_tokens, B,
+                     N, K, V, temperature, alpha, mode, seed, step, lse_in, logq_in, log_weights,
+                     out_tokens, out_num_tokens, out_logp, out_logq, out_lse, status, workspace,
+                     workspace_bytes, false, stream);
+}
+
+int smcsd_verify_static(const void *target_logits, const void *draft_logits, int dtype,
+                        int64_t row_stride, int seq_step, const int32_t *draft_tokens, int B,
+                        int N, int K, int V, float temperature, float alpha, int mode,
+                        uint64_t seed, uint64_t step, const float *lse_in, const float *logq_in,
+                        float *log_weights, int32_t *out_tokens, int32_t *out_num_tokens,
+                        float *out_logp, float *out_logq, float *out_lse, int32_t *status,
+                        void *stream) {
+  return verify_impl(target_logits, draft_logits, dtype, row_stride, seq_step, draft_tokens, B,
+                     N, K, V, temperature, alpha, mode, seed, step, lse_in, logq_in, log_weights,
+                     out_tokens, out_num_tokens, out_logp, out_logq, out_lse, status, nullptr, 0,
+                     true, stream);
 }
 
 int smcsd_draft_sample(const void *draft_logits, int dtype, int64_t row_stride, int n, int V,

@@ -45,7 +45,7 @@ def test_gfx950_code_object_present(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.smcsd_version() == 3
+    assert lib.smcsd_version() == 4
     assert sm.status_string(0) == "ok"
     assert "workspace" in sm.status_string(-4)
     assert "pool" in sm.status_string(sm.ST_NOSPACE)
@@ -163,3 +163,23 @@ def test_binding_refuses_host_tensors(lib):
     t = torch.zeros(4, dtype=torch.int32)
     with pytest.raises(sm.SmcsdError):
         sm.philox4x32_10(t.view(1, 4), torch.zeros(2, dtype=torch.int32).view(1, 2), t.view(1, 4))
+
+
+def test_verify_static_host_validation(lib):
+    p = ctypes.c_void_p(0x1000)
+
+    def rc(**kw):
+        a = dict(dtype=1, B=1, N=1, K=1, V=64, T=1.0, mode=0, lw=p)
+        a.update(kw)
+        return lib.smcsd_verify_static(p, p, a["dtype"], a["V"], 1, p, a["B"], a["N"], a["K"],
+                                       a["V"], a["T"], 1.0, a["mode"], 0, 0, None, None, a["lw"],
+                                       p, None, None, None, None, p, None)
+    assert rc(dtype=7) == -2
+    assert rc(K=33) == -1
+    assert rc(T=0.0) == -1
+    assert rc(lw=None) == -1
+    assert rc(B=0) == 0
+    # beyond the library's scratch array: refused before anything is enqueued
+    assert sm.workspace_bytes(sm.OP_VERIFY_SMC, 64, 64, 8, 128256) > sm.STATIC_SCRATCH_BYTES
+    assert rc(B=64, N=64, K=8, V=128256) == -5
+    assert sm.status_string(-5) == "call needs more scratch than the static array holds"
