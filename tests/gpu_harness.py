@@ -50,7 +50,9 @@ class Stats:
     max_dlogp: float = 0.0
     max_rel_ess: float = 0.0
     verify_rows_checked: int = 0
+    verify_seqs_checked: int = 0
     kv_calls_checked: int = 0
+    fused_calls_checked: int = 0
     resample_events: int = 0
     sps_checked: int = 0
     notes: list = dataclasses.field(default_factory=list)
@@ -85,12 +87,21 @@ class Pipeline:
     """GPU state of one configuration plus the lock-step checks."""
 
     def __init__(self, cfg: Config, sample: int | None = None, sps_sample: int | None = None,
-                 device: str = "cuda", check: bool = True):
+                 device: str = "cuda", check: bool = True, fused: str = "alternate",
+                 full_rounds=()):
+        """fused: "alternate" runs the Resample + KV step as smcsd_resample_kv_reassign (the
+        entry point the benchmark times) on odd rounds and as smcsd_resample then
+        smcsd_kv_reassign on even rounds; "always" / "never" use one form throughout.
+        full_rounds: rounds whose verify outputs are checked on every sequence even when
+        `sample` limits the others."""
         self.cfg = cfg
         self.dev = device
         self.sample = sample
         self.sps_sample = sps_sample
         self.check = check
+        assert fused in ("alternate", "always", "never")
+        self.fused = fused
+        self.full_rounds = set(full_rounds)
         self.stats = Stats()
         base = synth.zipf_base(cfg, device) if cfg.target_kind == "zipf" else None
         self.sets = []
@@ -149,10 +160,15 @@ class Pipeline:
         if not self.check:
             return
         torch.cuda.synchronize()
+        self._check_kv(before, anc, res, int(self.status.cpu()[0]), t)
+
+    def _check_kv(self, before, anc, res, st, t):
+        """The KV state after a reassign against the oracle's, given the ancestors and
+        decisions the GPU used (those are checked against the oracle's on their own)."""
+        cfg = self.cfg
         T0, rc0, fl0, top0 = before
         o = oracle.kv_reassign(anc.cpu().numpy().reshape(cfg.B, cfg.N), res.cpu().numpy(), T0,
                                cfg.block_size, self.L, cfg.K + 1, rc0, fl0, top0)
-        st = int(self.status.cpu()[0])
         top = int(self.free_top.cpu()[0])
         ncow = int(self.cow_count.cpu()[0])
         ok = (st == o["status"] and top == o["free_top"] and ncow == o["cow_count"]
@@ -162,6 +178,8 @@ class Pipeline:
               and np.array_equal(self.cow.cpu().numpy()[:ncow], o["cow"]))
         self.stats.decision(ok, math.inf, "kv state at t=%d" % t)
         self.stats.kv_calls_checked += 1
+        if t >= 0 and self._fused_round(t):
+            self.stats.fused_calls_checked += 1
 
     # ------------------------------------------------------------------ round
     def _select(self, t, S, k):
@@ -171,6 +189,9 @@ class Pipeline:
         pick = set(r.choice(S, size=k, replace=False).tolist())
         pick.add(0 if t % 2 == 0 else S - 1)
         return np.array(sorted(pick), dtype=np.int64)
+
+    def _fused_round(self, t: int) -> bool:
+        return self.fused == "always" or (self.fused == "alternate" and t % 2 == 1)
 
     def round(self, t: int):
         cfg = self.cfg
@@ -184,8 +205,20 @@ class Pipeline:
                   out_lse=self.lse)
         lw_post = self.lw.clone() if self.check else None
         st_verify = self.status.clone()
-        sm.resample(self.lw.view(B, N), B, N, cfg.tau, self.seed, t, self.anc, self.ess,
-                    self.resampled, self.status)
+        fused = self._fused_round(t)
+        if fused:
+            # Resample + KV exchange in one entry point: the KV state at its entry is kept
+            # for the oracle, whose reassign then takes the ancestors the GPU drew
+            kv_before = self._kv_snapshot() if self.check else None
+            self.status.zero_()
+            self.L += K + 1
+            sm.resample_kv_reassign(self.lw.view(B, N), B, N, cfg.tau, self.seed, t, self.anc,
+                                    self.ess, self.resampled, self.tables, cfg.block_size, self.L,
+                                    K + 1, self.rc, self.free_list, self.free_top, self.cow,
+                                    self.cow_count, self.status, self.ws_kv)
+        else:
+            sm.resample(self.lw.view(B, N), B, N, cfg.tau, self.seed, t, self.anc, self.ess,
+                        self.resampled, self.status)
         if cfg.sps:
             self.sps_status.zero_()
             sm.verify(tgt, drf, toks, B, 1, K, cfg.V, cfg.temperature, 1.0, sm.MODE_SPS,
@@ -197,13 +230,17 @@ class Pipeline:
             self._check_resample(t, lw_post)
             if cfg.sps:
                 self._check_sps(t, tgt, drf, toks)
-        self.L += K + 1
-        self._kv(self.anc, self.resampled, t)
+        if fused:
+            if self.check:
+                self._check_kv(kv_before, self.anc, self.resampled, int(self.status.cpu()[0]), t)
+        else:
+            self.L += K + 1
+            self._kv(self.anc, self.resampled, t)
 
     def _check_verify(self, t, tgt, drf, toks, lw_before, lw_post, status):
         cfg = self.cfg
         K = cfg.K
-        sel = self._select(t, cfg.S, self.sample)
+        sel = self._select(t, cfg.S, None if t in self.full_rounds else self.sample)
         selt = torch.from_numpy(sel).to(self.dev)
         x = toks[selt].cpu().numpy()
         o = oracle.verify_smc(host_logits(tgt[selt]), host_logits(drf[selt]) if K else
@@ -235,6 +272,7 @@ class Pipeline:
             d = np.abs(glq - o["logq"]) / np.maximum(1.0, np.abs(o["logq"]))
             st.max_dlogp = max(st.max_dlogp, float(d.max()))
         st.verify_rows_checked += len(sel) * (2 * K + 1)
+        st.verify_seqs_checked += len(sel)
 
     def _check_resample(self, t, lw_post):
         cfg = self.cfg
@@ -273,16 +311,28 @@ class Pipeline:
         gt = self.sps_tokens.cpu().numpy()[selb]
         gn = self.sps_num.cpu().numpy()[selb]
         assert int(self.sps_status.cpu()[0]) == o["status"]
+        glp = self.sps_logp.cpu().numpy()[selb].astype(np.float64)
+        st = self.stats
+        d = np.abs(glp[:, :K] - o["logp"][:, :K]) / np.maximum(1.0, np.abs(o["logp"][:, :K]))
+        st.max_dlogp = max(st.max_dlogp, float(d.max()) if d.size else 0.0)
         for i, b in enumerate(selb):
             same = gn[i] == o["num_tokens"][i] and np.array_equal(gt[i], o["tokens"][i])
             margin = min(o["margin_accept"][i], o["margin_final"][i])
-            self.stats.decision(same, margin, "sps b=%d t=%d" % (b, t))
-            self.stats.sps_checked += 1
+            st.decision(same, margin, "sps b=%d t=%d" % (b, t))
+            if same:  # the drawn token's target log-probability at its position
+                st.max_dlogp = max(st.max_dlogp, abs(glp[i, K] - o["logp"][i, K]) /
+                                   max(1.0, abs(o["logp"][i, K])))
+            st.sps_checked += 1
 
 
-def run(cfg: Config, iters: int, sample=None, sps_sample=None, label=""):
+def run(cfg: Config, iters: int, sample=None, sps_sample=None, label="", fused="alternate",
+        full_rounds=None):
+    """Lock-step over `iters` rounds.  With `sample`, rounds 0, 1 and the last still check
+    the verify outputs of every sequence (unless full_rounds says otherwise)."""
     t0 = time.time()
-    p = Pipeline(cfg, sample=sample, sps_sample=sps_sample)
+    if full_rounds is None:
+        full_rounds = (0, 1, iters - 1) if sample is not None else ()
+    p = Pipeline(cfg, sample=sample, sps_sample=sps_sample, fused=fused, full_rounds=full_rounds)
     print("[%s%s] setup %.1fs" % (cfg.name, label, time.time() - t0), flush=True)
     for t in range(iters):
         p.round(t)
@@ -291,5 +341,9 @@ def run(cfg: Config, iters: int, sample=None, sps_sample=None, label=""):
                 cfg.name, label, t + 1, iters, time.time() - t0, p.stats.decisions, p.stats.flagged,
                 p.stats.unflagged_mismatch), flush=True)
     msg = p.stats.assert_ok()
-    print("[%s%s] OK %s" % (cfg.name, label, msg), flush=True)
+    print("[%s%s] OK %s verify_seqs_checked=%d kv_calls=%d fused_calls=%d" % (
+        cfg.name, label, msg, p.stats.verify_seqs_checked, p.stats.kv_calls_checked,
+        p.stats.fused_calls_checked), flush=True)
+    if fused != "never" and iters > 1:
+        assert p.stats.fused_calls_checked > 0
     return p
