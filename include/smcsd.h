@@ -258,6 +258,12 @@ int smcsd_resample(float *log_weights, int B, int N, float tau, uint64_t seed, u
  * [ceil(seq_len/bs), ceil((seq_len+reserve_tokens)/bs)) pops a fresh block with
  * refcount 1.  Pops run in ascending (sequence, slot) order; when the stack is empty
  * the slot keeps its value (-1, or the shared tail) and SMCSD_ST_NOSPACE is set.
+ * Indices read from memory are checked first (SMCSD_ST_BAD_INPUT, nothing faults): a
+ * resampled prompt with an ancestor outside [0, N) is left unexchanged; a block id
+ * outside [0, P) in an allocated slot of a resampled prompt's old tables (such as a
+ * slot a NOSPACE call left at -1) changes no count; a tail block id >= P makes no
+ * copy-on-write; a free-stack entry outside [0, P) leaves its slot as it was, and a
+ * copy-on-write that pops one is listed with destination -1 and does nothing else.
  * *cow_count = number of copy-on-write entries written.
  * Call once with identity ancestors (resampled all 0) before the first round to
  * reserve its K+1 slots; after round t call with seq_len = tokens now held

@@ -28,6 +28,7 @@ ST_NAN_INPUT = 1
 ST_EMPTY_ROW = 2
 ST_NOSPACE = 4
 ST_DEGENERATE_WEIGHTS = 8
+ST_BAD_INPUT = 16
 
 TAG_BONUS = 1
 TAG_RESAMPLE = 2

@@ -44,6 +44,7 @@
 #define ORC_ST_EMPTY_ROW 2
 #define ORC_ST_NOSPACE 4
 #define ORC_ST_DEGENERATE_WEIGHTS 8
+#define ORC_ST_BAD_INPUT 16 /* a token, ancestor or block id out of range: never read */
 
 /* RNG stream tags (counter word 3) */
 #define ORC_TAG_BONUS 1u
@@ -299,17 +300,24 @@ int orc_verify_smc(const void *tgt, const void *drf, int dtype, int64_t V, int n
         st |= rst;
     }
 
-#pragma omp parallel for schedule(dynamic, 1)
+    int32_t bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
     for (int s = 0; s < nseq; ++s) {
         const double *L = lse + (int64_t)s * R;
         double incr = 0.0;
         for (int k = 0; k < K; ++k) {
             int32_t x = draft_tokens[(int64_t)s * K + k];
             const void *trow = row_ptr(tgt, dtype, (int64_t)s * (K + 1) + k, V);
-            double lp = load_elem(trow, dtype, x) / T - L[k];
-            double lq = logq_in ? logq_in[(int64_t)s * K + k]
-                                : load_elem(row_ptr(drf, dtype, (int64_t)s * K + k, V), dtype, x) / T -
-                                      L[K + 1 + k];
+            double lp = NAN, lq = NAN;
+            if (x < 0 || x >= V) {
+                /* a draft token outside the vocabulary is flagged, never read */
+                bad |= ORC_ST_BAD_INPUT;
+            } else {
+                lp = load_elem(trow, dtype, x) / T - L[k];
+                lq = logq_in ? logq_in[(int64_t)s * K + k]
+                             : load_elem(row_ptr(drf, dtype, (int64_t)s * K + k, V), dtype, x) / T -
+                                   L[K + 1 + k];
+            }
             logp[(int64_t)s * (K + 1) + k] = lp;
             logq[(int64_t)s * K + k] = lq;
             tokens[(int64_t)s * (K + 1) + k] = x;
@@ -335,7 +343,7 @@ int orc_verify_smc(const void *tgt, const void *drf, int dtype, int64_t V, int n
         bonus_u[s] = u;
         margin[s] = m;
     }
-    *status |= st;
+    *status |= st | bad;
     return 0;
 }
 
@@ -405,7 +413,8 @@ int orc_verify_sps(const void *tgt, const void *drf, int dtype, int64_t V, int n
         st |= rst;
     }
 
-#pragma omp parallel for schedule(dynamic, 1)
+    int32_t bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
     for (int s = 0; s < nseq; ++s) {
         const double *L = lse + (int64_t)s * R;
         const uint32_t g = (uint32_t)rng_index[s];
@@ -415,6 +424,12 @@ int orc_verify_sps(const void *tgt, const void *drf, int dtype, int64_t V, int n
             int32_t x = draft_tokens[(int64_t)s * K + k];
             const void *trow = row_ptr(tgt, dtype, (int64_t)s * (K + 1) + k, V);
             const void *drow = row_ptr(drf, dtype, (int64_t)s * K + k, V);
+            if (x < 0 || x >= V) {   /* flagged, never read; its ratio is NaN: rejected */
+                bad |= ORC_ST_BAD_INPUT;
+                logp[(int64_t)s * (K + 1) + k] = NAN;
+                logq[(int64_t)s * K + k] = NAN;
+                continue;
+            }
             logp[(int64_t)s * (K + 1) + k] = load_elem(trow, dtype, x) / T - L[k];
             logq[(int64_t)s * K + k] = load_elem(drow, dtype, x) / T - L[K + 1 + k];
         }
@@ -478,7 +493,7 @@ int orc_verify_sps(const void *tgt, const void *drf, int dtype, int64_t V, int n
         margin_accept[s] = macc;
         margin_final[s] = mfin;
     }
-    *status |= st;
+    *status |= st | bad;
     return 0;
 }
 
@@ -623,21 +638,41 @@ int orc_kv_reassign(const int32_t *ancestors, const int32_t *resampled, int B, i
         return -1;
     }
     int nfreed = 0;
+    int32_t bad = 0;
 
-    /* phase 1 */
+    /* phase 1.  Indices are checked before use (the library's error convention: an
+       ancestor outside [0, N) leaves its prompt unexchanged; a block id outside [0, P) in
+       an exchanged table - a slot a NOSPACE call could not fill holds -1 - changes no
+       count; both set BAD_INPUT) */
     for (int b = 0; b < B; ++b) {
         if (!resampled[b]) continue;
         const int32_t *a = ancestors + (int64_t)b * N;
         int32_t *T = tables + (int64_t)b * N * M_cap;
+        int valid = 1;
+        for (int i = 0; i < N; ++i)
+            if (a[i] < 0 || a[i] >= N) valid = 0;
+        if (!valid) {
+            bad |= ORC_ST_BAD_INPUT;
+            continue;
+        }
+        for (int j = 0; j < N; ++j)
+            for (int s = 0; s < nb_old; ++s) {
+                int32_t blk = T[(int64_t)j * M_cap + s];
+                if (blk < 0 || blk >= P) bad |= ORC_ST_BAD_INPUT;
+            }
         for (int j = 0; j < N; ++j) cnt[j] = 0;
         for (int i = 0; i < N; ++i) cnt[a[i]] += 1;
         for (int j = 0; j < N; ++j)
             if (cnt[j] > 1)
-                for (int s = 0; s < nb_old; ++s) rc[T[(int64_t)j * M_cap + s]] += cnt[j] - 1;
+                for (int s = 0; s < nb_old; ++s) {
+                    int32_t blk = T[(int64_t)j * M_cap + s];
+                    if (blk >= 0 && blk < P) rc[blk] += cnt[j] - 1;
+                }
         for (int j = 0; j < N; ++j)
             if (cnt[j] == 0)
                 for (int s = 0; s < nb_old; ++s) {
                     int32_t blk = T[(int64_t)j * M_cap + s];
+                    if (blk < 0 || blk >= P) continue;
                     rc[blk] -= 1;
                     if (rc[blk] == 0) freed[nfreed++] = blk;
                 }
@@ -658,7 +693,8 @@ int orc_kv_reassign(const int32_t *ancestors, const int32_t *resampled, int B, i
         for (int g = 0; g < S; ++g) {
             int b = g / N;
             int32_t blk = tables[(int64_t)g * M_cap + ts];
-            if (blk < 0) continue;
+            if (blk >= P) bad |= ORC_ST_BAD_INPUT;
+            if (blk < 0 || blk >= P) continue;
             for (int h = g + 1; h < (b + 1) * N; ++h)
                 if (tables[(int64_t)h * M_cap + ts] == blk) {
                     needs_cow[g] = 1;
@@ -671,13 +707,20 @@ int orc_kv_reassign(const int32_t *ancestors, const int32_t *resampled, int B, i
         int32_t *Tg = tables + (int64_t)g * M_cap;
         if (needs_cow[g]) {
             if (top > 0) {
+                /* a popped id outside [0, P) (a corrupt free stack) is flagged: the copy
+                   is listed with destination -1 and nothing else changes */
                 int32_t d = free_list[--top];
                 int32_t o = Tg[ts];
-                rc[o] -= 1;
-                rc[d] = 1;
-                Tg[ts] = d;
+                int ok = d >= 0 && d < P;
+                if (ok) {
+                    rc[o] -= 1;
+                    rc[d] = 1;
+                    Tg[ts] = d;
+                } else {
+                    bad |= ORC_ST_BAD_INPUT;
+                }
                 cow[3 * ncow + 0] = o;
-                cow[3 * ncow + 1] = d;
+                cow[3 * ncow + 1] = ok ? d : -1;
                 cow[3 * ncow + 2] = (int32_t)(L % bs);
                 ncow++;
             } else {
@@ -687,6 +730,10 @@ int orc_kv_reassign(const int32_t *ancestors, const int32_t *resampled, int B, i
         for (int s = nb_old; s < nb_new; ++s) {
             if (top > 0) {
                 int32_t d = free_list[--top];
+                if (d < 0 || d >= P) {      /* flagged; the slot keeps its value */
+                    bad |= ORC_ST_BAD_INPUT;
+                    continue;
+                }
                 rc[d] = 1;
                 Tg[s] = d;
             } else {
@@ -696,7 +743,7 @@ int orc_kv_reassign(const int32_t *ancestors, const int32_t *resampled, int B, i
     }
     *free_top = top;
     *cow_count = ncow;
-    (void)P;
+    *status |= bad;
     free(cnt); free(old); free(freed); free(needs_cow);
     return 0;
 }

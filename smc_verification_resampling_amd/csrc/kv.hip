@@ -278,6 +278,12 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
           for (int k = 0; k < kSeg; ++k)
             if (j0 + k < j1) tail_old[j0 + k] = v[k];
         }
+        // a block id outside [0, P) in an allocated slot (one a NOSPACE call left at -1, or a
+        // corrupt table) is flagged wherever it sits, and changes no count
+        bool oob = false;
+#pragma unroll
+        for (int k = 0; k < kSeg; ++k) oob |= j0 + k < j1 && (v[k] < 0 || v[k] >= P);
+        if (oob) atomicOr(&sFlags, SMCSD_ST_BAD_INPUT);
         if (nseg > 1 && colu[s]) continue;
         if (nseg == 1) {
           // the whole column is in this thread, and a thread's atomics on one address take
@@ -292,10 +298,7 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
             const bool end = k < N && (k == N - 1 || (k + 1 < kSeg && v[k + 1] != v[k]));
             accs[k] = end ? run : 0;
             if (end) run = 0;
-            if (accs[k] != 0 && (v[k] < 0 || v[k] >= P)) {
-              atomicOr(&sFlags, SMCSD_ST_BAD_INPUT);
-              accs[k] = 0;
-            }
+            if (v[k] < 0 || v[k] >= P) accs[k] = 0;
           }
 #pragma unroll
           for (int k = 0; k < kSeg; ++k)
@@ -313,9 +316,8 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
         int32_t blk = v[0];
         int acc = 0;
         auto flush = [&]() {
-          if (acc == 0) return;
-          if (blk < 0 || blk >= P) atomicOr(&sFlags, SMCSD_ST_BAD_INPUT);
-          else if (acc > 0) atomicAdd(&rc[blk], acc);
+          if (acc == 0 || blk < 0 || blk >= P) return;  // out-of-range ids flagged above
+          if (acc > 0) atomicAdd(&rc[blk], acc);
           else negl[atomicAdd(&sNeg, 1)] = make_int2(blk, acc);
         };
 #pragma unroll
@@ -500,7 +502,14 @@ __device__ __forceinline__ int kv_sequence_pops(int g, int32_t cs, int ce, int n
       const int64_t pos = avail - 1 - k;
       d = pos < P ? free_list[pos] : -1;
       if (d < 0 || d >= P) {
+        // a corrupt stack entry: flagged; a copy-on-write is listed with destination -1
+        // and nothing else changes
         flags |= SMCSD_ST_BAD_INPUT;
+        if (st < 0) {
+          cow[3 * ce + 0] = cs - 1;
+          cow[3 * ce + 1] = -1;
+          cow[3 * ce + 2] = tail_mod;
+        }
         continue;
       }
     }

@@ -275,6 +275,47 @@ def test_kv_nospace_and_bad_ancestor():
     assert np.array_equal(g["tables"], T)
 
 
+@pytest.mark.parametrize("N,shared", [(2, False), (5, True), (16, True), (40, False), (40, True)])
+def test_kv_after_nospace_and_bad_indices_match_the_oracle(N, shared):
+    """A pool too small for the reservations: NOSPACE leaves -1 in allocated slots, which
+    later resampling rounds (random ancestors) must flag and skip exactly as the oracle does;
+    then an out-of-range ancestor and a corrupt free-stack entry.  Bit-exact every call."""
+    B, bs, K, ctx0, rounds = 3, 4, 2, 9, 6
+    R = K + 1
+    M = math.ceil((ctx0 + (rounds + 2) * R) / bs)
+    cfg = C.C1.scaled(B=B, N=N, K=K, ctx0=ctx0, block_size=bs, shared_prefix=shared,
+                      iters=rounds + 1)
+    assert cfg.M_cap == M
+    kv = synth.initial_kv(cfg)
+    used = int(kv["refcounts"].astype(bool).sum())
+    P = used + (B * N) // 2 + 1                              # room for about half a round
+    T = kv["tables"][:, :M].copy()
+    rc = kv["refcounts"][:P].copy()
+    fl = np.arange(P - 1, -1, -1, dtype=np.int32)
+    top, L = P - used, ctx0
+    rng = np.random.default_rng(N * 7 + shared)
+    ident = np.tile(np.arange(N, dtype=np.int32), (B, 1))
+    seen = 0
+    for r in range(rounds + 2):
+        if r == 0:
+            anc, res = ident, np.zeros(B, np.int32)
+        else:
+            L += R
+            anc = np.sort(rng.integers(0, N, (B, N)), axis=1).astype(np.int32)
+            res = np.ones(B, np.int32)
+            if r == rounds:
+                anc[1, 0] = N + 2                            # prompt 1: a bad ancestor
+            if r == rounds + 1 and top > 0:
+                fl = fl.copy()
+                fl[top - 1] = P + 9                          # a corrupt entry on the stack
+        o = oracle.kv_reassign(anc, res, T, bs, L, R, rc, fl, top)
+        g = _kv_gpu(anc, res, B, N, T, bs, L, R, rc, fl, top)
+        assert _kv_equal(g, o), (r, g["status"], o["status"])
+        seen |= o["status"]
+        T, rc, fl, top = o["tables"], o["refcounts"], o["free_list"], o["free_top"]
+    assert seen & sm.ST_NOSPACE and seen & sm.ST_BAD_INPUT
+
+
 def test_empty_batch_is_noop():
     st = _i32(1)
     sm.verify(_f32(1, 2, 4), _f32(1, 1, 4), _i32(1, 1), 0, 4, 1, 4, 1.0, 1.0, sm.MODE_SMC, 0, 0,

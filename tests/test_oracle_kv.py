@@ -171,3 +171,66 @@ def test_nospace_is_reported(orc):
     assert st["status"] & orc.ST_NOSPACE
     assert st["free_top"] == 0
     assert st["tables"][0, 1:4].tolist() == [2, 3, 4] and st["tables"][1, 1:4].tolist() == [-1, -1, -1]
+
+
+def test_slots_left_by_nospace_are_flagged_and_skipped(orc):
+    """After a NOSPACE call some allocated slots hold -1; a later resampling call flags
+    BAD_INPUT, changes only the counts of real blocks and keeps rc = references."""
+    B, N, bs, M, P = 1, 2, 4, 6, 5
+    T, rc, fl, top = _initial(B, N, M, bs, P, 4, False)          # blocks 0, 1 used; 3 free
+    st = orc.kv_reassign(np.tile(np.arange(N), (B, 1)), np.zeros(B), T, bs, 4, 9, rc, fl, top)
+    assert st["status"] == orc.ST_NOSPACE
+    assert st["tables"][:, :4].tolist() == [[0, 2, 3, 4], [1, -1, -1, -1]]
+    # particle 0 dropped, particle 1 duplicated, one more token reserved (same slot count)
+    s2 = orc.kv_reassign(np.array([[1, 1]]), np.array([1]), st["tables"], bs, 13, 1,
+                         st["refcounts"], st["free_list"], st["free_top"])
+    assert s2["status"] == orc.ST_BAD_INPUT
+    assert s2["tables"][:, :4].tolist() == [[1, -1, -1, -1], [1, -1, -1, -1]]
+    assert s2["refcounts"].tolist() == [0, 2, 0, 0, 0]
+    assert s2["free_top"] == 4 and s2["free_list"][:4].tolist() == [4, 3, 2, 0]
+    assert s2["cow_count"] == 0                                   # a -1 tail is not shared
+
+
+def test_bad_ancestor_leaves_its_prompt_unexchanged(orc):
+    B, N, bs, M = 2, 3, 4, 8
+    P = B * N * M
+    T, rc, fl, top = _initial(B, N, M, bs, P, 8, False)
+    anc = np.array([[2, 2, 0], [0, 1, N + 1]], np.int32)
+    st = orc.kv_reassign(anc, np.array([1, 1]), T, bs, 8, 4, rc, fl, top)
+    good = orc.kv_reassign(np.array([[2, 2, 0], [0, 1, 2]], np.int32), np.array([1, 0]), T, bs, 8,
+                           4, rc, fl, top)
+    assert st["status"] == orc.ST_BAD_INPUT and good["status"] == 0
+    for k in ("tables", "refcounts", "free_list"):
+        assert np.array_equal(st[k], good[k]), k
+    assert st["free_top"] == good["free_top"]
+
+
+def test_corrupt_free_stack_entry_is_flagged(orc):
+    """A popped id outside [0, P) leaves its slot as it was; a copy-on-write that pops one
+    is listed with destination -1 and changes no count."""
+    B, N, bs, M = 1, 2, 4, 6
+    P = 12
+    T, rc, fl, top = _initial(B, N, M, bs, P, 6, True)            # tail slot 1 shared by both
+    fl = fl.copy()
+    fl[top - 1] = P + 7                                          # the first pop (g = 0's copy)
+    st = orc.kv_reassign(np.tile(np.arange(N), (B, 1)), np.zeros(B), T, bs, 6, 1, rc, fl, top)
+    assert st["status"] == orc.ST_BAD_INPUT
+    assert st["cow_count"] == 1 and st["cow"].tolist() == [[1, -1, 2]]
+    assert np.array_equal(st["refcounts"], rc) and np.array_equal(st["tables"], T)
+    assert st["free_top"] == top - 1
+
+
+def test_out_of_vocabulary_draft_token_is_flagged(orc):
+    rng = np.random.default_rng(3)
+    S, K, V = 3, 2, 40
+    tgt = rng.normal(size=(S, K + 1, V)).astype(np.float32)
+    drf = rng.normal(size=(S, K, V)).astype(np.float32)
+    toks = np.array([[1, 2], [V, 3], [-1, 0]], np.int32)
+    o = orc.verify_smc(tgt, drf, toks, 1.0, 1.0, 5, 0, np.zeros(S, np.float32))
+    assert o["status"] == orc.ST_BAD_INPUT
+    assert np.isfinite(o["lw"][0]) and np.isnan(o["lw"][1]) and np.isnan(o["lw"][2])
+    assert np.array_equal(o["tokens"][:, :K], toks)
+    assert np.isnan(o["logp"][1, 0]) and np.isnan(o["logq"][2, 0]) and np.isfinite(o["logp"][1, 1])
+    s = orc.verify_sps(tgt, drf, toks, 1.0, 5, 0)
+    assert s["status"] == orc.ST_BAD_INPUT
+    assert s["num_tokens"][1] == 1 and s["num_tokens"][2] == 1      # a NaN ratio is no acceptance

@@ -21,6 +21,7 @@ from tests import test_oracle_laws as laws
 from tests import test_oracle_race as race
 from tests import test_oracle_resample as rs
 from tests import test_oracle_rng as rng_t
+from tests import test_oracle_sps as sps
 from tests import test_oracle_verify as vf
 from tests.helpers import rocrand_probe
 
@@ -68,8 +69,8 @@ CASES = [
     ("LSE without the max shift", "return zmax + log(s);", "return log(s);",
      [lambda: vf.test_row_lse_matches_scipy_fp32(O, 1.0, 1000)]),
     ("temperature ignored in target gather",
-     "double lp = load_elem(trow, dtype, x) / T - L[k];",
-     "double lp = load_elem(trow, dtype, x) - L[k];",
+     "lp = load_elem(trow, dtype, x) / T - L[k];",
+     "lp = load_elem(trow, dtype, x) - L[k];",
      [lambda: vf.test_verify_gather_and_weights_vs_log_softmax(O, "f32", 1.0)]),
     ("log q gathered from the target row",
      "load_elem(row_ptr(drf, dtype, (int64_t)s * K + k, V), dtype, x) / T",
@@ -137,7 +138,43 @@ CASES = [
      [lambda: race.test_verify_race_bonus_is_the_race_and_reweights(O, 1.0)]),
     ("verify reads the wrong precomputed log q", "logq_in[(int64_t)s * K + k]", "logq_in[(int64_t)s * K]",
      [lambda: dr.test_verify_with_draft_logq_equals_reading_the_draft_rows(O)]),
+    ("SpS acceptance reads word 0 for every draft",
+     "ORC_TAG_SPS_ACCEPT | ((uint32_t)(k / 4) << 8), k % 4);",
+     "ORC_TAG_SPS_ACCEPT | ((uint32_t)(k / 4) << 8), 0);",
+     [lambda: _sps(sps.test_sps_accept_decisions_follow_the_rule, 4, 1.0)] if NEEDS_PROBE else []),
+    ("SpS acceptance tag ignores k div 4",
+     "ORC_TAG_SPS_ACCEPT | ((uint32_t)(k / 4) << 8), k % 4);", "ORC_TAG_SPS_ACCEPT, k % 4);",
+     [lambda: _sps(sps.test_sps_accept_decisions_follow_the_rule, 6, 1.3)] if NEEDS_PROBE else []),
+    ("SpS final draw with the acceptance tag", "orc_uniform(seed, g, t, ORC_TAG_SPS_FINAL, 0);",
+     "orc_uniform(seed, g, t, ORC_TAG_SPS_ACCEPT, 0);",
+     [lambda: _sps(sps.test_sps_final_draw_is_searchsorted_on_the_residual, 4, 1.0)]
+     if NEEDS_PROBE else []),
+    ("SpS residual q taken from the target row",
+     "const void *qrow = row_ptr(drf, dtype, (int64_t)s * K + kstar, V);",
+     "const void *qrow = row_ptr(tgt, dtype, (int64_t)s * (K + 1) + kstar, V);",
+     [lambda: _sps(sps.test_sps_final_draw_is_searchsorted_on_the_residual, 4, 1.0)]
+     if NEEDS_PROBE else []),
+    ("SpS residual q - p instead of p - q", "double rho = p - q > 0.0 ? p - q : 0.0;",
+     "double rho = q - p > 0.0 ? q - p : 0.0;",
+     [lambda: _sps(sps.test_sps_final_draw_is_searchsorted_on_the_residual, 4, 0.8)]
+     if NEEDS_PROBE else []),
+    ("SpS empty residual draws nothing", "} else if (isfinite(L[kstar])) {", "} else if (0) {",
+     [lambda: sps.test_sps_forced_rejection_and_empty_residual(O)] if NEEDS_PROBE else []),
+    ("SpS drawn token's log p from the bonus row",
+     "tok >= 0 ? load_elem(prow, dtype, tok) / T - L[kstar] : NAN;",
+     "tok >= 0 ? load_elem(prow, dtype, tok) / T - L[K] : NAN;",
+     [lambda: _sps(sps.test_sps_final_draw_is_searchsorted_on_the_residual, 4, 1.0)]
+     if NEEDS_PROBE else []),
 ]
+
+
+def _sps(fn, K, T):
+    """An SpS pin on fresh oracle output (its cached run is computed before the swap)."""
+    sps._run.cache_clear()
+    try:
+        fn(O, K, T)
+    finally:
+        sps._run.cache_clear()
 
 
 @pytest.mark.parametrize("name,old,new,pins", CASES, ids=[c[0] for c in CASES])
