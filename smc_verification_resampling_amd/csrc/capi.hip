@@ -243,6 +243,9 @@ static int kv_check(int B, int N, const int32_t *block_tables, int M_cap, int bl
   if (ceil_div(seq_len + reserve_tokens, block_size) > M_cap) return SMCSD_EINVAL;
   if (B == 0) return 1;
   if ((int64_t)B * N * M_cap >= INT32_MAX) return SMCSD_EINVAL;  // 32-bit table indexing
+  // one exchange workgroup per prompt part: the dispatch must stay under 2^32 threads
+  const KvSplit ks = kv_split(N, (int)ceil_div(seq_len, block_size), (int)(seq_len % block_size));
+  if ((int64_t)B * ks.parts * kKvThreads > (int64_t)0xFFFFFFFF) return SMCSD_EINVAL;
   if (!block_tables || !refcounts || !free_list || !free_top || !cow || !cow_count || !status)
     return SMCSD_EINVAL;
   const size_t need = kv_ws_layout((int64_t)B * N, P).total;

@@ -3,6 +3,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+
+#include <algorithm>
 #include <stdint.h>
 
 namespace smcsd {
@@ -36,6 +38,16 @@ static_assert(kBigTileElems % kChunkElemsBf16 == 0 && kBigTileElems % kChunkElem
 constexpr int kMaxK = 32;
 constexpr int kMaxN = 1024;
 constexpr int kMaxV = 1 << 24;  // largest vocabulary taken (and tested); ids fit every index type used
+
+// A dispatch's size in work-items is a 32-bit field of the launch packet: a grid of more
+// than 2^32 - 1 threads does not launch as asked.  Kernels whose item count can exceed
+// that stride over their items with a grid of at most this many workgroups (still far more
+// than the 256 compute units hold at once).
+constexpr int64_t kMaxGridBlocks = 1 << 22;
+inline unsigned grid_blocks(int64_t items, int threads_per_block) {
+  const int64_t cap = std::min<int64_t>(kMaxGridBlocks, (int64_t)0xFFFFFFFF / threads_per_block);
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(items, cap));
+}
 
 inline int chunk_elems(int dtype) { return dtype == 1 ? kChunkElemsBf16 : kChunkElemsF32; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -31,8 +31,8 @@
 
 namespace smcsd {
 
-constexpr int kKvBlock = 256;
-constexpr int kKvTileInts = 8192;  // table entries staged per column tile (32 KiB)
+constexpr int kKvBlock = kKvThreads;
+constexpr int kKvTileInts = kKvTileEntries;  // table entries staged per column tile (32 KiB)
 constexpr int kStage = 16;         // table loads in flight per thread while staging
 constexpr int kNegBatch = 4;       // decrements in flight per thread
 constexpr int kHash = 2 * kMaxN;   // open-addressing table of the tail blocks (load <= 1/2)
@@ -735,18 +735,10 @@ hipError_t launch_kv(const int32_t *anc, const int32_t *resampled, const FusedRe
   const int tail_slot = (int)(L / bs), tail_mod = (int)(L % bs);
   const int fast = S <= kKvFastSeqMax && w.ngroups <= kKvFastGroupMax;
   const unsigned grid2 = (unsigned)(w.ngroups + (S + kKvBlock - 1) / kKvBlock);
-  // A prompt whose old table spans more than one column tile is split over workgroups of
-  // a quarter tile's columns each.  Measured on the MI355X: B = 8, N = 128 with ~330 blocks
-  // per sequence spent 91 us in one workgroup per prompt, 31 us with one per tile and 26 us
-  // with one per quarter tile.  With the resample fused in, each part resamples the prompt
-  // and the pop kernel resets the log-weights.
-  const int wcap = std::max(1, kKvTileInts / N);
-  // With a partial tail the tail column gets a part of its own: its workgroup also makes the
-  // copy-on-write decision (B = 8, N = 128: that part was the last to finish).
-  const bool split = (int64_t)N * nb_old > kKvTileInts;  // then nb_old > 8
-  const int tail_alone = split && tail_mod != 0;
-  const int span = split ? std::max(1, wcap / 4) : std::max(nb_old, 1);
-  const int parts = split ? (int)ceil_div(nb_old - tail_alone, span) + tail_alone : 1;
+  // prompts split over column parts (kv_split); with the resample fused in, each part
+  // resamples the prompt and the pop kernel resets the log-weights
+  const KvSplit ks = kv_split(N, nb_old, tail_mod);
+  const int tail_alone = ks.tail_alone, span = ks.span, parts = ks.parts;
   const LwReset lr = fr.lw && parts > 1 ? LwReset{fr.lw, fr.res, N} : LwReset{nullptr, nullptr, 1};
   hipLaunchKernelGGL(k_kv, dim3((unsigned)((int64_t)B * parts)), dim3(kKvBlock), 0, stream, anc,
                      resampled, fr, B, N, parts, span, tail_alone, tables, M_cap, nb_old, nb_new,

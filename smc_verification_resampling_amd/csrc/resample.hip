@@ -5,16 +5,18 @@
 
 namespace smcsd {
 
-__global__ __launch_bounds__(kResBlock) void k_resample(float *__restrict__ lw, int N, float tau,
+__global__ __launch_bounds__(kResBlock) void k_resample(float *__restrict__ lw, int B, int N, float tau,
                                                         uint64_t seed, uint64_t step,
                                                         int32_t *__restrict__ anc,
                                                         float *__restrict__ ess,
                                                         int32_t *__restrict__ resampled,
                                                         int32_t *status) {
   __shared__ ResampleLds L;
-  const int b = blockIdx.x;
-  resample_prompt_block(lw + (int64_t)b * N, N, tau, seed, b, step, anc + (int64_t)b * N, ess + b,
-                        resampled + b, status, nullptr, L, true, true);
+  for (int b = blockIdx.x; b < B; b += gridDim.x) {  // a grid smaller than B strides over it
+    resample_prompt_block(lw + (int64_t)b * N, N, tau, seed, b, step, anc + (int64_t)b * N,
+                          ess + b, resampled + b, status, nullptr, L, true, true);
+    __syncthreads();  // the next prompt reuses the LDS
+  }
 }
 
 // Up to 64 particles: one wave per prompt, four prompts per workgroup, no workgroup
@@ -25,25 +27,27 @@ __global__ __launch_bounds__(kWave * kResWaves) void k_resample_wave(
     float *__restrict__ lw, int B, int N, float tau, uint64_t seed, uint64_t step,
     int32_t *__restrict__ anc, float *__restrict__ ess, int32_t *__restrict__ resampled,
     int32_t *status) {
-  const int b = blockIdx.x * kResWaves + threadIdx.x / kWave;
-  if (b >= B) return;  // a whole wave: no barrier below
   const int lane = threadIdx.x % kWave;
-  float *lwb = lw + (int64_t)b * N;
-  const float x = lane < N ? lwb[lane] : 0.0f;
-  resample_prompt_wave(x, lwb, N, tau, seed, b, step, anc + (int64_t)b * N, ess + b, resampled + b,
-                       status, nullptr, true, true);
+  // one prompt per wave, no workgroup barrier; a grid smaller than B strides over it
+  for (int b = blockIdx.x * kResWaves + threadIdx.x / kWave; b < B; b += gridDim.x * kResWaves) {
+    float *lwb = lw + (int64_t)b * N;
+    const float x = lane < N ? lwb[lane] : 0.0f;
+    resample_prompt_wave(x, lwb, N, tau, seed, b, step, anc + (int64_t)b * N, ess + b,
+                         resampled + b, status, nullptr, true, true);
+  }
 }
 
 hipError_t launch_resample(float *lw, int B, int N, float tau, uint64_t seed, uint64_t step,
                            int32_t *anc, float *ess, int32_t *resampled, int32_t *status,
                            hipStream_t stream) {
   if (N <= kWave)
-    hipLaunchKernelGGL(k_resample_wave, dim3((B + kResWaves - 1) / kResWaves),
+    hipLaunchKernelGGL(k_resample_wave,
+                       dim3(grid_blocks(((int64_t)B + kResWaves - 1) / kResWaves, kWave * kResWaves)),
                        dim3(kWave * kResWaves), 0, stream, lw, B, N, tau, seed, step, anc, ess,
                        resampled, status);
   else
-    hipLaunchKernelGGL(k_resample, dim3(B), dim3(kResBlock), 0, stream, lw, N, tau, seed, step,
-                       anc, ess, resampled, status);
+    hipLaunchKernelGGL(k_resample, dim3(grid_blocks(B, kResBlock)), dim3(kResBlock), 0, stream, lw, B,
+                       N, tau, seed, step, anc, ess, resampled, status);
   return hipGetLastError();
 }
 

@@ -559,7 +559,7 @@ static_assert(kSlabElems<SMCSD_DTYPE_BF16> + 16 <= 8 * kSmcFinalBlock * kSmcUnit
 
 template <int DT, bool RACE>
 __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
-    RowMap rm, const int32_t *__restrict__ draft_tokens, int V, int chunk_elems, int chunks,
+    RowMap rm, int nseq, const int32_t *__restrict__ draft_tokens, int V, int chunk_elems, int chunks,
     int chunks_big, float c, float alpha, uint64_t seed, uint64_t step, uint32_t bonus_tag,
     const float2 *__restrict__ part, const float *__restrict__ logq_in,
     const float *__restrict__ sub, const int2 *__restrict__ race, float *__restrict__ lw,
@@ -569,7 +569,7 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
     int32_t *status) {
   using E = Elt<DT>;
   const int K = rm.K, R = 2 * K + 1;
-  const int g = blockIdx.x, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   __shared__ float sMc[2 * kMaxK + 1];
   __shared__ double sS[2 * kMaxK + 1], sL2[2 * kMaxK + 1];
   __shared__ double sLogp[kMaxK + 1], sLogq[kMaxK + 1];
@@ -582,6 +582,8 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
   __shared__ double sBase;
   __shared__ float sPickLogit;
   __shared__ int sFlags;
+  // one sequence per workgroup; a grid smaller than the batch strides over it
+  for (int g = blockIdx.x; g < nseq; g += gridDim.x) {
   if (tid == 0) sFlags = 0;
   const float lw_old = tid == 0 && lw ? lw[g] : 0.0f;  // loaded early: used only at the end
 
@@ -772,6 +774,8 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
     if (out_logp) out_logp[(int64_t)g * (K + 1) + K] = (float)lpK;
     if (sFlags) atomicOr(status, sFlags);
   }
+  __syncthreads();  // the next sequence reuses the LDS
+  }
 }
 
 // ---------------------------------------------------------------------------------
@@ -781,20 +785,21 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
 // pair is (LSE*log2(e), 1).  ws_norm[g] = {Mc_p, inv_p, Mc_q, inv_q} for row pair k*.
 template <int DT>
 __global__ __launch_bounds__(kWave) void k_sps_decide(
-    RowMap rm, const int32_t *__restrict__ draft_tokens, int V, int chunks, int chunks_big, float c,
+    RowMap rm, int nseq, const int32_t *__restrict__ draft_tokens, int V, int chunks, int chunks_big, float c,
     uint64_t seed, uint64_t step, const float2 *__restrict__ part, const float *__restrict__ lse_in,
     int32_t *__restrict__ ws_kstar, float4 *__restrict__ ws_norm, int32_t *__restrict__ out_tokens,
     int32_t *__restrict__ out_num, float *__restrict__ out_logp, float *__restrict__ out_logq,
     float *__restrict__ out_lse, int32_t *status) {
   using E = Elt<DT>;
   const int K = rm.K, R = 2 * K + 1;
-  const int g = blockIdx.x, tid = threadIdx.x;
-  const int64_t src = (int64_t)g * rm.seq_step;
+  const int tid = threadIdx.x;
   __shared__ double sL2[2 * kMaxK + 1], sS[2 * kMaxK + 1];
   __shared__ float sMc[2 * kMaxK + 1];
   __shared__ double sLogp[kMaxK + 1], sLogq[kMaxK + 1];
   __shared__ int32_t sTok[kMaxK + 1];
   __shared__ int sFlags;
+  for (int g = blockIdx.x; g < nseq; g += gridDim.x) {
+  const int64_t src = (int64_t)g * rm.seq_step;
   if (tid == 0) sFlags = 0;
   __syncthreads();
   for (int r = tid; r < R; r += kWave) {
@@ -853,6 +858,8 @@ __global__ __launch_bounds__(kWave) void k_sps_decide(
     if (out_lse)
       for (int r = 0; r < R; ++r) out_lse[(int64_t)g * R + r] = (float)(sL2[r] * kLn2);
     if (sFlags) atomicOr(status, sFlags);
+  }
+  __syncthreads();  // the next sequence reuses the LDS
   }
 }
 
@@ -944,22 +951,23 @@ struct ResidRow {
 
 template <int DT>
 __global__ __launch_bounds__(kSpsFinalBlock) void k_sps_final(
-    RowMap rm, int V, int chunk_elems, int chunks, float c, uint64_t seed, uint64_t step,
+    RowMap rm, int nseq, int V, int chunk_elems, int chunks, float c, uint64_t seed, uint64_t step,
     const int32_t *__restrict__ ws_kstar, const float4 *__restrict__ ws_norm,
     const float2 *__restrict__ part2, int32_t *__restrict__ out_tokens, float *__restrict__ out_logp,
     int32_t *status) {
   const int K = rm.K;
-  const int g = blockIdx.x, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   __shared__ double sScan[kSpsFinalBlock / kWave];
   __shared__ int sMisc[4];
   __shared__ float sPickLogit;
+  __shared__ double sTot, sBase;
+  __shared__ int sUse, sCh;
+  for (int g = blockIdx.x; g < nseq; g += gridDim.x) {
   const int kstar = ws_kstar[g];
   const float4 nm = ws_norm[g];
   const char *prow = rm.row(g, kstar);
   const char *qrow = kstar < K ? rm.row(g, K + 1 + kstar) : nullptr;
   const float2 *p2 = part2 + (int64_t)g * chunks;
-  __shared__ double sTot, sBase;
-  __shared__ int sUse, sCh;
   const double u = philox_uniform(seed, (uint32_t)g, step, 4u, 0);
   if (tid < kWave) {
     // wave 0, one lane per chunk: the residual and target totals, then the first chunk
@@ -1032,6 +1040,8 @@ __global__ __launch_bounds__(kSpsFinalBlock) void k_sps_final(
     }
     if (tok < 0) atomicOr(status, isnan(total) ? SMCSD_ST_NAN_INPUT : SMCSD_ST_EMPTY_ROW);
   }
+  __syncthreads();  // the next sequence reuses the LDS
+  }
 }
 
 // ---------------------------------------------------------------------------------
@@ -1099,7 +1109,7 @@ static hipError_t launch_verify_t(const VerifyArgs &a) {
   const int chunks_big = (int)ceil_div(a.V, big_tile_elems(esz, a.mode == SMCSD_MODE_SMC_RACE));
   const int nb_per_seq = a.logq_in ? K : 2 * K;
   const int64_t ntiles = (int64_t)a.nseq * (chunks + (int64_t)nb_per_seq * chunks_big);
-  const unsigned grid = (unsigned)std::min<int64_t>(ntiles, (int64_t)1 << 30);
+  const unsigned grid = grid_blocks(ntiles, kStreamBlock);
   size_t pad = 0;
   if (K > 0 && a.mode != SMCSD_MODE_SMC_RACE) {
     const hipError_t e = lse_occupancy_pad<DT>(&pad);
@@ -1110,9 +1120,9 @@ static hipError_t launch_verify_t(const VerifyArgs &a) {
     hipLaunchKernelGGL((k_lse_partials<DT, false>), dim3(grid), dim3(kStreamBlock), pad, a.stream, rm,
                        a.nseq, a.V, ce, chunks, chunks_big, nb_per_seq, a.c, part, sub, ntiles,
                        a.seed, a.step, race);
-    hipLaunchKernelGGL((k_smc_finalize<DT, false>), dim3(a.nseq), dim3(kSmcFinalBlock), 0, a.stream,
-                       rm, a.draft_tokens, a.V, ce, chunks, chunks_big, a.c, a.alpha, a.seed, a.step,
-                       a.bonus_tag, part, a.logq_in, sub, race,
+    hipLaunchKernelGGL((k_smc_finalize<DT, false>), dim3(grid_blocks(a.nseq, kSmcFinalBlock)), dim3(kSmcFinalBlock), 0, a.stream,
+                       rm, a.nseq, a.draft_tokens, a.V, ce, chunks, chunks_big, a.c, a.alpha, a.seed,
+                       a.step, a.bonus_tag, part, a.logq_in, sub, race,
                        a.log_weights, a.out_tokens, a.out_num_tokens, a.out_logp, a.out_logq,
                        a.out_lse, a.status);
     return hipGetLastError();
@@ -1121,9 +1131,9 @@ static hipError_t launch_verify_t(const VerifyArgs &a) {
     hipLaunchKernelGGL((k_lse_partials<DT, true>), dim3(grid), dim3(kStreamBlock), 0, a.stream, rm,
                        a.nseq, a.V, ce, chunks, chunks_big, nb_per_seq, a.c, part, sub, ntiles,
                        a.seed, a.step, race);
-    hipLaunchKernelGGL((k_smc_finalize<DT, true>), dim3(a.nseq), dim3(kSmcFinalBlock), 0, a.stream,
-                       rm, a.draft_tokens, a.V, ce, chunks, chunks_big, a.c, a.alpha, a.seed, a.step,
-                       a.bonus_tag, part, a.logq_in, sub, race,
+    hipLaunchKernelGGL((k_smc_finalize<DT, true>), dim3(grid_blocks(a.nseq, kSmcFinalBlock)), dim3(kSmcFinalBlock), 0, a.stream,
+                       rm, a.nseq, a.draft_tokens, a.V, ce, chunks, chunks_big, a.c, a.alpha, a.seed,
+                       a.step, a.bonus_tag, part, a.logq_in, sub, race,
                        a.log_weights, a.out_tokens, a.out_num_tokens, a.out_logp, a.out_logq,
                        a.out_lse, a.status);
     return hipGetLastError();
@@ -1135,17 +1145,18 @@ static hipError_t launch_verify_t(const VerifyArgs &a) {
     hipLaunchKernelGGL((k_lse_partials<DT, false>), dim3(grid), dim3(kStreamBlock), pad, a.stream, rm,
                        a.nseq, a.V, ce, chunks, chunks_big, nb_per_seq, a.c, part, sub, ntiles,
                        a.seed, a.step, race);
-  hipLaunchKernelGGL(k_sps_decide<DT>, dim3(a.nseq), dim3(kWave), 0, a.stream, rm, a.draft_tokens,
-                     a.V, chunks, chunks_big, a.c, a.seed, a.step, part, a.lse_in, kstar, norm,
+  hipLaunchKernelGGL(k_sps_decide<DT>, dim3(grid_blocks(a.nseq, kWave)), dim3(kWave), 0, a.stream, rm,
+                     a.nseq, a.draft_tokens, a.V, chunks, chunks_big, a.c, a.seed, a.step, part,
+                     a.lse_in, kstar, norm,
                      a.out_tokens,
                      a.out_num_tokens, a.out_logp, a.out_logq, a.out_lse, a.status);
   const int64_t ntiles2 = (int64_t)a.nseq * chunks;
-  hipLaunchKernelGGL(k_sps_residual<DT>, dim3((unsigned)std::min<int64_t>(ntiles2, (int64_t)1 << 30)),
+  hipLaunchKernelGGL(k_sps_residual<DT>, dim3(grid_blocks(ntiles2, kStreamBlock)),
                      dim3(kStreamBlock), 0, a.stream, rm, a.V, ce, chunks, a.c, kstar, norm, part2,
                      ntiles2);
-  hipLaunchKernelGGL(k_sps_final<DT>, dim3(a.nseq), dim3(kSpsFinalBlock), 0, a.stream, rm, a.V, ce,
-                     chunks, a.c, a.seed, a.step, kstar, norm, part2, a.out_tokens, a.out_logp,
-                     a.status);
+  hipLaunchKernelGGL(k_sps_final<DT>, dim3(grid_blocks(a.nseq, kSpsFinalBlock)), dim3(kSpsFinalBlock), 0,
+                     a.stream, rm, a.nseq, a.V, ce, chunks, a.c, a.seed, a.step, kstar, norm, part2,
+                     a.out_tokens, a.out_logp, a.status);
   return hipGetLastError();
 }
 

@@ -431,3 +431,68 @@ def test_kv_table_filled_to_capacity(L, R):
         o = oracle.kv_reassign(anc, np.array([res], np.int32), T, bs, L, R, rc, fl, len(free))
         g = _kv_gpu(anc, np.array([res], np.int32), B, N, T, bs, L, R, rc, fl, len(free))
         assert _kv_equal(g, o)
+
+
+def _tiny_rows(n, rows, V, seed):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    return torch.randn((n, rows, V), generator=g, device="cuda") * 1.5
+
+
+@pytest.mark.parametrize("mode", ["smc", "sps", "resample_wave", "resample_block"])
+def test_batches_beyond_one_dispatch(mode):
+    """Batches whose one-workgroup-per-item kernels would need more than 2^32 threads (the
+    width of a dispatch): the kernels stride over their items with a capped grid, and every
+    item's result still matches the oracle."""
+    V = 8
+    if mode == "smc":                      # finalize: 256 threads per sequence
+        S, K = (1 << 24) + 1000, 0
+        tgt = _tiny_rows(S, 1, V, 1)
+        drf = torch.zeros((S, 0, V), device="cuda")
+        toks = _i32(S, 0)
+        out, st = _i32(S, 1), _i32(1)
+        lw = torch.zeros(S, device="cuda")
+        ws = sm.alloc_workspace(sm.OP_VERIFY_SMC, S, 1, K, V)
+        sm.verify(tgt, drf, toks, S, 1, K, V, 1.0, 1.0, sm.MODE_SMC, 3, 4, out, st, ws, log_weights=lw)
+        torch.cuda.synchronize()
+        o = oracle.verify_smc(tgt.cpu().numpy(), np.zeros((S, 0, V), np.float32),
+                              np.zeros((S, 0), np.int32), 1.0, 1.0, 3, 4, np.zeros(S, np.float32))
+        ok = o["margin"] >= H.MARGIN
+        g = out.cpu().numpy()[:, 0]
+        assert int(st.cpu()[0]) == o["status"] == 0
+        assert np.array_equal(g[ok], o["tokens"][ok, 0]) and (g >= 0).all()
+        assert np.max(np.abs(lw.cpu().numpy() - o["lw"])) <= H.TOL_LW
+    elif mode == "sps":                    # SpS final draw: 1024 threads per sequence
+        S, K = (1 << 22) + 300, 1
+        tgt = _tiny_rows(S, K + 1, V, 2)
+        drf = (tgt[:, :K] + _tiny_rows(S, K, V, 3)).contiguous()
+        toks = torch.randint(0, V, (S, K), device="cuda", dtype=torch.int32)
+        out, num, st = _i32(S, K + 1), _i32(S), _i32(1)
+        ws = sm.alloc_workspace(sm.OP_VERIFY_SPS, S, 1, K, V)
+        sm.verify(tgt, drf, toks, S, 1, K, V, 1.0, 1.0, sm.MODE_SPS, 5, 6, out, st, ws,
+                  out_num_tokens=num)
+        torch.cuda.synchronize()
+        o = oracle.verify_sps(tgt.cpu().numpy(), drf.cpu().numpy(), toks.cpu().numpy(), 1.0, 5, 6)
+        ok = np.minimum(o["margin_accept"], o["margin_final"]) >= H.MARGIN
+        assert int(st.cpu()[0]) == o["status"]
+        assert np.array_equal(num.cpu().numpy()[ok], o["num_tokens"][ok])
+        assert np.array_equal(out.cpu().numpy()[ok], o["tokens"][ok])
+    else:                                  # resample: one wave or one workgroup per prompt
+        N = 2 if mode == "resample_wave" else 65
+        B = (1 << 24) + 77 if mode == "resample_wave" else (1 << 22) + 77
+        g = torch.Generator(device="cuda").manual_seed(B)
+        lw = torch.randn((B, N), generator=g, device="cuda") * 2.0
+        lw_in = lw.cpu().numpy()
+        anc, ess, res, st = _i32(B, N), torch.zeros(B, device="cuda"), _i32(B), _i32(1)
+        sm.resample(lw, B, N, 0.6, 7, 8, anc, ess, res, st)
+        torch.cuda.synchronize()
+        o = oracle.resample(lw_in, float(np.float32(0.6)), 7, 8)
+        ok = o["margin_ess"] >= H.MARGIN
+        assert np.array_equal(res.cpu().numpy()[ok], o["resampled"][ok])
+        a = anc.cpu().numpy()
+        both = ok & (o["resampled"] == 1)
+        okp = both[:, None] & (o["margin_pos"] >= H.MARGIN)
+        assert np.array_equal(a[okp], o["ancestors"][okp])
+        kept = ok & (o["resampled"] == 0)
+        assert (a[kept] == np.arange(N)[None, :]).all()
+        e = ess.cpu().numpy().astype(np.float64)
+        assert np.max(np.abs(e - o["ess"]) / o["ess"]) <= H.TOL_ESS_REL

@@ -10,6 +10,11 @@ The same construction as the oracle's law pins (prefix-dependent seeded logit ta
   and by the exponential race.
 * SpS: rounds of the modified-rejection verify until three tokens are emitted -> the
   target law (the speculative-sampling notes: the output follows the target exactly).
+* Many particles: the same SIR round at N = 8, 16, 64 against P_N by Rao-Blackwellised
+  Monte Carlo, and the decay of the sampler's distance to the target with N (SMC
+  explainers, section 3: L1 error O(1/sqrt N), bias O(1/N)): the empirical L1 distance of
+  the GPU's samples and an unbiased estimate of their squared L2 distance, fitted on a
+  log-log scale beside the analytic slopes of ||P_N - pi||.
 
 Each GPU call draws its randomness from (seed, step, sequence index); the chi-square
 tests use p > 1e-4 on merged cells, like the oracle's pins.
@@ -142,3 +147,93 @@ def test_temperature_sweep_runs_and_reports_ranges(capsys):
         assert d["smc_tokens_per_round"] == d["K"] + 1
         assert 0.0 < d["smc_mean_ess_fraction"] <= 1.0
         assert 0.0 <= d["smc_resample_rate"] <= 1.0
+
+
+def _gpu_sir_counts(tgt, drf, N, runs, seed, alpha=1.0, mode=sm.MODE_SMC):
+    """Counts of the 512 continuations from one SMC-SD round on the GPU: drafts drawn with
+    torch on the device (no host copies of the rows), verify, forced resampling, and one
+    uniformly chosen output particle per prompt."""
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    S = runs * N
+    t = {d: torch.from_numpy(tgt[d]).cuda() for d in range(3)}
+    q0 = torch.softmax(torch.from_numpy(drf[0][0]).double().cuda(), -1)
+    q1 = torch.softmax(torch.from_numpy(drf[1]).double().cuda(), -1)
+    x1 = torch.multinomial(q0.float(), S, replacement=True, generator=g)
+    u = torch.rand(S, 1, generator=g, device="cuda", dtype=torch.float64)
+    x2 = (torch.cumsum(q1, -1)[x1] < u).sum(1).clamp(max=V - 1)
+    t_rows = torch.stack([t[0][0].expand(S, V), t[1][x1], t[2][x1 * V + x2]], 1).contiguous()
+    d0 = torch.from_numpy(drf[0][0]).cuda()
+    d1 = torch.from_numpy(drf[1]).cuda()
+    d_rows = torch.stack([d0.expand(S, V), d1[x1]], 1).contiguous()
+    toks = torch.stack([x1, x2], 1).to(torch.int32).contiguous()
+    del u
+    lw = torch.zeros(S, dtype=torch.float32, device="cuda")
+    out, st = _i32(S, K + 1), _i32(1)
+    ws = sm.alloc_workspace(sm.OP_VERIFY_SMC, runs, N, K, V)
+    sm.verify(t_rows, d_rows, toks, runs, N, K, V, 1.0, alpha, mode, seed, 0, out, st, ws,
+              log_weights=lw)
+    del t_rows, d_rows, ws
+    anc, ess, res = _i32(runs, N), torch.zeros(runs, device="cuda"), _i32(runs)
+    sm.resample(lw.view(runs, N), runs, N, 2.0, seed, 0, anc, ess, res, st)   # tau > 1: always
+    pick = torch.randint(0, N, (runs,), generator=g, device="cuda")
+    r = torch.arange(runs, device="cuda")
+    y = out[r * N + anc[r, pick].long()].long()
+    assert int(st.cpu()[0]) == 0 and bool((res == 1).all())
+    assert bool((y[:, :K] == toks[r * N + anc[r, pick].long()].long()).all())
+    ys = y[:, 0] * 64 + y[:, 1] * 8 + y[:, 2]
+    return torch.bincount(ys, minlength=V ** 3).double().cpu().numpy()
+
+
+@pytest.mark.parametrize("N", [8, 16, 64])
+def test_gpu_smc_round_follows_sir_law_many_particles(N):
+    tgt, drf = L._tables(31337)
+    P, PI = L._sir_law_mc(tgt, drf, N, 400000, seed=1000 + N)
+    P = P / P.sum()
+    counts = _gpu_sir_counts(tgt, drf, N, 100000, seed=300 + N)
+    assert L._chi2_pvalue(counts, P) > 1e-4
+    if N == 8:
+        assert L._chi2_pvalue(counts, PI) < 1e-12   # and it can tell P_8 from the target
+
+
+def test_gpu_error_decays_with_particles():
+    """||emp_N - pi||_1 of the GPU's samples and an unbiased estimate of ||P_N - pi||_2^2
+    from them (sum c(c-1)/(n(n-1)) - 2 sum pi c / n + sum pi^2), N = 1 .. 64, 10^6 prompts
+    each; log-log slopes printed beside the analytic ones.  The L1 fit stops at N = 8,
+    where the bias still exceeds the sampling noise of 10^6 draws (~0.015); the L2 fit
+    stops at N = 32 for the same reason."""
+    tgt, drf = L._tables(31337)
+    pi = L._target_law(tgt)
+    Ns = [1, 2, 4, 8, 16, 32, 64]
+    n = 1000000
+    l1_emp, l2_emp, l1_ana, l2_ana = [], [], [], []
+    for N in Ns:
+        if N <= 4:
+            P, PI = L._sir_law(tgt, drf, N, 1.0)
+        else:
+            P, PI = L._sir_law_mc(tgt, drf, N, 200000, seed=N)
+        assert np.allclose(PI, pi)
+        c = _gpu_sir_counts(tgt, drf, N, n, seed=500 + N)
+        assert c.sum() == n
+        l1_emp.append(np.abs(c / n - pi).sum())
+        l2_emp.append(np.sum(c * (c - 1)) / (n * (n - 1)) - 2 * np.sum(pi * c) / n + np.sum(pi ** 2))
+        l1_ana.append(np.abs(P - PI).sum())
+        l2_ana.append(np.sum((P - PI) ** 2))
+    logN = np.log(Ns)
+    s_l1_emp = np.polyfit(logN[:4], np.log(l1_emp[:4]), 1)[0]
+    s_l1_ana = np.polyfit(logN, np.log(l1_ana), 1)[0]
+    s_l2_emp = np.polyfit(logN[:6], 0.5 * np.log(np.maximum(l2_emp[:6], 1e-30)), 1)[0]
+    s_l2_ana = np.polyfit(logN, 0.5 * np.log(l2_ana), 1)[0]
+    print("\n[error decay] N = %s" % Ns)
+    print("[error decay] L1 GPU samples  %s  slope(N<=8) %.3f" % (
+        " ".join("%.4f" % x for x in l1_emp), s_l1_emp))
+    print("[error decay] L1 analytic     %s  slope %.3f" % (
+        " ".join("%.4f" % x for x in l1_ana), s_l1_ana))
+    print("[error decay] L2 GPU (unbiased) %s  slope(N<=32) %.3f" % (
+        " ".join("%.2e" % np.sqrt(max(x, 0.0)) for x in l2_emp), s_l2_emp))
+    print("[error decay] L2 analytic       %s  slope %.3f" % (
+        " ".join("%.2e" % np.sqrt(x) for x in l2_ana), s_l2_ana), flush=True)
+    assert s_l1_emp <= -0.4 and s_l1_ana <= -0.4
+    assert s_l2_emp <= -0.4 and s_l2_ana <= -0.4
+    # each unbiased L2 estimate agrees with the analytic value within its sampling error
+    for e, a in zip(l2_emp[:6], l2_ana[:6]):
+        assert abs(e - a) <= 0.25 * a + 6.0 / n, (e, a)
