@@ -3,9 +3,10 @@
 Workload (default): B=32 prompts x N=16 particles, K=4 draft tokens, V=128256, bf16 logits
 with the Zipf generator (one seeded vocabulary permutation, noise 0.3; draft = target +
 Normal(0, 0.8)), temperature 0.8, tau = 0.5, 2048-token shared prefix in 16-token blocks.
-A step is one pass of the whole hot path over one batch: smcsd_verify (LSE pass, gathers,
-bonus token, weight update), smcsd_resample (ESS, systematic resampling), smcsd_kv_reassign
-(refcounted block-table exchange + reservation).  Inputs are resident in HBM: four distinct
+A step is one pass of the whole hot path over one batch: the verify (LSE pass, gathers,
+bonus token, weight update), the resample (ESS, systematic resampling) and the KV exchange
+(refcounted block-table exchange + reservation), timed as one smcsd_step call per round
+(--two-calls: smcsd_verify + smcsd_resample_kv_reassign; --separate-kv: three calls).  Inputs are resident in HBM: four distinct
 logit sets (4.7 GB, far above the 256 MB last-level cache) are generated untimed and step t
 uses set t mod 4.
 
@@ -84,9 +85,12 @@ def _parse():
     ap.add_argument("--race-bonus", action="store_true",
                     help="SMCSD_MODE_SMC_RACE: the bonus token by an exponential race inside the "
                          "LSE pass instead of the inverse CDF with its one-slab re-read")
+    ap.add_argument("--two-calls", action="store_true",
+                    help="time smcsd_verify then smcsd_resample_kv_reassign instead of smcsd_step "
+                         "(the whole round in one call; same results)")
     ap.add_argument("--separate-kv", action="store_true",
-                    help="time smcsd_resample and smcsd_kv_reassign as two calls instead of the "
-                         "fused smcsd_resample_kv_reassign (same results)")
+                    help="time smcsd_verify, smcsd_resample and smcsd_kv_reassign as three calls "
+                         "(same results)")
     ap.add_argument("--graph", action="store_true",
                     help="record each run of timed steps in a HIP graph (untimed) and time its "
                          "replay: the same launches with the same arguments, without the host's "
@@ -172,9 +176,20 @@ def main():
     # the block pool holds M_cap slots per sequence: an episode is at most cfg.iters rounds
     max_rounds = cfg.iters
 
+    one_call = not (args.two_calls or args.separate_kv)
+
     def step(ev=None):
         t = state["t"]
         tgt, drf, toks, lq_in = sets[t % cfg.n_sets]
+        if one_call:
+            state["L"] += K + 1
+            sm.step(tgt, None if lq_in is not None else drf, toks, B, N, K, V, cfg.temperature,
+                    cfg.alpha, mode, cfg.tau, seed, t, lw, tokens, anc, ess, resampled, tables,
+                    cfg.block_size, state["L"], K + 1, rc, fl, top, cow, ncow, status, ws_v, ws_kv,
+                    out_num_tokens=num, out_logp=logp, out_logq=logq, logq_in=lq_in)
+            state["t"] += 1
+            state["round"] += 1
+            return
         if ev is not None:
             ev[0].record()
         sm.verify(tgt, None if lq_in is not None else drf, toks, B, N, K, V, cfg.temperature,
@@ -231,8 +246,8 @@ def main():
     while done < args.steps:
         n = steps_in_episode(args.steps - done)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               if (not args.graph and i > 0 and (done + i) % EVENT_EVERY == 0) else None
-               for i in range(n)]
+               if (not args.graph and not one_call and i > 0 and (done + i) % EVENT_EVERY == 0)
+               else None for i in range(n)]
         graph = None
         if args.graph:
             # record the run's steps (nothing executes during capture), then replay them once
@@ -322,12 +337,12 @@ def main():
                             cfg.dtype, cfg.target_kind, cfg.temperature, cfg.alpha, cfg.tau,
                             cfg.ctx0, cfg.block_size, ", shared prefix" if cfg.shared_prefix else ""),
             "logits_dtype": cfg.dtype,
-            "step": "smcsd_verify%s%s + %s%s" % (
-                " (logq_in: target rows only)" if args.draft_logq else "",
-                " (race-mode bonus)" if args.race_bonus else "",
-                "smcsd_resample + smcsd_kv_reassign" if args.separate_kv else
-                "smcsd_resample_kv_reassign (smcsd_resample + smcsd_kv_reassign in one launch fewer)",
-                "; timed as HIP graph replays" if args.graph else ""),
+            "step": ("smcsd_step (verify + resample + KV exchange in one call)" if one_call else
+                     "smcsd_verify + %s" % ("smcsd_resample + smcsd_kv_reassign" if args.separate_kv
+                                            else "smcsd_resample_kv_reassign"))
+                    + (" (logq_in: target rows only)" if args.draft_logq else "")
+                    + (" (race-mode bonus)" if args.race_bonus else "")
+                    + ("; timed as HIP graph replays" if args.graph else ""),
             "settle": {"ms": args.settle_ms, "steps": settle_steps},
             "draft_sample": draft_info,
             "logit_sets": cfg.n_sets,

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SMCSD_VERSION 4
+#define SMCSD_VERSION 5
 
 /* logits element type */
 #define SMCSD_DTYPE_F32 0
@@ -298,6 +298,34 @@ int smcsd_resample_kv_reassign(float *log_weights, int B, int N, float tau, uint
                                int32_t *free_top, int64_t P, int32_t *cow, int32_t *cow_count,
                                int32_t *status, void *workspace, size_t workspace_bytes,
                                void *stream);
+
+/*
+ * smcsd_step - one whole SMC-SD round on the batch: smcsd_verify (SMC or SMC race mode;
+ * row_stride and the draft's optional log q as there, seq_step 1) followed by
+ * smcsd_resample_kv_reassign, with the same outputs and the same bits as those two calls
+ * (SMC explainers, methodology "core flow": Score, Bonus, Reweight, then Resample and the
+ * KV pointer exchange of "system optimisation design").  It enqueues the two calls'
+ * kernels in order on `stream` with one host call, for callers that run a whole round per
+ * call; both workspaces stay separate, so a round can also be split into the two calls.
+ * Arguments: those of smcsd_verify (log_weights [B, N] in/out; out_tokens required;
+ * out_num_tokens, out_logp, out_logq, out_lse nullable) and of smcsd_resample_kv_reassign
+ * (tau; ancestors [B, N], ess [B], resampled [B]; the KV state; seq_len is the length
+ * after this round's K+1 tokens, as there); verify_workspace sized by
+ * smcsd_workspace_bytes(SMCSD_OP_VERIFY_SMC, B, N, K, V, 0) and kv_workspace by
+ * smcsd_workspace_bytes(SMCSD_OP_KV, B, N, 0, 0, P) (zero-filled before first use and kept,
+ * shared with smcsd_kv_reassign and smcsd_resample_kv_reassign).  Limits, errors and status
+ * bits: those of both calls; mode SMCSD_MODE_SPS is SMCSD_EINVAL.
+ */
+int smcsd_step(const void *target_logits, const void *draft_logits, int dtype, int64_t row_stride,
+               const int32_t *draft_tokens, int B, int N, int K, int V, float temperature,
+               float alpha, int mode, float tau, uint64_t seed, uint64_t step,
+               const float *logq_in, float *log_weights, int32_t *out_tokens,
+               int32_t *out_num_tokens, float *out_logp, float *out_logq, float *out_lse,
+               int32_t *ancestors, float *ess, int32_t *resampled, int32_t *block_tables,
+               int M_cap, int block_size, int64_t seq_len, int reserve_tokens, int32_t *refcounts,
+               int32_t *free_list, int32_t *free_top, int64_t P, int32_t *cow, int32_t *cow_count,
+               int32_t *status, void *verify_workspace, size_t verify_workspace_bytes,
+               void *kv_workspace, size_t kv_workspace_bytes, void *stream);
 
 /*
  * smcsd_philox4x32_10 - the library's device Philox4x32-10 block function (SC'11),

@@ -30,7 +30,7 @@ ST_BAD_INPUT = 16
 
 EXPORTED = ("smcsd_version", "smcsd_status_string", "smcsd_workspace_bytes", "smcsd_verify",
             "smcsd_verify_static", "smcsd_draft_sample", "smcsd_resample", "smcsd_kv_reassign",
-            "smcsd_resample_kv_reassign", "smcsd_philox4x32_10")
+            "smcsd_resample_kv_reassign", "smcsd_step", "smcsd_philox4x32_10")
 
 _DT = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
 
@@ -73,6 +73,10 @@ def load_library(path: str = LIB_PATH):
     lib.smcsd_resample_kv_reassign.argtypes = [P, i32, i32, f32, u64, u64, P, P, P, P, i32, i32, i64,
                                                i32, P, P, P, i64, P, P, P, P, sz, P]
     lib.smcsd_resample_kv_reassign.restype = i32
+    lib.smcsd_step.argtypes = [P, P, i32, i64, P, i32, i32, i32, i32, f32, f32, i32, f32, u64, u64,
+                               P, P, P, P, P, P, P, P, P, P, P, i32, i32, i64, i32, P, P, P, i64,
+                               P, P, P, P, sz, P, sz, P]
+    lib.smcsd_step.restype = i32
     lib.smcsd_philox4x32_10.argtypes = [P, P, i32, P, P]
     lib.smcsd_philox4x32_10.restype = i32
     if path == LIB_PATH:
@@ -274,6 +278,52 @@ def resample_kv_reassign(log_weights: torch.Tensor, B: int, N: int, tau: float, 
         _dev(status, "status", torch.int32, 1), _dev(workspace, "workspace", torch.uint8),
         workspace.numel(), _stream(stream))
     _check(rc, "smcsd_resample_kv_reassign")
+
+
+def step(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: Optional[torch.Tensor],
+         B: int, N: int, K: int, V: int, temperature: float, alpha: float, mode: int, tau: float,
+         seed: int, step: int, log_weights: torch.Tensor, out_tokens: torch.Tensor,
+         ancestors: torch.Tensor, ess: torch.Tensor, resampled: torch.Tensor,
+         block_tables: torch.Tensor, block_size: int, seq_len: int, reserve_tokens: int,
+         refcounts: torch.Tensor, free_list: torch.Tensor, free_top: torch.Tensor,
+         cow: torch.Tensor, cow_count: torch.Tensor, status: torch.Tensor,
+         verify_workspace: torch.Tensor, kv_workspace: torch.Tensor, out_num_tokens=None,
+         out_logp=None, out_logq=None, out_lse=None, logq_in=None,
+         row_stride: Optional[int] = None, stream=None) -> None:
+    """smcsd_step: smcsd_verify (MODE_SMC or MODE_SMC_RACE) then smcsd_resample_kv_reassign
+    in one call (the same bits); seq_len is the length after this round's K+1 tokens."""
+    if target.dtype not in _DT:
+        raise SmcsdError("logits must be bfloat16 or float32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B * N:
+        raise SmcsdError("block_tables must be [B*N, M_cap]")
+    rs = V if row_stride is None else int(row_stride)
+    S = B * N
+    M_cap = block_tables.shape[1]
+    P = refcounts.numel()
+    tp = _dev(target, "target", target.dtype, S * (K + 1) * rs - (rs - V) if S else 0)
+    dp = _dev(draft, "draft", target.dtype, S * K * rs - (rs - V) if S and K else 0) \
+        if K > 0 and (draft is not None or logq_in is None) else None
+    xp = _dev(draft_tokens, "draft_tokens", torch.int32, S * K) if K > 0 else None
+    rc = _L().smcsd_step(
+        tp, dp, _DT[target.dtype], rs, xp, B, N, K, V, float(temperature), float(alpha), mode,
+        float(tau), int(seed) & (2**64 - 1), int(step) & (2**64 - 1),
+        _dev(logq_in, "logq_in", torch.float32, S * K),
+        _dev(log_weights, "log_weights", torch.float32, S),
+        _dev(out_tokens, "out_tokens", torch.int32, S * (K + 1)),
+        _dev(out_num_tokens, "out_num_tokens", torch.int32, S),
+        _dev(out_logp, "out_logp", torch.float32, S * (K + 1)),
+        _dev(out_logq, "out_logq", torch.float32, S * K),
+        _dev(out_lse, "out_lse", torch.float32, S * (2 * K + 1)),
+        _dev(ancestors, "ancestors", torch.int32, S), _dev(ess, "ess", torch.float32, B),
+        _dev(resampled, "resampled", torch.int32, B),
+        _dev(block_tables, "block_tables", torch.int32), M_cap, block_size, int(seq_len),
+        reserve_tokens, _dev(refcounts, "refcounts", torch.int32),
+        _dev(free_list, "free_list", torch.int32, P), _dev(free_top, "free_top", torch.int32, 1), P,
+        _dev(cow, "cow", torch.int32, 3 * S), _dev(cow_count, "cow_count", torch.int32, 1),
+        _dev(status, "status", torch.int32, 1),
+        _dev(verify_workspace, "verify_workspace", torch.uint8), verify_workspace.numel(),
+        _dev(kv_workspace, "kv_workspace", torch.uint8), kv_workspace.numel(), _stream(stream))
+    _check(rc, "smcsd_step")
 
 
 def philox4x32_10(counters: torch.Tensor, keys: torch.Tensor, out: torch.Tensor, stream=None):

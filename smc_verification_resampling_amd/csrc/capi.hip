@@ -290,6 +290,76 @@ int smcsd_resample_kv_reassign(float *log_weights, int B, int N, float tau, uint
                           status, static_cast<char *>(workspace), as_stream(stream)));
 }
 
+int smcsd_step(const void *target_logits, const void *draft_logits, int dtype, int64_t row_stride,
+               const int32_t *draft_tokens, int B, int N, int K, int V, float temperature,
+               float alpha, int mode, float tau, uint64_t seed, uint64_t step,
+               const float *logq_in, float *log_weights, int32_t *out_tokens,
+               int32_t *out_num_tokens, float *out_logp, float *out_logq, float *out_lse,
+               int32_t *ancestors, float *ess, int32_t *resampled, int32_t *block_tables,
+               int M_cap, int block_size, int64_t seq_len, int reserve_tokens, int32_t *refcounts,
+               int32_t *free_list, int32_t *free_top, int64_t P, int32_t *cow, int32_t *cow_count,
+               int32_t *status, void *verify_workspace, size_t verify_workspace_bytes,
+               void *kv_workspace, size_t kv_workspace_bytes, void *stream) {
+  // the checks of smcsd_verify (SMC modes) and of smcsd_resample_kv_reassign
+  if (dtype != SMCSD_DTYPE_F32 && dtype != SMCSD_DTYPE_BF16) return SMCSD_EDTYPE;
+  if (mode != SMCSD_MODE_SMC && mode != SMCSD_MODE_SMC_RACE) return SMCSD_EINVAL;
+  if (B < 0 || N < 1 || N > kMaxN || K < 0 || K > kMaxK || V < 1 || V > kMaxV) return SMCSD_EINVAL;
+  if (row_stride < V) return SMCSD_EINVAL;
+  if (!(temperature > 0.0f) || !std::isfinite(temperature) || !std::isfinite(alpha) ||
+      !std::isfinite(tau))
+    return SMCSD_EINVAL;
+  const int chk = kv_check(B, N, block_tables, M_cap, block_size, seq_len, reserve_tokens,
+                           refcounts, free_list, free_top, P, cow, cow_count, status, kv_workspace,
+                           kv_workspace_bytes);
+  if (chk == 1) return SMCSD_OK;
+  if (chk != SMCSD_OK) return chk;
+  const int64_t S = (int64_t)B * N;
+  if (S > INT32_MAX / 2) return SMCSD_EINVAL;
+  const size_t esz = dtype == SMCSD_DTYPE_BF16 ? 2 : 4;
+  if (!target_logits || !aligned(target_logits, esz)) return SMCSD_EINVAL;
+  if (K > 0 && (!draft_tokens || (!logq_in && (!draft_logits || !aligned(draft_logits, esz)))))
+    return SMCSD_EINVAL;
+  if (!out_tokens || !log_weights || !ancestors || !ess || !resampled) return SMCSD_EINVAL;
+  const size_t need = verify_ws_layout(S, K, V, 0).total;
+  if (!verify_workspace || !aligned(verify_workspace, 256) || verify_workspace_bytes < need)
+    return SMCSD_EWORKSPACE;
+
+  VerifyArgs a{};
+  a.tgt = target_logits;
+  a.drf = draft_logits;
+  a.dtype = dtype;
+  a.row_stride = row_stride;
+  a.seq_step = 1;
+  a.draft_tokens = draft_tokens;
+  a.nseq = (int)S;
+  a.K = K;
+  a.V = V;
+  a.c = (float)(1.4426950408889634073599246810018921 / (double)temperature);
+  a.alpha = alpha;
+  a.mode = mode;
+  a.seed = seed;
+  a.step = step;
+  a.logq_in = logq_in;
+  a.bonus_tag = 1u;
+  a.log_weights = log_weights;
+  a.out_tokens = out_tokens;
+  a.out_num_tokens = out_num_tokens;
+  a.out_logp = out_logp;
+  a.out_logq = out_logq;
+  a.out_lse = out_lse;
+  a.status = status;
+  a.ws = static_cast<char *>(verify_workspace);
+  a.stream = as_stream(stream);
+  // The verify's kernels, then the resample + exchange kernels on the same stream: the
+  // latter read the log-weights the verify wrote.
+  const hipError_t e = launch_verify(a);
+  if (e != hipSuccess) return hip_rc(e);
+  const FusedResample fr{log_weights, tau, seed, step, ancestors, ess, resampled};
+  return hip_rc(launch_kv(nullptr, nullptr, fr, B, N, block_tables, M_cap, block_size, seq_len,
+                          reserve_tokens, refcounts, free_list, free_top, P, cow, cow_count, status,
+                          static_cast<char *>(kv_workspace), as_stream(stream)));
+}
+
 int smcsd_philox4x32_10(const uint32_t *counters, const uint32_t *keys, int n, uint32_t *out,
                         void *stream) {
   if (n < 0) return SMCSD_EINVAL;

@@ -53,6 +53,7 @@ class Stats:
     verify_seqs_checked: int = 0
     kv_calls_checked: int = 0
     fused_calls_checked: int = 0
+    step_calls_checked: int = 0
     resample_events: int = 0
     sps_checked: int = 0
     notes: list = dataclasses.field(default_factory=list)
@@ -89,9 +90,12 @@ class Pipeline:
     def __init__(self, cfg: Config, sample: int | None = None, sps_sample: int | None = None,
                  device: str = "cuda", check: bool = True, fused: str = "alternate",
                  full_rounds=()):
-        """fused: "alternate" runs the Resample + KV step as smcsd_resample_kv_reassign (the
-        entry point the benchmark times) on odd rounds and as smcsd_resample then
-        smcsd_kv_reassign on even rounds; "always" / "never" use one form throughout.
+        """fused: "alternate" cycles through the three forms of a round: smcsd_verify then
+        smcsd_resample then smcsd_kv_reassign (rounds t = 0 mod 3), smcsd_verify then
+        smcsd_resample_kv_reassign (t = 1 mod 3), and smcsd_step, the whole round in one call
+        (t = 2 mod 3; the entry point the benchmark times), which is also compared bit for bit
+        with the two-call form run on a copy of the state; "always" uses the second form
+        throughout, "never" the first.
         full_rounds: rounds whose verify outputs are checked on every sequence even when
         `sample` limits the others."""
         self.cfg = cfg
@@ -190,23 +194,88 @@ class Pipeline:
         pick.add(0 if t % 2 == 0 else S - 1)
         return np.array(sorted(pick), dtype=np.int64)
 
+    def _form(self, t: int) -> str:
+        if self.fused == "always":
+            return "fused"
+        if self.fused == "never" or t < 0:
+            return "separate"
+        return ("separate", "fused", "step")[t % 3]
+
     def _fused_round(self, t: int) -> bool:
-        return self.fused == "always" or (self.fused == "alternate" and t % 2 == 1)
+        return self._form(t) in ("fused", "step")
+
+    def _step_round(self, t: int, tgt, drf, toks):
+        """The round through smcsd_step, and on a copy of the state through smcsd_verify then
+        smcsd_resample_kv_reassign: every output must agree bit for bit.  Returns the copy's
+        log-weights after its verify (the resample's input, which smcsd_step does not expose)
+        and that verify's status."""
+        cfg = self.cfg
+        B, N, K, S = cfg.B, cfg.N, cfg.K, cfg.S
+        sh = {k: getattr(self, k).clone() for k in ("lw", "tables", "rc", "free_list", "free_top",
+                                                    "ws_kv")}
+        i32 = dict(dtype=torch.int32, device=self.dev)
+        f32 = dict(dtype=torch.float32, device=self.dev)
+        out = dict(tok=torch.zeros((S, K + 1), **i32), num=torch.zeros(S, **i32),
+                   logp=torch.zeros((S, K + 1), **f32), logq=torch.zeros((S, max(K, 1)), **f32),
+                   lse=torch.zeros((S, 2 * K + 1), **f32), anc=torch.zeros((B, N), **i32),
+                   ess=torch.zeros(B, **f32), res=torch.zeros(B, **i32),
+                   cow=torch.zeros((S, 3), **i32), ncow=torch.zeros(1, **i32),
+                   st=torch.zeros(1, **i32))
+        sm.step(tgt, drf, toks, B, N, K, cfg.V, cfg.temperature, cfg.alpha, sm.MODE_SMC, cfg.tau,
+                self.seed, t, self.lw, self.tokens, self.anc, self.ess, self.resampled, self.tables,
+                cfg.block_size, self.L, K + 1, self.rc, self.free_list, self.free_top, self.cow,
+                self.cow_count, self.status, self.ws_v, self.ws_kv, out_num_tokens=self.num,
+                out_logp=self.logp, out_logq=self.logq, out_lse=self.lse)
+        sm.verify(tgt, drf, toks, B, N, K, cfg.V, cfg.temperature, cfg.alpha, sm.MODE_SMC, self.seed,
+                  t, out["tok"], out["st"], self.ws_v, log_weights=sh["lw"], out_num_tokens=out["num"],
+                  out_logp=out["logp"], out_logq=out["logq"], out_lse=out["lse"])
+        lw_post = sh["lw"].clone()
+        st_verify = out["st"].clone()
+        sm.resample_kv_reassign(sh["lw"].view(B, N), B, N, cfg.tau, self.seed, t, out["anc"],
+                                out["ess"], out["res"], sh["tables"], cfg.block_size, self.L, K + 1,
+                                sh["rc"], sh["free_list"], sh["free_top"], out["cow"], out["ncow"],
+                                out["st"], sh["ws_kv"])
+        if not self.check:
+            return lw_post, st_verify
+        torch.cuda.synchronize()
+
+        def bits(x):
+            return x.view(torch.int32) if x.dtype == torch.float32 else x
+
+        top = int(self.free_top.cpu()[0])
+        n = int(self.cow_count.cpu()[0])
+        pairs = [(self.tokens, out["tok"]), (self.num, out["num"]), (self.logp, out["logp"]),
+                 (self.logq, out["logq"]), (self.lse, out["lse"]), (self.lw, sh["lw"]),
+                 (self.anc, out["anc"]), (self.ess, out["ess"]), (self.resampled, out["res"]),
+                 (self.tables, sh["tables"]), (self.rc, sh["rc"]), (self.free_top, sh["free_top"]),
+                 (self.free_list[:top], sh["free_list"][:top]), (self.cow_count, out["ncow"]),
+                 (self.cow[:n], out["cow"][:n]), (self.status, out["st"])]
+        same = all(torch.equal(bits(a), bits(b)) for a, b in pairs)
+        self.stats.decision(same, math.inf, "smcsd_step vs the two calls at t=%d" % t)
+        self.stats.step_calls_checked += 1
+        return lw_post, st_verify
 
     def round(self, t: int):
         cfg = self.cfg
         B, N, K, S = cfg.B, cfg.N, cfg.K, cfg.S
         tgt, drf, toks = self.sets[t % cfg.n_sets]
         lw_before = self.lw.clone() if self.check else None
+        form = self._form(t)
         self.status.zero_()
-        sm.verify(tgt, drf, toks, B, N, K, cfg.V, cfg.temperature, cfg.alpha, sm.MODE_SMC,
-                  self.seed, t, self.tokens, self.status, self.ws_v, log_weights=self.lw,
-                  out_num_tokens=self.num, out_logp=self.logp, out_logq=self.logq,
-                  out_lse=self.lse)
-        lw_post = self.lw.clone() if self.check else None
-        st_verify = self.status.clone()
-        fused = self._fused_round(t)
-        if fused:
+        kv_before = None
+        if form == "step":
+            # the whole round in one call; the KV state at its entry is kept for the oracle
+            kv_before = self._kv_snapshot() if self.check else None
+            self.L += K + 1
+            lw_post, st_verify = self._step_round(t, tgt, drf, toks)
+        else:
+            sm.verify(tgt, drf, toks, B, N, K, cfg.V, cfg.temperature, cfg.alpha, sm.MODE_SMC,
+                      self.seed, t, self.tokens, self.status, self.ws_v, log_weights=self.lw,
+                      out_num_tokens=self.num, out_logp=self.logp, out_logq=self.logq,
+                      out_lse=self.lse)
+            lw_post = self.lw.clone() if self.check else None
+            st_verify = self.status.clone()
+        if form == "fused":
             # Resample + KV exchange in one entry point: the KV state at its entry is kept
             # for the oracle, whose reassign then takes the ancestors the GPU drew
             kv_before = self._kv_snapshot() if self.check else None
@@ -216,7 +285,7 @@ class Pipeline:
                                     self.ess, self.resampled, self.tables, cfg.block_size, self.L,
                                     K + 1, self.rc, self.free_list, self.free_top, self.cow,
                                     self.cow_count, self.status, self.ws_kv)
-        else:
+        elif form == "separate":
             sm.resample(self.lw.view(B, N), B, N, cfg.tau, self.seed, t, self.anc, self.ess,
                         self.resampled, self.status)
         if cfg.sps:
@@ -230,12 +299,11 @@ class Pipeline:
             self._check_resample(t, lw_post)
             if cfg.sps:
                 self._check_sps(t, tgt, drf, toks)
-        if fused:
-            if self.check:
-                self._check_kv(kv_before, self.anc, self.resampled, int(self.status.cpu()[0]), t)
-        else:
+        if form == "separate":
             self.L += K + 1
             self._kv(self.anc, self.resampled, t)
+        elif self.check:
+            self._check_kv(kv_before, self.anc, self.resampled, int(self.status.cpu()[0]), t)
 
     def _check_verify(self, t, tgt, drf, toks, lw_before, lw_post, status):
         cfg = self.cfg
@@ -341,9 +409,11 @@ def run(cfg: Config, iters: int, sample=None, sps_sample=None, label="", fused="
                 cfg.name, label, t + 1, iters, time.time() - t0, p.stats.decisions, p.stats.flagged,
                 p.stats.unflagged_mismatch), flush=True)
     msg = p.stats.assert_ok()
-    print("[%s%s] OK %s verify_seqs_checked=%d kv_calls=%d fused_calls=%d" % (
+    print("[%s%s] OK %s verify_seqs_checked=%d kv_calls=%d fused_calls=%d step_calls=%d" % (
         cfg.name, label, msg, p.stats.verify_seqs_checked, p.stats.kv_calls_checked,
-        p.stats.fused_calls_checked), flush=True)
+        p.stats.fused_calls_checked, p.stats.step_calls_checked), flush=True)
     if fused != "never" and iters > 1:
         assert p.stats.fused_calls_checked > 0
+    if fused == "alternate" and iters > 2:
+        assert p.stats.step_calls_checked > 0
     return p

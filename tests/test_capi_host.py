@@ -45,7 +45,7 @@ def test_gfx950_code_object_present(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.smcsd_version() == 4
+    assert lib.smcsd_version() == 5
     assert sm.status_string(0) == "ok"
     assert "workspace" in sm.status_string(-4)
     assert "pool" in sm.status_string(sm.ST_NOSPACE)
@@ -183,3 +183,26 @@ def test_verify_static_host_validation(lib):
     assert sm.workspace_bytes(sm.OP_VERIFY_SMC, 64, 64, 8, 128256) > sm.STATIC_SCRATCH_BYTES
     assert rc(B=64, N=64, K=8, V=128256) == -5
     assert sm.status_string(-5) == "call needs more scratch than the static array holds"
+
+
+def test_step_host_validation(lib):
+    p = ctypes.c_void_p(0x1000)
+
+    def rc(**kw):
+        a = dict(dtype=1, B=2, N=4, K=1, V=64, T=1.0, mode=0, tau=0.5, lw=p, M=8, bs=4, L=4, R=2,
+                 P=64, vws=p, vwsb=1 << 20, kws=p, kwsb=1 << 20)
+        a.update(kw)
+        return lib.smcsd_step(p, p, a["dtype"], a["V"], p, a["B"], a["N"], a["K"], a["V"], a["T"],
+                              1.0, a["mode"], a["tau"], 0, 0, None, a["lw"], p, None, None, None, None,
+                              p, p, p, p, a["M"], a["bs"], a["L"], a["R"], p, p, p, a["P"], p, p, p,
+                              a["vws"], a["vwsb"], a["kws"], a["kwsb"], None)
+    assert rc(dtype=7) == -2
+    assert rc(mode=1) == -1                     # SpS is not a round of SMC-SD
+    assert rc(tau=float("nan")) == -1
+    assert rc(T=0.0) == -1
+    assert rc(N=0) == -1 and rc(K=33) == -1
+    assert rc(L=30, R=8) == -1                  # beyond M_cap slots
+    assert rc(lw=None) == -1
+    assert rc(vwsb=16) == -4 and rc(kwsb=16) == -4
+    assert rc(vws=ctypes.c_void_p(0x1010)) == -4
+    assert rc(B=0) == 0
