@@ -56,12 +56,15 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // A tile of the bonus row also sums its kSlabs slabs (one slab = the kStreamBlock vectors a
 // workgroup loads together) so that the bonus draw re-reads one slab, not the whole chunk.
 constexpr int kSlabs = kStreamUnroll;
+// Residual slabs per chunk of the SpS draw (one per wave of a kStreamBlock workgroup).
+constexpr int kSpsSlabsWs = kStreamBlock / 64;
 
 // Verify workspace: [row partials float2 x nseq*(2K+1)*chunks][bonus slab sums float x nseq*chunks*kSlabs]
 //                   [bonus race winners int2 x nseq*chunks]
-//                   [kstar int32 x nseq][L2 pair double2 x nseq][residual partials float2 x nseq*chunks]
+//                   [kstar int32 x nseq][L2 pair double2 x nseq]
+//                   [residual slab sums float2 x nseq*chunks*kSpsSlabsWs][arrival counters int32 x nseq]
 struct VerifyWs {
-  size_t part, sub, race, kstar, l2, part2, total;
+  size_t part, sub, race, kstar, l2, part2, arrivals, total;
 };
 inline VerifyWs verify_ws_layout(int64_t nseq, int K, int V, int mode) {
   VerifyWs w{};
@@ -79,7 +82,9 @@ inline VerifyWs verify_ws_layout(int64_t nseq, int K, int V, int mode) {
     w.l2 = off;
     off += align256(sizeof(double) * 2 * (size_t)nseq);
     w.part2 = off;
-    off += align256(sizeof(float) * 2 * (size_t)(nseq * chunks));
+    off += align256(sizeof(float) * 2 * (size_t)(nseq * chunks * kSpsSlabsWs));
+    w.arrivals = off;
+    off += align256(sizeof(int32_t) * (size_t)nseq);
   }
   w.total = off;
   return w;

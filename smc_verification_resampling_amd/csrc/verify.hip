@@ -22,10 +22,11 @@
 //                    the finalize takes the best of the tiles' winners and reads only the
 //                    winner's logit: no slab sums and no re-read, for one Philox block per
 //                    four vocabulary entries and two logarithms per entry.
-//   k_sps_decide / k_sps_residual / k_sps_final
-//                    SpS: acceptance tests from the gathered log-probabilities, one pass
-//                    over the residual max(0, p - q) (or p_K) of the single row pair that is
-//                    needed, and its inverse CDF.
+//   k_sps_resid      SpS: acceptance tests from the gathered log-probabilities (in every
+//                    workgroup, or from k_sps_decide for rows of many chunks), one pass over
+//                    the residual max(0, p - q) (or p_K) of the single row pair that is
+//                    needed with per-slab sums, and its inverse CDF by the sequence's last
+//                    workgroup, which re-reads one slab.
 #include <algorithm>
 #include <climits>
 
@@ -187,7 +188,8 @@ __global__ __launch_bounds__(kStreamBlock) void k_lse_partials(RowMap rm, int ns
                                                                 float *__restrict__ sub,
                                                                 int64_t ntiles, uint64_t seed,
                                                                 uint64_t step,
-                                                                int2 *__restrict__ race) {
+                                                                int2 *__restrict__ race,
+                                                                int32_t *__restrict__ zero_seq) {
   using E = Elt<DT>;
   constexpr int EPV = E::kPerVec;
   __shared__ Lse lds[kStreamBlock / kWave];
@@ -207,6 +209,8 @@ __global__ __launch_bounds__(kStreamBlock) void k_lse_partials(RowMap rm, int ns
   const int64_t M = min(nB, (int64_t)(RACE ? 0 : kTailBonusTiles));
   const int64_t n1 = ntiles - M, nB1 = nB - M;
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    // zero_seq (SpS: the draw's arrival counters) gets one zero per sequence (ntiles >= nseq)
+    if (zero_seq && t < nseq && tid == 0) zero_seq[t] = 0;
     int64_t tt;
     bool isb;
     if (t < n1) {
@@ -379,7 +383,7 @@ __device__ __forceinline__ RowNorm row_norm(const float2 *p, int chunks, float c
   return r;
 }
 
-// Inverse CDF inside one chunk [e0, e1) of a row: the first v whose running sum
+// Inverse CDF inside one range [e0, e1) of a row (a chunk or a slab): the first v whose running sum
 // base + sum_{w<=v} val(w) exceeds target.  The chunk is cut into units of 8 consecutive
 // elements; thread t loads units [t*UPT, (t+1)*UPT) once and keeps them in registers.
 // Unit sums are fp32 (fn.reduce), running sums fp64.  One workgroup exclusive scan finds
@@ -388,17 +392,15 @@ __device__ __forceinline__ RowNorm row_norm(const float2 *p, int chunks, float c
 // margin is at rounding level; then the last element with a positive value before the
 // crossing point is returned.  Every thread must call it; every thread gets the index
 // (-1 if there is none) and *logit the pick's logit (fn.logit).  UPT * 8 * BLOCK must
-// cover the chunk.
-// Workgroup sizes of the kernels that re-read one chunk: the SMC finalize runs one
-// workgroup per sequence (hundreds at a time), the SpS draw one per SpS sequence (few).
+// cover the range.
+// Workgroup size of the SMC finalize, one workgroup per sequence (hundreds at a time).
 constexpr int kSmcFinalBlock = 256;
-constexpr int kSpsFinalBlock = 1024;
 
 // 8-element units per thread when a BLOCK-thread workgroup re-reads one chunk
 template <int DT, int BLOCK>
 constexpr int kUnitsPerThread = (DT == SMCSD_DTYPE_BF16 ? kChunkElemsBf16 : kChunkElemsF32) / 8 /
                                 BLOCK;
-static_assert(kChunkElemsF32 % (8 * kSpsFinalBlock) == 0 && kChunkElemsF32 % (8 * kSmcFinalBlock) == 0,
+static_assert(kChunkElemsF32 % (8 * kSmcFinalBlock) == 0,
               "a chunk must split evenly into the workgroup's units");
 
 template <int BLOCK, int UPT, typename Fn>
@@ -863,78 +865,48 @@ __global__ __launch_bounds__(kWave) void k_sps_decide(
   }
 }
 
-// Residual element values, identical in the pass and in the re-read.
-constexpr int kResidBatch = 32;
-
-template <int DT>
-__global__ __launch_bounds__(kStreamBlock) void k_sps_residual(
-    RowMap rm, int V, int chunk_elems, int chunks, float c, const int32_t *__restrict__ ws_kstar,
-    const float4 *__restrict__ ws_norm, float2 *__restrict__ part2, int64_t ntiles) {
-  __shared__ float red[kStreamBlock / kWave];
-  const int K = rm.K;
-  const int tid = threadIdx.x;
-  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const int g = (int)(t / chunks);
-    const int ch = (int)(t - (int64_t)g * chunks);
-    const int kstar = ws_kstar[g];
-    const float4 nm = ws_norm[g];
-    const char *prow = rm.row(g, kstar);
-    const char *qrow = kstar < K ? rm.row(g, K + 1 + kstar) : nullptr;
-    const int64_t e0 = (int64_t)ch * chunk_elems;
-    const int64_t e1 = min((int64_t)V, e0 + (int64_t)chunk_elems);
-    float srho = 0.0f, sp = 0.0f;
-    // kResidBatch strided elements per thread per pass, every load issued before the first
-    // use (the two rows may differ in alignment, so the loads are scalar); the sums run in
-    // the same element order as a one-at-a-time loop
-    for (int64_t v0 = e0 + tid; v0 < e1; v0 += (int64_t)kStreamBlock * kResidBatch) {
-      float xp[kResidBatch], xq[kResidBatch];
-#pragma unroll
-      for (int u = 0; u < kResidBatch; ++u) {
-        const int64_t v = min(v0 + (int64_t)u * kStreamBlock, e1 - 1);  // clamped: in bounds
-        xp[u] = Elt<DT>::load(prow, v);
-        xq[u] = qrow ? Elt<DT>::load(qrow, v) : 0.0f;
-      }
-#pragma unroll
-      for (int u = 0; u < kResidBatch; ++u) {
-        if (v0 + (int64_t)u * kStreamBlock < e1) {
-          const float p = fast_exp2(fmaf(xp[u], c, -nm.x)) * nm.y;
-          sp += p;
-          if (qrow) srho += fmaxf(p - fast_exp2(fmaf(xq[u], c, -nm.z)) * nm.w, 0.0f);
-        }
-      }
-    }
-    srho = block_sum<float, kStreamBlock>(srho, red);
-    sp = block_sum<float, kStreamBlock>(sp, red);
-    if (tid == 0) part2[(int64_t)g * chunks + ch] = make_float2(srho, sp);
-    __syncthreads();
-  }
-}
-
-// Residual (or target) row values for the SpS draw; scalar loads because the two rows
-// may sit at different alignments.
+// Residual (or target) row values for the SpS draw: the same fp32 expression in the
+// residual pass and in the re-read, so a slab's re-read values are the ones it summed.
 template <int DT>
 struct ResidRow {
   const char *prow, *qrow;
   float c, Mcp, invp, Mcq, invq;
   bool use_rho;
+  bool vec;  // both rows start 16-byte aligned: whole units are read as 16-byte vectors
   struct Raw {
     float p[8], q[8];
   };
-  __device__ __forceinline__ float val_from(float xp, float xq) const {
-    const float p = fast_exp2(fmaf(xp, c, -Mcp)) * invp;
-    return use_rho ? fmaxf(p - fast_exp2(fmaf(xq, c, -Mcq)) * invq, 0.0f) : p;
+  __device__ __forceinline__ float pval(float xp) const {
+    return fast_exp2(fmaf(xp, c, -Mcp)) * invp;
   }
-  __device__ __forceinline__ float val(int64_t v) const {
-    return val_from(Elt<DT>::load(prow, v), use_rho ? Elt<DT>::load(qrow, v) : 0.0f);
+  __device__ __forceinline__ float rho(float p, float xq) const {
+    return fmaxf(p - fast_exp2(fmaf(xq, c, -Mcq)) * invq, 0.0f);
+  }
+  __device__ __forceinline__ float val_from(float xp, float xq) const {
+    const float p = pval(xp);
+    return use_rho ? rho(p, xq) : p;
   }
   __device__ __forceinline__ void load(int64_t a, int64_t b, Raw &r) const {
-    const char *qr = use_rho ? qrow : prow;
+    using E = Elt<DT>;
+    if (vec && a + 8 <= b) {
+      const uint4 *pp = reinterpret_cast<const uint4 *>(prow + a * E::kBytes);
+      const uint4 *pq = reinterpret_cast<const uint4 *>((use_rho ? qrow : prow) + a * E::kBytes);
+#pragma unroll
+      for (int k = 0; k < 8 / E::kPerVec; ++k) {
+        E::unpack(pp[k], r.p + k * E::kPerVec);
+        if (use_rho) E::unpack(pq[k], r.q + k * E::kPerVec);
+      }
+      if (!use_rho)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r.q[i] = 0.0f;
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int64_t v = min(a + i, b - 1);
-      const float xp = Elt<DT>::load(prow, v), xq = Elt<DT>::load(qr, v);
+      const float xp = E::load(prow, v);
       r.p[i] = a + i < b ? xp : kNegInf;
-      r.q[i] = xq;
+      r.q[i] = use_rho ? E::load(qrow, v) : 0.0f;
     }
   }
   __device__ __forceinline__ float val_from_raw(const Raw &r, int i) const {
@@ -949,85 +921,251 @@ struct ResidRow {
   }
 };
 
+// SpS after the LSE pass: k_sps_resid, one workgroup of kStreamBlock threads per
+// (sequence, vocabulary chunk).
+//   * the decision.  FUSED (rows of at most kSpsFusedChunksMax chunk pairs): every
+//     workgroup forms it from the chunk pairs - the row normalisers (wave 0), the draft
+//     tokens' logits (wave 1), then one lane per draft position tests r_k < p/q and a
+//     ballot gives the first rejection k* (K when all pass); the chunk-0 workgroup writes
+//     the per-sequence outputs.  Otherwise k_sps_decide has written k* and the norms.
+//   * the residual pass over this chunk of row pair k* (the target row alone when k* = K):
+//     wave w sums slab w, a contiguous quarter of the chunk, of max(0, p - q) and of p.
+//   * the last workgroup of the sequence to finish (an arrival counter per sequence, which
+//     the LSE pass zeroes) draws the token: the slab where the running sum of the slab
+//     sums crosses u * total, then one re-read of that slab and its inverse CDF.  The slab
+//     sums travel as agent-scope atomic stores and loads, ordered by waiting for the
+//     stores before the counter increment: device-scope fences instead (an L2 write-back
+//     in every workgroup and an invalidate in the last) made the kernel 3x slower on the
+//     MI355X (16 sequences, V = 128256 fp32: 49.7 us against 15.3 us), and a separate draw
+//     kernel cost one more launch (11.5 + 4.8 us of kernels, 10 us more per call).
+constexpr int kSpsSlabs = kStreamBlock / kWave;
 template <int DT>
-__global__ __launch_bounds__(kSpsFinalBlock) void k_sps_final(
-    RowMap rm, int nseq, int V, int chunk_elems, int chunks, float c, uint64_t seed, uint64_t step,
-    const int32_t *__restrict__ ws_kstar, const float4 *__restrict__ ws_norm,
-    const float2 *__restrict__ part2, int32_t *__restrict__ out_tokens, float *__restrict__ out_logp,
-    int32_t *status) {
-  const int K = rm.K;
-  const int tid = threadIdx.x;
-  __shared__ double sScan[kSpsFinalBlock / kWave];
-  __shared__ int sMisc[4];
-  __shared__ float sPickLogit;
-  __shared__ double sTot, sBase;
-  __shared__ int sUse, sCh;
-  for (int g = blockIdx.x; g < nseq; g += gridDim.x) {
-  const int kstar = ws_kstar[g];
-  const float4 nm = ws_norm[g];
-  const char *prow = rm.row(g, kstar);
-  const char *qrow = kstar < K ? rm.row(g, K + 1 + kstar) : nullptr;
-  const float2 *p2 = part2 + (int64_t)g * chunks;
+constexpr int kSpsSlabElems =
+    (DT == SMCSD_DTYPE_BF16 ? kChunkElemsBf16 : kChunkElemsF32) / kSpsSlabs;
+template <int DT>
+constexpr int kSpsVecsPerLane = kSpsSlabElems<DT> / Elt<DT>::kPerVec / kWave;
+static_assert(kSpsSlabs == kSpsSlabsWs, "the workspace holds one slab sum pair per wave");
+static_assert(kSpsVecsPerLane<SMCSD_DTYPE_F32> * Elt<SMCSD_DTYPE_F32>::kPerVec * kWave ==
+                      kSpsSlabElems<SMCSD_DTYPE_F32> &&
+                  kSpsVecsPerLane<SMCSD_DTYPE_BF16> * Elt<SMCSD_DTYPE_BF16>::kPerVec * kWave ==
+                      kSpsSlabElems<SMCSD_DTYPE_BF16>,
+              "a slab is whole vectors of every lane of one wave");
+static_assert(kSpsSlabElems<SMCSD_DTYPE_F32> % (8 * kStreamBlock) == 0 &&
+                  kSpsSlabElems<SMCSD_DTYPE_BF16> % (8 * kStreamBlock) == 0,
+              "a slab splits evenly into the re-read's units");
+
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+  for (int m = kWave / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+__device__ __forceinline__ int wave_or(int v) {
+#pragma unroll
+  for (int m = kWave / 2; m >= 1; m >>= 1) v |= __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// Elements [a, a + kPerVec) of a row as one 16-byte word (bf16: element 2i in the low half
+// of word i); with the row unaligned or the vector crossing b, element loads at indices
+// clamped to b - 1 (those at or beyond b are then garbage the caller masks).
+template <int DT>
+__device__ __forceinline__ uint4 load_vec_any(const char *row, int64_t a, int64_t b, bool vec) {
+  using E = Elt<DT>;
+  if (vec && a + E::kPerVec <= b) return *reinterpret_cast<const uint4 *>(row + a * E::kBytes);
+  uint32_t w[4];
+  if (DT == SMCSD_DTYPE_F32) {
+    const uint32_t *r = reinterpret_cast<const uint32_t *>(row);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = r[min(a + i, b - 1)];
+  } else {
+    const uint16_t *r = reinterpret_cast<const uint16_t *>(row);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = (uint32_t)r[min(a + 2 * i, b - 1)] | ((uint32_t)r[min(a + 2 * i + 1, b - 1)] << 16);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+struct SpsDecision {
+  double L2[2 * kMaxK + 1], S[2 * kMaxK + 1];
+  float Mc[2 * kMaxK + 1];
+  double lp[kMaxK], lq[kMaxK];
+  float x[2 * kMaxK];  // the draft tokens' logits: target rows, then draft rows
+  int32_t tok[kMaxK];
+  int fl[2];
+  float4 nm;
+  int kstar, flags;
+};
+
+constexpr int kSpsFusedChunksMax = 32;
+
+// The SpS decision of sequence g into D (every thread calls it; ends with a barrier).
+template <int DT>
+__device__ __forceinline__ void sps_decide(const RowMap &rm, int g, const int32_t *__restrict__ draft_tokens,
+                                           int V, int chunks, int chunks_big, float c, uint64_t seed,
+                                           uint64_t step, const float2 *__restrict__ part,
+                                           const float *__restrict__ lse_in, SpsDecision &D) {
+  const int K = rm.K, R = 2 * K + 1;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int64_t src = (int64_t)g * rm.seq_step;
+  if (tid < kWave) {
+    int fl = 0;
+    for (int r = lane; r < R; r += kWave) {
+      if (lse_in) {
+        const double L2 = (double)lse_in[src * R + r] * kLog2e;
+        D.L2[r] = L2;
+        D.S[r] = 1.0;
+        D.Mc[r] = (float)L2;
+        if (isnan(L2) || L2 == __builtin_inf()) fl |= SMCSD_ST_NAN_INPUT;
+        else if (L2 == -__builtin_inf()) fl |= SMCSD_ST_EMPTY_ROW;
+      } else {
+        const RowNorm rn = row_norm(part + ((int64_t)g * R + r) * chunks, r == K ? chunks : chunks_big, c);
+        D.L2[r] = rn.L2;
+        D.S[r] = rn.S;
+        D.Mc[r] = rn.Mc;
+        fl |= rn.flags;
+      }
+    }
+    fl = wave_or(fl);
+    if (lane == 0) D.fl[0] = fl;
+  } else if (tid < 2 * kWave) {
+    int fl = 0;
+    if (lane < 2 * K) {
+      const int k = lane < K ? lane : lane - K;
+      const int slot = lane < K ? k : K + 1 + k;
+      const int32_t x = draft_tokens[src * K + k];
+      float xv = __builtin_nanf("");
+      if (x < 0 || x >= V) fl = SMCSD_ST_BAD_INPUT;
+      else xv = Elt<DT>::load(rm.row(g, slot), x);
+      D.x[lane] = xv;
+      if (lane < K) D.tok[k] = x;
+    }
+    fl = wave_or(fl);
+    if (lane == 0) D.fl[1] = fl;
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    bool rej = false;
+    if (lane < K) {
+      const double lp = ((double)D.x[lane] * (double)c - D.L2[lane]) * kLn2;
+      const double lq = ((double)D.x[K + lane] * (double)c - D.L2[K + 1 + lane]) * kLn2;
+      D.lp[lane] = lp;
+      D.lq[lane] = lq;
+      const double ratio = exp(lp - lq);
+      const double r = philox_uniform(seed, (uint32_t)g, step, 3u | ((uint32_t)(lane / 4) << 8), lane % 4);
+      rej = !(r < ratio);
+    }
+    const unsigned long long m = __ballot(rej);
+    if (lane == 0) {
+      const int kstar = m ? __ffsll(m) - 1 : K;
+      const int qs = K + 1 + kstar;
+      D.kstar = kstar;
+      D.nm = make_float4(D.Mc[kstar], (float)(1.0 / D.S[kstar]), kstar < K ? D.Mc[qs] : 0.0f,
+                         kstar < K ? (float)(1.0 / D.S[qs]) : 0.0f);
+      D.flags = D.fl[0] | D.fl[1];
+    }
+  }
+  __syncthreads();
+}
+
+// One slab-sum pair, published by one workgroup and read by another of the same launch:
+// agent-scope atomic store and load (written through to, and read from, the point where
+// the chip's L2 caches are coherent), so no L2 write-back or invalidate is needed.
+__device__ __forceinline__ void slab_store(float2 *p, float2 v) {
+  const unsigned long long b =
+      (unsigned long long)__float_as_uint(v.x) | ((unsigned long long)__float_as_uint(v.y) << 32);
+  __hip_atomic_store(reinterpret_cast<unsigned long long *>(p), b, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 slab_load(const float2 *p) {
+  const unsigned long long b = __hip_atomic_load(reinterpret_cast<const unsigned long long *>(p),
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32)));
+}
+
+struct SpsDrawLds {
+  double scan[kStreamBlock / kWave];
+  int misc[4];
+  float pick_logit;
+  double tot, base;
+  int use, sl;
+};
+
+// The SpS token of sequence g (every thread of a kStreamBlock workgroup calls it): the slab
+// where the running sum of the slab sums crosses u * total, then the inverse CDF inside it.
+template <int DT>
+__device__ __forceinline__ void sps_draw(int g, int K, int kstar, float4 nm, const char *prow,
+                                         const char *qrow, bool vec, int V, int chunk_elems,
+                                         int chunks, float c, uint64_t seed, uint64_t step,
+                                         const float2 *__restrict__ slab, SpsDrawLds &L,
+                                         int32_t *__restrict__ out_tokens,
+                                         float *__restrict__ out_logp, int32_t *status) {
+  constexpr int Q = kSpsSlabElems<DT>;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int nsl = chunks * kSpsSlabs;
+  const float2 *p2 = slab + (int64_t)g * nsl;
   const double u = philox_uniform(seed, (uint32_t)g, step, 4u, 0);
   if (tid < kWave) {
-    // wave 0, one lane per chunk: the residual and target totals, then the first chunk
-    // whose running sum exceeds u * total, by lane prefix sums and one ballot per 64
-    // chunks.  Both passes add the same values in the same order (scan within 64 chunks,
-    // then block by block), so the running sum ends exactly at the total and, as u < 1,
-    // some chunk crosses.
+    // one lane per slab: the residual and target totals, then the first slab whose running
+    // sum exceeds u * total (scan within 64 slabs, then block by block, the same order in
+    // both passes: the running sum ends exactly at the total, and u < 1)
     double rt = 0.0, pt = 0.0;
-    for (int j0 = 0; j0 < chunks; j0 += kWave) {
-      const int j = j0 + tid;
-      const float2 v = j < chunks ? p2[j] : make_float2(0.0f, 0.0f);
-      rt += __shfl(wave_inclusive_scan((double)v.x), kWave - 1, kWave);
-      pt += __shfl(wave_inclusive_scan((double)v.y), kWave - 1, kWave);
+    for (int j0 = 0; j0 < nsl; j0 += kWave) {
+      const int j = j0 + lane;
+      const float2 v = j < nsl ? slab_load(p2 + j) : make_float2(0.0f, 0.0f);
+      rt += wave_sum((double)v.x);
+      pt += wave_sum((double)v.y);
     }
     const bool use_rho = qrow != nullptr && rt > 0.0;
     const double total = use_rho ? rt : pt;
     const double target = u * total;
     double base = 0.0;
-    int ch = -1;
+    int sl = -1;
     if (isfinite(total) && total > 0.0) {
-      for (int j0 = 0; j0 < chunks && ch < 0; j0 += kWave) {
-        const int j = j0 + tid;
-        const float2 v = j < chunks ? p2[j] : make_float2(0.0f, 0.0f);
-        const double t = use_rho ? (double)v.x : (double)v.y;
-        const double inc = wave_inclusive_scan(t);
-        const unsigned long long hit = __ballot(j < chunks && base + inc > target);
+      int lastpos = -1;
+      double lastval = 0.0;
+      for (int j0 = 0; j0 < nsl && sl < 0; j0 += kWave) {
+        const int j = j0 + lane;
+        const float2 v = j < nsl ? slab_load(p2 + j) : make_float2(0.0f, 0.0f);
+        const double x = use_rho ? (double)v.x : (double)v.y;
+        const double inc = wave_inclusive_scan(x);
+        const unsigned long long hit = __ballot(j < nsl && base + inc > target);
+        const unsigned long long pos = __ballot(x > 0.0);
+        if (pos) {
+          const int f = 63 - __clzll(pos);
+          lastpos = j0 + f;
+          lastval = __shfl(x, f, kWave);
+        }
         if (hit) {
           const int f = __ffsll(hit) - 1;
-          ch = j0 + f;
-          base += __shfl(inc - t, f, kWave);
+          sl = j0 + f;
+          base += __shfl(inc - x, f, kWave);
         } else {
           base += __shfl(inc, kWave - 1, kWave);
         }
       }
-      if (ch < 0) {  // not reached (see above); kept as the last chunk from its start
-        ch = chunks - 1;
-        const float2 v = p2[ch];
-        base -= use_rho ? (double)v.x : (double)v.y;
+      if (sl < 0) {  // not reached (see above): the last slab with a positive sum
+        sl = lastpos;
+        base = total - lastval;
       }
     }
-    if (tid == 0) {
-      sTot = total;
-      sUse = use_rho;
-      sCh = ch;
-      sBase = base;
+    if (lane == 0) {
+      L.tot = total;
+      L.use = use_rho;
+      L.sl = sl;
+      L.base = base;
     }
   }
   __syncthreads();
-  const double total = sTot;
-  const bool use_rho = sUse != 0;
-  const double target = u * total;
+  const double total = L.tot;
   int tok = -1;
-  if (isfinite(total) && total > 0.0) {
-    const int ch = sCh;
-    const double base = sBase;
-    const int64_t e0 = (int64_t)ch * chunk_elems;
-    const int64_t e1 = min((int64_t)V, e0 + (int64_t)chunk_elems);
-    const ResidRow<DT> fn{prow, qrow, c, nm.x, nm.y, nm.z, nm.w, use_rho};
-    tok = chunk_inverse_cdf<kSpsFinalBlock, kUnitsPerThread<DT, kSpsFinalBlock>>(
-        e0, e1, base, target, fn, sScan, sMisc, &sPickLogit);
+  if (isfinite(total) && total > 0.0 && L.sl >= 0) {
+    const int sl = L.sl;
+    const int64_t a0 = (int64_t)(sl / kSpsSlabs) * chunk_elems + (int64_t)(sl % kSpsSlabs) * Q;
+    const int64_t a1 = min((int64_t)V, a0 + (int64_t)Q);
+    const ResidRow<DT> fd{prow, qrow, c, nm.x, nm.y, nm.z, nm.w, L.use != 0, vec};
+    tok = chunk_inverse_cdf<kStreamBlock, Q / 8 / kStreamBlock>(a0, a1, L.base, u * total, fd,
+                                                                L.scan, L.misc, &L.pick_logit);
   }
   if (tid == 0) {
     out_tokens[(int64_t)g * (K + 1) + kstar] = tok;
@@ -1035,13 +1173,122 @@ __global__ __launch_bounds__(kSpsFinalBlock) void k_sps_final(
       // log p of the drawn token: (x*c - L2)*ln2 with L2 = Mc + log2(1/inv)
       double lp = __builtin_nan("");
       if (tok >= 0)
-        lp = ((double)sPickLogit * (double)c - ((double)nm.x - log2((double)nm.y))) * kLn2;
+        lp = ((double)L.pick_logit * (double)c - ((double)nm.x - log2((double)nm.y))) * kLn2;
       out_logp[(int64_t)g * (K + 1) + K] = (float)lp;
     }
     if (tok < 0) atomicOr(status, isnan(total) ? SMCSD_ST_NAN_INPUT : SMCSD_ST_EMPTY_ROW);
   }
-  __syncthreads();  // the next sequence reuses the LDS
+}
+
+template <int DT, bool FUSED>
+__global__ __launch_bounds__(kStreamBlock) void k_sps_resid(
+    RowMap rm, int nseq, const int32_t *__restrict__ draft_tokens, int V, int chunk_elems,
+    int chunks, int chunks_big, float c, uint64_t seed, uint64_t step,
+    const float2 *__restrict__ part, const float *__restrict__ lse_in,
+    const int32_t *__restrict__ ws_kstar, const float4 *__restrict__ ws_norm,
+    float2 *__restrict__ slab, int32_t *__restrict__ arrivals, int32_t *__restrict__ out_tokens,
+    int32_t *__restrict__ out_num, float *__restrict__ out_logp, float *__restrict__ out_logq,
+    float *__restrict__ out_lse, int32_t *status) {
+  using E = Elt<DT>;
+  constexpr int EPV = E::kPerVec, NV = kSpsVecsPerLane<DT>, Q = kSpsSlabElems<DT>;
+  __shared__ SpsDecision D;
+  __shared__ SpsDrawLds DL;
+  __shared__ int sLast;
+  const int K = rm.K, R = 2 * K + 1;
+  const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+  const int64_t ntiles = (int64_t)nseq * chunks;
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int g = (int)(t / chunks);
+    const int ch = (int)(t - (int64_t)g * chunks);
+    int kstar;
+    float4 nm;
+    if (FUSED) {
+      sps_decide<DT>(rm, g, draft_tokens, V, chunks, chunks_big, c, seed, step, part, lse_in, D);
+      kstar = D.kstar;
+      nm = D.nm;
+      if (ch == 0 && tid < kWave) {
+        // the per-sequence outputs; the token at k* is the draw's
+        int32_t *tok = out_tokens + (int64_t)g * (K + 1);
+        if (lane <= K && lane != kstar) tok[lane] = lane < kstar ? D.tok[lane] : -1;
+        if (lane < K) {
+          if (out_logp) out_logp[(int64_t)g * (K + 1) + lane] = (float)D.lp[lane];
+          if (out_logq) out_logq[(int64_t)g * K + lane] = (float)D.lq[lane];
+        }
+        if (out_lse)
+          for (int r = lane; r < R; r += kWave) out_lse[(int64_t)g * R + r] = (float)(D.L2[r] * kLn2);
+        if (lane == 0) {
+          if (out_num) out_num[g] = kstar + 1;
+          if (D.flags) atomicOr(status, D.flags);
+        }
+      }
+    } else {
+      kstar = ws_kstar[g];
+      nm = ws_norm[g];
+    }
+    const char *prow = rm.row(g, kstar);
+    const char *qrow = kstar < K ? rm.row(g, K + 1 + kstar) : nullptr;
+    const bool vec = ((uintptr_t)prow % 16 == 0) && ((uintptr_t)qrow % 16 == 0);
+    const ResidRow<DT> fn{prow, qrow, c, nm.x, nm.y, nm.z, nm.w, qrow != nullptr, vec};
+
+    // residual pass: slab wv of this chunk, NV vectors per lane per row
+    const int64_t e0 = (int64_t)ch * chunk_elems;
+    const int64_t e1 = min((int64_t)V, e0 + (int64_t)chunk_elems);
+    const int64_t s0 = e0 + (int64_t)wv * Q;
+    const int64_t s1 = min(e1, s0 + (int64_t)Q);
+    float srho = 0.0f, sp = 0.0f;
+    auto accum = [&](const uint4 &wp, const uint4 &wq, int64_t a) {
+      float xp[EPV], xq[EPV];
+      E::unpack(wp, xp);
+      E::unpack(wq, xq);
+#pragma unroll
+      for (int i = 0; i < EPV; ++i) {
+        if (a + i < s1) {
+          const float p = fn.pval(xp[i]);
+          sp += p;
+          if (qrow) srho += fn.rho(p, xq[i]);
+        }
+      }
+    };
+    if (vec && s1 - s0 == Q) {
+      // a whole slab of aligned rows: every 16-byte load issued before the first use
+      uint4 rp[NV], rq[NV];
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int64_t a = s0 + (int64_t)(lane + u * kWave) * EPV;
+        rp[u] = *reinterpret_cast<const uint4 *>(prow + a * E::kBytes);
+        rq[u] = qrow ? *reinterpret_cast<const uint4 *>(qrow + a * E::kBytes) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < NV; ++u) accum(rp[u], rq[u], s0 + (int64_t)(lane + u * kWave) * EPV);
+    } else if (s0 < s1) {
+      // a partial slab or unaligned rows: element loads at clamped indices
+      for (int u = 0; u < NV; ++u) {
+        const int64_t a = s0 + (int64_t)(lane + u * kWave) * EPV;
+        const uint4 wp = load_vec_any<DT>(prow, a, s1, vec);
+        const uint4 wq = qrow ? load_vec_any<DT>(qrow, a, s1, vec) : make_uint4(0, 0, 0, 0);
+        accum(wp, wq, a);
+      }
+    }
+    srho = wave_sum_f(srho);
+    sp = wave_sum_f(sp);
+    if (lane == 0) slab_store(slab + t * kSpsSlabs + wv, make_float2(srho, sp));
+    // arrival: every wave's slab store has completed (waited for) before the workgroup's
+    // counter increment is issued, so the workgroup that sees the count reach `chunks`
+    // reads every slab of the sequence; it draws the token
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) sLast = atomicAdd(&arrivals[g], 1) == chunks - 1;
+    __syncthreads();
+    if (sLast)
+      sps_draw<DT>(g, K, kstar, nm, prow, qrow, vec, V, chunk_elems, chunks, c, seed, step, slab,
+                   DL, out_tokens, out_logp, status);
+    __syncthreads();  // the next tile reuses the LDS
   }
+}
+
+__global__ void k_zero_i32(int32_t *__restrict__ p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
 }
 
 // ---------------------------------------------------------------------------------
@@ -1119,7 +1366,7 @@ static hipError_t launch_verify_t(const VerifyArgs &a) {
   if (a.mode == SMCSD_MODE_SMC) {
     hipLaunchKernelGGL((k_lse_partials<DT, false>), dim3(grid), dim3(kStreamBlock), pad, a.stream, rm,
                        a.nseq, a.V, ce, chunks, chunks_big, nb_per_seq, a.c, part, sub, ntiles,
-                       a.seed, a.step, race);
+                       a.seed, a.step, race, nullptr);
     hipLaunchKernelGGL((k_smc_finalize<DT, false>), dim3(grid_blocks(a.nseq, kSmcFinalBlock)), dim3(kSmcFinalBlock), 0, a.stream,
                        rm, a.nseq, a.draft_tokens, a.V, ce, chunks, chunks_big, a.c, a.alpha, a.seed,
                        a.step, a.bonus_tag, part, a.logq_in, sub, race,
@@ -1130,7 +1377,7 @@ static hipError_t launch_verify_t(const VerifyArgs &a) {
   if (a.mode == SMCSD_MODE_SMC_RACE) {
     hipLaunchKernelGGL((k_lse_partials<DT, true>), dim3(grid), dim3(kStreamBlock), 0, a.stream, rm,
                        a.nseq, a.V, ce, chunks, chunks_big, nb_per_seq, a.c, part, sub, ntiles,
-                       a.seed, a.step, race);
+                       a.seed, a.step, race, nullptr);
     hipLaunchKernelGGL((k_smc_finalize<DT, true>), dim3(grid_blocks(a.nseq, kSmcFinalBlock)), dim3(kSmcFinalBlock), 0, a.stream,
                        rm, a.nseq, a.draft_tokens, a.V, ce, chunks, chunks_big, a.c, a.alpha, a.seed,
                        a.step, a.bonus_tag, part, a.logq_in, sub, race,
@@ -1140,23 +1387,34 @@ static hipError_t launch_verify_t(const VerifyArgs &a) {
   }
   int32_t *kstar = reinterpret_cast<int32_t *>(a.ws + w.kstar);
   float4 *norm = reinterpret_cast<float4 *>(a.ws + w.l2);
-  float2 *part2 = reinterpret_cast<float2 *>(a.ws + w.part2);
+  float2 *slab = reinterpret_cast<float2 *>(a.ws + w.part2);
+  int32_t *arrivals = reinterpret_cast<int32_t *>(a.ws + w.arrivals);
   if (!a.lse_in)
     hipLaunchKernelGGL((k_lse_partials<DT, false>), dim3(grid), dim3(kStreamBlock), pad, a.stream, rm,
                        a.nseq, a.V, ce, chunks, chunks_big, nb_per_seq, a.c, part, sub, ntiles,
-                       a.seed, a.step, race);
-  hipLaunchKernelGGL(k_sps_decide<DT>, dim3(grid_blocks(a.nseq, kWave)), dim3(kWave), 0, a.stream, rm,
-                     a.nseq, a.draft_tokens, a.V, chunks, chunks_big, a.c, a.seed, a.step, part,
-                     a.lse_in, kstar, norm,
-                     a.out_tokens,
-                     a.out_num_tokens, a.out_logp, a.out_logq, a.out_lse, a.status);
-  const int64_t ntiles2 = (int64_t)a.nseq * chunks;
-  hipLaunchKernelGGL(k_sps_residual<DT>, dim3(grid_blocks(ntiles2, kStreamBlock)),
-                     dim3(kStreamBlock), 0, a.stream, rm, a.V, ce, chunks, a.c, kstar, norm, part2,
-                     ntiles2);
-  hipLaunchKernelGGL(k_sps_final<DT>, dim3(grid_blocks(a.nseq, kSpsFinalBlock)), dim3(kSpsFinalBlock), 0,
-                     a.stream, rm, a.nseq, a.V, ce, chunks, a.c, a.seed, a.step, kstar, norm, part2,
-                     a.out_tokens, a.out_logp, a.status);
+                       a.seed, a.step, race, arrivals);
+  else
+    hipLaunchKernelGGL(k_zero_i32, dim3(grid_blocks(a.nseq, kStreamBlock)), dim3(kStreamBlock), 0,
+                       a.stream, arrivals, a.nseq);
+  // the decision inside every residual workgroup while a row has few chunk pairs, else a
+  // decide kernel first
+  const bool fused = chunks <= kSpsFusedChunksMax;
+  if (!fused)
+    hipLaunchKernelGGL(k_sps_decide<DT>, dim3(grid_blocks(a.nseq, kWave)), dim3(kWave), 0, a.stream, rm,
+                       a.nseq, a.draft_tokens, a.V, chunks, chunks_big, a.c, a.seed, a.step, part,
+                       a.lse_in, kstar, norm, a.out_tokens, a.out_num_tokens, a.out_logp, a.out_logq,
+                       a.out_lse, a.status);
+  const unsigned grid2 = grid_blocks((int64_t)a.nseq * chunks, kStreamBlock);
+  if (fused)
+    hipLaunchKernelGGL((k_sps_resid<DT, true>), dim3(grid2), dim3(kStreamBlock), 0, a.stream, rm,
+                       a.nseq, a.draft_tokens, a.V, ce, chunks, chunks_big, a.c, a.seed, a.step, part,
+                       a.lse_in, kstar, norm, slab, arrivals, a.out_tokens, a.out_num_tokens,
+                       a.out_logp, a.out_logq, a.out_lse, a.status);
+  else
+    hipLaunchKernelGGL((k_sps_resid<DT, false>), dim3(grid2), dim3(kStreamBlock), 0, a.stream, rm,
+                       a.nseq, a.draft_tokens, a.V, ce, chunks, chunks_big, a.c, a.seed, a.step, part,
+                       a.lse_in, kstar, norm, slab, arrivals, a.out_tokens, a.out_num_tokens,
+                       a.out_logp, a.out_logq, a.out_lse, a.status);
   return hipGetLastError();
 }
 

@@ -461,8 +461,8 @@ def test_batches_beyond_one_dispatch(mode):
         assert int(st.cpu()[0]) == o["status"] == 0
         assert np.array_equal(g[ok], o["tokens"][ok, 0]) and (g >= 0).all()
         assert np.max(np.abs(lw.cpu().numpy() - o["lw"])) <= H.TOL_LW
-    elif mode == "sps":                    # SpS final draw: 1024 threads per sequence
-        S, K = (1 << 22) + 300, 1
+    elif mode == "sps":                    # SpS residual + draw: 256 threads per sequence
+        S, K = (1 << 24) + 300, 1
         tgt = _tiny_rows(S, K + 1, V, 2)
         drf = (tgt[:, :K] + _tiny_rows(S, K, V, 3)).contiguous()
         toks = torch.randint(0, V, (S, K), device="cuda", dtype=torch.int32)

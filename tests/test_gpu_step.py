@@ -118,7 +118,7 @@ def _run(cfg, rounds, mode=sm.MODE_SMC, draft_logq=False, nan_row=False):
 
 
 @pytest.mark.parametrize("case", ["c3_shape", "n5_unshared", "race", "fp32", "draft_logq", "k0",
-                                  "nan_row", "n40_two_kernels", "split_tables", "many_sequences"])
+                                  "nan_row", "n40", "split_tables", "many_sequences"])
 def test_step_equals_verify_then_fused_resample_kv(case):
     if case == "c3_shape":          # the benchmark's step shape at 4 prompts
         _run(C.C3.scaled(name="s", B=4, n_sets=2, iters=8), 6)
@@ -134,9 +134,79 @@ def test_step_equals_verify_then_fused_resample_kv(case):
         _run(C.C2.scaled(name="s", B=3, K=0, V=5000, n_sets=2, iters=8, tau=0.9), 6)
     elif case == "nan_row":
         _run(C.C3.scaled(name="s", B=2, V=20011, n_sets=2, iters=8), 4, nan_row=True)
-    elif case == "n40_two_kernels":  # N > 16: the verify's finalize, then the exchange kernel
+    elif case == "n40":              # N > 16: the exchange over a workgroup-wide resample
         _run(C.C3.scaled(name="s", B=2, N=40, V=20011, n_sets=2, iters=8), 5)
     elif case == "split_tables":     # tables over several column tiles (C5-like)
         _run(C.C5.scaled(name="s", B=1, N=128, V=20011, n_sets=2, iters=6), 4)
     else:                            # more than 8192 sequences: the many-sequence pop path
         _run(C.C2.scaled(name="s", B=1100, N=8, V=300, n_sets=2, iters=8, ctx0=40), 4)
+
+
+def _graph_run(cfg, rounds, passes=2):
+    """Rounds of smcsd_step recorded in HIP graphs (one graph per round, captured once with
+    nothing executing) and replayed in order, against the same rounds called directly: every
+    output bit-identical after every replay.  The replays are run `passes` times from the
+    initial state, restored by eager copies between passes, so replays after the first one
+    are checked too; the status word is cleared eagerly before each round on both sides."""
+    B, N, K, V, S = cfg.B, cfg.N, cfg.K, cfg.V, cfg.S
+    base = synth.zipf_base(cfg, "cuda") if cfg.target_kind == "zipf" else None
+    sets = []
+    for s in range(cfg.n_sets):
+        t, d = synth.make_logit_set(cfg, s, "cuda", base)
+        sets.append((t, d, synth.sample_draft_tokens(cfg, d, s)))
+    kv = synth.initial_kv(cfg)
+    lw0 = torch.randn(S, generator=torch.Generator(device="cuda").manual_seed(7), device="cuda")
+    A, G = _Copy(cfg, kv, lw0), _Copy(cfg, kv, lw0)
+    L0 = int(kv["seq_len"])
+    ident = torch.arange(N, dtype=torch.int32, device="cuda").repeat(B, 1)
+    for c in (A, G):
+        sm.kv_reassign(ident, torch.zeros(B, dtype=torch.int32, device="cuda"), B, N, c.tables,
+                       cfg.block_size, L0, K + 1, c.rc, c.fl, c.top, c.cow, c.ncow, c.st, c.ws_kv)
+    torch.cuda.synchronize()
+    state_names = ("lw", "tables", "rc", "fl", "top")
+    init = {k: getattr(G, k).clone() for k in state_names}
+    ws_kv0 = G.ws_kv.clone()
+
+    def call(c, t):
+        tgt, drf, x = sets[t % cfg.n_sets]
+        sm.step(tgt, drf, x, B, N, K, V, cfg.temperature, cfg.alpha, sm.MODE_SMC, cfg.tau,
+                cfg.rng_seed, t, c.lw, c.tok, c.anc, c.ess, c.res, c.tables, cfg.block_size,
+                L0 + (t + 1) * (K + 1), K + 1, c.rc, c.fl, c.top, c.cow, c.ncow, c.st, c.ws_v,
+                c.ws_kv, out_num_tokens=c.num, out_logp=c.logp, out_logq=c.logq, out_lse=c.lse)
+
+    want = []
+    for t in range(rounds):
+        A.st.zero_()
+        call(A, t)
+        torch.cuda.synchronize()
+        want.append(A.snapshot())
+    graphs = []
+    for t in range(rounds):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            call(G, t)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for p in range(passes):
+        for k in state_names:
+            getattr(G, k).copy_(init[k])
+        G.ws_kv.copy_(ws_kv0)
+        for t in range(rounds):
+            G.st.zero_()
+            graphs[t].replay()
+            torch.cuda.synchronize()
+            bad = _same(want[t], G.snapshot())
+            assert bad is None, (p, t, bad)
+    assert any(w["res"].any() for w in want)
+
+
+@pytest.mark.parametrize("name", ["c1_tiny", "c2_single_prompt", "c3_small"])
+def test_step_graph_replays_equal_direct_calls(name):
+    """The launch-bound shapes (C1, C2 at full size) and C3 at 4 prompts, replayed from HIP
+    graphs: the form that removes the host's per-call cost."""
+    if name == "c1_tiny":
+        _graph_run(C.C1.scaled(name="g", iters=10), 8)
+    elif name == "c2_single_prompt":
+        _graph_run(C.C2.scaled(name="g", iters=10, n_sets=8), 8)
+    else:
+        _graph_run(C.C3.scaled(name="g", B=4, n_sets=2, iters=8), 6)
