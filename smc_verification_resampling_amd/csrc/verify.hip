@@ -559,7 +559,7 @@ static_assert(kSlabElems<SMCSD_DTYPE_BF16> + 16 <= 8 * kSmcFinalBlock * kSmcUnit
                   kSlabElems<SMCSD_DTYPE_F32> + 16 <= 8 * kSmcFinalBlock * kSmcUnits,
               "the finalize workgroup must cover one slab");
 
-template <int DT, bool RACE>
+template <int DT, bool RACE, bool STRIDE>
 __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
     RowMap rm, int nseq, const int32_t *__restrict__ draft_tokens, int V, int chunk_elems, int chunks,
     int chunks_big, float c, float alpha, uint64_t seed, uint64_t step, uint32_t bonus_tag,
@@ -776,7 +776,8 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
     if (out_logp) out_logp[(int64_t)g * (K + 1) + K] = (float)lpK;
     if (sFlags) atomicOr(status, sFlags);
   }
-  __syncthreads();  // the next sequence reuses the LDS
+  if (!STRIDE) break;  // the grid covers the batch: one sequence, no loop kept
+  __syncthreads();      // the next sequence reuses the LDS
   }
 }
 
@@ -785,7 +786,7 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
 // ---------------------------------------------------------------------------------
 // Per row: the element probability is 2^(x*c - Mc) * inv (inv = 1/S); from lse_in the
 // pair is (LSE*log2(e), 1).  ws_norm[g] = {Mc_p, inv_p, Mc_q, inv_q} for row pair k*.
-template <int DT>
+template <int DT, bool STRIDE>
 __global__ __launch_bounds__(kWave) void k_sps_decide(
     RowMap rm, int nseq, const int32_t *__restrict__ draft_tokens, int V, int chunks, int chunks_big, float c,
     uint64_t seed, uint64_t step, const float2 *__restrict__ part, const float *__restrict__ lse_in,
@@ -861,6 +862,7 @@ __global__ __launch_bounds__(kWave) void k_sps_decide(
       for (int r = 0; r < R; ++r) out_lse[(int64_t)g * R + r] = (float)(sL2[r] * kLn2);
     if (sFlags) atomicOr(status, sFlags);
   }
+  if (!STRIDE) break;
   __syncthreads();  // the next sequence reuses the LDS
   }
 }
@@ -1180,7 +1182,7 @@ __device__ __forceinline__ void sps_draw(int g, int K, int kstar, float4 nm, con
   }
 }
 
-template <int DT, bool FUSED>
+template <int DT, bool FUSED, bool STRIDE>
 __global__ __launch_bounds__(kStreamBlock) void k_sps_resid(
     RowMap rm, int nseq, const int32_t *__restrict__ draft_tokens, int V, int chunk_elems,
     int chunks, int chunks_big, float c, uint64_t seed, uint64_t step,
@@ -1283,6 +1285,7 @@ __global__ __launch_bounds__(kStreamBlock) void k_sps_resid(
     if (sLast)
       sps_draw<DT>(g, K, kstar, nm, prow, qrow, vec, V, chunk_elems, chunks, c, seed, step, slab,
                    DL, out_tokens, out_logp, status);
+    if (!STRIDE) break;
     __syncthreads();  // the next tile reuses the LDS
   }
 }
@@ -1363,26 +1366,26 @@ static hipError_t launch_verify_t(const VerifyArgs &a) {
     if (e != hipSuccess) return e;
   }
 
-  if (a.mode == SMCSD_MODE_SMC) {
-    hipLaunchKernelGGL((k_lse_partials<DT, false>), dim3(grid), dim3(kStreamBlock), pad, a.stream, rm,
-                       a.nseq, a.V, ce, chunks, chunks_big, nb_per_seq, a.c, part, sub, ntiles,
-                       a.seed, a.step, race, nullptr);
-    hipLaunchKernelGGL((k_smc_finalize<DT, false>), dim3(grid_blocks(a.nseq, kSmcFinalBlock)), dim3(kSmcFinalBlock), 0, a.stream,
-                       rm, a.nseq, a.draft_tokens, a.V, ce, chunks, chunks_big, a.c, a.alpha, a.seed,
-                       a.step, a.bonus_tag, part, a.logq_in, sub, race,
-                       a.log_weights, a.out_tokens, a.out_num_tokens, a.out_logp, a.out_logq,
-                       a.out_lse, a.status);
-    return hipGetLastError();
-  }
-  if (a.mode == SMCSD_MODE_SMC_RACE) {
-    hipLaunchKernelGGL((k_lse_partials<DT, true>), dim3(grid), dim3(kStreamBlock), 0, a.stream, rm,
-                       a.nseq, a.V, ce, chunks, chunks_big, nb_per_seq, a.c, part, sub, ntiles,
-                       a.seed, a.step, race, nullptr);
-    hipLaunchKernelGGL((k_smc_finalize<DT, true>), dim3(grid_blocks(a.nseq, kSmcFinalBlock)), dim3(kSmcFinalBlock), 0, a.stream,
-                       rm, a.nseq, a.draft_tokens, a.V, ce, chunks, chunks_big, a.c, a.alpha, a.seed,
-                       a.step, a.bonus_tag, part, a.logq_in, sub, race,
-                       a.log_weights, a.out_tokens, a.out_num_tokens, a.out_logp, a.out_logq,
-                       a.out_lse, a.status);
+  if (a.mode == SMCSD_MODE_SMC || a.mode == SMCSD_MODE_SMC_RACE) {
+    const bool rc = a.mode == SMCSD_MODE_SMC_RACE;
+    if (rc)
+      hipLaunchKernelGGL((k_lse_partials<DT, true>), dim3(grid), dim3(kStreamBlock), 0, a.stream, rm,
+                         a.nseq, a.V, ce, chunks, chunks_big, nb_per_seq, a.c, part, sub, ntiles,
+                         a.seed, a.step, race, nullptr);
+    else
+      hipLaunchKernelGGL((k_lse_partials<DT, false>), dim3(grid), dim3(kStreamBlock), pad, a.stream,
+                         rm, a.nseq, a.V, ce, chunks, chunks_big, nb_per_seq, a.c, part, sub, ntiles,
+                         a.seed, a.step, race, nullptr);
+    // one workgroup per sequence; the looping form only where the grid cap leaves fewer
+    // workgroups than sequences (its loop costs registers: 157 VGPRs against 59)
+    const unsigned gf = grid_blocks(a.nseq, kSmcFinalBlock);
+    const bool stride = (int64_t)gf < a.nseq;
+    auto fin = rc ? (stride ? k_smc_finalize<DT, true, true> : k_smc_finalize<DT, true, false>)
+                  : (stride ? k_smc_finalize<DT, false, true> : k_smc_finalize<DT, false, false>);
+    hipLaunchKernelGGL(fin, dim3(gf), dim3(kSmcFinalBlock), 0, a.stream, rm, a.nseq,
+                       a.draft_tokens, a.V, ce, chunks, chunks_big, a.c, a.alpha, a.seed, a.step,
+                       a.bonus_tag, part, a.logq_in, sub, race, a.log_weights, a.out_tokens,
+                       a.out_num_tokens, a.out_logp, a.out_logq, a.out_lse, a.status);
     return hipGetLastError();
   }
   int32_t *kstar = reinterpret_cast<int32_t *>(a.ws + w.kstar);
@@ -1399,22 +1402,22 @@ static hipError_t launch_verify_t(const VerifyArgs &a) {
   // the decision inside every residual workgroup while a row has few chunk pairs, else a
   // decide kernel first
   const bool fused = chunks <= kSpsFusedChunksMax;
-  if (!fused)
-    hipLaunchKernelGGL(k_sps_decide<DT>, dim3(grid_blocks(a.nseq, kWave)), dim3(kWave), 0, a.stream, rm,
-                       a.nseq, a.draft_tokens, a.V, chunks, chunks_big, a.c, a.seed, a.step, part,
-                       a.lse_in, kstar, norm, a.out_tokens, a.out_num_tokens, a.out_logp, a.out_logq,
-                       a.out_lse, a.status);
-  const unsigned grid2 = grid_blocks((int64_t)a.nseq * chunks, kStreamBlock);
-  if (fused)
-    hipLaunchKernelGGL((k_sps_resid<DT, true>), dim3(grid2), dim3(kStreamBlock), 0, a.stream, rm,
-                       a.nseq, a.draft_tokens, a.V, ce, chunks, chunks_big, a.c, a.seed, a.step, part,
-                       a.lse_in, kstar, norm, slab, arrivals, a.out_tokens, a.out_num_tokens,
-                       a.out_logp, a.out_logq, a.out_lse, a.status);
-  else
-    hipLaunchKernelGGL((k_sps_resid<DT, false>), dim3(grid2), dim3(kStreamBlock), 0, a.stream, rm,
-                       a.nseq, a.draft_tokens, a.V, ce, chunks, chunks_big, a.c, a.seed, a.step, part,
-                       a.lse_in, kstar, norm, slab, arrivals, a.out_tokens, a.out_num_tokens,
-                       a.out_logp, a.out_logq, a.out_lse, a.status);
+  if (!fused) {
+    const unsigned gd = grid_blocks(a.nseq, kWave);
+    hipLaunchKernelGGL(((int64_t)gd < a.nseq ? k_sps_decide<DT, true> : k_sps_decide<DT, false>),
+                       dim3(gd), dim3(kWave), 0, a.stream, rm, a.nseq, a.draft_tokens, a.V, chunks,
+                       chunks_big, a.c, a.seed, a.step, part, a.lse_in, kstar, norm, a.out_tokens,
+                       a.out_num_tokens, a.out_logp, a.out_logq, a.out_lse, a.status);
+  }
+  const int64_t ntiles2 = (int64_t)a.nseq * chunks;
+  const unsigned grid2 = grid_blocks(ntiles2, kStreamBlock);
+  const bool stride2 = (int64_t)grid2 < ntiles2;
+  auto resid = fused ? (stride2 ? k_sps_resid<DT, true, true> : k_sps_resid<DT, true, false>)
+                     : (stride2 ? k_sps_resid<DT, false, true> : k_sps_resid<DT, false, false>);
+  hipLaunchKernelGGL(resid, dim3(grid2), dim3(kStreamBlock), 0, a.stream, rm, a.nseq,
+                     a.draft_tokens, a.V, ce, chunks, chunks_big, a.c, a.seed, a.step, part,
+                     a.lse_in, kstar, norm, slab, arrivals, a.out_tokens, a.out_num_tokens,
+                     a.out_logp, a.out_logq, a.out_lse, a.status);
   return hipGetLastError();
 }
 
