@@ -167,13 +167,24 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
   const int W = max(1, min(c_end - c_begin, kKvTileInts / N));
   const int w0 = min(W, c_end - c_begin), nw0 = N * w0;
   int32_t pre[kPre];
+  {
+    // entry e = pid + k * pthr sits at row j = e / w0, column s = e % w0: two divisions up
+    // front, then a carry per step instead of a division per entry
+    const int wd = max(w0, 1);  // w0 = 0 (no columns): nothing is loaded
+    const int dj = pthr / wd, ds = pthr - dj * wd;
+    int j = pid >= 0 ? pid / wd : 0;
+    int s = pid >= 0 ? pid - j * wd : 0;
 #pragma unroll
-  for (int k = 0; k < kPre; ++k) {
-    const int e = pid + k * pthr;
-    pre[k] = 0;
-    if (pid >= 0 && e < nw0) {
-      const int j = e / w0, s = e - j * w0;
-      pre[k] = T[(row0 + j) * M_cap + c_begin + s];
+    for (int k = 0; k < kPre; ++k) {
+      const int e = pid + k * pthr;
+      pre[k] = 0;
+      if (pid >= 0 && e < nw0) pre[k] = T[(row0 + j) * M_cap + c_begin + s];
+      j += dj;
+      s += ds;
+      if (s >= wd) {
+        s -= wd;
+        ++j;
+      }
     }
   }
   int res;
