@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SMCSD_VERSION 5
+#define SMCSD_VERSION 6
 
 /* logits element type */
 #define SMCSD_DTYPE_F32 0
@@ -77,12 +77,17 @@ extern "C" {
 #define SMCSD_ST_NOSPACE 4            /* the free stack ran out during a reservation      */
 #define SMCSD_ST_DEGENERATE_WEIGHTS 8 /* a prompt whose weights are all zero or NaN       */
 #define SMCSD_ST_BAD_INPUT 16         /* token, ancestor or block id out of range         */
+#define SMCSD_ST_KV_INCONSISTENT 32   /* smcsd_kv_check found a violated invariant        */
 
 /* workspace query ops */
 #define SMCSD_OP_VERIFY_SMC 0
 #define SMCSD_OP_VERIFY_SPS 1
 #define SMCSD_OP_KV 2
 #define SMCSD_OP_DRAFT 3
+#define SMCSD_OP_KV_CHECK 4
+
+/* kinds of violation counted by smcsd_kv_check */
+#define SMCSD_KV_CHECK_KINDS 5
 
 /* Library version (SMCSD_VERSION). */
 int smcsd_version(void);
@@ -95,6 +100,7 @@ const char *smcsd_status_string(int code);
  * start must be 256-byte aligned (SMCSD_EWORKSPACE otherwise).
  *   SMCSD_OP_VERIFY_SMC / _SPS: B, N, K, V as passed to smcsd_verify (P ignored).
  *   SMCSD_OP_DRAFT: B = number of rows, N = 1, V as passed to smcsd_draft_sample.
+ *   SMCSD_OP_KV_CHECK: the pool size P (B, N, K, V ignored); no initial contents needed.
  *   SMCSD_OP_KV: B, N and the pool size P (K, V ignored).  The KV workspace must be
  *   zero-filled before its first use and then passed, unmodified, to every later call
  *   with the same B, N and P: calls keep its contents consistent (it alternates two
@@ -326,6 +332,36 @@ int smcsd_step(const void *target_logits, const void *draft_logits, int dtype, i
                int32_t *free_list, int32_t *free_top, int64_t P, int32_t *cow, int32_t *cow_count,
                int32_t *status, void *verify_workspace, size_t verify_workspace_bytes,
                void *kv_workspace, size_t kv_workspace_bytes, void *stream);
+
+/*
+ * smcsd_kv_check - debugging check of the refcounted block-table state that
+ * smcsd_kv_reassign, smcsd_resample_kv_reassign and smcsd_step maintain (SMC explainers,
+ * "system optimisation design": KV blocks shared by pointer and released by reference
+ * count; Spanish page, cache management).  It recounts everything from the arrays
+ * themselves, independently of the exchange kernels, and counts violations per kind:
+ *   violations[0]  blocks whose refcount differs from the number of allocated table
+ *                  slots naming them;
+ *   violations[1]  allocated table slots holding an id outside [0, P) other than the
+ *                  -1 of a slot a NOSPACE call left unfilled;
+ *   violations[2]  free-stack entries outside [0, P), extra occurrences of a block on
+ *                  the stack, and a top outside [0, P] (then clamped);
+ *   violations[3]  blocks on the free stack with a positive refcount;
+ *   violations[4]  blocks with refcount <= 0 that are not on the free stack (leaked).
+ * A consistent state has all five at 0: live and free blocks then partition the pool.
+ * block_tables [S, M_cap] int32 with slots [0, slots) allocated in every row (after a
+ * reassign call with seq_len L and reserve R: slots = ceil((L + R) / block_size));
+ * refcounts [P], free_list [P], free_top [1] int32 as in smcsd_kv_reassign; all read
+ * only.  violations [SMCSD_KV_CHECK_KINDS] int32 device output, overwritten (not
+ * accumulated); SMCSD_ST_KV_INCONSISTENT is OR'ed into *status when any is nonzero.
+ * workspace: smcsd_workspace_bytes(SMCSD_OP_KV_CHECK, 0, 0, 0, 0, P), 256-byte
+ * aligned, any contents.  Limits: S >= 0, 0 <= slots <= M_cap, 1 <= P <= 2^31 - 1.
+ * Five small launches; meant for tests and debug runs (the Python binding runs it after
+ * every KV call when the environment variable SMCSD_DEBUG_CHECK is 1), not the timed path.
+ */
+int smcsd_kv_check(const int32_t *block_tables, int64_t S, int M_cap, int slots,
+                   const int32_t *refcounts, const int32_t *free_list, const int32_t *free_top,
+                   int64_t P, int32_t *violations, int32_t *status, void *workspace,
+                   size_t workspace_bytes, void *stream);
 
 /*
  * smcsd_philox4x32_10 - the library's device Philox4x32-10 block function (SC'11),

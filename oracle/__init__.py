@@ -29,6 +29,7 @@ ST_EMPTY_ROW = 2
 ST_NOSPACE = 4
 ST_DEGENERATE_WEIGHTS = 8
 ST_BAD_INPUT = 16
+ST_KV_INCONSISTENT = 32
 
 TAG_BONUS = 1
 TAG_RESAMPLE = 2
@@ -301,3 +302,38 @@ def kv_reassign(ancestors: np.ndarray, resampled: np.ndarray, tables: np.ndarray
         raise ValueError("orc_kv_reassign rejected its arguments (capacity or allocation)")
     return {"tables": T, "refcounts": rc, "free_list": fl, "free_top": int(top[0]),
             "cow": cow[: int(ncow[0])].copy(), "cow_count": int(ncow[0]), "status": int(st[0])}
+
+
+def kv_check(tables: np.ndarray, slots: int, refcounts: np.ndarray, free_list: np.ndarray,
+             free_top: int) -> np.ndarray:
+    """The block-table state's invariants, counted by kind (SMC explainers, "system
+    optimisation design": blocks shared by pointer and released by reference count).  The
+    definition, in numpy, of what a consistent state is:
+      [0] blocks whose refcount differs from the number of allocated slots naming them;
+      [1] allocated slots holding an id outside [0, P) other than the -1 of an unfilled slot;
+      [2] free-stack entries outside [0, P), extra occurrences of a block on the stack, and
+          a top outside [0, P] (counted once, then clamped);
+      [3] blocks on the free stack whose refcount is positive;
+      [4] blocks whose refcount is <= 0 and that are not on the free stack.
+    All zero: live and free blocks partition the pool and every count is exact."""
+    T = np.asarray(tables, dtype=np.int64)[:, :slots]
+    rc = np.asarray(refcounts, dtype=np.int64)
+    P = rc.shape[0]
+    v = np.zeros(5, dtype=np.int64)
+    ids = T.ravel()
+    inr = (ids >= 0) & (ids < P)
+    v[1] = np.count_nonzero(~inr & (ids != -1))
+    refs = np.bincount(ids[inr], minlength=P)
+    v[0] = np.count_nonzero(refs != rc)
+    top = int(free_top)
+    if top < 0 or top > P:
+        v[2] += 1
+        top = min(max(top, 0), P)
+    fr = np.asarray(free_list, dtype=np.int64)[:top]
+    okf = (fr >= 0) & (fr < P)
+    v[2] += np.count_nonzero(~okf)
+    occ = np.bincount(fr[okf], minlength=P)
+    v[2] += int(np.maximum(occ - 1, 0).sum())
+    v[3] = np.count_nonzero((occ > 0) & (rc > 0))
+    v[4] = np.count_nonzero((occ == 0) & (rc <= 0))
+    return v

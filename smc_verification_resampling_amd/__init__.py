@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libsmcsd.so")
 
 DTYPE_F32, DTYPE_BF16 = 0, 1
 MODE_SMC, MODE_SPS, MODE_SMC_RACE = 0, 1, 2  # MODE_SMC_RACE: SMC with the exponential-race bonus
-OP_VERIFY_SMC, OP_VERIFY_SPS, OP_KV, OP_DRAFT = 0, 1, 2, 3
+OP_VERIFY_SMC, OP_VERIFY_SPS, OP_KV, OP_DRAFT, OP_KV_CHECK = 0, 1, 2, 3, 4
 STATIC_SCRATCH_BYTES = 4 << 20  # smcsd_verify_static's per-GPU scratch array
 
 ST_NAN_INPUT = 1
@@ -27,10 +27,15 @@ ST_EMPTY_ROW = 2
 ST_NOSPACE = 4
 ST_DEGENERATE_WEIGHTS = 8
 ST_BAD_INPUT = 16
+ST_KV_INCONSISTENT = 32
+KV_CHECK_KINDS = 5
+KV_CHECK_NAMES = ("refcount != table references", "table id out of range",
+                  "free-stack entry out of range or repeated", "referenced block on the free stack",
+                  "unreferenced block not on the free stack")
 
 EXPORTED = ("smcsd_version", "smcsd_status_string", "smcsd_workspace_bytes", "smcsd_verify",
             "smcsd_verify_static", "smcsd_draft_sample", "smcsd_resample", "smcsd_kv_reassign",
-            "smcsd_resample_kv_reassign", "smcsd_step", "smcsd_philox4x32_10")
+            "smcsd_resample_kv_reassign", "smcsd_step", "smcsd_kv_check", "smcsd_philox4x32_10")
 
 _DT = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
 
@@ -77,6 +82,8 @@ def load_library(path: str = LIB_PATH):
                                P, P, P, P, P, P, P, P, P, P, P, i32, i32, i64, i32, P, P, P, i64,
                                P, P, P, P, sz, P, sz, P]
     lib.smcsd_step.restype = i32
+    lib.smcsd_kv_check.argtypes = [P, i64, i32, i32, P, P, P, i64, P, P, P, sz, P]
+    lib.smcsd_kv_check.restype = i32
     lib.smcsd_philox4x32_10.argtypes = [P, P, i32, P, P]
     lib.smcsd_philox4x32_10.restype = i32
     if path == LIB_PATH:
@@ -252,6 +259,8 @@ def kv_reassign(ancestors: torch.Tensor, resampled: torch.Tensor, B: int, N: int
         _dev(cow_count, "cow_count", torch.int32, 1), _dev(status, "status", torch.int32, 1),
         _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
     _check(rc, "smcsd_kv_reassign")
+    _debug_kv_check(block_tables, block_size, seq_len, reserve_tokens, refcounts, free_list,
+                    free_top, "smcsd_kv_reassign", stream)
 
 
 def resample_kv_reassign(log_weights: torch.Tensor, B: int, N: int, tau: float, seed: int,
@@ -278,6 +287,8 @@ def resample_kv_reassign(log_weights: torch.Tensor, B: int, N: int, tau: float, 
         _dev(status, "status", torch.int32, 1), _dev(workspace, "workspace", torch.uint8),
         workspace.numel(), _stream(stream))
     _check(rc, "smcsd_resample_kv_reassign")
+    _debug_kv_check(block_tables, block_size, seq_len, reserve_tokens, refcounts, free_list,
+                    free_top, "smcsd_resample_kv_reassign", stream)
 
 
 def step(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: Optional[torch.Tensor],
@@ -324,6 +335,46 @@ def step(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: Opti
         _dev(verify_workspace, "verify_workspace", torch.uint8), verify_workspace.numel(),
         _dev(kv_workspace, "kv_workspace", torch.uint8), kv_workspace.numel(), _stream(stream))
     _check(rc, "smcsd_step")
+    _debug_kv_check(block_tables, block_size, seq_len, reserve_tokens, refcounts, free_list,
+                    free_top, "smcsd_step", stream)
+
+
+def kv_check(block_tables: torch.Tensor, slots: int, refcounts: torch.Tensor,
+             free_list: torch.Tensor, free_top: torch.Tensor, violations: torch.Tensor,
+             status: torch.Tensor, workspace: torch.Tensor, stream=None) -> None:
+    """smcsd_kv_check: violations [KV_CHECK_KINDS] int32 receives the counts (KV_CHECK_NAMES);
+    workspace from alloc_workspace(OP_KV_CHECK, 0, 0, P=P)."""
+    if block_tables.dim() != 2:
+        raise SmcsdError("block_tables must be [S, M_cap]")
+    S, M_cap = block_tables.shape
+    P = refcounts.numel()
+    rc = _L().smcsd_kv_check(
+        _dev(block_tables, "block_tables", torch.int32), S, M_cap, int(slots),
+        _dev(refcounts, "refcounts", torch.int32), _dev(free_list, "free_list", torch.int32, P),
+        _dev(free_top, "free_top", torch.int32, 1), P,
+        _dev(violations, "violations", torch.int32, KV_CHECK_KINDS),
+        _dev(status, "status", torch.int32, 1), _dev(workspace, "workspace", torch.uint8),
+        workspace.numel(), _stream(stream))
+    _check(rc, "smcsd_kv_check")
+
+
+def _debug_kv_check(block_tables, block_size, seq_len, reserve_tokens, refcounts, free_list,
+                    free_top, what, stream):
+    """With SMCSD_DEBUG_CHECK=1 in the environment: smcsd_kv_check after a KV call, waited
+    for, raising SmcsdError on any violation (debug runs only: it synchronises the stream)."""
+    if os.environ.get("SMCSD_DEBUG_CHECK") != "1":
+        return
+    dev = block_tables.device
+    P = refcounts.numel()
+    ws = alloc_workspace(OP_KV_CHECK, 0, 0, P=P, device=dev)
+    viol = torch.zeros(KV_CHECK_KINDS, dtype=torch.int32, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    slots = -(-(int(seq_len) + int(reserve_tokens)) // int(block_size))
+    kv_check(block_tables, slots, refcounts, free_list, free_top, viol, st, ws, stream)
+    counts = viol.cpu().tolist()
+    if any(counts):
+        raise SmcsdError("%s left an inconsistent KV state: %s" % (what, ", ".join(
+            "%s: %d" % (n, c) for n, c in zip(KV_CHECK_NAMES, counts) if c)))
 
 
 def philox4x32_10(counters: torch.Tensor, keys: torch.Tensor, out: torch.Tensor, stream=None):

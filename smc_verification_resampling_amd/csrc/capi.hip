@@ -36,6 +36,7 @@ const char *smcsd_status_string(int code) {
     case SMCSD_ST_NOSPACE: return "block pool exhausted";
     case SMCSD_ST_DEGENERATE_WEIGHTS: return "all particle weights zero or NaN";
     case SMCSD_ST_BAD_INPUT: return "token, ancestor or block id out of range";
+    case SMCSD_ST_KV_INCONSISTENT: return "block tables, refcounts and free stack disagree";
     default: return "unknown code";
   }
 }
@@ -54,6 +55,10 @@ size_t smcsd_workspace_bytes(int op, int B, int N, int K, int V, int64_t P) {
   if (op == SMCSD_OP_KV) {
     if (P < 1) return 0;
     return kv_ws_layout(S, P).total;
+  }
+  if (op == SMCSD_OP_KV_CHECK) {
+    if (P < 1 || P > INT32_MAX) return 0;
+    return kv_check_ws_bytes(P);
   }
   return 0;
 }
@@ -358,6 +363,21 @@ int smcsd_step(const void *target_logits, const void *draft_logits, int dtype, i
   return hip_rc(launch_kv(nullptr, nullptr, fr, B, N, block_tables, M_cap, block_size, seq_len,
                           reserve_tokens, refcounts, free_list, free_top, P, cow, cow_count, status,
                           static_cast<char *>(kv_workspace), as_stream(stream)));
+}
+
+int smcsd_kv_check(const int32_t *block_tables, int64_t S, int M_cap, int slots,
+                   const int32_t *refcounts, const int32_t *free_list, const int32_t *free_top,
+                   int64_t P, int32_t *violations, int32_t *status, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+  if (S < 0 || M_cap < 1 || slots < 0 || slots > M_cap || P < 1 || P > INT32_MAX)
+    return SMCSD_EINVAL;
+  if ((S > 0 && !block_tables) || !refcounts || !free_list || !free_top || !violations || !status)
+    return SMCSD_EINVAL;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < kv_check_ws_bytes(P))
+    return SMCSD_EWORKSPACE;
+  return hip_rc(launch_kv_check(block_tables, S, M_cap, slots, refcounts, free_list, free_top, P,
+                                violations, status, static_cast<char *>(workspace),
+                                as_stream(stream)));
 }
 
 int smcsd_philox4x32_10(const uint32_t *counters, const uint32_t *keys, int n, uint32_t *out,

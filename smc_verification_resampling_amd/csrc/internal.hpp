@@ -134,6 +134,13 @@ hipError_t launch_kv(const int32_t *anc, const int32_t *resampled, const FusedRe
                      int32_t *free_list, int32_t *free_top, int64_t P, int32_t *cow,
                      int32_t *cow_count, int32_t *status, char *ws, hipStream_t stream);
 
+// The block-table state check (kvcheck.hip): workspace bytes and launches.
+size_t kv_check_ws_bytes(int64_t P);
+hipError_t launch_kv_check(const int32_t *T, int64_t S, int M_cap, int slots,
+                           const int32_t *rc, const int32_t *fl, const int32_t *free_top,
+                           int64_t P, int32_t *viol, int32_t *status, char *ws,
+                           hipStream_t stream);
+
 hipError_t launch_philox(const uint32_t *ctr, const uint32_t *key, int n, uint32_t *out,
                          hipStream_t stream);
 

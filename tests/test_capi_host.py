@@ -45,10 +45,11 @@ def test_gfx950_code_object_present(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.smcsd_version() == 5
+    assert lib.smcsd_version() == 6
     assert sm.status_string(0) == "ok"
     assert "workspace" in sm.status_string(-4)
     assert "pool" in sm.status_string(sm.ST_NOSPACE)
+    assert "free stack" in sm.status_string(sm.ST_KV_INCONSISTENT)
 
 
 def test_workspace_sizes(lib):
@@ -59,6 +60,8 @@ def test_workspace_sizes(lib):
     assert sm.workspace_bytes(sm.OP_VERIFY_SMC, 1, 1, 33, 10) == 0   # K above the limit
     assert sm.workspace_bytes(sm.OP_KV, 1, 1, 0, 0, 0) == 0
     assert sm.workspace_bytes(sm.OP_DRAFT, 512, 1, 0, 128256) >= 512 * 16 * 8
+    assert sm.workspace_bytes(sm.OP_KV_CHECK, 0, 0, 0, 0, 1000) >= 2 * 4 * 1000
+    assert sm.workspace_bytes(sm.OP_KV_CHECK, 0, 0, 0, 0, 0) == 0
 
 
 def _verify_rc(lib, **kw):
@@ -206,3 +209,20 @@ def test_step_host_validation(lib):
     assert rc(vwsb=16) == -4 and rc(kwsb=16) == -4
     assert rc(vws=ctypes.c_void_p(0x1010)) == -4
     assert rc(B=0) == 0
+
+
+def test_kv_check_host_validation(lib):
+    p = ctypes.c_void_p(0x1000)
+
+    def rc(**kw):
+        a = dict(T=p, S=4, M=8, slots=3, P=100, viol=p, st=p, ws=p, wsb=1 << 20)
+        a.update(kw)
+        return lib.smcsd_kv_check(a["T"], a["S"], a["M"], a["slots"], p, p, p, a["P"], a["viol"],
+                                  a["st"], a["ws"], a["wsb"], None)
+    assert rc(S=-1) == -1 and rc(M=0) == -1
+    assert rc(slots=9) == -1 and rc(slots=-1) == -1   # beyond M_cap
+    assert rc(P=0) == -1 and rc(P=1 << 31) == -1
+    assert rc(T=None) == -1 and rc(viol=None) == -1 and rc(st=None) == -1
+    assert rc(wsb=799) == -4                          # two counters of 4 bytes per block
+    assert rc(ws=ctypes.c_void_p(0x1010)) == -4       # not 256-byte aligned
+    assert rc(ws=None) == -4

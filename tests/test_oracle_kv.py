@@ -234,3 +234,62 @@ def test_out_of_vocabulary_draft_token_is_flagged(orc):
     s = orc.verify_sps(tgt, drf, toks, 1.0, 5, 0)
     assert s["status"] == orc.ST_BAD_INPUT
     assert s["num_tokens"][1] == 1 and s["num_tokens"][2] == 1      # a NaN ratio is no acceptance
+
+
+def test_kv_check_definition_on_a_hand_built_state():
+    """The invariant counts on a hand-built pool of 8 blocks: two sequences sharing block 0,
+    each with a private block, the other five on the free stack; then one corruption at a
+    time, each with the count it must give."""
+    import oracle
+
+    T = np.array([[0, 1, -1], [0, 2, -1]], np.int32)
+    rc = np.array([2, 1, 1, 0, 0, 0, 0, 0], np.int32)
+    fl = np.array([7, 6, 5, 4, 3, 0, 0, 0], np.int32)
+    assert oracle.kv_check(T, 2, rc, fl, 5).tolist() == [0, 0, 0, 0, 0]
+    r = rc.copy(); r[1] = 2                                     # a refcount one too high
+    assert oracle.kv_check(T, 2, r, fl, 5).tolist() == [1, 0, 0, 0, 0]
+    t = T.copy(); t[1, 1] = 9                                   # an id past the pool
+    assert oracle.kv_check(t, 2, rc, fl, 5).tolist() == [1, 1, 0, 0, 0]
+    t = T.copy(); t[1, 1] = -1                                  # an unfilled slot: allowed
+    assert oracle.kv_check(t, 2, rc, fl, 5).tolist() == [1, 0, 0, 0, 0]
+    f = fl.copy(); f[5] = 3                                     # block 3 pushed twice
+    assert oracle.kv_check(T, 2, rc, f, 6).tolist() == [0, 0, 1, 0, 0]
+    f = fl.copy(); f[5] = 0                                     # a live block on the stack
+    assert oracle.kv_check(T, 2, rc, f, 6).tolist() == [0, 0, 0, 1, 0]
+    assert oracle.kv_check(T, 2, rc, fl, 4).tolist() == [0, 0, 0, 0, 1]   # block 3 leaked
+    f = fl.copy(); f[2] = -3                                    # a corrupt stack entry
+    assert oracle.kv_check(T, 2, rc, f, 5).tolist() == [0, 0, 1, 0, 1]   # and 5 is lost
+    # a top past the pool (1), clamped to 8: block 0 three times on the stack (2 extra) and
+    # live (1)
+    assert oracle.kv_check(T, 2, rc, fl, 9).tolist() == [0, 0, 3, 1, 0]
+    assert oracle.kv_check(T, 3, rc, fl, 5).tolist() == [0, 0, 0, 0, 0]  # -1 slots skipped
+    r = rc.copy(); r[2] = 0                                     # a live block's count lost
+    assert oracle.kv_check(T, 2, r, fl, 5).tolist() == [1, 0, 0, 0, 1]
+
+
+@pytest.mark.parametrize("shared", [False, True])
+def test_kv_check_is_clean_after_oracle_rounds(orc, shared):
+    """Every state the oracle's exchange leaves passes the invariant check, rounds with
+    and without resampling, with copy-on-write and fresh reservations."""
+    import oracle
+
+    rng = np.random.default_rng(7 + shared)
+    B, N, bs, K, ctx0, rounds = 3, 6, 4, 3, 9, 12
+    R = K + 1
+    M = math.ceil((ctx0 + (rounds + 1) * R) / bs)
+    P = B * N * M
+    T, rc, fl, top = _initial(B, N, M, bs, P, ctx0, shared)
+    L = ctx0
+    st = orc.kv_reassign(np.tile(np.arange(N, dtype=np.int32), (B, 1)), np.zeros(B, np.int32), T,
+                         bs, L, R, rc, fl, top)
+    assert oracle.kv_check(st["tables"], math.ceil((L + R) / bs), st["refcounts"], st["free_list"],
+                           st["free_top"]).tolist() == [0] * 5
+    for t in range(rounds):
+        L += R
+        anc = np.sort(rng.integers(0, N, (B, N)), axis=1).astype(np.int32)
+        res = (rng.random(B) < 0.7).astype(np.int32)
+        st = orc.kv_reassign(anc, res, st["tables"], bs, L, R, st["refcounts"], st["free_list"],
+                             st["free_top"])
+        assert oracle.kv_check(st["tables"], math.ceil((L + R) / bs), st["refcounts"],
+                               st["free_list"], st["free_top"]).tolist() == [0] * 5, t
+        _check_invariants(st, P)
