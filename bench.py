@@ -38,14 +38,14 @@ EVENT_EVERY = 16
 # only for the kernel sources they were taken on: any change to them reports null.
 VERIFY_TRAFFIC = {
     "workload": "c3_batched",
-    "bytes": 1186544688,
+    "bytes": 1186514842,
     "sources": {
         "smc_verification_resampling_amd/csrc/verify.hip":
-            "da2ebf9c595b8052a2d1f25a8985e36056aa2ba328ccef31cfde3191a72b98a0",
+            "5a97901980fe30daf3c7873867cbff12b5ff05bcf51c4b1aa33fb00d1bc9bcd0",
         "smc_verification_resampling_amd/csrc/device.hpp":
             "052e9639476c02ca5093ff5435e86d38bb86ed9e9cd9eac50112402c4a58b14d",
         "smc_verification_resampling_amd/csrc/internal.hpp":
-            "eee11a3a5c7749718f84f1f816eacb03cc128d53658a1fa7ca6bf5564dac0731",
+            "67643da46ac8d764d60de1f09d402b777dcfa235bf6a9bfb3f8d2e06ccbb2bcd",
     },
 }
 
