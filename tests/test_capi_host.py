@@ -226,3 +226,17 @@ def test_kv_check_host_validation(lib):
     assert rc(wsb=799) == -4                          # two counters of 4 bytes per block
     assert rc(ws=ctypes.c_void_p(0x1010)) == -4       # not 256-byte aligned
     assert rc(ws=None) == -4
+
+
+def test_header_is_c99_and_a_c_client_links(lib, tmp_path):
+    """include/smcsd.h compiles as strict C99 and a C program linked against libsmcsd.so
+    gets the documented host-side answers (tests/helpers/abi_c_client.c)."""
+    exe = tmp_path / "abi_c_client"
+    libdir = os.path.dirname(sm.LIB_PATH)
+    cmd = ["gcc", "-std=c99", "-pedantic", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+           os.path.join(ROOT, "tests", "helpers", "abi_c_client.c"), "-L", libdir, "-lsmcsd",
+           "-Wl,-rpath," + libdir, "-o", str(exe)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
