@@ -163,3 +163,51 @@ def test_draft_logq_path_equals_reading_the_draft_rows():
     assert np.array_equal(outs[0][0], outs[1][0])
     assert np.max(np.abs(outs[0][1] - outs[1][1])) < 1e-4
     assert np.max(np.abs(outs[0][2] - outs[1][2])) < 1e-4
+
+
+def test_draft_side_round_at_the_benchmark_shape():
+    """The --draft-logq flow of bench.py at the C3 shape (32 prompts x 16 particles, K = 4,
+    V = 128256, bf16 Zipf logits), every sequence against the oracle: the K draft positions
+    from smcsd_draft_sample (strided rows of the draft tensor, as the benchmark passes them)
+    against oracle.draft_sample, then smcsd_verify with those log q against the oracle's
+    verify with logq_in."""
+    from workloads import configs as C
+    from workloads import synth
+
+    cfg = C.C3
+    B, N, K, V, S = cfg.B, cfg.N, cfg.K, cfg.V, cfg.S
+    tgt, drf = synth.make_logit_set(cfg, 0, "cuda", synth.zipf_base(cfg, "cuda"))
+    T32 = float(np.float32(cfg.temperature))
+    dh = _host(drf)
+    toks, lq = _i32(S, K), torch.zeros((S, K), device="cuda")
+    flat = drf.reshape(-1)
+    ws_d = sm.alloc_workspace(sm.OP_DRAFT, S, 1, 0, V)
+    st = _i32(1)
+    for k in range(K):
+        tk, lk = _i32(S), torch.zeros(S, device="cuda")
+        sm.draft_sample(flat[k * V:], S, V, cfg.temperature, cfg.rng_seed, 0, k, tk, st, ws_d,
+                        out_logq=lk, row_stride=K * V)
+        torch.cuda.synchronize()
+        o = oracle.draft_sample(np.ascontiguousarray(dh[:, k]), T32, cfg.rng_seed, 0, k)
+        ok = o["margin"] >= MARGIN
+        assert ok.mean() > 0.9        # ~3 % of Zipf draws land within 1e-6 of a CDF step
+        assert np.array_equal(tk.cpu().numpy()[ok], o["tokens"][ok]), k
+        d = np.abs(lk.cpu().numpy().astype(np.float64) - o["logq"])
+        assert np.all(d[ok] <= 1e-5 * np.maximum(1.0, np.abs(o["logq"][ok]))), k
+        toks[:, k] = torch.from_numpy(o["tokens"]).cuda()     # the oracle's draws feed both sides
+        lq[:, k] = lk
+    assert int(st.cpu()[0]) == 0
+    lw = torch.zeros(S, device="cuda")
+    out, num = _i32(S, K + 1), _i32(S)
+    ws = sm.alloc_workspace(sm.OP_VERIFY_SMC, B, N, K, V)
+    sm.verify(tgt, None, toks, B, N, K, V, cfg.temperature, cfg.alpha, sm.MODE_SMC, cfg.rng_seed, 1,
+              out, st, ws, log_weights=lw, out_num_tokens=num, logq_in=lq)
+    torch.cuda.synchronize()
+    o = oracle.verify_smc(_host(tgt), None, toks.cpu().numpy(), T32, float(np.float32(cfg.alpha)),
+                          cfg.rng_seed, 1, np.zeros(S, np.float32),
+                          logq_in=lq.cpu().numpy().astype(np.float64))
+    ok = o["margin"] >= MARGIN
+    assert int(st.cpu()[0]) == o["status"] == 0
+    assert np.array_equal(out.cpu().numpy()[ok], o["tokens"][ok])
+    assert np.max(np.abs(lw.cpu().numpy() - o["lw"])) <= 1e-4
+    assert np.all(num.cpu().numpy() == K + 1)
