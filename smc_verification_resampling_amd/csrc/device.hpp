@@ -224,56 +224,6 @@ __device__ __forceinline__ Lse lse_block_reduce(Lse st, float c, Lse *lds) {
   return st;
 }
 
-// Workgroup reduction of the online state together with NS sums that share its
-// reference (each is relative to the thread's mc and is rescaled with s at every
-// combine).  Results valid in thread 0: the state, and the sums relative to its mc.
-template <int BLOCK, int NS>
-__device__ __forceinline__ Lse lse_block_reduce_with(Lse st, float (&v)[NS], float c,
-                                                     float *lds) {
-  auto combine = [&](float om, float omc, float os, const float *ov) {
-    const float M = fmaxf(st.m, om);
-    if (M == kNegInf) {
-      st.s += os;
-#pragma unroll
-      for (int q = 0; q < NS; ++q) v[q] += ov[q];
-      return;
-    }
-    const float Mc = __fmul_rn(M, c);
-    const bool ainf = st.m == kNegInf, binf = om == kNegInf;
-    const float fa = ainf ? 0.0f : fast_exp2(st.mc - Mc);
-    const float fb = binf ? 0.0f : fast_exp2(omc - Mc);
-    st.s = (ainf ? st.s * 0.0f : st.s * fa) + (binf ? os * 0.0f : os * fb);
-#pragma unroll
-    for (int q = 0; q < NS; ++q) v[q] = (ainf ? v[q] * 0.0f : v[q] * fa) + (binf ? ov[q] * 0.0f : ov[q] * fb);
-    st.m = M;
-    st.mc = Mc;
-  };
-#pragma unroll
-  for (int mask = 1; mask < kWave; mask <<= 1) {
-    float ov[NS];
-#pragma unroll
-    for (int q = 0; q < NS; ++q) ov[q] = __shfl_xor(v[q], mask, kWave);
-    combine(__shfl_xor(st.m, mask, kWave), __shfl_xor(st.mc, mask, kWave),
-            __shfl_xor(st.s, mask, kWave), ov);
-  }
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  constexpr int kRec = 3 + NS;
-  if (lane == 0) {
-    lds[wave * kRec + 0] = st.m;
-    lds[wave * kRec + 1] = st.mc;
-    lds[wave * kRec + 2] = st.s;
-#pragma unroll
-    for (int q = 0; q < NS; ++q) lds[wave * kRec + 3 + q] = v[q];
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-#pragma unroll
-    for (int w = 1; w < BLOCK / kWave; ++w)
-      combine(lds[w * kRec + 0], lds[w * kRec + 1], lds[w * kRec + 2], lds + w * kRec + 3);
-  }
-  return st;
-}
-
 // ---------------------------------------------------------------------------------
 // scans and sums
 // ---------------------------------------------------------------------------------
@@ -319,6 +269,83 @@ __device__ __forceinline__ double wave_sum(double v) {
   const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)b, kWave - 1);
   const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(b >> 32), kWave - 1);
   return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+// 32-bit values moved across lanes by DPP.  dpp_f: lanes whose source is outside the
+// pattern, or whose row is not in ROW_MASK, read 0 (for sums); dpp_f_keep: they read
+// their own value (for maxima).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, true));
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f_keep(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+// The sum (max) over the 64 lanes, in every lane: the DPP scan pattern above, then the
+// last lane read as a uniform value.  A fixed order, so the same bits every time.
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += dpp_f<0x111, 0xf>(v);
+  v += dpp_f<0x112, 0xf>(v);
+  v += dpp_f<0x114, 0xf>(v);
+  v += dpp_f<0x118, 0xf>(v);
+  v += dpp_f<0x142, 0xa>(v);
+  v += dpp_f<0x143, 0xc>(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = fmaxf(v, dpp_f_keep<0x111, 0xf>(v));
+  v = fmaxf(v, dpp_f_keep<0x112, 0xf>(v));
+  v = fmaxf(v, dpp_f_keep<0x114, 0xf>(v));
+  v = fmaxf(v, dpp_f_keep<0x118, 0xf>(v));
+  v = fmaxf(v, dpp_f_keep<0x142, 0xa>(v));
+  v = fmaxf(v, dpp_f_keep<0x143, 0xc>(v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
+}
+
+// Workgroup reduction of the online state with NS sums that share its reference, in two
+// phases: the workgroup's max first, then every thread's s and sums rescaled once to that
+// max and added with DPP wave sums (no cross-lane permutes, no per-step rescaling).
+// Results valid in thread 0: the state, and the sums relative to its mc.  lds holds
+// (BLOCK / 64) * (NS + 2) floats and must not be reused before the next barrier.
+template <int BLOCK, int NS>
+__device__ __forceinline__ Lse lse_block_reduce_sums(Lse st, float *v, float c, float *lds) {
+  constexpr int W = BLOCK / kWave;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const float wm = wave_max_f32(st.m);
+  if (lane == 0) lds[wave] = wm;
+  __syncthreads();
+  float M = lds[0];
+#pragma unroll
+  for (int w = 1; w < W; ++w) M = fmaxf(M, lds[w]);
+  const float Mc = M == kNegInf ? 0.0f : __fmul_rn(M, c);
+  const bool inf = st.m == kNegInf;
+  const float f = inf ? 0.0f : fast_exp2(st.mc - Mc);
+  const float s = wave_sum_f32(inf ? st.s * 0.0f : st.s * f);
+  float t[NS > 0 ? NS : 1];
+#pragma unroll
+  for (int q = 0; q < NS; ++q) t[q] = wave_sum_f32(inf ? v[q] * 0.0f : v[q] * f);
+  float *l2 = lds + W;
+  if (lane == 0) {
+    l2[wave * (NS + 1)] = s;
+#pragma unroll
+    for (int q = 0; q < NS; ++q) l2[wave * (NS + 1) + 1 + q] = t[q];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float S = l2[0];
+#pragma unroll
+    for (int q = 0; q < NS; ++q) v[q] = l2[1 + q];
+#pragma unroll
+    for (int w = 1; w < W; ++w) {
+      S += l2[w * (NS + 1)];
+#pragma unroll
+      for (int q = 0; q < NS; ++q) v[q] += l2[w * (NS + 1) + 1 + q];
+    }
+    st = Lse{M, Mc, S};
+  }
+  return st;
 }
 
 template <typename T>

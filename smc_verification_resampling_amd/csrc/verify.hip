@@ -195,7 +195,7 @@ __global__ __launch_bounds__(kStreamBlock) void k_lse_partials(RowMap rm, int ns
   __shared__ Lse lds[kStreamBlock / kWave];
   __shared__ RaceBest sRace[kStreamBlock / kWave];
   __shared__ RaceBest sRaceT[RACE ? kStreamBlock : 1];
-  __shared__ float sRed[(kStreamBlock / kWave) * (3 + kSlabs)];
+  __shared__ float sRed[(kStreamBlock / kWave) * (2 + kSlabs)];
   __shared__ float sSlabT[kStreamBlock][kSlabs + 1];  // per-thread slab sums (bonus tiles)
   const int K = rm.K;
   const int R = 2 * K + 1;
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(kStreamBlock) void k_lse_partials(RowMap rm, int ns
         for (int u = 0; u < kSlabs; ++u)
           if (u == ts) slab[u] += t;
       }
-      st = lse_block_reduce_with<kStreamBlock, kSlabs>(st, slab, c, sRed);
+      st = lse_block_reduce_sums<kStreamBlock, kSlabs>(st, slab, c, sRed);
       if (tid == 0) {
         part[((int64_t)g * R + slot) * chunks + ch] = make_float2(st.m, st.s);
         float *o = sub + ((int64_t)g * chunks + ch) * kSlabs;
