@@ -123,9 +123,11 @@ def test_race_verify_full_c3_shape_sampled():
 
 def test_race_mode_matches_smc_mode_apart_from_the_bonus():
     """Race and inverse-CDF modes on the same inputs: the bonus row is cut into the same
-    tiles in both, so its normaliser is bit-equal; the other rows are cut into larger big
-    tiles in race mode, so their normalisers, the gathered log-probabilities and the
-    log-weights agree to rounding (checked ten times tighter than the oracle bar)."""
+    tiles in both but reduced in a different order (the inverse-CDF tiles carry their slab
+    sums through a two-phase reduction, the race tiles their race winners through a
+    butterfly), and the other rows into larger big tiles in race mode, so the normalisers,
+    the gathered log-probabilities and the log-weights agree to rounding (checked ten times
+    tighter than the oracle bar)."""
     g = torch.Generator(device="cuda").manual_seed(4)
     B, N, K, V = 2, 16, 4, 50000
     S = B * N
@@ -138,7 +140,7 @@ def test_race_mode_matches_smc_mode_apart_from_the_bonus():
     assert a["status"] == 0 and b["status"] == 0
     assert np.array_equal(a["tokens"][:, :K], b["tokens"][:, :K])
     lse_a, lse_b = a["lse"].reshape(S, 2 * K + 1), b["lse"].reshape(S, 2 * K + 1)
-    assert np.array_equal(lse_a[:, K], lse_b[:, K])
+    assert np.all(np.abs(lse_a[:, K] - lse_b[:, K]) <= 1e-6 * np.abs(lse_a[:, K]))
     assert np.all(np.abs(lse_a - lse_b) <= 1e-6 * np.abs(lse_a))
     assert np.max(np.abs(a["logp"][:, :K] - b["logp"][:, :K])) <= 1e-6 * max(1.0, np.max(np.abs(a["logp"][:, :K])))
     assert np.max(np.abs(a["lw"] - b["lw"])) <= 1e-5  # alpha = 1: the bonus adds nothing
