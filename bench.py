@@ -38,12 +38,12 @@ EVENT_EVERY = 16
 # only for the kernel sources they were taken on: any change to them reports null.
 VERIFY_TRAFFIC = {
     "workload": "c3_batched",
-    "bytes": 1186514842,
+    "bytes": 1186492478,
     "sources": {
         "smc_verification_resampling_amd/csrc/verify.hip":
-            "5a97901980fe30daf3c7873867cbff12b5ff05bcf51c4b1aa33fb00d1bc9bcd0",
+            "83253b39652ead03d46738f3a01a3cc8fab4e558f88b28345889481974c01434",
         "smc_verification_resampling_amd/csrc/device.hpp":
-            "052e9639476c02ca5093ff5435e86d38bb86ed9e9cd9eac50112402c4a58b14d",
+            "2522278716f37d21a7304625ff4722f81d617ddcbba29605d41050dbafd80786",
         "smc_verification_resampling_amd/csrc/internal.hpp":
             "67643da46ac8d764d60de1f09d402b777dcfa235bf6a9bfb3f8d2e06ccbb2bcd",
     },
