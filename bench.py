@@ -41,7 +41,7 @@ VERIFY_TRAFFIC = {
     "bytes": 1186492478,
     "sources": {
         "smc_verification_resampling_amd/csrc/verify.hip":
-            "83253b39652ead03d46738f3a01a3cc8fab4e558f88b28345889481974c01434",
+            "25f99e339a52ec5339f07fafaa97d1482465177281cbf625d9b1647d54e458e8",
         "smc_verification_resampling_amd/csrc/device.hpp":
             "2522278716f37d21a7304625ff4722f81d617ddcbba29605d41050dbafd80786",
         "smc_verification_resampling_amd/csrc/internal.hpp":

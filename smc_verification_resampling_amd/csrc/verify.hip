@@ -956,11 +956,6 @@ static_assert(kSpsSlabElems<SMCSD_DTYPE_F32> % (8 * kStreamBlock) == 0 &&
                   kSpsSlabElems<SMCSD_DTYPE_BF16> % (8 * kStreamBlock) == 0,
               "a slab splits evenly into the re-read's units");
 
-__device__ __forceinline__ float wave_sum_f(float v) {
-#pragma unroll
-  for (int m = kWave / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-  return v;
-}
 __device__ __forceinline__ int wave_or(int v) {
 #pragma unroll
   for (int m = kWave / 2; m >= 1; m >>= 1) v |= __shfl_xor(v, m, kWave);
@@ -1271,8 +1266,8 @@ __global__ __launch_bounds__(kStreamBlock) void k_sps_resid(
         accum(wp, wq, a);
       }
     }
-    srho = wave_sum_f(srho);
-    sp = wave_sum_f(sp);
+    srho = wave_sum_f32(srho);
+    sp = wave_sum_f32(sp);
     if (lane == 0) slab_store(slab + t * kSpsSlabs + wv, make_float2(srho, sp));
     // arrival: every wave's slab store has completed (waited for) before the workgroup's
     // counter increment is issued, so the workgroup that sees the count reach `chunks`
