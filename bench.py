@@ -41,7 +41,7 @@ VERIFY_TRAFFIC = {
     "bytes": 1186492478,
     "sources": {
         "smc_verification_resampling_amd/csrc/verify.hip":
-            "25f99e339a52ec5339f07fafaa97d1482465177281cbf625d9b1647d54e458e8",
+            "e6eafe5c3261750fece750842bae49610e6f712a173f808db909b3da3f4bc275",
         "smc_verification_resampling_amd/csrc/device.hpp":
             "2522278716f37d21a7304625ff4722f81d617ddcbba29605d41050dbafd80786",
         "smc_verification_resampling_amd/csrc/internal.hpp":

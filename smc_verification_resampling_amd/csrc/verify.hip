@@ -1344,7 +1344,7 @@ static hipError_t launch_verify_t(const VerifyArgs &a) {
   const int esz = Elt<DT>::kBytes;
   const int ce = chunk_elems(DT);
   const int chunks = (int)ceil_div(a.V, ce);
-  const int K = a.K, R = 2 * K + 1;
+  const int K = a.K;
   RowMap rm{static_cast<const char *>(a.tgt), static_cast<const char *>(a.drf),
             a.row_stride * esz, a.seq_step, K};
   const VerifyWs w = verify_ws_layout(a.nseq, K, a.V, a.mode);
