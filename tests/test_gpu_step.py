@@ -210,3 +210,53 @@ def test_step_graph_replays_equal_direct_calls(name):
         _graph_run(C.C2.scaled(name="g", iters=10, n_sets=8), 8)
     else:
         _graph_run(C.C3.scaled(name="g", B=4, n_sets=2, iters=8), 6)
+
+
+def test_rounds_on_two_streams_do_not_interfere():
+    """The library keeps no state: two independent batches, each with its own workspaces
+    and state, stepped on two streams at once (default priority) give the bits of the same
+    rounds run one after the other on the default stream."""
+    cfg = C.C3.scaled(name="s2", B=3, V=30011, n_sets=2, iters=8)
+    B, N, K, V, S = cfg.B, cfg.N, cfg.K, cfg.V, cfg.S
+    base = synth.zipf_base(cfg, "cuda")
+    sets = []
+    for s in range(cfg.n_sets):
+        t, d = synth.make_logit_set(cfg, s, "cuda", base)
+        sets.append((t, d, synth.sample_draft_tokens(cfg, d, s)))
+    kv = synth.initial_kv(cfg)
+    lw0 = torch.zeros(S, device="cuda")
+
+    def fresh():
+        c = _Copy(cfg, kv, lw0)
+        ident = torch.arange(N, dtype=torch.int32, device="cuda").repeat(B, 1)
+        sm.kv_reassign(ident, torch.zeros(B, dtype=torch.int32, device="cuda"), B, N, c.tables,
+                       cfg.block_size, int(kv["seq_len"]), K + 1, c.rc, c.fl, c.top, c.cow, c.ncow,
+                       c.st, c.ws_kv)
+        return c
+
+    def rounds(c, seed, stream=None):
+        L = int(kv["seq_len"])
+        for t in range(5):
+            tgt, drf, x = sets[t % cfg.n_sets]
+            L += K + 1
+            sm.step(tgt, drf, x, B, N, K, V, cfg.temperature, cfg.alpha, sm.MODE_SMC, cfg.tau, seed, t,
+                    c.lw, c.tok, c.anc, c.ess, c.res, c.tables, cfg.block_size, L, K + 1, c.rc, c.fl,
+                    c.top, c.cow, c.ncow, c.st, c.ws_v, c.ws_kv, out_num_tokens=c.num,
+                    out_logp=c.logp, out_lse=c.lse, stream=stream)
+
+    ref = [fresh(), fresh()]
+    torch.cuda.synchronize()
+    rounds(ref[0], 11)
+    rounds(ref[1], 12)
+    torch.cuda.synchronize()
+    par = [fresh(), fresh()]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for c, seed, st in zip(par, (11, 12), streams):
+        with torch.cuda.stream(st):
+            rounds(c, seed, stream=st)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, par):
+        bad = _same(a.snapshot(), b.snapshot())
+        assert bad is None, bad
+    assert _same(ref[0].snapshot(), ref[1].snapshot()) is not None   # the seeds differ
