@@ -41,7 +41,7 @@ VERIFY_TRAFFIC = {
     "bytes": 1186492478,
     "sources": {
         "smc_verification_resampling_amd/csrc/verify.hip":
-            "e6eafe5c3261750fece750842bae49610e6f712a173f808db909b3da3f4bc275",
+            "cdf823e44c1c3eda882d360f4efd5a6b310c432fa95607be852c5619deffe37c",
         "smc_verification_resampling_amd/csrc/device.hpp":
             "2522278716f37d21a7304625ff4722f81d617ddcbba29605d41050dbafd80786",
         "smc_verification_resampling_amd/csrc/internal.hpp":

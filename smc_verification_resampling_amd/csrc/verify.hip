@@ -6,12 +6,14 @@
 // No MFMA: nothing here is a contraction.
 //
 // Kernels
-//   k_lse_partials   grid = tiles (row, 32 KiB vocabulary chunk), 256 threads.  One
-//                    streaming pass with 16-byte loads; per lane an online (max, sum of
-//                    2^(x*c - max*c)); wave shuffles + LDS combine; writes one (max, sum)
-//                    pair per tile.  Tiles of the bonus row (position K) also write the
-//                    sums of their 8 slabs (one slab = the 256 vectors loaded together),
-//                    so the bonus draw re-reads one slab instead of a whole chunk.
+//   k_lse_partials   grid = tiles, 256 threads: 32768-entry big tiles for the non-bonus
+//                    rows and 32 KiB tiles for the bonus row (position K).  One streaming
+//                    pass with 16-byte nontemporal loads; per lane an online (max, sum of
+//                    2^(x*c - max*c)); a workgroup reduction; one (max, sum) pair per tile.
+//                    Bonus tiles also write the sums of their 8 slabs (one slab = the 256
+//                    vectors loaded together), reduced in two phases (the workgroup max,
+//                    then DPP wave sums of the rescaled values), so the bonus draw re-reads
+//                    one slab instead of a whole chunk.
 //   k_smc_finalize   grid = sequences.  Combines the chunk pairs in fp64 into each row's
 //                    normaliser, gathers the draft-token log-probabilities, draws the bonus
 //                    token by inverse CDF (selects the slab from the slab sums of all the
