@@ -45,7 +45,7 @@ VERIFY_TRAFFIC = {
         "smc_verification_resampling_amd/csrc/device.hpp":
             "2522278716f37d21a7304625ff4722f81d617ddcbba29605d41050dbafd80786",
         "smc_verification_resampling_amd/csrc/internal.hpp":
-            "67643da46ac8d764d60de1f09d402b777dcfa235bf6a9bfb3f8d2e06ccbb2bcd",
+            "c1df9ac52d4d346b56e1092cd1ecd845b5763068679591040034332b09b7f00c",
     },
 }
 
@@ -96,7 +96,7 @@ def _parse():
                          "replay: the same launches with the same arguments, without the host's "
                          "per-launch cost (for the launch-bound small workloads)")
     ap.add_argument("--probe-mib", type=int, default=1024,
-                    help="size of the reference copy / read kernels (0 = skip)")
+                    help="size of the reference copy kernel (0 = skip)")
     return ap.parse_args()
 
 
@@ -308,6 +308,7 @@ def main():
     verify_avg_s = ev[0].elapsed_time(ev[1]) / 1e3 / verify_reps
     achieved_gbs = bytes_per_verify / verify_avg_s / 1e9
 
+    ceiling = read_ceiling(bytes_per_verify)
     sps = sps_timing(cfg, sets, args.steps) if cfg.sps else None
     ref = reference_kernels(args.probe_mib) if args.probe_mib > 0 else None
 
@@ -369,6 +370,10 @@ def main():
             "timing": "back-to-back verify calls between one event pair after the timed region",
             "in_region_median_us": round(float(np.median(in_region_us)), 2) if in_region_us else None,
             "in_region_launches": len(in_region_us),
+            # the achievable read rate on this GPU (smcsd_stream_read over as many bytes),
+            # and the verify call's rate as a fraction of it
+            "read_ceiling": ceiling,
+            "frac_of_read_ceiling": round(achieved_gbs / ceiling["GBps"], 4),
         },
         "cpu_baseline": cpu,
     }
@@ -457,33 +462,52 @@ def sps_timing(cfg, sets, steps):
             "status": int(status.cpu()[0])}
 
 
+def read_ceiling(nbytes, reps=50):
+    """The achievable HBM read rate of this GPU: smcsd_stream_read (the LSE pass's 16-byte
+    nontemporal loads, nothing else) over a buffer of the verify call's byte count, several
+    times the 256 MB last-level cache, `reps` back-to-back calls between one event pair."""
+    import torch
+
+    import smc_verification_resampling_amd as sm
+
+    n = (int(nbytes) + 15) // 16 * 16
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda")    # contents do not matter
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        sm.stream_read(buf, out)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(reps):
+        sm.stream_read(buf, out)
+    ev[1].record()
+    torch.cuda.synchronize()
+    s = ev[0].elapsed_time(ev[1]) / 1e3 / reps
+    del buf
+    return {"bytes": n, "reps": reps, "avg_us": round(s * 1e6, 2),
+            "GBps": round(n / s / 1e9, 1), "kernel": "smcsd_stream_read"}
+
+
 def reference_kernels(mib):
-    """Plain kernels of known size on the same GPU: a device copy (reads and writes `mib`
-    MiB; also the calibration kernel for the HBM byte counters) and a read-only sum."""
+    """A plain kernel of known size on the same GPU: a device copy (reads and writes `mib`
+    MiB), the calibration kernel for the HBM byte counters."""
     import torch
 
     n = mib * (1 << 20)
     src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     for _ in range(2):
         dst.copy_(src)
-        src.sum()
     torch.cuda.synchronize()
     reps = 5
     ev[0].record()
     for _ in range(reps):
         dst.copy_(src)
     ev[1].record()
-    ev[2].record()
-    for _ in range(reps):
-        src.sum()
-    ev[3].record()
     torch.cuda.synchronize()
     copy_s = ev[0].elapsed_time(ev[1]) / 1e3 / reps
-    sum_s = ev[2].elapsed_time(ev[3]) / 1e3 / reps
-    return {"bytes": n, "copy_GBps": round(2 * n / copy_s / 1e9, 1),
-            "read_sum_GBps": round(n / sum_s / 1e9, 1)}
+    return {"bytes": n, "copy_GBps": round(2 * n / copy_s / 1e9, 1)}
 
 
 def cpu_baseline(cfg, sets, budget_s, bonus="cdf"):

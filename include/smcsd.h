@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SMCSD_VERSION 6
+#define SMCSD_VERSION 7
 
 /* logits element type */
 #define SMCSD_DTYPE_F32 0
@@ -370,6 +370,22 @@ int smcsd_kv_check(const int32_t *block_tables, int64_t S, int M_cap, int slots,
  */
 int smcsd_philox4x32_10(const uint32_t *counters, const uint32_t *keys, int n, uint32_t *out,
                         void *stream);
+
+/*
+ * smcsd_stream_read - a measurement aid, not a step of the method.  The verify's LSE pass
+ * is one streaming read of the logits with a few operations per element (decoding is
+ * bound by memory bandwidth: SMC explainers, problem statement), so its speed of light is
+ * the rate at which this GPU streams reads from HBM.  This call reads each 16-byte word of
+ * [p, p + bytes) once, with the LSE pass's load instruction (16-byte nontemporal buffer
+ * loads) and in contiguous 128 KiB tiles, and XORs all the 32-bit words read into
+ * *xor_out (one device uint32, accumulated: the caller zeroes it first; bytes = 0 leaves it
+ * unchanged); bytes divided by the time of the call is the achievable read rate that the
+ * LSE pass's rate is compared with.  p: device memory, 16-byte aligned (may be NULL when
+ * bytes = 0); bytes a multiple of 16, 0 <= bytes <= SMCSD_STREAM_READ_MAX_BYTES; otherwise
+ * SMCSD_EINVAL before any launch.  One launch (none for bytes = 0).
+ */
+#define SMCSD_STREAM_READ_MAX_BYTES (1LL << 40)
+int smcsd_stream_read(const void *p, int64_t bytes, uint32_t *xor_out, void *stream);
 
 #ifdef __cplusplus
 }

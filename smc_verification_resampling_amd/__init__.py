@@ -35,7 +35,8 @@ KV_CHECK_NAMES = ("refcount != table references", "table id out of range",
 
 EXPORTED = ("smcsd_version", "smcsd_status_string", "smcsd_workspace_bytes", "smcsd_verify",
             "smcsd_verify_static", "smcsd_draft_sample", "smcsd_resample", "smcsd_kv_reassign",
-            "smcsd_resample_kv_reassign", "smcsd_step", "smcsd_kv_check", "smcsd_philox4x32_10")
+            "smcsd_resample_kv_reassign", "smcsd_step", "smcsd_kv_check", "smcsd_philox4x32_10",
+            "smcsd_stream_read")
 
 _DT = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
 
@@ -86,6 +87,8 @@ def load_library(path: str = LIB_PATH):
     lib.smcsd_kv_check.restype = i32
     lib.smcsd_philox4x32_10.argtypes = [P, P, i32, P, P]
     lib.smcsd_philox4x32_10.restype = i32
+    lib.smcsd_stream_read.argtypes = [P, i64, P, P]
+    lib.smcsd_stream_read.restype = i32
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -384,3 +387,15 @@ def philox4x32_10(counters: torch.Tensor, keys: torch.Tensor, out: torch.Tensor,
                                   _dev(keys, "keys", torch.int32, 2 * n), n,
                                   _dev(out, "out", torch.int32, 4 * n), _stream(stream))
     _check(rc, "smcsd_philox4x32_10")
+
+
+def stream_read(buf: torch.Tensor, xor_out: torch.Tensor, stream=None):
+    """Reads every byte of the contiguous device tensor `buf` once (16-byte aligned, a
+    multiple of 16 bytes) and XORs its 32-bit words into xor_out[0] (int32, accumulated: zero
+    it first): the achievable HBM read rate that the LSE pass is compared with."""
+    if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous():
+        raise SmcsdError("buf must be a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    rc = _L().smcsd_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes,
+                                _dev(xor_out, "xor_out", torch.int32, 1), _stream(stream))
+    _check(rc, "smcsd_stream_read")

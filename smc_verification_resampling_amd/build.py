@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 BUILD = os.path.join(ROOT, "_build", "smcsd")
 LIB = os.path.join(HERE, "libsmcsd.so")
-SOURCES = ["capi.hip", "verify.hip", "resample.hip", "kv.hip", "kvcheck.hip"]
+SOURCES = ["capi.hip", "verify.hip", "resample.hip", "kv.hip", "kvcheck.hip", "streamread.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -39,7 +39,7 @@ def _compile(src: str) -> str:
 def build(verbose: bool = False) -> str:
     """Compile every source for gfx950 and link libsmcsd.so (always rebuilds)."""
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(5, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs

@@ -51,6 +51,9 @@ int main(void) {
   /* the KV check: slots beyond M_cap; a workspace too small */
   CHECK(smcsd_kv_check(ip, 4, 8, 9, ip, ip, ip, 100, ip, ip, p, 1 << 20, NULL) == SMCSD_EINVAL);
   CHECK(smcsd_kv_check(ip, 4, 8, 3, ip, ip, ip, 100, ip, ip, p, 16, NULL) == SMCSD_EWORKSPACE);
+  /* the read-rate aid: a size that is not a multiple of 16; a pointer not 16-byte aligned */
+  CHECK(smcsd_stream_read(p, 24, (uint32_t *)p, NULL) == SMCSD_EINVAL);
+  CHECK(smcsd_stream_read((char *)p + 8, 32, (uint32_t *)p, NULL) == SMCSD_EINVAL);
   /* empty batches are no-ops that succeed without touching anything */
   CHECK(smcsd_resample(fp, 0, 4, 0.5f, 0, 0, ip, fp, ip, ip, NULL) == SMCSD_OK);
 

@@ -45,7 +45,7 @@ def test_gfx950_code_object_present(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.smcsd_version() == 6
+    assert lib.smcsd_version() == 7
     assert sm.status_string(0) == "ok"
     assert "workspace" in sm.status_string(-4)
     assert "pool" in sm.status_string(sm.ST_NOSPACE)
@@ -226,6 +226,16 @@ def test_kv_check_host_validation(lib):
     assert rc(wsb=799) == -4                          # two counters of 4 bytes per block
     assert rc(ws=ctypes.c_void_p(0x1010)) == -4       # not 256-byte aligned
     assert rc(ws=None) == -4
+
+
+def test_stream_read_host_validation(lib):
+    p, out = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000)
+    f = lib.smcsd_stream_read
+    assert f(p, -16, out, None) == -1                             # negative size
+    assert f(p, 24, out, None) == -1                              # not a multiple of 16
+    assert f(ctypes.c_void_p(0x1008), 32, out, None) == -1        # not 16-byte aligned
+    assert f(None, 32, out, None) == -1 and f(p, 32, None, None) == -1
+    assert f(p, (1 << 40) + 16, out, None) == -1                  # beyond the limit
 
 
 def test_header_is_c99_and_a_c_client_links(lib, tmp_path):
