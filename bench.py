@@ -45,7 +45,7 @@ VERIFY_TRAFFIC = {
         "smc_verification_resampling_amd/csrc/device.hpp":
             "2522278716f37d21a7304625ff4722f81d617ddcbba29605d41050dbafd80786",
         "smc_verification_resampling_amd/csrc/internal.hpp":
-            "c1df9ac52d4d346b56e1092cd1ecd845b5763068679591040034332b09b7f00c",
+            "1495395d34926e9467773decac26e006b2edf60ffc9dec391a279e939d4e627d",
     },
 }
 
@@ -464,15 +464,17 @@ def sps_timing(cfg, sets, steps):
 
 def read_ceiling(nbytes, reps=50):
     """The achievable HBM read rate of this GPU: smcsd_stream_read (the LSE pass's 16-byte
-    nontemporal loads, nothing else) over a buffer of the verify call's byte count, several
-    times the 256 MB last-level cache, `reps` back-to-back calls between one event pair."""
+    nontemporal loads, nothing else) over a buffer of random bits of the verify call's byte
+    count, several times the 256 MB last-level cache, `reps` back-to-back calls between
+    one event pair."""
     import torch
 
     import smc_verification_resampling_amd as sm
 
     n = (int(nbytes) + 15) // 16 * 16
-    buf = torch.empty(n, dtype=torch.uint8, device="cuda")    # contents do not matter
-    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    buf = torch.empty(n // 4, dtype=torch.int32, device="cuda")
+    buf.random_()                                   # random bits, as incompressible as logits
+    out = torch.empty(-(-n // sm.STREAM_READ_TILE_BYTES), dtype=torch.int32, device="cuda")
     for _ in range(3):
         sm.stream_read(buf, out)
     torch.cuda.synchronize()

@@ -377,15 +377,17 @@ int smcsd_philox4x32_10(const uint32_t *counters, const uint32_t *keys, int n, u
  * bound by memory bandwidth: SMC explainers, problem statement), so its speed of light is
  * the rate at which this GPU streams reads from HBM.  This call reads each 16-byte word of
  * [p, p + bytes) once, with the LSE pass's load instruction (16-byte nontemporal buffer
- * loads) and in contiguous 128 KiB tiles, and XORs all the 32-bit words read into
- * *xor_out (one device uint32, accumulated: the caller zeroes it first; bytes = 0 leaves it
- * unchanged); bytes divided by the time of the call is the achievable read rate that the
- * LSE pass's rate is compared with.  p: device memory, 16-byte aligned (may be NULL when
- * bytes = 0); bytes a multiple of 16, 0 <= bytes <= SMCSD_STREAM_READ_MAX_BYTES; otherwise
- * SMCSD_EINVAL before any launch.  One launch (none for bytes = 0).
+ * loads), one workgroup per contiguous tile of SMCSD_STREAM_READ_TILE_BYTES, and writes
+ * tile_xor[b] = the XOR of the 32-bit words of tile b (bytes [b*T, min(bytes, (b+1)*T)),
+ * T the tile size), for b < ceil(bytes / T): a device uint32 array, overwritten.  bytes
+ * divided by the time of the call is the achievable read rate that the LSE pass's rate is
+ * compared with.  p: device memory, 16-byte aligned; bytes a multiple of 16,
+ * 0 <= bytes <= SMCSD_STREAM_READ_MAX_BYTES (bytes = 0: nothing is read or written, and p
+ * and tile_xor may be NULL); otherwise SMCSD_EINVAL before any launch.  One launch.
  */
+#define SMCSD_STREAM_READ_TILE_BYTES 131072
 #define SMCSD_STREAM_READ_MAX_BYTES (1LL << 40)
-int smcsd_stream_read(const void *p, int64_t bytes, uint32_t *xor_out, void *stream);
+int smcsd_stream_read(const void *p, int64_t bytes, uint32_t *tile_xor, void *stream);
 
 #ifdef __cplusplus
 }

@@ -29,6 +29,7 @@ ST_DEGENERATE_WEIGHTS = 8
 ST_BAD_INPUT = 16
 ST_KV_INCONSISTENT = 32
 KV_CHECK_KINDS = 5
+STREAM_READ_TILE_BYTES = 131072
 KV_CHECK_NAMES = ("refcount != table references", "table id out of range",
                   "free-stack entry out of range or repeated", "referenced block on the free stack",
                   "unreferenced block not on the free stack")
@@ -389,13 +390,15 @@ def philox4x32_10(counters: torch.Tensor, keys: torch.Tensor, out: torch.Tensor,
     _check(rc, "smcsd_philox4x32_10")
 
 
-def stream_read(buf: torch.Tensor, xor_out: torch.Tensor, stream=None):
+def stream_read(buf: torch.Tensor, tile_xor: torch.Tensor, stream=None):
     """Reads every byte of the contiguous device tensor `buf` once (16-byte aligned, a
-    multiple of 16 bytes) and XORs its 32-bit words into xor_out[0] (int32, accumulated: zero
-    it first): the achievable HBM read rate that the LSE pass is compared with."""
+    multiple of 16 bytes) and writes the XOR of each STREAM_READ_TILE_BYTES tile's 32-bit
+    words to tile_xor (int32, one word per tile): the achievable HBM read rate that the LSE
+    pass is compared with."""
     if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous():
         raise SmcsdError("buf must be a contiguous device tensor")
     nbytes = buf.numel() * buf.element_size()
+    ntiles = -(-nbytes // STREAM_READ_TILE_BYTES)
     rc = _L().smcsd_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes,
-                                _dev(xor_out, "xor_out", torch.int32, 1), _stream(stream))
+                                _dev(tile_xor, "tile_xor", torch.int32, ntiles), _stream(stream))
     _check(rc, "smcsd_stream_read")

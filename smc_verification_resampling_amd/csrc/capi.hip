@@ -380,11 +380,11 @@ int smcsd_kv_check(const int32_t *block_tables, int64_t S, int M_cap, int slots,
                                 as_stream(stream)));
 }
 
-int smcsd_stream_read(const void *p, int64_t bytes, uint32_t *xor_out, void *stream) {
-  if (bytes < 0 || bytes > SMCSD_STREAM_READ_MAX_BYTES || (bytes & 15) || !xor_out)
-    return SMCSD_EINVAL;
-  if (bytes > 0 && (!p || !aligned(p, 16))) return SMCSD_EINVAL;
-  return hip_rc(launch_stream_read(p, bytes, xor_out, as_stream(stream)));
+int smcsd_stream_read(const void *p, int64_t bytes, uint32_t *tile_xor, void *stream) {
+  if (bytes < 0 || bytes > SMCSD_STREAM_READ_MAX_BYTES || (bytes & 15)) return SMCSD_EINVAL;
+  if (bytes == 0) return SMCSD_OK;
+  if (!p || !aligned(p, 16) || !tile_xor) return SMCSD_EINVAL;
+  return hip_rc(launch_stream_read(p, bytes, tile_xor, as_stream(stream)));
 }
 
 int smcsd_philox4x32_10(const uint32_t *counters, const uint32_t *keys, int n, uint32_t *out,

@@ -141,7 +141,7 @@ hipError_t launch_kv_check(const int32_t *T, int64_t S, int M_cap, int slots,
                            int64_t P, int32_t *viol, int32_t *status, char *ws,
                            hipStream_t stream);
 
-hipError_t launch_stream_read(const void *p, int64_t bytes, uint32_t *xor_out,
+hipError_t launch_stream_read(const void *p, int64_t bytes, uint32_t *tile_xor,
                               hipStream_t stream);
 hipError_t launch_philox(const uint32_t *ctr, const uint32_t *key, int n, uint32_t *out,
                          hipStream_t stream);

@@ -236,6 +236,7 @@ def test_stream_read_host_validation(lib):
     assert f(ctypes.c_void_p(0x1008), 32, out, None) == -1        # not 16-byte aligned
     assert f(None, 32, out, None) == -1 and f(p, 32, None, None) == -1
     assert f(p, (1 << 40) + 16, out, None) == -1                  # beyond the limit
+    assert f(None, 0, None, None) == 0                            # empty: nothing to do
 
 
 def test_header_is_c99_and_a_c_client_links(lib, tmp_path):
