@@ -38,14 +38,14 @@ EVENT_EVERY = 16
 # only for the kernel sources they were taken on: any change to them reports null.
 VERIFY_TRAFFIC = {
     "workload": "c3_batched",
-    "bytes": 1186492478,
+    "bytes": 1186532669,
     "sources": {
         "smc_verification_resampling_amd/csrc/verify.hip":
-            "cdf823e44c1c3eda882d360f4efd5a6b310c432fa95607be852c5619deffe37c",
+            "f1adaca6c2cc01ab6c785d27a901f66334b3149c5995741afa3e2cb3771ef810",
         "smc_verification_resampling_amd/csrc/device.hpp":
             "2522278716f37d21a7304625ff4722f81d617ddcbba29605d41050dbafd80786",
         "smc_verification_resampling_amd/csrc/internal.hpp":
-            "1495395d34926e9467773decac26e006b2edf60ffc9dec391a279e939d4e627d",
+            "4a016fe91d6021388ca83e215e05941ba82ad8452bdd54161636b5fa25b3d46b",
     },
 }
 

@@ -168,10 +168,9 @@ __device__ __forceinline__ int slab_of(int64_t v, int64_t a0) {
 }
 
 // Tiles: the rows other than the bonus row (nb_per_seq per sequence: the K target rows,
-// then the K draft rows unless the draft's log q is given) in big tiles of
-// big_tile_elems(element bytes, RACE), and the bonus rows in chunks of chunk_elems (one
-// unrolled step
-// each), in the order described at the tile loop.  Tile indices below ntiles_big are big
+// then the K draft rows unless the draft's log q is given) in chunks_big big tiles each,
+// of big_elems elements (the last takes the rest), and the bonus rows in chunks of
+// chunk_elems (one unrolled step each), in the order described at the tile loop.  Tile indices below ntiles_big are big
 // tiles, the rest bonus tiles.  Partials of row (g, slot) start at
 // part[(g * R + slot) * chunks].
 // RACE: the bonus tiles write the winner of their race to race[g * chunks + ch] as
@@ -184,8 +183,8 @@ constexpr int kTailBonusTiles = 640;
 template <int DT, bool RACE>
 __global__ __launch_bounds__(kStreamBlock) void k_lse_partials(RowMap rm, int nseq, int V,
                                                                 int chunk_elems, int chunks,
-                                                                int chunks_big, int nb_per_seq,
-                                                                float c,
+                                                                int chunks_big, int big_elems,
+                                                                int nb_per_seq, float c,
                                                                 float2 *__restrict__ part,
                                                                 float *__restrict__ sub,
                                                                 int64_t ntiles, uint64_t seed,
@@ -239,7 +238,7 @@ __global__ __launch_bounds__(kStreamBlock) void k_lse_partials(RowMap rm, int ns
       g = (int)(r / nb_per_seq);
       const int j = (int)(r - (int64_t)g * nb_per_seq);
       slot = j < K ? j : j + 1;
-      ce = big_tile_elems(E::kBytes, RACE);
+      ce = big_elems;
     }
     const char *row = rm.row(g, slot);
     const int64_t e0 = (int64_t)ch * ce;
@@ -1353,7 +1352,11 @@ static hipError_t launch_verify_t(const VerifyArgs &a) {
   float2 *part = reinterpret_cast<float2 *>(a.ws + w.part);
   float *sub = reinterpret_cast<float *>(a.ws + w.sub);
   int2 *race = reinterpret_cast<int2 *>(a.ws + w.race);
+  // a row's big tiles share it equally (whole 16-byte vectors each; the last takes the
+  // rest, never nothing: the rounding adds under chunks_big * 8 elements, far below a
+  // tile), rather than full tiles and a short remainder
   const int chunks_big = (int)ceil_div(a.V, big_tile_elems(esz, a.mode == SMCSD_MODE_SMC_RACE));
+  const int big_elems = (int)(ceil_div(ceil_div(a.V, chunks_big), 16 / esz) * (16 / esz));
   const int nb_per_seq = a.logq_in ? K : 2 * K;
   const int64_t ntiles = (int64_t)a.nseq * (chunks + (int64_t)nb_per_seq * chunks_big);
   const unsigned grid = grid_blocks(ntiles, kStreamBlock);
@@ -1367,11 +1370,11 @@ static hipError_t launch_verify_t(const VerifyArgs &a) {
     const bool rc = a.mode == SMCSD_MODE_SMC_RACE;
     if (rc)
       hipLaunchKernelGGL((k_lse_partials<DT, true>), dim3(grid), dim3(kStreamBlock), 0, a.stream, rm,
-                         a.nseq, a.V, ce, chunks, chunks_big, nb_per_seq, a.c, part, sub, ntiles,
+                         a.nseq, a.V, ce, chunks, chunks_big, big_elems, nb_per_seq, a.c, part, sub, ntiles,
                          a.seed, a.step, race, nullptr);
     else
       hipLaunchKernelGGL((k_lse_partials<DT, false>), dim3(grid), dim3(kStreamBlock), pad, a.stream,
-                         rm, a.nseq, a.V, ce, chunks, chunks_big, nb_per_seq, a.c, part, sub, ntiles,
+                         rm, a.nseq, a.V, ce, chunks, chunks_big, big_elems, nb_per_seq, a.c, part, sub, ntiles,
                          a.seed, a.step, race, nullptr);
     // one workgroup per sequence; the looping form only where the grid cap leaves fewer
     // workgroups than sequences (its loop costs registers: 157 VGPRs against 59)
@@ -1391,7 +1394,7 @@ static hipError_t launch_verify_t(const VerifyArgs &a) {
   int32_t *arrivals = reinterpret_cast<int32_t *>(a.ws + w.arrivals);
   if (!a.lse_in)
     hipLaunchKernelGGL((k_lse_partials<DT, false>), dim3(grid), dim3(kStreamBlock), pad, a.stream, rm,
-                       a.nseq, a.V, ce, chunks, chunks_big, nb_per_seq, a.c, part, sub, ntiles,
+                       a.nseq, a.V, ce, chunks, chunks_big, big_elems, nb_per_seq, a.c, part, sub, ntiles,
                        a.seed, a.step, race, arrivals);
   else
     hipLaunchKernelGGL(k_zero_i32, dim3(grid_blocks(a.nseq, kStreamBlock)), dim3(kStreamBlock), 0,
