@@ -41,7 +41,7 @@ VERIFY_TRAFFIC = {
     "bytes": 1186532669,
     "sources": {
         "smc_verification_resampling_amd/csrc/verify.hip":
-            "f1adaca6c2cc01ab6c785d27a901f66334b3149c5995741afa3e2cb3771ef810",
+            "f178c984e6971ff23dbc4956798a49d8e62defaf23035800f2fca273b250cfa4",
         "smc_verification_resampling_amd/csrc/device.hpp":
             "2522278716f37d21a7304625ff4722f81d617ddcbba29605d41050dbafd80786",
         "smc_verification_resampling_amd/csrc/internal.hpp":

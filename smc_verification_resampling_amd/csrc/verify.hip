@@ -367,19 +367,25 @@ struct RowNorm {
 // p points to LDS or to global memory; a caller passes a pointer of one known kind (not a
 // select between the two), so the loads are LDS or global loads, not flat ones, and the
 // unrolled loops keep several in flight.
-__device__ __forceinline__ RowNorm row_norm(const float2 *p, int chunks, float c) {
+// The row's reference Mc (its max times c) and S = sum of its chunk terms; returns the max.
+__device__ __forceinline__ float row_mc_s(const float2 *p, int chunks, float c, float &Mc,
+                                          double &S) {
   float M = kNegInf;
 #pragma unroll 8
   for (int i = 0; i < chunks; ++i) M = fmaxf(M, p[i].x);
-  RowNorm r{};
-  r.Mc = M == kNegInf ? 0.0f : __fmul_rn(M, c);
-  double S = 0.0;
+  Mc = M == kNegInf ? 0.0f : __fmul_rn(M, c);
+  S = 0.0;
 #pragma unroll 8
-  for (int i = 0; i < chunks; ++i) S += chunk_term(p[i], c, r.Mc);
-  r.S = S;
-  r.L2 = (double)r.Mc + log2(S);
+  for (int i = 0; i < chunks; ++i) S += chunk_term(p[i], c, Mc);
+  return M;
+}
+
+__device__ __forceinline__ RowNorm row_norm(const float2 *p, int chunks, float c) {
+  RowNorm r{};
+  const float M = row_mc_s(p, chunks, c, r.Mc, r.S);
+  r.L2 = (double)r.Mc + log2(r.S);
   r.flags = 0;
-  if (isnan(S) || isinf(S)) r.flags |= SMCSD_ST_NAN_INPUT;
+  if (isnan(r.S) || isinf(r.S)) r.flags |= SMCSD_ST_NAN_INPUT;
   else if (M == kNegInf) r.flags |= SMCSD_ST_EMPTY_ROW;
   return r;
 }
@@ -573,8 +579,7 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
   using E = Elt<DT>;
   const int K = rm.K, R = 2 * K + 1;
   const int tid = threadIdx.x;
-  __shared__ float sMc[2 * kMaxK + 1];
-  __shared__ double sS[2 * kMaxK + 1], sL2[2 * kMaxK + 1];
+  __shared__ double sL2[2 * kMaxK + 1];
   __shared__ double sLogp[kMaxK + 1], sLogq[kMaxK + 1];
   __shared__ int32_t sTok[kMaxK + 1];
   __shared__ float2 sPart[kMaxPartLds];
@@ -640,36 +645,26 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
   __syncthreads();
   const float xv = xv_lane ? xv_raw : 0.0f;
 
-  // row normalisers: chunk pairs combined in fp64;
-  // the draft rows only when their log q is not given
-  if (tid < (logq_in ? K + 1 : R)) {
-    const int n = tid == K ? chunks : chunks_big;
-    const RowNorm rn = part_in_lds ? row_norm(sPart + tid * chunks, n, c)
-                                   : row_norm(gpart + tid * chunks, n, c);
-    sMc[tid] = rn.Mc;
-    sS[tid] = rn.S;
-    sL2[tid] = rn.L2;
+  // The bonus draw needs only the bonus row's Mc_K and S_K: every wave forms them itself
+  // (the same loop, so the same bits; a wave's instructions cost the same whatever its
+  // active lanes), so they are uniform with no barrier, and wave 0 goes straight on to the
+  // slab pick while waves 1 and 2 combine every row's chunk pairs in fp64, log2 included
+  // (the draft rows only when their log q is not given), for the log-probabilities.
+  float McK;
+  double SK;
+  if (part_in_lds) row_mc_s(sPart + K * chunks, chunks, c, McK, SK);
+  else row_mc_s(gpart + K * chunks, chunks, c, McK, SK);
+  if (tid >= kWave && tid < kWave + (logq_in ? K + 1 : R)) {
+    const int r = tid - kWave;
+    const int n = r == K ? chunks : chunks_big;
+    const RowNorm rn = part_in_lds ? row_norm(sPart + r * chunks, n, c)
+                                   : row_norm(gpart + r * chunks, n, c);
+    sL2[r] = rn.L2;
     if (rn.flags) atomicOr(&sFlags, rn.flags);
-  }
-  __syncthreads();
-
-  if (tid < 2 * K) {
-    const int k = tid < K ? tid : tid - K;
-    double lp = __builtin_nan("");
-    if (x < 0 || x >= V) atomicOr(&sFlags, SMCSD_ST_BAD_INPUT);
-    else if (logq_in && tid >= K) lp = (double)lq_given;
-    else lp = ((double)xv * (double)c - sL2[slot]) * kLn2;
-    if (tid < K) {
-      sLogp[k] = lp;
-      sTok[k] = x;
-    } else {
-      sLogq[k] = lp;
-    }
   }
 
   // Bonus: u = U(seed; g, step, BONUS); first v whose running sum of 2^(x*c - Mc_K)
   // exceeds u * S_K (the unnormalised CDF; the common factor 2^Mc_K cancels).
-  const double SK = sS[K];
   const double u = philox_uniform(seed, (uint32_t)g, step, bonus_tag, 0);
   const double target = u * SK;
   const char *brow = rm.row(g, K);
@@ -700,7 +695,6 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
       // leaves no crossing, the last slab with a positive term.
       const int lane = tid;
       const int nsl = chunks * kSlabs;
-      const float McK = sMc[K];
       double base = 0.0, base_last = 0.0;
       int sel = -1, last = -1;
       // sb / pk both in LDS or both in global memory (never a select between the two)
@@ -750,10 +744,25 @@ __global__ __launch_bounds__(kSmcFinalBlock) void k_smc_finalize(
     __syncthreads();
     const int64_t lo = sLo, hi = sHi;
     if (hi > lo) {
-      const ExpRow<DT> fn{brow, c, sMc[K],
+      const ExpRow<DT> fn{brow, c, McK,
                           (reinterpret_cast<uintptr_t>(brow + lo * E::kBytes) & 15) == 0};
       bonus = chunk_inverse_cdf<kSmcFinalBlock, kSmcUnits>(lo, hi, sBase, target, fn, sScan, sMisc,
                                                            &sPickLogit);
+    }
+  }
+
+  __syncthreads();  // every row's normaliser is in
+  if (tid < 2 * K) {
+    const int k = tid < K ? tid : tid - K;
+    double lp = __builtin_nan("");
+    if (x < 0 || x >= V) atomicOr(&sFlags, SMCSD_ST_BAD_INPUT);
+    else if (logq_in && tid >= K) lp = (double)lq_given;
+    else lp = ((double)xv * (double)c - sL2[slot]) * kLn2;
+    if (tid < K) {
+      sLogp[k] = lp;
+      sTok[k] = x;
+    } else {
+      sLogq[k] = lp;
     }
   }
 
