@@ -187,6 +187,15 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
       }
     }
   }
+  // with the one-wave resample, waves 1-3 stage the first tile in LDS as soon as their
+  // loads are in, while wave 0 resamples (the resample does not touch the tile)
+  if (split && pid >= 0) {
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) {
+      const int e = pid + k * pthr;
+      if (e < nw0) tile[e] = pre[k];
+    }
+  }
   int res;
   if (fr.lw) {
     __shared__ ResampleLds sResL;
@@ -231,7 +240,7 @@ __global__ __launch_bounds__(kKvBlock) void k_kv(
     const int nseg = (N + kSeg - 1) / kSeg;
     for (int s0 = c_begin; s0 < c_end; s0 += W) {
       const int w = min(W, c_end - s0), nw = N * w;
-      if (s0 == c_begin) {
+      if (s0 == c_begin && !split) {
         // the first tile is W columns wide (W = min(c_end - c_begin, kKvTileInts / N) = w),
         // so entry e = j * w + s sits at tile[e]: no division on this path
 #pragma unroll
