@@ -25,13 +25,16 @@ constexpr int kChunkElemsMin = kChunkElemsF32;  // workspace is sized for the sm
 // (B = 16, N = 64, K = 8: 719 against 712 steps/s for 64 KiB).  Race mode keeps 128 KiB
 // for both dtypes: its ALU-heavy bonus tiles, spread among the big tiles, ran 7 % slower
 // among 64 KiB bf16 tiles (4,541 against 4,894 steps/s at the B = 32 shape).
-// These are upper bounds: a row's ceil(V / bound) big tiles share its V elements equally
-// (rounded up to whole 16-byte vectors).  A plain read of 8.93 GB in the fp32 rows of a
-// 128K vocabulary took 1,275-1,278 us in three 128 KiB tiles and a 117 KiB remainder per
-// row and 1,247-1,250 us in four equal tiles (aligned 128 KiB tiles: 1,241-1,244 us); in
-// the LSE pass equal tiles gave 5,014-5,023 against 4,984-4,994 steps/s at B = 32,
-// N = 16, K = 4, V = 128256 bf16, and 738.6-740.9 against 737.0-739.6 at B = 16, N = 64,
-// K = 8 fp32 (two boxes, two reps each).
+// In the plain verify (target and draft rows read, inverse-CDF bonus or SpS) these are
+// upper bounds: a row's ceil(V / bound) big tiles share its V elements equally (rounded
+// up to whole 16-byte vectors).  A plain read of 8.93 GB in the fp32 rows of a 128K
+// vocabulary took 1,275-1,278 us in three 128 KiB tiles and a 117 KiB remainder per row
+// and 1,247-1,250 us in four equal tiles (aligned 128 KiB tiles: 1,241-1,244 us); in the
+// LSE pass equal tiles gave 5,014-5,023 against 4,984-4,994 steps/s at B = 32, N = 16,
+// K = 4, V = 128256 bf16, and 738.6-740.9 against 737.0-739.6 at B = 16, N = 64, K = 8
+// fp32 (two boxes, two reps each).  Race mode and the verify with the draft's log q given
+// keep full tiles and a remainder: equal tiles cost them 0.9 % and 1.1 % at the B = 32
+// shape (4,917 against 4,962 and 7,848 against 7,933 steps/s, same box).
 constexpr int kBigTileElems = 32768;
 constexpr int kRaceBigTileBytes = 128 * 1024;
 constexpr int big_tile_elems(int elt_bytes, bool race) {

@@ -1361,11 +1361,15 @@ static hipError_t launch_verify_t(const VerifyArgs &a) {
   float2 *part = reinterpret_cast<float2 *>(a.ws + w.part);
   float *sub = reinterpret_cast<float *>(a.ws + w.sub);
   int2 *race = reinterpret_cast<int2 *>(a.ws + w.race);
-  // a row's big tiles share it equally (whole 16-byte vectors each; the last takes the
-  // rest, never nothing: the rounding adds under chunks_big * 8 elements, far below a
-  // tile), rather than full tiles and a short remainder
+  // In the plain verify (inverse-CDF bonus or SpS, target and draft rows read) a row's big
+  // tiles share it equally (whole 16-byte vectors each; the last takes the rest, never
+  // nothing: the rounding adds under chunks_big * 8 elements, far below a tile); in race
+  // mode and with the draft's log q given they are full tiles and a shorter remainder.
+  // Chosen by measurement per mode (no model of why it differs).
   const int chunks_big = (int)ceil_div(a.V, big_tile_elems(esz, a.mode == SMCSD_MODE_SMC_RACE));
-  const int big_elems = (int)(ceil_div(ceil_div(a.V, chunks_big), 16 / esz) * (16 / esz));
+  const bool balance = a.mode != SMCSD_MODE_SMC_RACE && !a.logq_in;
+  const int big_elems = balance ? (int)(ceil_div(ceil_div(a.V, chunks_big), 16 / esz) * (16 / esz))
+                                : big_tile_elems(esz, a.mode == SMCSD_MODE_SMC_RACE);
   const int nb_per_seq = a.logq_in ? K : 2 * K;
   const int64_t ntiles = (int64_t)a.nseq * (chunks + (int64_t)nb_per_seq * chunks_big);
   const unsigned grid = grid_blocks(ntiles, kStreamBlock);
