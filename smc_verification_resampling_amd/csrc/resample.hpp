@@ -34,13 +34,8 @@ __device__ __forceinline__ int resample_prompt_wave(float x_in, float *__restric
   const int lane = threadIdx.x % kWave;
   const bool act = lane < N;
   const float x = act ? x_in : kNegInf;
-  int bad = act && isnan(x);
-  float m = act && !isnan(x) ? x : kNegInf;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    m = fmaxf(m, __shfl_xor(m, d, kWave));
-    bad |= __shfl_xor(bad, d, kWave);
-  }
+  const bool bad = __ballot(act && isnan(x)) != 0ull;
+  const float m = wave_max_f32(act && !isnan(x) ? x : kNegInf);  // in every lane
   if (bad || !isfinite(m)) {
     if (act) {
       if (out) ab[lane] = lane;
@@ -72,6 +67,7 @@ __device__ __forceinline__ int resample_prompt_wave(float x_in, float *__restric
   }
   const double cum = wave_inclusive_scan(w);  // inclusive prefix over the lanes
   const double tot = __shfl(cum, N - 1, kWave);
+  const double cn = cum / tot;  // C_j, each lane's divided once (the search compares these)
   const double u0 = philox_uniform(seed, (uint32_t)b, step, 2u, 0);
   const double pos = ((double)lane + u0) / (double)N;
   // number of j with C_j <= pos (C non-decreasing) = first j with C_j > pos
@@ -79,8 +75,8 @@ __device__ __forceinline__ int resample_prompt_wave(float x_in, float *__restric
 #pragma unroll
   for (int stp = kWave / 2; stp >= 1; stp >>= 1) {
     const int cand = idx + stp - 1;
-    const double cv = __shfl(cum, min(cand, N - 1), kWave);
-    if (cand < N && !(cv / tot > pos)) idx += stp;
+    const double cv = __shfl(cn, min(cand, N - 1), kWave);
+    if (cand < N && !(cv > pos)) idx += stp;
   }
   if (act) {
     const int a = idx < N ? idx : N - 1;
@@ -192,14 +188,19 @@ __device__ __forceinline__ int resample_prompt_block(float *__restrict__ lwb, in
     L.w[j] = run;
   }
   __syncthreads();
-  const double tot = L.w[N - 1];  // C_{N-1}
+  const double tot = L.w[N - 1];  // the prefix's last entry
+  __syncthreads();                // read by every thread before its owner rescales it
+  // C_j = prefix_j / tot, each entry divided once by the thread that wrote it (the search
+  // compares these)
+  for (int j = j0; j < j1; ++j) L.w[j] = L.w[j] / tot;
+  __syncthreads();
   const double u0 = philox_uniform(seed, (uint32_t)b, step, 2u, 0);
   for (int i = tid; i < N; i += kResBlock) {
     const double pos = ((double)i + u0) / (double)N;
-    int lo = 0, hi = N;  // first j with w[j]/tot > pos, N if none
+    int lo = 0, hi = N;  // first j with C_j > pos, N if none
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
-      if (L.w[mid] / tot > pos) hi = mid;
+      if (L.w[mid] > pos) hi = mid;
       else lo = mid + 1;
     }
     const int a = lo < N ? lo : N - 1;
