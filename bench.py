@@ -43,7 +43,7 @@ VERIFY_TRAFFIC = {
     "bytes": 1186553475,
     "sources": {
         "smc_verification_resampling_amd/csrc/verify.hip":
-            "087fd7dbe996007d73398e24476751afe90ef943a379b08b07418702a05db159",
+            "b8001d90a3b8f29615b9f3940ba9837605be9cef89d69535d3c1f18d8835a71a",
         "smc_verification_resampling_amd/csrc/device.hpp":
             "2522278716f37d21a7304625ff4722f81d617ddcbba29605d41050dbafd80786",
         "smc_verification_resampling_amd/csrc/internal.hpp":

@@ -6,8 +6,9 @@
 // No MFMA: nothing here is a contraction.
 //
 // Kernels
-//   k_lse_partials   grid = tiles, 256 threads: 32768-entry big tiles for the non-bonus
-//                    rows and 32 KiB tiles for the bonus row (position K).  One streaming
+//   k_lse_partials   grid = tiles, 256 threads: big tiles of at most 32768 entries for the
+//                    non-bonus rows (a row's big tiles of equal size in the plain verify)
+//                    and 32 KiB tiles for the bonus row (position K).  One streaming
 //                    pass with 16-byte nontemporal loads; per lane an online (max, sum of
 //                    2^(x*c - max*c)); a workgroup reduction; one (max, sum) pair per tile.
 //                    Bonus tiles also write the sums of their 8 slabs (one slab = the 256
@@ -17,8 +18,9 @@
 //   k_smc_finalize   grid = sequences.  Combines the chunk pairs in fp64 into each row's
 //                    normaliser, gathers the draft-token log-probabilities, draws the bonus
 //                    token by inverse CDF (selects the slab from the slab sums of all the
-//                    row's chunks in one scan, re-reads only that slab) and updates the
-//                    log-weight.
+//                    row's chunks in one scan, re-reads only that slab; the draw starts from
+//                    the bonus row's own normaliser, not waiting for the other rows') and
+//                    updates the log-weight.
 //   race mode        the bonus row's tiles also run an exponential race (exponential-races
 //                    summary page, key design) over their elements and keep the winner;
 //                    the finalize takes the best of the tiles' winners and reads only the
