@@ -78,8 +78,10 @@ def test_ragged_and_misaligned_rows(dtype, V, pad):
     """Rows whose length or stride is not a multiple of the 16-byte vector (so rows start
     misaligned), single-element rows, and tiles split one element past a boundary; rows
     made only of whole load groups (8 vectors per lane over the workgroup) and rows one
-    element short of or past them; rows of exactly one or two big tiles (32768 elements)
-    and one element short of or past them."""
+    element short of or past them; rows at one or two times the big-tile bound (32768
+    elements) and one element short of or past it, where a row's big tiles share it
+    equally (32769 elements: two tiles of 16392 and 16377, whole vectors each; with a
+    padded stride every tile also starts misaligned)."""
     K, S = 3, 5
     rs = V + pad
     g = torch.Generator(device="cuda").manual_seed(V * 7 + pad)
